@@ -1,0 +1,248 @@
+"""gated_deltanet_causal_amd -- the Gated DeltaNet sublayer hot path on MI355X.
+
+A thin ctypes binding over ``libgdn.so`` (hand-written HIP for gfx950, C ABI in
+``include/gdn.h``).  Every step of the path runs in the library's kernels;
+this module only marshals torch device tensors (device memory and the current
+stream) into the C calls and raises :class:`GDNError` on a failed status.
+There is no CPU or PyTorch fallback: without the built library, importing the
+binding's entry points raises.
+
+Build the library with ``python -m gated_deltanet_causal_amd.build``.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(6)
+GDN_F32, GDN_BF16 = 0, 1
+
+# Every symbol include/gdn.h declares.
+EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_conv1d_prefill",
+           "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
+           "gdn_gated_rmsnorm", "gdn_decode_step")
+
+
+class GDNError(RuntimeError):
+    def __init__(self, call: str, status: int, message: str):
+        super().__init__(f"{call}: {message} (status {status})")
+        self.status = status
+
+
+class GDNConfig(ctypes.Structure):
+    """Mirror of gdn_config_t."""
+    _fields_ = [
+        ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
+        ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
+        ("conv_width", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+        ("conv_act", ctypes.c_int32), ("decay_per_key_channel", ctypes.c_int32),
+        ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("q_scale", ctypes.c_float),
+    ]
+
+    @property
+    def conv_channels(self) -> int:
+        return 2 * self.num_k_heads * self.head_k_dim + self.num_v_heads * self.head_v_dim
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libgdn.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libgdn.so not built at {path}; run python -m gated_deltanet_causal_amd.build")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp = ctypes.POINTER(GDNConfig)
+    sig = {
+        "gdn_abi_version": ([], ctypes.c_int),
+        "gdn_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "gdn_config_default": ([cfgp], ctypes.c_int),
+        "gdn_conv1d_prefill": ([cfgp, ctypes.c_int, vp, i64, vp, vp, vp, vp, i64, vp, vp, i32, i32, vp], ctypes.c_int),
+        "gdn_conv1d_step": ([cfgp, ctypes.c_int, vp, i64, vp, vp, vp, i64, i32, vp], ctypes.c_int),
+        "gdn_chunk_prefill_workspace_size": ([cfgp, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "gdn_chunk_prefill": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp,
+                               i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_gated_rmsnorm": ([cfgp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, vp], ctypes.c_int),
+        "gdn_decode_step": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp],
+                            ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(call: str, status: int) -> None:
+    if status != GDN_OK:
+        msg = load_library().gdn_status_string(status).decode()
+        raise GDNError(call, status, msg)
+
+
+def config(**overrides) -> GDNConfig:
+    """gdn_config_default() with fields overridden by keyword."""
+    cfg = GDNConfig()
+    _check("gdn_config_default", load_library().gdn_config_default(ctypes.byref(cfg)))
+    for k, v in overrides.items():
+        if not hasattr(cfg, k):
+            raise AttributeError(k)
+        setattr(cfg, k, v)
+    return cfg
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == GDN_BF16 else torch.float32
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must be on the GPU")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _row_stride(t: torch.Tensor) -> int:
+    """Elements between rows of a [rows, ...] tensor whose inner dims are contiguous."""
+    inner = 1
+    for s, n in zip(reversed(t.stride()[1:]), reversed(t.shape[1:])):
+        if s != inner:
+            raise ValueError("inner dimensions must be contiguous")
+        inner *= n
+    return t.stride(0) if t.dim() > 1 else inner
+
+
+def _cu_host(cu: torch.Tensor, cu_host) -> ctypes.Array:
+    vals = cu.cpu().tolist() if cu_host is None else list(cu_host)
+    return (ctypes.c_int32 * len(vals))(*vals)
+
+
+def conv1d_prefill(x: torch.Tensor, w: torch.Tensor, cu: torch.Tensor, *, cu_host=None,
+                   conv_state_in: Optional[torch.Tensor] = None,
+                   conv_state_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   cfg: Optional[GDNConfig] = None) -> torch.Tensor:
+    """x [T, Cc] (row stride free) -> y [T, Cc] in x's dtype; see gdn_conv1d_prefill."""
+    cfg = cfg or config()
+    T = x.shape[0]
+    N = cu.numel() - 1
+    if y is None:
+        y = torch.empty((T, cfg.conv_channels), dtype=x.dtype, device=x.device)
+    hc = _cu_host(cu, cu_host)
+    _check("gdn_conv1d_prefill", load_library().gdn_conv1d_prefill(
+        ctypes.byref(cfg), _dtype(x), _ptr(x), _row_stride(x), _ptr(w), _ptr(conv_state_in),
+        _ptr(conv_state_out), _ptr(y), _row_stride(y), _ptr(cu), hc, N, T, _stream()))
+    return y
+
+
+def conv1d_step(x: torch.Tensor, w: torch.Tensor, conv_state: torch.Tensor, *,
+                y: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None) -> torch.Tensor:
+    """x [B, Cc], conv_state [B, 3, Cc] (updated in place) -> y [B, Cc]."""
+    cfg = cfg or config()
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty((B, cfg.conv_channels), dtype=x.dtype, device=x.device)
+    _check("gdn_conv1d_step", load_library().gdn_conv1d_step(
+        ctypes.byref(cfg), _dtype(x), _ptr(x), _row_stride(x), _ptr(w), _ptr(conv_state), _ptr(y),
+        _row_stride(y), B, _stream()))
+    return y
+
+
+def chunk_prefill_workspace_size(N: int, T: int, cfg: Optional[GDNConfig] = None) -> int:
+    cfg = cfg or config()
+    out = ctypes.c_size_t(0)
+    _check("gdn_chunk_prefill_workspace_size",
+           load_library().gdn_chunk_prefill_workspace_size(ctypes.byref(cfg), N, T, ctypes.byref(out)))
+    return out.value
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                  beta: torch.Tensor, cu: torch.Tensor, *, cu_host=None,
+                  initial_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  final_state: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+    """Chunk-wise gated delta rule; q, k [T, Hk*dk] (or [T, Hk, dk]), v [T, Hv*dv], views with
+    a shared row stride allowed.  Returns (out [T, Hv, dv], final_state [N, Hv, dv, dk])."""
+    cfg = cfg or config()
+    T = q.shape[0]
+    N = cu.numel() - 1
+    qs, ks = _row_stride(q), _row_stride(k)
+    if qs != ks:
+        raise ValueError("q and k must share a row stride")
+    odt = out_dtype or q.dtype
+    if out is None:
+        out = torch.empty((T, cfg.num_v_heads, cfg.head_v_dim), dtype=odt, device=q.device)
+    if final_state is None:
+        final_state = torch.empty((N, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim),
+                                  dtype=torch.float32, device=q.device)
+    need = chunk_prefill_workspace_size(N, T, cfg)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    hc = _cu_host(cu, cu_host)
+    _check("gdn_chunk_prefill", load_library().gdn_chunk_prefill(
+        ctypes.byref(cfg), _dtype(q), _dtype(out), _ptr(q), _ptr(k), qs, _ptr(v), _row_stride(v),
+        _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out, final_state
+
+
+def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,
+                  out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                  cfg: Optional[GDNConfig] = None) -> torch.Tensor:
+    """o, z [rows, Hv, dv] -> sigmoid-gated RMSNorm output."""
+    cfg = cfg or config()
+    rows = o.shape[0]
+    if out is None:
+        out = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=o.device)
+    for t in (o, z, out):
+        if not t.is_contiguous():
+            raise ValueError("gated_rmsnorm tensors must be contiguous")
+    _check("gdn_gated_rmsnorm", load_library().gdn_gated_rmsnorm(
+        ctypes.byref(cfg), _dtype(o), _dtype(z), _dtype(out), _ptr(o), _ptr(z), _ptr(w), _ptr(out),
+        rows, _stream()))
+    return out
+
+
+def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: torch.Tensor,
+                beta: torch.Tensor, z: torch.Tensor, norm_w: torch.Tensor, state: torch.Tensor, *,
+                out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+                cfg: Optional[GDNConfig] = None) -> torch.Tensor:
+    """One fused decode step; conv_state and state are updated in place.  Returns out [B, Hv, dv]."""
+    cfg = cfg or config()
+    B = x.shape[0]
+    if out is None:
+        out = torch.empty((B, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype, device=x.device)
+    for t in (x, conv_state, g, beta, z, state, out):
+        if not t.is_contiguous():
+            raise ValueError("decode_step tensors must be contiguous")
+    _check("gdn_decode_step", load_library().gdn_decode_step(
+        ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(g),
+        _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, _stream()))
+    return out
+
+
+def default_q_scale(cfg: GDNConfig) -> float:
+    return cfg.q_scale if cfg.q_scale > 0 else 1.0 / math.sqrt(cfg.head_k_dim)

@@ -1,0 +1,214 @@
+// gdn_api.hip -- the C ABI of libgdn.so: argument checks on the host, then
+// the launchers.  Nothing here allocates, synchronises or reads environment
+// variables; a failed check returns before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "gdn.h"
+#include "gdn_launch.h"
+
+namespace {
+
+using gdn::Dims;
+
+gdn_status_t resolve(const gdn_config_t* cfg, Dims* d) {
+  if (!cfg) return GDN_ERR_INVALID_ARG;
+  if (cfg->num_k_heads <= 0 || cfg->num_v_heads <= 0) return GDN_ERR_INVALID_ARG;
+  if (cfg->num_v_heads % cfg->num_k_heads != 0) return GDN_ERR_INVALID_ARG;
+  if (cfg->head_k_dim != 128 || cfg->head_v_dim != 128) return GDN_ERR_UNSUPPORTED;
+  if (cfg->conv_width != 4 || cfg->chunk_size != 64) return GDN_ERR_UNSUPPORTED;
+  if (cfg->conv_act != 0 && cfg->conv_act != 1) return GDN_ERR_INVALID_ARG;
+  if (cfg->decay_per_key_channel != 0 && cfg->decay_per_key_channel != 1) return GDN_ERR_INVALID_ARG;
+  if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return GDN_ERR_INVALID_ARG;
+  d->hk = cfg->num_k_heads;
+  d->hv = cfg->num_v_heads;
+  d->dk = cfg->head_k_dim;
+  d->dv = cfg->head_v_dim;
+  d->cc = 2 * d->hk * d->dk + d->hv * d->dv;
+  d->act = cfg->conv_act;
+  d->per_channel = cfg->decay_per_key_channel;
+  d->l2_eps = cfg->l2_eps;
+  d->rms_eps = cfg->rms_eps;
+  d->q_scale = cfg->q_scale > 0.0f ? cfg->q_scale : 1.0f / sqrtf((float)cfg->head_k_dim);
+  return GDN_OK;
+}
+
+bool valid_dtype(gdn_dtype_t t) { return t == GDN_F32 || t == GDN_BF16; }
+size_t dsize(gdn_dtype_t t) { return t == GDN_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a+na) and [b, b+nb) overlap.
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return na && nb && pa < pb + nb && pb < pa + na;
+}
+
+gdn_status_t check_seqlens(const int32_t* cu_host, int32_t n, int32_t t) {
+  if (!cu_host || n < 0 || t < 0) return GDN_ERR_INVALID_ARG;
+  if (cu_host[0] != 0 || cu_host[n] != t) return GDN_ERR_SEQLENS;
+  for (int32_t i = 0; i < n; ++i)
+    if (cu_host[i + 1] < cu_host[i]) return GDN_ERR_SEQLENS;
+  return GDN_OK;
+}
+
+gdn_status_t hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_abi_version(void) { return GDN_ABI_VERSION; }
+
+const char* gdn_status_string(gdn_status_t s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument";
+    case GDN_ERR_UNSUPPORTED: return "unsupported geometry or dtype";
+    case GDN_ERR_SEQLENS: return "invalid cu_seqlens";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+gdn_status_t gdn_config_default(gdn_config_t* cfg) {
+  if (!cfg) return GDN_ERR_INVALID_ARG;
+  cfg->num_k_heads = 16;
+  cfg->num_v_heads = 48;
+  cfg->head_k_dim = 128;
+  cfg->head_v_dim = 128;
+  cfg->conv_width = 4;
+  cfg->chunk_size = 64;
+  cfg->conv_act = 1;
+  cfg->decay_per_key_channel = 0;
+  cfg->l2_eps = 1e-6f;
+  cfg->rms_eps = 1e-6f;
+  cfg->q_scale = 1.0f / sqrtf(128.0f);
+  return GDN_OK;
+}
+
+gdn_status_t gdn_conv1d_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, const void* x,
+                                int64_t x_stride, const float* w, const void* conv_state_in,
+                                void* conv_state_out, void* y, int64_t y_stride,
+                                const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                int32_t T, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+  if (N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
+  if (!cu_dev || !w) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !y)) return GDN_ERR_INVALID_ARG;
+  if (x_stride < d.cc || y_stride < d.cc || x_stride % 8 || y_stride % 8) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x) || !aligned16(y) || !aligned16(w))) return GDN_ERR_INVALID_ARG;
+  st = check_seqlens(cu_host, N, T);
+  if (st != GDN_OK) return st;
+  const size_t es = dsize(dtype);
+  if (T > 0 && overlaps(x, ((size_t)(T - 1) * x_stride + d.cc) * es, y, ((size_t)(T - 1) * y_stride + d.cc) * es))
+    return GDN_ERR_INVALID_ARG;
+  if (conv_state_in && !aligned16(conv_state_in)) return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_conv1d_prefill(d, dtype == GDN_BF16, x, x_stride, w, conv_state_in,
+                                               conv_state_out, y, y_stride, cu_dev, N, T,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_conv1d_step(const gdn_config_t* cfg, gdn_dtype_t dtype, const void* x,
+                             int64_t x_stride, const float* w, void* conv_state, void* y,
+                             int64_t y_stride, int32_t B, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+  if (B < 0) return GDN_ERR_INVALID_ARG;
+  if (B > 0 && (!x || !w || !conv_state || !y)) return GDN_ERR_INVALID_ARG;
+  if (x_stride < d.cc || y_stride < d.cc) return GDN_ERR_INVALID_ARG;
+  if (B > 0 && !aligned16(w)) return GDN_ERR_INVALID_ARG;
+  if (B > 65535) return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_conv1d_step(d, dtype == GDN_BF16, x, x_stride, w, conv_state, y,
+                                            y_stride, B, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_chunk_prefill_workspace_size(const gdn_config_t* cfg, int32_t N, int32_t T,
+                                              size_t* bytes) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!bytes || N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
+  *bytes = gdn::chunk_workspace_bytes(d, N, T);
+  return GDN_OK;
+}
+
+gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                               gdn_dtype_t out_dtype, const void* q, const void* k,
+                               int64_t qk_stride, const void* v, int64_t v_stride,
+                               const float* g, const float* beta, const float* initial_state,
+                               const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                               int32_t T, void* out, float* final_state, void* ws,
+                               size_t ws_bytes, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
+  if (d.per_channel) return GDN_ERR_UNSUPPORTED;
+  if (N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
+  if (!cu_dev) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID_ARG;
+  const int64_t vec = in_dtype == GDN_BF16 ? 8 : 4;   // elements per 16-byte load
+  if (qk_stride < (int64_t)d.hk * d.dk || v_stride < (int64_t)d.hv * d.dv) return GDN_ERR_INVALID_ARG;
+  if (qk_stride % vec || v_stride % vec) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return GDN_ERR_INVALID_ARG;
+  if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
+    return GDN_ERR_INVALID_ARG;
+  st = check_seqlens(cu_host, N, T);
+  if (st != GDN_OK) return st;
+  if ((size_t)N * d.hk > (size_t)1 << 24) return GDN_ERR_INVALID_ARG;
+  const size_t need = gdn::chunk_workspace_bytes(d, N, T);
+  if (N > 0 && (!ws || ws_bytes < need || !aligned16(ws))) return GDN_ERR_WORKSPACE;
+  const size_t out_bytes = (size_t)T * d.hv * d.dv * dsize(out_dtype);
+  const size_t state_bytes = (size_t)N * d.hv * d.dv * d.dk * sizeof(float);
+  if (overlaps(out, out_bytes, ws, need) || overlaps(final_state, state_bytes, ws, need))
+    return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_chunk_prefill(d, in_dtype == GDN_BF16, out_dtype == GDN_BF16, q, k,
+                                              qk_stride, v, v_stride, g, beta, initial_state,
+                                              cu_dev, cu_host, N, T, out, final_state, ws,
+                                              ws_bytes, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn_dtype_t z_dtype,
+                               gdn_dtype_t out_dtype, const void* o, const void* z,
+                               const float* w, void* out, int64_t rows, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(o_dtype) || !valid_dtype(z_dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
+  if (rows < 0) return GDN_ERR_INVALID_ARG;
+  if (rows > 0 && (!o || !z || !w || !out)) return GDN_ERR_INVALID_ARG;
+  if (out != o && rows > 0) {
+    const size_t n = (size_t)rows * d.hv * d.dv;
+    if (overlaps(out, n * dsize(out_dtype), o, n * dsize(o_dtype))) return GDN_ERR_INVALID_ARG;
+  }
+  if (out == o && o_dtype != out_dtype) return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_gated_rmsnorm(d, o_dtype == GDN_BF16, z_dtype == GDN_BF16,
+                                              out_dtype == GDN_BF16, o, z, w, out, rows,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                             const void* x, const float* conv_w, void* conv_state, const float* g,
+                             const float* beta, const void* z, const float* norm_w, float* state,
+                             void* out, int32_t B, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
+  if (B < 0 || B > 65535 * 64) return GDN_ERR_INVALID_ARG;
+  if (B > 0 && (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out))
+    return GDN_ERR_INVALID_ARG;
+  if (B > 0 && (!aligned16(conv_w) || !aligned16(state) || (d.per_channel && !aligned16(g))))
+    return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_decode_step(d, dtype == GDN_BF16, out_dtype == GDN_BF16, x, conv_w,
+                                            conv_state, g, beta, z, norm_w, state, out, B,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

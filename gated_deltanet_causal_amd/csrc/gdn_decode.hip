@@ -1,0 +1,204 @@
+// gdn_decode.hip -- one fused GDN decode step for B sequences: conv step,
+// L2 / q scale, the gated delta rule for the single token, and the sigmoid
+// gated RMSNorm, with the conv state and the fp32 recurrent state updated in
+// place.
+//
+// Follows the Qwen3.8 kernel TDD ledger (dense kernel map: scalar GDN
+// recurrence with fused output gate), the Qwen3SsmLayer field notes on the
+// fused conv + recurrence + norm decode kernels and their state traffic (two
+// reads and one write of the state cut to one read and one write), and the
+// GLM-5.3 ledger's KDA decode slice (fp32 [value,key] state, decay by
+// exp(g), beta-scaled delta, separate q output scale 1/sqrt(dk)).
+//
+// Per value head h with state S [dv][dk] and per-column decay a_j = exp(g)
+// (or exp(g_j) per key channel), the token gives, in one pass over S:
+//     Sd  = S diag(a)                       (decayed state, kept in registers)
+//     p   = Sd khat,  r = Sd qtil           (two row sums per row of S)
+//     u   = beta (v - p)
+//     S'  = Sd + u khat^T                   (written back)
+//     o   = S' qtil = r + u (khat . qtil)
+// so S is read once and written once.
+//
+// Work split: one workgroup per (sequence, key head).  It owns that key head's
+// q/k conv channels and the conv channels of its Hv/Hk value heads, so every
+// conv-state element has exactly one writer and the in-place update is
+// race-free.  The 64 KiB state of a head is spread over 256 threads as 16 rows
+// x one float4 each; a wavefront loads two full 512-byte rows per instruction.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kD = 128;                 // head_k_dim == head_v_dim
+constexpr int kRowsPerThread = 16;      // 128 rows / 8 row groups
+constexpr int kRedPitch = 33;           // padded pitch of the row-sum exchange
+
+template <typename T>
+__device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_w, T* cs_row,
+                                              int c, int cc, int act) {
+  T* p = cs_row + c;
+  const float s0 = ld(p), s1 = ld(p + cc), s2 = ld(p + 2 * cc);
+  const float xv = ld(x_row + c);
+  const f32x4_t w = *reinterpret_cast<const f32x4_t*>(conv_w + (int64_t)c * 4);
+  float y = w[0] * s0;
+  y = fmaf(w[1], s1, y);
+  y = fmaf(w[2], s2, y);
+  y = fmaf(w[3], xv, y);
+  st(p, s1);
+  st(p + cc, s2);
+  st(p + 2 * cc, xv);
+  return act ? y * sigmoidf_(y) : y;
+}
+
+template <typename T, typename To, bool kPerChannel>
+__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
+    const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
+    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
+    const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
+    int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
+  const int b = blockIdx.x;
+  const int kh = blockIdx.y;
+  const int ratio = hv / hk;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int cg = tid % 32;          // column group: columns 4cg .. 4cg+3
+  const int rg = tid / 32;          // row group: rows rg + 8m
+
+  __shared__ float s_q[kD], s_k[kD], s_v[kD], s_u[kD];
+  __shared__ float s_red[2][kD][kRedPitch];
+  __shared__ float s_scal[8];
+
+  const T* x_row = x + (int64_t)b * cc;
+  T* cs_row = conv_state + (int64_t)b * 3 * cc;
+
+  // --- q / k conv channels of this key head, then L2 norms ----------------
+  {
+    const int c = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
+    const float y = conv_channel(x_row, conv_w, cs_row, c, cc, act);
+    if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
+  }
+  __syncthreads();
+  if (wave < 2) {
+    const float* src = wave == 0 ? s_q : s_k;
+    const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
+    const float ss = wave_sum(a0 * a0 + a1 * a1);
+    if (lane == 0) s_scal[wave] = 1.0f / sqrtf(ss + l2_eps);
+  }
+  __syncthreads();
+  if (tid < kD) s_q[tid] *= s_scal[0] * q_scale;
+  else s_k[tid - kD] *= s_scal[1];
+  __syncthreads();
+  if (wave == 0) {
+    const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]);
+    if (lane == 0) s_scal[2] = kq;
+  }
+  // this thread's key / query columns
+  float kcol[4], qcol[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e]; qcol[e] = s_q[4 * cg + e]; }
+
+  for (int hh = 0; hh < ratio; ++hh) {
+    const int h = kh * ratio + hh;
+    float* S = state + ((int64_t)b * hv + h) * kD * kD;
+    // issue the state loads first; the v conv below overlaps their latency
+    f32x4_t sreg[kRowsPerThread];
+#pragma unroll
+    for (int m = 0; m < kRowsPerThread; ++m)
+      sreg[m] = *reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg);
+
+    if (tid < kD) s_v[tid] = conv_channel(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + tid, cc, act);
+    float a[4];
+    if constexpr (kPerChannel) {
+      const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)b * hv + h) * kD + 4 * cg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+    } else {
+      const float av = __expf(g[(int64_t)b * hv + h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = av;
+    }
+
+    // decay, then the two row sums over this thread's four columns
+#pragma unroll
+    for (int m = 0; m < kRowsPerThread; ++m) {
+      float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sreg[m][e] *= a[e];
+        pk = fmaf(sreg[m][e], kcol[e], pk);
+        pq = fmaf(sreg[m][e], qcol[e], pq);
+      }
+      s_red[0][rg + 8 * m][cg] = pk;
+      s_red[1][rg + 8 * m][cg] = pq;
+    }
+    __syncthreads();
+
+    // rows: u = beta (v - p), o = r + u (khat . qtil), then the gated norm
+    if (tid < kD) {
+      float pk = 0.0f, pq = 0.0f;
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) { pk += s_red[0][tid][j]; pq += s_red[1][tid][j]; }
+      const float u = beta[(int64_t)b * hv + h] * (s_v[tid] - pk);
+      s_u[tid] = u;
+      const float o = fmaf(u, s_scal[2], pq);
+      const float ss = wave_sum(o * o);
+      if (lane == 0) s_scal[4 + wave] = ss;
+      // the two waves' sums meet below; keep o in a register meanwhile
+      s_v[tid] = o;
+    }
+    __syncthreads();
+    if (tid < kD) {
+      const float r = rsqrtf((s_scal[4] + s_scal[5]) * (1.0f / kD) + rms_eps);
+      const int64_t off = ((int64_t)b * hv + h) * kD + tid;
+      const float y = s_v[tid] * r * norm_w[tid] * sigmoidf_(ld(z + off));
+      st(out + off, y);
+    }
+
+    // write the updated state: S' = Sd + u khat^T
+#pragma unroll
+    for (int m = 0; m < kRowsPerThread; ++m) {
+      const float u = s_u[rg + 8 * m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+      *reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg) = sreg[m];
+    }
+    __syncthreads();  // s_red / s_u / s_v are reused by the next head
+  }
+}
+
+template <typename T, typename To>
+hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* conv_state,
+                       const float* g, const float* beta, const void* z, const float* norm_w,
+                       float* state, void* out, int b, hipStream_t s) {
+  dim3 grid(b, d.hk);
+  if (d.per_channel)
+    hipLaunchKernelGGL((decode_step_kernel<T, To, true>), grid, dim3(kDecThreads), 0, s,
+                       static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
+                       static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv,
+                       d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
+  else
+    hipLaunchKernelGGL((decode_step_kernel<T, To, false>), grid, dim3(kDecThreads), 0, s,
+                       static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
+                       static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv,
+                       d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
+                              const float* conv_w, void* conv_state, const float* g,
+                              const float* beta, const void* z, const float* norm_w,
+                              float* state, void* out, int b, hipStream_t s) {
+  if (b == 0) return hipSuccess;
+  if (bf16)
+    return out_bf16 ? decode_impl<uint16_t, uint16_t>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
+                    : decode_impl<uint16_t, float>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
+  return out_bf16 ? decode_impl<float, uint16_t>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
+                  : decode_impl<float, float>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
+}
+
+}  // namespace gdn

@@ -1,0 +1,93 @@
+// gdn_device.h -- device helpers for the gfx950 GDN kernels: bf16 storage
+// conversion, hi/lo splitting of fp32 operands, MFMA tile wrappers and
+// wavefront reductions.  Internal to libgdn.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Storage types.  bf16 values are carried as raw 16-bit patterns (uint16_t)
+// in memory; arithmetic is always fp32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest even (the hardware conversion of gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+
+template <typename T> struct Storage;
+template <> struct Storage<float> {
+  __device__ static __forceinline__ float load(const float* p) { return *p; }
+  __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Storage<uint16_t> {
+  __device__ static __forceinline__ float load(const uint16_t* p) { return bf16_bits_to_f32(*p); }
+  __device__ static __forceinline__ void store(uint16_t* p, float v) { *p = f32_to_bf16_bits(v); }
+};
+
+template <typename T> __device__ __forceinline__ float ld(const T* p) { return Storage<T>::load(p); }
+template <typename T> __device__ __forceinline__ void st(T* p, float v) { Storage<T>::store(p, v); }
+
+// ---------------------------------------------------------------------------
+// hi/lo split of an fp32 value into two bf16 values with hi + lo equal to x
+// up to 2^-17 relative: hi = rne(x), lo = rne(x - hi); x - hi is exact.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(x);
+  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 output tiles.  Accumulator layout (both instructions): lane l
+// holds C[4*(l/16) + r][l%16] in element r (r = 0..3).  Operand layout: lane l
+// holds A[l%16][k0 + E*(l/16) + e] and B[k0 + E*(l/16) + e][l%16], e < E, with
+// E = 8 (bf16, K = 32 per instruction) or E = 1 (fp32, K = 4).  Only the
+// pairing of A's and B's k slots matters for the product, and both operands
+// are always loaded with the same k mapping.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {  // 16-byte aligned
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ bf16x8_t load_bf16x8(const __bf16* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront reductions (64 lanes).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+}  // namespace gdn

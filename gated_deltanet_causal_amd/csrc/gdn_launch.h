@@ -1,0 +1,44 @@
+// gdn_launch.h -- internal launchers behind the C ABI.  Each takes already
+// validated arguments and only enqueues kernels on the stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdn {
+
+// Geometry resolved from gdn_config_t.
+struct Dims {
+  int hk, hv, dk, dv;
+  int cc;           // conv channels 2*hk*dk + hv*dv
+  int act;          // conv activation: 0 none, 1 SiLU
+  int per_channel;  // decay per key channel
+  float l2_eps, rms_eps, q_scale;
+};
+
+hipError_t launch_conv1d_prefill(const Dims& d, bool bf16, const void* x, int64_t x_stride,
+                                 const float* w, const void* cs_in, void* cs_out, void* y,
+                                 int64_t y_stride, const int32_t* cu, int n, int t,
+                                 hipStream_t s);
+hipError_t launch_conv1d_step(const Dims& d, bool bf16, const void* x, int64_t x_stride,
+                              const float* w, void* cs, void* y, int64_t y_stride, int b,
+                              hipStream_t s);
+hipError_t launch_gated_rmsnorm(const Dims& d, bool o_bf16, bool z_bf16, bool out_bf16,
+                                const void* o, const void* z, const float* w, void* out,
+                                int64_t rows, hipStream_t s);
+hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
+                              const float* conv_w, void* conv_state, const float* g,
+                              const float* beta, const void* z, const float* norm_w,
+                              float* state, void* out, int b, hipStream_t s);
+
+// Chunk prefill.  Workspace layout is private to gdn_chunk.hip.
+size_t chunk_workspace_bytes(const Dims& d, int n, int t);
+hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
+                                const void* k, int64_t qk_stride, const void* v,
+                                int64_t v_stride, const float* g, const float* beta,
+                                const float* init_state, const int32_t* cu_dev,
+                                const int32_t* cu_host, int n, int t, void* out,
+                                float* final_state, void* ws, size_t ws_bytes, hipStream_t s);
+
+}  // namespace gdn

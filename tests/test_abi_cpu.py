@@ -1,0 +1,158 @@
+"""C-ABI contract of libgdn.so, checked on a host without a GPU.
+
+The library must load, export every symbol ``include/gdn.h`` declares, carry the
+header's ABI version and struct layout, and reject bad arguments with a status
+code before anything reaches the GPU (the GLM-5.3 ledger's host ABI contract
+test freezes buffer order, fp32 state and the separate q scale the same way).
+No call here launches a kernel.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_causal_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gdn.LIBRARY):
+        from gated_deltanet_causal_amd import build
+        build.build()
+    return gdn.load_library()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:gdn_status_t|int|const char\*)\s+(gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(gdn.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", gdn.LIBRARY], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(gdn_\w+)", out))
+    missing = set(header_functions()) - exported
+    assert not missing, f"not exported: {missing}"
+    for name in header_functions():
+        assert hasattr(lib, name)
+
+
+def test_abi_version_matches_header(lib):
+    m = re.search(r"#define\s+GDN_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert lib.gdn_abi_version() == int(m.group(1))
+
+
+def test_config_struct_layout_and_defaults(lib):
+    assert ctypes.sizeof(gdn.GDNConfig) == 11 * 4
+    cfg = gdn.config()
+    assert (cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim) == (16, 48, 128, 128)
+    assert (cfg.conv_width, cfg.chunk_size, cfg.conv_act, cfg.decay_per_key_channel) == (4, 64, 1, 0)
+    assert cfg.l2_eps == pytest.approx(1e-6) and cfg.rms_eps == pytest.approx(1e-6)
+    assert cfg.q_scale == pytest.approx(1 / 128 ** 0.5)
+    assert cfg.conv_channels == 10240
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.gdn_status_string(s)
+    assert lib.gdn_status_string(99) == b"unknown status"
+
+
+def _cfg(**kw):
+    return gdn.config(**kw)
+
+
+def test_config_validation(lib):
+    size = ctypes.c_size_t()
+    ok = lib.gdn_chunk_prefill_workspace_size(ctypes.byref(_cfg()), 1, 4096, ctypes.byref(size))
+    assert ok == gdn.GDN_OK and size.value > 0
+    for kw, want in [(dict(head_k_dim=64), gdn.GDN_ERR_UNSUPPORTED), (dict(conv_width=3), gdn.GDN_ERR_UNSUPPORTED),
+                     (dict(chunk_size=32), gdn.GDN_ERR_UNSUPPORTED), (dict(num_v_heads=47), gdn.GDN_ERR_INVALID_ARG),
+                     (dict(num_k_heads=0), gdn.GDN_ERR_INVALID_ARG), (dict(conv_act=2), gdn.GDN_ERR_INVALID_ARG),
+                     (dict(l2_eps=-1.0), gdn.GDN_ERR_INVALID_ARG)]:
+        got = lib.gdn_chunk_prefill_workspace_size(ctypes.byref(_cfg(**kw)), 1, 64, ctypes.byref(size))
+        assert got == want, kw
+    assert lib.gdn_chunk_prefill_workspace_size(None, 1, 64, ctypes.byref(size)) == gdn.GDN_ERR_INVALID_ARG
+
+
+def test_workspace_size_grows_with_tokens_and_sequences(lib):
+    def ws(n, t):
+        s = ctypes.c_size_t()
+        assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(_cfg()), n, t, ctypes.byref(s)) == 0
+        return s.value
+    assert ws(1, 4096) < ws(1, 8192) and ws(1, 4096) < ws(8, 4096)
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: validation fails first
+
+
+def test_seqlens_validation_before_launch(lib):
+    cfg = _cfg()
+    for cu, want in [([1, 5], gdn.GDN_ERR_SEQLENS), ([0, 4], gdn.GDN_ERR_SEQLENS), ([0, 6, 5], gdn.GDN_ERR_SEQLENS)]:
+        hc = (ctypes.c_int32 * len(cu))(*cu)
+        got = lib.gdn_conv1d_prefill(ctypes.byref(cfg), gdn.GDN_BF16, FAKE, 10240, FAKE, None, None,
+                                     ctypes.c_void_p(0x20000), 10240, FAKE, hc, len(cu) - 1, 5, None)
+        assert got == want, cu
+
+
+def test_conv_prefill_argument_checks(lib):
+    cfg = _cfg()
+    hc = (ctypes.c_int32 * 2)(0, 5)
+    call = lambda **kw: lib.gdn_conv1d_prefill(
+        ctypes.byref(cfg), kw.get("dtype", gdn.GDN_BF16), kw.get("x", FAKE), kw.get("xs", 10240), FAKE,
+        None, None, kw.get("y", ctypes.c_void_p(0x200000)), kw.get("ys", 10240), FAKE, hc, 1, 5, None)
+    assert call(x=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(xs=10000) == gdn.GDN_ERR_INVALID_ARG                 # stride < channels
+    assert call(xs=10244) == gdn.GDN_ERR_INVALID_ARG                 # stride not a multiple of 8
+    assert call(y=ctypes.c_void_p(0x10000 + 64)) == gdn.GDN_ERR_INVALID_ARG   # y overlaps x
+    assert call(dtype=7) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_chunk_prefill_argument_checks(lib):
+    cfg = _cfg()
+    hc = (ctypes.c_int32 * 2)(0, 64)
+
+    def call(**kw):
+        return lib.gdn_chunk_prefill(
+            ctypes.byref(kw.get("cfg", cfg)), gdn.GDN_BF16, gdn.GDN_F32, FAKE, FAKE, kw.get("qks", 10240),
+            FAKE, 10240, FAKE, FAKE, None, FAKE, hc, 1, 64, ctypes.c_void_p(0x4000000), None,
+            kw.get("ws", ctypes.c_void_p(0x8000000)), kw.get("wsb", 0), None)
+    assert call() == gdn.GDN_ERR_WORKSPACE                                  # zero-size workspace
+    assert call(ws=None, wsb=1 << 30) == gdn.GDN_ERR_WORKSPACE
+    assert call(qks=100) == gdn.GDN_ERR_INVALID_ARG
+    assert call(cfg=_cfg(decay_per_key_channel=1)) == gdn.GDN_ERR_UNSUPPORTED
+
+
+def test_decode_and_norm_argument_checks(lib):
+    cfg = _cfg()
+    got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, None, FAKE, 4, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                  # state missing
+    got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, -1, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG
+    got = lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE,
+                                FAKE, 4, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                  # in place across dtypes
+    got = lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_F32, FAKE, FAKE, FAKE,
+                                ctypes.c_void_p(0x10000 + 256), 4, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                  # partial overlap
+
+
+def test_empty_calls_launch_nothing(lib):
+    """Zero-sized work returns OK without touching the device."""
+    cfg = _cfg()
+    assert lib.gdn_conv1d_step(ctypes.byref(cfg), gdn.GDN_BF16, None, 10240, None, None, None, 10240, 0, None) == 0
+    assert lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, None, None, None, None, None,
+                               None, None, None, None, 0, None) == 0
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_F32, gdn.GDN_F32, None, None, None,
+                                 None, 0, None) == 0

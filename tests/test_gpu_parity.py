@@ -1,0 +1,370 @@
+"""Parity of every C-ABI call against the fp64 oracle, on the GPU.
+
+Inputs are seeded and synthetic (gdn_inputs), with the pages' geometry (16 key
+and 48 value heads of 128, conv 4, chunk 64) and the workloads' distributions.
+Small cases compare every element; the full-size workloads (4096-token
+prefill, 64-sequence decode, the ~32k-token varlen batch) run whole on the GPU
+and are compared on sampled heads that the oracle computes over every token.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_deltanet_causal_amd as gdn
+import gdn_inputs as gi
+import oracle
+from gpu_common import TOL_BF16, TOL_F32, check, dev, dev_i32, host, worst_ratio
+
+pytestmark = pytest.mark.gpu
+
+HK, HV, D = gi.HK, gi.HV, gi.DK
+
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def split_qkv(y, T, hk=HK, hv=HV):
+    q = y[:, : hk * D].reshape(T, hk, D)
+    k = y[:, hk * D: 2 * hk * D].reshape(T, hk, D)
+    v = y[:, 2 * hk * D:].reshape(T, hv, D)
+    return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# conv1d
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+@pytest.mark.parametrize("act", [1, 0], ids=["silu", "noact"])
+def test_conv1d_prefill_varlen(orc, bf16, act):
+    lengths = [5, 0, 70, 1, 2, 33, 16]
+    d = gi.gen_prefill(7, lengths, bf16=bf16, conv_state=True, init_state=False)
+    cfg = gdn.config(conv_act=act)
+    x, w, cs = dev(d["x"], bf16), dev(d["conv_w"]), dev(d["conv_state_in"], bf16)
+    cs_out = torch.empty_like(cs)
+    cu = dev_i32(d["cu"])
+    y = gdn.conv1d_prefill(x, w, cu, cu_host=d["cu"], conv_state_in=cs, conv_state_out=cs_out, cfg=cfg)
+    torch.cuda.synchronize()
+    y_ref, so_ref = orc.conv1d(d["x"], d["conv_w"], d["cu"], d["conv_state_in"], act)
+    if bf16:
+        y_ref = oracle.round_bf16(y_ref)
+    check(host(y), y_ref, TOL_BF16 if bf16 else TOL_F32, "conv y", stored_bf16=bf16)
+    assert np.array_equal(host(cs_out), so_ref), "conv state out must be exact"
+
+
+def test_conv1d_prefill_inplace_state_and_strided_views(orc):
+    """conv_state_out == conv_state_in, and x / y as column views of wider rows."""
+    lengths = [3, 40, 2]
+    d = gi.gen_prefill(8, lengths, bf16=True, conv_state=True, init_state=False)
+    T, C = d["x"].shape
+    wide = torch.zeros((T, C + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, 32:32 + C] = dev(d["x"], True)
+    x = wide[:, 32:32 + C]
+    ywide = torch.full((T, C + 16), float("nan"), dtype=torch.bfloat16, device="cuda")
+    y = ywide[:, 8:8 + C]
+    cs = dev(d["conv_state_in"], True)
+    cu = dev_i32(d["cu"])
+    gdn.conv1d_prefill(x, dev(d["conv_w"]), cu, cu_host=d["cu"], conv_state_in=cs, conv_state_out=cs, y=y)
+    torch.cuda.synchronize()
+    y_ref, so_ref = orc.conv1d(d["x"], d["conv_w"], d["cu"], d["conv_state_in"], 1)
+    check(host(y), oracle.round_bf16(y_ref), TOL_BF16, "conv y (views)", stored_bf16=True)
+    assert np.array_equal(host(cs), so_ref)
+    assert torch.isnan(ywide[:, :8].float()).all() and torch.isnan(ywide[:, 8 + C:].float()).all(), \
+        "writes outside the y view"
+
+
+def test_conv1d_prefill_full_length(orc):
+    d = gi.gen_prefill(1003, [4096], bf16=True, init_state=False)
+    y = gdn.conv1d_prefill(dev(d["x"], True), dev(d["conv_w"]), dev_i32(d["cu"]), cu_host=d["cu"])
+    torch.cuda.synchronize()
+    y_ref, _ = orc.conv1d(d["x"], d["conv_w"], d["cu"], None, 1)
+    check(host(y), oracle.round_bf16(y_ref), TOL_BF16, "conv y S=4096", stored_bf16=True)
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_conv1d_step_matches_oracle_and_prefill(orc, bf16):
+    B, T = 3, 6
+    d = gi.gen_prefill(9, [T] * B, bf16=bf16, conv_state=True, init_state=False)
+    C = d["x"].shape[1]
+    x = d["x"].reshape(B, T, C)
+    cs = dev(d["conv_state_in"], bf16)
+    w = dev(d["conv_w"])
+    state_ref = d["conv_state_in"].astype(np.float64)
+    for t in range(T):
+        y = gdn.conv1d_step(dev(x[:, t], bf16), w, cs)
+        torch.cuda.synchronize()
+        y_ref, state_ref = orc.conv1d_step(x[:, t], d["conv_w"], state_ref, 1)
+        if bf16:
+            y_ref = oracle.round_bf16(y_ref)
+        check(host(y), y_ref, TOL_BF16 if bf16 else TOL_F32, f"conv step t={t}", stored_bf16=bf16)
+        assert np.array_equal(host(cs), state_ref)
+    # the step's final state equals the prefill's state out over the same tokens
+    cs2 = dev(d["conv_state_in"], bf16)
+    gdn.conv1d_prefill(dev(d["x"], bf16), w, dev_i32(d["cu"]), cu_host=d["cu"], conv_state_in=cs2,
+                       conv_state_out=cs2)
+    torch.cuda.synchronize()
+    assert torch.equal(cs2, cs)
+
+
+# ---------------------------------------------------------------------------
+# gated RMSNorm
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("o_bf16,z_bf16,out_bf16", [(False, True, True), (False, True, False),
+                                                    (True, True, True), (False, False, False)])
+def test_gated_rmsnorm(orc, o_bf16, z_bf16, out_bf16):
+    rng = np.random.default_rng(31)
+    rows = 37
+    o = rng.standard_normal((rows, HV, D)).astype(np.float32) * 3
+    if o_bf16:
+        o = gi.bf16_round(o)
+    z = rng.standard_normal((rows, HV, D)).astype(np.float32)
+    if z_bf16:
+        z = gi.bf16_round(z)
+    w = (1 + 0.1 * rng.standard_normal(D)).astype(np.float32)
+    out = gdn.gated_rmsnorm(dev(o, o_bf16), dev(z, z_bf16), dev(w),
+                            out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.gated_rmsnorm(o, z, w, 1e-6)
+    tol = TOL_BF16 if (o_bf16 or out_bf16 or z_bf16) else TOL_F32
+    check(host(out), ref, tol, "gated norm", stored_bf16=out_bf16)
+
+
+def test_gated_rmsnorm_in_place(orc):
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((5, HV, D)).astype(np.float32)
+    z = gi.bf16_round(rng.standard_normal((5, HV, D)).astype(np.float32))
+    w = np.ones(D, dtype=np.float32)
+    ot = dev(o)
+    gdn.gated_rmsnorm(ot, dev(z, True), dev(w), out=ot)
+    torch.cuda.synchronize()
+    check(host(ot), orc.gated_rmsnorm(o, z, w, 1e-6), TOL_F32, "gated norm in place")
+
+
+# ---------------------------------------------------------------------------
+# fused decode step
+# ---------------------------------------------------------------------------
+
+def run_decode(d, bf16, out_bf16, cfg=None):
+    cs = dev(d["conv_state"], bf16)
+    st = dev(d["state"])
+    out = gdn.decode_step(dev(d["x"], bf16), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], bf16), dev(d["norm_w"]), st,
+                          out_dtype=torch.bfloat16 if out_bf16 else torch.float32, cfg=cfg)
+    torch.cuda.synchronize()
+    return out, cs, st
+
+
+def test_decode_step_batch64_bf16(orc):
+    """The decode workload at full size: 64 sequences, bf16 activations, fp32 state."""
+    d = gi.gen_decode(1002, 64)
+    out, cs, st = run_decode(d, True, True)
+    o_ref, cs_ref, st_ref = orc.decode_step(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"],
+                                            d["z"], d["norm_w"], d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    check(host(out), o_ref, TOL_BF16, "decode out", stored_bf16=True)
+    check(host(st), st_ref, TOL_BF16, "decode state")
+    assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
+
+
+@pytest.mark.parametrize("per_channel", [False, True], ids=["scalar", "per_channel"])
+def test_decode_step_f32_two_steps(orc, per_channel):
+    d = gi.gen_decode(21, 5, bf16=False, per_channel=per_channel)
+    cfg = gdn.config(decay_per_key_channel=int(per_channel))
+    cs, st = dev(d["conv_state"]), dev(d["state"])
+    cs_ref, st_ref = d["conv_state"], d["state"]
+    rng = np.random.default_rng(5)
+    for step in range(2):
+        x = d["x"] if step == 0 else rng.standard_normal(d["x"].shape).astype(np.float32)
+        out = gdn.decode_step(dev(x), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]), dev(d["z"]),
+                              dev(d["norm_w"]), st, out_dtype=torch.float32, cfg=cfg)
+        torch.cuda.synchronize()
+        o_ref, cs_ref, st_ref = orc.decode_step(x, d["conv_w"], cs_ref, d["g"], d["beta"], d["z"],
+                                                d["norm_w"], st_ref, Hk=HK, Hv=HV, dk=D, dv=D)
+        check(host(out), o_ref, TOL_F32, f"decode f32 out step {step}")
+        check(host(st), st_ref, TOL_F32, f"decode f32 state step {step}")
+        assert np.allclose(host(cs), cs_ref, rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# chunk prefill
+# ---------------------------------------------------------------------------
+
+def test_prefill_s80_fp32_pipeline(orc):
+    """80 tokens (crosses one chunk boundary), fp32, zero states: conv -> chunk -> norm at 1e-5."""
+    d = gi.gen_prefill(1001, [80], bf16=False, init_state=False)
+    T = 80
+    cu = dev_i32(d["cu"])
+    y = gdn.conv1d_prefill(dev(d["x"]), dev(d["conv_w"]), cu, cu_host=d["cu"])
+    q, k, v = y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:]
+    o, fs = gdn.chunk_prefill(q, k, v, dev(d["g"]), dev(d["beta"]), cu, cu_host=d["cu"],
+                              out_dtype=torch.float32)
+    out = gdn.gated_rmsnorm(o, dev(d["z"]), dev(d["norm_w"]))
+    torch.cuda.synchronize()
+    out_ref, o_ref, s_ref, _, y_ref = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"],
+                                                  d["norm_w"], Hk=HK, Hv=HV, dk=D, dv=D)
+    check(host(y), y_ref, TOL_F32, "S=80 conv")
+    # the chunk stage is checked on the library's own conv output (stage parity)
+    yq, yk, yv = split_qkv(host(y), T)
+    o_st, s_st = orc.delta_rule(yq, yk, yv, d["g"], d["beta"], d["cu"])
+    check(host(o), o_st, TOL_F32, "S=80 chunk out")
+    check(host(fs), s_st, TOL_F32, "S=80 final state")
+    check(host(out), out_ref, TOL_F32, "S=80 gated out (end to end)")
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129])
+def test_chunk_prefill_bf16_boundary_lengths(orc, T):
+    d = gi.gen_qkv(100 + T, [T])
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                              initial_state=dev(d["state_in"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"chunk out T={T}")
+    check(host(fs), s_ref, TOL_BF16, f"chunk state T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 64, 129])
+def test_chunk_prefill_fp32_boundary_lengths(orc, T):
+    d = gi.gen_qkv(200 + T, [T], bf16=False)
+    o, fs = gdn.chunk_prefill(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["g"]), dev(d["beta"]),
+                              dev_i32(d["cu"]), cu_host=d["cu"], initial_state=dev(d["state_in"]),
+                              out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_F32, f"fp32 chunk out T={T}")
+    check(host(fs), s_ref, TOL_F32, f"fp32 chunk state T={T}")
+
+
+def test_chunk_prefill_varlen_empty_and_inplace_state(orc):
+    """Packed sequences including empty ones; final_state written over initial_state;
+    bf16 output; a zero initial state for one call."""
+    lengths = [0, 65, 1, 0, 130, 64]
+    d = gi.gen_qkv(33, lengths)
+    st = dev(d["state_in"])
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"], initial_state=st,
+                              final_state=st, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "varlen out (bf16 stored)", stored_bf16=True)
+    check(host(st), s_ref, TOL_BF16, "varlen state in place")
+    assert np.array_equal(host(st)[0], d["state_in"][0]), "empty sequence keeps its state"
+    o2, fs2 = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                                dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o_ref2, s_ref2 = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], None)
+    check(host(o2), o_ref2, TOL_BF16, "varlen out, zero state")
+    check(host(fs2), s_ref2, TOL_BF16, "varlen state, zero state")
+
+
+def _sampled_heads(orc, d, kheads):
+    """Oracle over every token for the value heads of the given key heads."""
+    ratio = HV // HK
+    vheads = [kh * ratio + r for kh in kheads for r in range(ratio)]
+    q = d["q"][:, kheads]
+    k = d["k"][:, kheads]
+    v = d["v"][:, vheads]
+    s_in = None if d["state_in"] is None else d["state_in"][:, vheads]
+    o, s = orc.delta_rule(q, k, v, d["g"][:, vheads], d["beta"][:, vheads], d["cu"], s_in)
+    return vheads, o, s
+
+
+def test_chunk_prefill_s4096_full_size_sampled(orc):
+    """The 4096-token prefill workload (bf16, random initial state) run whole; heads of
+    key heads 0, 7 and 15 compared with the oracle over all tokens."""
+    d = gi.gen_qkv(1003, [4096])
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                              initial_state=dev(d["state_in"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vheads, o_ref, s_ref = _sampled_heads(orc, d, [0, 7, 15])
+    check(host(o)[:, vheads], o_ref, TOL_BF16, "S=4096 out (9 heads)")
+    check(host(fs)[:, vheads], s_ref, TOL_BF16, "S=4096 state (9 heads)")
+    assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
+
+
+def test_varlen_32k_full_size_sampled(orc):
+    """The varlen workload: 63, 64, 65 plus five lengths in [1, 8192] (~32k tokens), per-sequence
+    initial states; value heads of key head 5 compared over every token."""
+    lengths, seed = gi.varlen_lengths()
+    d = gi.gen_qkv(1004, lengths)
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                              initial_state=dev(d["state_in"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vheads, o_ref, s_ref = _sampled_heads(orc, d, [5])
+    check(host(o)[:, vheads], o_ref, TOL_BF16, f"varlen {lengths} out")
+    check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen state")
+
+
+# ---------------------------------------------------------------------------
+# composition and negative controls
+# ---------------------------------------------------------------------------
+
+def test_prefill_then_decode_equals_oracle(orc):
+    """Prefill T1 tokens on the GPU, then decode T2 tokens with the carried conv and
+    recurrent states: every output equals the oracle's prefill over T1 + T2."""
+    T1, T2 = 70, 3
+    d = gi.gen_prefill(41, [T1 + T2], bf16=False, init_state=True, conv_state=True)
+    out_ref, _, s_ref, cs_ref, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"],
+                                               d["norm_w"], Hk=HK, Hv=HV, dk=D, dv=D,
+                                               conv_state_in=d["conv_state_in"], state_in=d["state_in"])
+    cu1 = np.array([0, T1], dtype=np.int32)
+    cs = dev(d["conv_state_in"])
+    y = gdn.conv1d_prefill(dev(d["x"][:T1]), dev(d["conv_w"]), dev_i32(cu1), cu_host=cu1,
+                           conv_state_in=cs, conv_state_out=cs)
+    st = dev(d["state_in"])
+    o, _ = gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], dev(d["g"][:T1]),
+                             dev(d["beta"][:T1]), dev_i32(cu1), cu_host=cu1, initial_state=st, final_state=st,
+                             out_dtype=torch.float32)
+    out1 = gdn.gated_rmsnorm(o, dev(d["z"][:T1]), dev(d["norm_w"]))
+    outs = [host(out1)]
+    for t in range(T1, T1 + T2):
+        od = gdn.decode_step(dev(d["x"][t:t + 1]), dev(d["conv_w"]), cs, dev(d["g"][t:t + 1]),
+                             dev(d["beta"][t:t + 1]), dev(d["z"][t:t + 1]), dev(d["norm_w"]), st.view(1, HV, D, D),
+                             out_dtype=torch.float32)
+        outs.append(host(od))
+    torch.cuda.synchronize()
+    check(np.concatenate(outs), out_ref, TOL_F32, "prefill + decode vs prefill")
+    check(host(st), s_ref, TOL_F32, "carried state")
+    assert np.allclose(host(cs), cs_ref, rtol=0, atol=0)
+
+
+def test_negative_controls(orc, tmp_path):
+    """The golden PR's negative controls, planted in the oracle (CPU): a sigmoid->SiLU
+    gate, a skipped conv, and a dropped state carry must each put the GPU result past
+    the 2e-3 bound by at least 10x on its worst element."""
+    d = gi.gen_prefill(51, [128], bf16=True, init_state=True)
+    T = 128
+    cu = dev_i32(d["cu"])
+    y = gdn.conv1d_prefill(dev(d["x"], True), dev(d["conv_w"]), cu, cu_host=d["cu"])
+    o, _ = gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], dev(d["g"]),
+                             dev(d["beta"]), cu, cu_host=d["cu"], initial_state=dev(d["state_in"]),
+                             out_dtype=torch.float32)
+    out = host(gdn.gated_rmsnorm(o, dev(d["z"], True), dev(d["norm_w"]), out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    good, _, _, _, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                   Hk=HK, Hv=HV, dk=D, dv=D, state_in=d["state_in"], round_y_bf16=True)
+    check(out, good, TOL_BF16, "negative-control baseline")
+    # SiLU gate: a mutant oracle build
+    src = open(oracle.SOURCE).read().replace("w[i] * sigmoid(zrow[i])", "w[i] * zrow[i] * sigmoid(zrow[i])")
+    (tmp_path / "silu.c").write_text(src)
+    oracle.compile_oracle(str(tmp_path / "silu.c"), str(tmp_path / "libsilu.so"))
+    silu = oracle.Oracle(oracle.load(str(tmp_path / "libsilu.so")))
+    bad, _, _, _, _ = silu.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                   Hk=HK, Hv=HV, dk=D, dv=D, state_in=d["state_in"], round_y_bf16=True)
+    assert worst_ratio(out, bad, TOL_BF16) >= 10, "SiLU-gate control did not fail"
+    # skipped conv: the oracle fed the raw projections
+    xq, xk, xv = split_qkv(d["x"].astype(np.float64), T)
+    o_nc, _ = orc.delta_rule(xq, xk, xv, d["g"], d["beta"], d["cu"], d["state_in"])
+    bad = orc.gated_rmsnorm(o_nc, d["z"], d["norm_w"])
+    assert worst_ratio(out, bad, TOL_BF16) >= 10, "skipped-conv control did not fail"
+    # dropped carry: the second chunk restarted from zero state; the first chunk still matches
+    yq, yk, yv = split_qkv(oracle.round_bf16(orc.conv1d(d["x"], d["conv_w"], d["cu"], None, 1)[0]), T)
+    o_a, _ = orc.delta_rule(yq[:64], yk[:64], yv[:64], d["g"][:64], d["beta"][:64], [0, 64], d["state_in"])
+    o_b, _ = orc.delta_rule(yq[64:], yk[64:], yv[64:], d["g"][64:], d["beta"][64:], [0, 64], None)
+    bad = orc.gated_rmsnorm(np.concatenate([o_a, o_b]), d["z"], d["norm_w"])
+    assert worst_ratio(out[:64], bad[:64], TOL_BF16) <= 1.0, "dropped-carry control: head must match"
+    assert worst_ratio(out[64:], bad[64:], TOL_BF16) >= 10, "dropped-carry control did not fail"
