@@ -209,6 +209,209 @@ __device__ __forceinline__ void load_rows(typename Ops<F32>::E* dst, int pitch, 
   }
 }
 
+
+// Number of (row tile, k step) fragment slots of a lower-triangular 64x64
+// operand in lane layout: k steps up to the diagonal of each 16-row tile.
+template <bool F32> struct Tri;
+template <> struct Tri<false> {            // bf16: k step 32 -> 1,1,2,2 steps
+  static constexpr int kSlots = 6;
+  __device__ static constexpr int slot(int mt, int ks) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + ks; }
+};
+template <> struct Tri<true> {             // fp32: k step 4 -> 4,8,12,16 steps
+  static constexpr int kSlots = 40;
+  __device__ static constexpr int slot(int mt, int ks) { return 2 * mt * (mt + 1) + ks; }
+};
+
+// All of this lane's fragments of a triangular operand record (hi and lo).
+template <bool F32>
+__device__ __forceinline__ void load_tri_frags(const uint8_t* src, int lane, typename Ops<F32>::F* fh,
+                                               typename Ops<F32>::F* fl) {
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int ks = 0; ks * Ops<F32>::kKs <= 16 * mt + 15; ++ks) {
+      const int sl = Tri<F32>::slot(mt, ks);
+      if constexpr (F32) {
+        fh[sl] = reinterpret_cast<const float*>(src)[(mt * 16 + ks) * kWave + lane];
+      } else {
+        const int f = mt * 2 + ks;
+        fh[sl] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
+        fl[sl] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
+      }
+    }
+  }
+}
+
+// 64 x 32 value tile (rows past L zero) as fp32 into LDS, 16-byte loads.
+template <typename Tin>
+__device__ __forceinline__ void load_values(float* sV, int pitch, const Tin* src, int64_t stride, int L) {
+  constexpr int kPer = 16 / sizeof(Tin);
+  for (int p = threadIdx.x; p < kC * (kTile / kPer); p += kThreads) {
+    const int t = p / (kTile / kPer);
+    const int i = (p % (kTile / kPer)) * kPer;
+    float vals[kPer];
+    if constexpr (sizeof(Tin) == 2) {
+      u32x4_t u = {0u, 0u, 0u, 0u};
+      if (t < L) u = *reinterpret_cast<const u32x4_t*>(src + (int64_t)t * stride + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vals[2 * e] = __uint_as_float(u[e] << 16);
+        vals[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    } else {
+      f32x4_t u = {0.f, 0.f, 0.f, 0.f};
+      if (t < L) u = *reinterpret_cast<const f32x4_t*>(src + (int64_t)t * stride + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vals[e] = u[e];
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) sV[t * pitch + i + e] = vals[e];
+  }
+}
+
+
+// 16x16x16 fp32 product on fp32 MFMA: acc += X Y with X, Y in LDS (pitches px, py).
+__device__ __forceinline__ f32x4_t mm16_f32(const float* X, int px, const float* Y, int py, f32x4_t acc) {
+  const int l = threadIdx.x % kWave;
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+    acc = mfma_f32(X[(l & 15) * px + 4 * s4 + (l >> 4)], Y[(4 * s4 + (l >> 4)) * py + (l & 15)], acc);
+  return acc;
+}
+
+// Store a 16x16 accumulator tile to LDS (pitch p), scaled.
+__device__ __forceinline__ void st16(float* M, int p, f32x4_t acc, float scale) {
+  const int l = threadIdx.x % kWave;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) M[(4 * (l >> 4) + i) * p + (l & 15)] = scale * acc[i];
+}
+
+// T = (I + A)^-1 for the strictly lower 64x64 A in LDS (pitch kAP), written to
+// sT (same pitch; the strictly upper 16x16 blocks are left unwritten).  Blocked:
+// the four 16x16 diagonal blocks by forward substitution (one wave each, lane =
+// (column, quarter of the rows)), then the off-diagonal blocks level by level,
+//   T[b+1][b] = -D[b+1] A[b+1][b] D[b]
+//   T[b+2][b] = -D[b+2] (A[b+2][b] D[b] + A[b+2][b+1] T[b+1][b])
+//   T[3][0]   = -D[3] (A[3][0] D[0] + A[3][1] T[1][0] + A[3][2] T[2][0])
+// on exact-product fp32 MFMA.  Called by all threads of the block.
+template <int kAP>
+__device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, float* sM) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  {
+    const int b = wave, c = lane >> 2, part = lane & 3;
+    const float* Ab = sA + 16 * b * kAP + 16 * b;
+    float tc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) tc[m] = (4 * m + part == c) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        if (4 * m < r) {
+          const float a = Ab[r * kAP + 4 * m + part];
+          acc = fmaf(4 * m + part < r ? a : 0.0f, tc[m], acc);
+        }
+      }
+      acc = group_sum<4>(acc);
+      if (r > c && (r & 3) == part) tc[r >> 2] = -acc;
+    }
+    float* Tb = sT + 16 * b * kAP + 16 * b;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Tb[(4 * m + part) * kAP + c] = tc[m];
+  }
+  constexpr int kMP = 17;
+  auto blk = [](const float* base, int i, int j) { return base + 16 * i * kAP + 16 * j; };
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int lvl = 1; lvl < 4; ++lvl) {
+    __syncthreads();
+    const int b = wave;                      // block row b + lvl, column b
+    const bool on = b + lvl < 4;
+    if (on) {
+      f32x4_t m = zero;
+      m = mm16_f32(blk(sA, b + lvl, b), kAP, blk(sT, b, b), kAP, m);
+      for (int j = b + 1; j < b + lvl; ++j) m = mm16_f32(blk(sA, b + lvl, j), kAP, blk(sT, j, b), kAP, m);
+      st16(sM + b * 16 * kMP, kMP, m, 1.0f);
+    }
+    __syncthreads();
+    if (on) {
+      f32x4_t t = zero;
+      t = mm16_f32(blk(sT, b + lvl, b + lvl), kAP, sM + b * 16 * kMP, kMP, t);
+      st16(const_cast<float*>(blk(sT, b + lvl, b)), kAP, t, -1.0f);
+    }
+  }
+  __syncthreads();
+}
+
+
+// Register staging of one chunk's bf16 K, Q, V rows and its vectors, so the
+// next chunk's global loads are in flight while the current chunk computes.
+// Piece maps: K = 2 x (8 columns of a row pair), consecutive lanes on
+// consecutive row pairs; Q = 4 x 16 bytes of a row; V = 16 bytes of a row's
+// 32-column tile; one vector element.
+struct ChunkStage {
+  u32x4_t k0[2], k1[2], q[4], v;
+  float vec;
+};
+
+__device__ __forceinline__ void stage_issue(ChunkStage& cs, const uint16_t* k, const uint16_t* q,
+                                            int64_t qk_stride, const uint16_t* v, int64_t v_stride,
+                                            const float* vec, int L) {
+  const int tid = threadIdx.x;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + i * kThreads;
+    const int t = 2 * (p % (kC / 2)), j0 = 8 * (p / (kC / 2));
+    cs.k0[i] = t < L ? *reinterpret_cast<const u32x4_t*>(k + (int64_t)t * qk_stride + j0) : z;
+    cs.k1[i] = t + 1 < L ? *reinterpret_cast<const u32x4_t*>(k + (int64_t)(t + 1) * qk_stride + j0) : z;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + i * kThreads;
+    const int t = p / (kD / 8), j0 = 8 * (p % (kD / 8));
+    cs.q[i] = t < L ? *reinterpret_cast<const u32x4_t*>(q + (int64_t)t * qk_stride + j0) : z;
+  }
+  {
+    const int t = tid / (kTile / 8), i0 = 8 * (tid % (kTile / 8));
+    cs.v = t < L ? *reinterpret_cast<const u32x4_t*>(v + (int64_t)t * v_stride + i0) : z;
+  }
+  cs.vec = tid < 3 * kC + 1 ? vec[tid] : 0.0f;
+}
+
+__device__ __forceinline__ void stage_commit(const ChunkStage& cs, uint16_t* sK, int pitch, uint16_t* sKt,
+                                             int tpitch, uint16_t* sQ, float* sV, int vpitch, float* s_vec) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int p = tid + i * kThreads;
+    const int t = 2 * (p % (kC / 2)), j0 = 8 * (p / (kC / 2));
+    *reinterpret_cast<u32x4_t*>(sK + t * pitch + j0) = cs.k0[i];
+    *reinterpret_cast<u32x4_t*>(sK + (t + 1) * pitch + j0) = cs.k1[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t a = (cs.k0[i][e / 2] >> (16 * (e % 2))) & 0xffffu;
+      const uint32_t b = (cs.k1[i][e / 2] >> (16 * (e % 2))) & 0xffffu;
+      *reinterpret_cast<uint32_t*>(sKt + (j0 + e) * tpitch + t) = a | (b << 16);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = tid + i * kThreads;
+    const int t = p / (kD / 8), j0 = 8 * (p % (kD / 8));
+    *reinterpret_cast<u32x4_t*>(sQ + t * pitch + j0) = cs.q[i];
+  }
+  {
+    const int t = tid / (kTile / 8), i0 = 8 * (tid % (kTile / 8));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sV[t * vpitch + i0 + 2 * e] = __uint_as_float(cs.v[e] << 16);
+      sV[t * vpitch + i0 + 2 * e + 1] = __uint_as_float(cs.v[e] & 0xffff0000u);
+    }
+  }
+  if (tid < 3 * kC + 1) s_vec[tid] = cs.vec;
+}
+
 // ---------------------------------------------------------------------------
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
 // ---------------------------------------------------------------------------
@@ -221,10 +424,17 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   using E = typename O::E;
   constexpr int kPitch = kD + O::kPadK;
   constexpr int kAP = kC + 1;        // fp32 64x64 scratch pitch
-  __shared__ __attribute__((aligned(16))) E sK[kC * kPitch];
-  __shared__ __attribute__((aligned(16))) E sQ[kC * kPitch];
-  __shared__ float sA[kC * kAP];
-  __shared__ float sP[kC * kAP];
+  // K / Q tiles are dead once the Gram tiles are in registers, so the 64x64
+  // scratch (A, Pt, T) reuses their LDS.
+  constexpr int kKQBytes = 2 * kC * kPitch * (int)sizeof(E);
+  constexpr int kScratchBytes = 3 * kC * kAP * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) uint8_t s_pool[kKQBytes > kScratchBytes ? kKQBytes : kScratchBytes];
+  E* sK = reinterpret_cast<E*>(s_pool);
+  E* sQ = sK + kC * kPitch;
+  float* sA = reinterpret_cast<float*>(s_pool);
+  float* sP = sA + kC * kAP;
+  float* sT = sP + kC * kAP;
+  __shared__ float sM[3 * 16 * 17];
   __shared__ float s_rk[kC], s_rq[kC], s_gam[kC], s_beta[kC];
 
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
@@ -310,36 +520,14 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     }
     __syncthreads();
 
-    // T = (I + A)^-1, column-parallel forward substitution: thread (col, part)
-    // keeps T[4m + part][col] for m = 0..15 in registers.
-    {
-      const int col = tid / 4, part = tid % 4;
-      float tc[16];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) tc[m] = (4 * m + part == col) ? 1.0f : 0.0f;
-#pragma unroll
-      for (int r = 1; r < kC; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int m = 0; m < 16; ++m)
-          if (4 * m < r) {
-            const float a = sA[r * kAP + 4 * m + part];
-            acc = fmaf(4 * m + part < r ? a : 0.0f, tc[m], acc);
-          }
-        acc = group_sum<4>(acc);
-        if (r > col && (r & 3) == part) tc[r >> 2] = -acc;
-      }
-      __syncthreads();  // every thread has finished reading A
-      const float bc = s_beta[col];
-#pragma unroll
-      for (int m = 0; m < 16; ++m) sA[(4 * m + part) * kAP + col] = tc[m] * bc;
-    }
-    __syncthreads();
+    // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
+    unit_lower_inverse<kAP>(sA, sT, sM);
 
     // write Tt and Pt in A-operand lane layout, masked to the lower triangle
     uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
     for (int which = 0; which < 2; ++which) {
-      const float* src = which == 0 ? sA : sP;
+      const float* src = which == 0 ? sT : sP;
+      const bool scale_cols = which == 0;
       uint8_t* dst = rec + which * kFragBytes;
       if constexpr (F32) {
         // fragment (mt, ks): lane l holds src[16mt + l%16][4ks + l/16]
@@ -347,7 +535,8 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
           const int l = p % kWave, f = p / kWave;   // f = mt * 16 + ks
           const int mt = f / 16, ks = f % 16;
           const int r = 16 * mt + (l & 15), kk = 4 * ks + (l >> 4);
-          reinterpret_cast<float*>(dst)[p] = kk <= r ? src[r * kAP + kk] : 0.0f;
+          reinterpret_cast<float*>(dst)[p] =
+              kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
         }
       } else {
         // fragment (mt, ks, term): lane l holds src[16mt + l%16][32ks + 8(l/16) + e]
@@ -358,7 +547,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
           bf16x8_t hi, lo;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float v = (k0 + e) <= r ? src[r * kAP + k0 + e] : 0.0f;
+            const float v = (k0 + e) <= r ? src[r * kAP + k0 + e] * (scale_cols ? s_beta[k0 + e] : 1.0f) : 0.0f;
             __bf16 a, b;
             split_bf16(v, a, b);
             hi[e] = a;
@@ -446,25 +635,46 @@ __global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
   const int sub = wave & 1;
   const bool y_role = wave < 2;
 
+  // bf16 inputs: chunk c+1's K / Q / V / vectors are loaded into registers
+  // while chunk c computes (ChunkStage); fp32 inputs stage synchronously.
+  [[maybe_unused]] ChunkStage stage;
+  auto chunk_ptrs = [&](int t0c, int cidx, const Tin*& kp, const Tin*& qp, const Tin*& vp, const float*& vecp) {
+    kp = k + (int64_t)t0c * qk_stride + kh * kD;
+    qp = q + (int64_t)t0c * qk_stride + kh * kD;
+    vp = v + (int64_t)t0c * v_stride + h * kD + i0;
+    vecp = reinterpret_cast<const float*>(recs + ((size_t)cidx * hv + h) * kRecBytes + 2 * kFragBytes);
+  };
+  if constexpr (!F32) {
+    if (seq_beg < seq_end) {
+      const Tin *kp, *qp, *vp;
+      const float* vecp;
+      chunk_ptrs(seq_beg, chunk0, kp, qp, vp, vecp);
+      stage_issue(stage, kp, qp, qk_stride, vp, v_stride, vecp, min(kC, seq_end - seq_beg));
+    }
+  }
   for (int t0 = seq_beg, c = chunk0; t0 < seq_end; t0 += kC, ++c) {
     const int L = min(kC, seq_end - t0);
     const uint8_t* rec = recs + ((size_t)c * hv + h) * kRecBytes;
+    // this wave's triangular operand (Tt for waves 0,1, Pt for waves 2,3):
+    // issued first, in flight while K / Q / V are committed and product 1 runs
+    F fh[Tri<F32>::kSlots], fl[Tri<F32>::kSlots];
+    load_tri_frags<F32>(rec + (y_role ? 0 : kFragBytes), lane, fh, fl);
     __syncthreads();   // previous chunk finished with sK / sQ / sV / tiles
-    load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-    load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-    for (int p = tid; p < kC * kTile; p += kThreads) {
-      const int t = p / kTile, i = p % kTile;
-      sV[t * kVP + i] = t < L ? ld(v + (int64_t)(t0 + t) * v_stride + h * kD + i0 + i) : 0.0f;
-    }
-    if (tid < 3 * kC + 1) s_vec[tid] = reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid];
-    __syncthreads();
-    if constexpr (!F32) {
-      // K^T for the state update's B operand
-      for (int p = tid; p < kC * kD; p += kThreads) {
-        const int t = p % kC, j = p / kC;
-        sKt[j * kTP + t] = sK[t * kPitch + j];
+    if constexpr (F32) {
+      load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
+      load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
+      load_values(sV, kVP, v + (int64_t)t0 * v_stride + h * kD + i0, v_stride, L);
+      if (tid < 3 * kC + 1) s_vec[tid] = reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid];
+    } else {
+      stage_commit(stage, sK, kPitch, sKt, kTP, sQ, sV, kVP, s_vec);
+      if (t0 + kC < seq_end) {
+        const Tin *kp, *qp, *vp;
+        const float* vecp;
+        chunk_ptrs(t0 + kC, c + 1, kp, qp, vp, vecp);
+        stage_issue(stage, kp, qp, qk_stride, vp, v_stride, vecp, min(kC, seq_end - t0 - kC));
       }
     }
+    __syncthreads();
 
     // ---- Y = K S0^T (waves 0,1) and Z = Q S0^T (waves 2,3): 64 x 16 each ----
     f32x4_t acc[4];
@@ -500,31 +710,24 @@ __global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
 
     // ---- Vnew = Tt R (waves 0,1) ----
     if (y_role) {
-      f32x4_t vn[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        vn[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks <= 16 * mt + 15; ks += O::kKs) {
-          F ah, al;
-          if constexpr (F32) {
-            ah = reinterpret_cast<const float*>(rec)[(mt * 16 + ks / 4) * kWave + lane];
-          } else {
-            const int f = mt * 2 + ks / 32;
-            ah = *reinterpret_cast<const bf16x8_t*>(rec + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
-            al = *reinterpret_cast<const bf16x8_t*>(rec + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
-          }
-          const F bh = frag<F32>(sRh, kTP, 16 * sub, ks);
-          vn[mt] = mma<F32>(ah, bh, vn[mt]);
+        f32x4_t vn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks * O::kKs <= 16 * mt + 15; ++ks) {
+          const int sl = Tri<F32>::slot(mt, ks);
+          const F bh = frag<F32>(sRh, kTP, 16 * sub, ks * O::kKs);
+          vn = mma<F32>(fh[sl], bh, vn);
           if constexpr (!F32) {
-            const F bl = frag<F32>(sRl, kTP, 16 * sub, ks);
-            vn[mt] = mma<F32>(ah, bl, vn[mt]);
-            vn[mt] = mma<F32>(al, bh, vn[mt]);
+            const F bl = frag<F32>(sRl, kTP, 16 * sub, ks * O::kKs);
+            vn = mma<F32>(fh[sl], bl, vn);
+            vn = mma<F32>(fl[sl], bh, vn);
           }
         }
-        store_acc_transposed<F32>(sNh, sNl, kTP, 16 * sub, 16 * mt, vn[mt]);
+        store_acc_transposed<F32>(sNh, sNl, kTP, 16 * sub, 16 * mt, vn);
         f32x4_t w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[mt][e];
+        for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[e];
         store_acc_transposed<F32>(sWh, sWl, kTP, 16 * sub, 16 * mt, w);
       }
     }
@@ -536,22 +739,15 @@ __global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[mt][e] *= s_vec[kC + 16 * mt + 4 * (lane >> 4) + e];
-        for (int ks = 0; ks <= 16 * mt + 15; ks += O::kKs) {
-          F ah, al;
-          const uint8_t* pt = rec + kFragBytes;
-          if constexpr (F32) {
-            ah = reinterpret_cast<const float*>(pt)[(mt * 16 + ks / 4) * kWave + lane];
-          } else {
-            const int f = mt * 2 + ks / 32;
-            ah = *reinterpret_cast<const bf16x8_t*>(pt + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
-            al = *reinterpret_cast<const bf16x8_t*>(pt + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
-          }
-          const F bh = frag<F32>(sNh, kTP, 16 * sub, ks);
-          acc[mt] = mma<F32>(ah, bh, acc[mt]);
+#pragma unroll
+        for (int ks = 0; ks * O::kKs <= 16 * mt + 15; ++ks) {
+          const int sl = Tri<F32>::slot(mt, ks);
+          const F bh = frag<F32>(sNh, kTP, 16 * sub, ks * O::kKs);
+          acc[mt] = mma<F32>(fh[sl], bh, acc[mt]);
           if constexpr (!F32) {
-            const F bl = frag<F32>(sNl, kTP, 16 * sub, ks);
-            acc[mt] = mma<F32>(ah, bl, acc[mt]);
-            acc[mt] = mma<F32>(al, bh, acc[mt]);
+            const F bl = frag<F32>(sNl, kTP, 16 * sub, ks * O::kKs);
+            acc[mt] = mma<F32>(fh[sl], bl, acc[mt]);
+            acc[mt] = mma<F32>(fl[sl], bh, acc[mt]);
           }
         }
 #pragma unroll

@@ -19,11 +19,15 @@
 //     o   = S' qtil = r + u (khat . qtil)
 // so S is read once and written once.
 //
-// Work split: one workgroup per (sequence, key head).  It owns that key head's
-// q/k conv channels and the conv channels of its Hv/Hk value heads, so every
-// conv-state element has exactly one writer and the in-place update is
-// race-free.  The 64 KiB state of a head is spread over 256 threads as 16 rows
-// x one float4 each; a wavefront loads two full 512-byte rows per instruction.
+// Work split: one workgroup per (sequence, value head), 256 threads, so a
+// 64-sequence batch is 3072 equal workgroups (three full rounds at four
+// resident workgroups per CU).  The 64 KiB state of the head is spread as
+// 16 rows x one float4 per thread; a wavefront loads two full 512-byte rows
+// per instruction.  Each workgroup computes its key head's q/k conv outputs
+// from the OLD conv state without writing it (three value heads read the same
+// channels), and owns its value channels' conv state, which it shifts in
+// place.  A second, tiny kernel launched behind it on the same stream shifts
+// the q/k conv-state rows once all readers are done.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -32,10 +36,12 @@ namespace {
 
 constexpr int kDecThreads = 256;
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
-constexpr int kRowsPerThread = 16;      // 128 rows / 8 row groups
+constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
 constexpr int kRedPitch = 33;           // padded pitch of the row-sum exchange
 
-template <typename T>
+// Conv of one channel for one token: y = act(w . (s0, s1, s2, x)).  With kShift
+// the channel's state rows become (s1, s2, x).
+template <bool kShift, typename T>
 __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_w, T* cs_row,
                                               int c, int cc, int act) {
   T* p = cs_row + c;
@@ -46,9 +52,11 @@ __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_
   y = fmaf(w[1], s1, y);
   y = fmaf(w[2], s2, y);
   y = fmaf(w[3], xv, y);
-  st(p, s1);
-  st(p + cc, s2);
-  st(p + 2 * cc, xv);
+  if constexpr (kShift) {
+    st(p, s1);
+    st(p + cc, s2);
+    st(p + 2 * cc, xv);
+  }
   return act ? y * sigmoidf_(y) : y;
 }
 
@@ -58,9 +66,9 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
     const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
     int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
-  const int b = blockIdx.x;
-  const int kh = blockIdx.y;
-  const int ratio = hv / hk;
+  const int b = blockIdx.x / hv;
+  const int h = blockIdx.x % hv;
+  const int kh = h / (hv / hk);
   const int tid = threadIdx.x;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
@@ -71,14 +79,22 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
   __shared__ float s_red[2][kD][kRedPitch];
   __shared__ float s_scal[8];
 
+  // issue the state loads first; the conv and norms below overlap their latency.
+  // The state is streamed once per step (no reuse), so its loads and stores are
+  // non-temporal.
+  float* S = state + ((int64_t)b * hv + h) * kD * kD;
+  f32x4_t sreg[kRowsPerThread];
+#pragma unroll
+  for (int m = 0; m < kRowsPerThread; ++m)
+    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+
   const T* x_row = x + (int64_t)b * cc;
   T* cs_row = conv_state + (int64_t)b * 3 * cc;
-
-  // --- q / k conv channels of this key head, then L2 norms ----------------
   {
     const int c = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
-    const float y = conv_channel(x_row, conv_w, cs_row, c, cc, act);
+    const float y = conv_channel<false>(x_row, conv_w, cs_row, c, cc, act);
     if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
+    if (tid < kD) s_v[tid] = conv_channel<true>(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + tid, cc, act);
   }
   __syncthreads();
   if (wave < 2) {
@@ -88,92 +104,90 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
     if (lane == 0) s_scal[wave] = 1.0f / sqrtf(ss + l2_eps);
   }
   __syncthreads();
-  if (tid < kD) s_q[tid] *= s_scal[0] * q_scale;
-  else s_k[tid - kD] *= s_scal[1];
-  __syncthreads();
+  const float rq = s_scal[0] * q_scale, rk = s_scal[1];
   if (wave == 0) {
     const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]);
-    if (lane == 0) s_scal[2] = kq;
+    if (lane == 0) s_scal[2] = kq * rq * rk;
   }
-  // this thread's key / query columns
-  float kcol[4], qcol[4];
+  // this thread's normalised key / query columns and decay factors
+  float kcol[4], qcol[4], a[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e]; qcol[e] = s_q[4 * cg + e]; }
+  for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e] * rk; qcol[e] = s_q[4 * cg + e] * rq; }
+  if constexpr (kPerChannel) {
+    const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)b * hv + h) * kD + 4 * cg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+  } else {
+    const float av = __expf(g[(int64_t)b * hv + h]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = av;
+  }
 
-  for (int hh = 0; hh < ratio; ++hh) {
-    const int h = kh * ratio + hh;
-    float* S = state + ((int64_t)b * hv + h) * kD * kD;
-    // issue the state loads first; the v conv below overlaps their latency
-    f32x4_t sreg[kRowsPerThread];
+  // decay, then the two row sums over this thread's four columns
 #pragma unroll
-    for (int m = 0; m < kRowsPerThread; ++m)
-      sreg[m] = *reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg);
-
-    if (tid < kD) s_v[tid] = conv_channel(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + tid, cc, act);
-    float a[4];
-    if constexpr (kPerChannel) {
-      const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)b * hv + h) * kD + 4 * cg);
+  for (int m = 0; m < kRowsPerThread; ++m) {
+    float pk = 0.0f, pq = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
-    } else {
-      const float av = __expf(g[(int64_t)b * hv + h]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = av;
+    for (int e = 0; e < 4; ++e) {
+      sreg[m][e] *= a[e];
+      pk = fmaf(sreg[m][e], kcol[e], pk);
+      pq = fmaf(sreg[m][e], qcol[e], pq);
     }
+    s_red[0][rg + 8 * m][cg] = pk;
+    s_red[1][rg + 8 * m][cg] = pq;
+  }
+  __syncthreads();
 
-    // decay, then the two row sums over this thread's four columns
-#pragma unroll
-    for (int m = 0; m < kRowsPerThread; ++m) {
-      float pk = 0.0f, pq = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sreg[m][e] *= a[e];
-        pk = fmaf(sreg[m][e], kcol[e], pk);
-        pq = fmaf(sreg[m][e], qcol[e], pq);
-      }
-      s_red[0][rg + 8 * m][cg] = pk;
-      s_red[1][rg + 8 * m][cg] = pq;
-    }
-    __syncthreads();
-
-    // rows: u = beta (v - p), o = r + u (khat . qtil), then the gated norm
-    if (tid < kD) {
-      float pk = 0.0f, pq = 0.0f;
+  // rows: u = beta (v - p), o = r + u (khat . qtil), then the gated norm
+  if (tid < kD) {
+    float pk = 0.0f, pq = 0.0f;
 #pragma unroll 8
-      for (int j = 0; j < 32; ++j) { pk += s_red[0][tid][j]; pq += s_red[1][tid][j]; }
-      const float u = beta[(int64_t)b * hv + h] * (s_v[tid] - pk);
-      s_u[tid] = u;
-      const float o = fmaf(u, s_scal[2], pq);
-      const float ss = wave_sum(o * o);
-      if (lane == 0) s_scal[4 + wave] = ss;
-      // the two waves' sums meet below; keep o in a register meanwhile
-      s_v[tid] = o;
-    }
-    __syncthreads();
-    if (tid < kD) {
-      const float r = rsqrtf((s_scal[4] + s_scal[5]) * (1.0f / kD) + rms_eps);
-      const int64_t off = ((int64_t)b * hv + h) * kD + tid;
-      const float y = s_v[tid] * r * norm_w[tid] * sigmoidf_(ld(z + off));
-      st(out + off, y);
-    }
-
-    // write the updated state: S' = Sd + u khat^T
-#pragma unroll
-    for (int m = 0; m < kRowsPerThread; ++m) {
-      const float u = s_u[rg + 8 * m];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
-      *reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg) = sreg[m];
-    }
-    __syncthreads();  // s_red / s_u / s_v are reused by the next head
+    for (int j = 0; j < 32; ++j) { pk += s_red[0][tid][j]; pq += s_red[1][tid][j]; }
+    const float u = beta[(int64_t)b * hv + h] * (s_v[tid] - pk);
+    s_u[tid] = u;
+    const float o = fmaf(u, s_scal[2], pq);
+    const float ss = wave_sum(o * o);
+    if (lane == 0) s_scal[4 + wave] = ss;
+    s_v[tid] = o;
   }
+  __syncthreads();
+  if (tid < kD) {
+    const float r = rsqrtf((s_scal[4] + s_scal[5]) * (1.0f / kD) + rms_eps);
+    const int64_t off = ((int64_t)b * hv + h) * kD + tid;
+    st(out + off, s_v[tid] * r * norm_w[tid] * sigmoidf_(ld(z + off)));
+  }
+
+  // write the updated state: S' = Sd + u khat^T
+#pragma unroll
+  for (int m = 0; m < kRowsPerThread; ++m) {
+    const float u = s_u[rg + 8 * m];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  }
+}
+
+// Shift the q/k conv-state rows (s0, s1, s2) <- (s1, s2, x) for every sequence,
+// after every value head has read the old rows.
+template <typename T>
+__global__ __launch_bounds__(256) void decode_qk_shift_kernel(const T* __restrict__ x,
+                                                               T* __restrict__ conv_state,
+                                                               int qk_channels, int cc) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int b = blockIdx.y;
+  if (c >= qk_channels) return;
+  T* p = conv_state + (int64_t)b * 3 * cc + c;
+  const T s1 = p[cc], s2 = p[2 * cc], xv = x[(int64_t)b * cc + c];
+  p[0] = s1;
+  p[cc] = s2;
+  p[2 * cc] = xv;
 }
 
 template <typename T, typename To>
 hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                        const float* g, const float* beta, const void* z, const float* norm_w,
                        float* state, void* out, int b, hipStream_t s) {
-  dim3 grid(b, d.hk);
+  dim3 grid(b * d.hv);
   if (d.per_channel)
     hipLaunchKernelGGL((decode_step_kernel<T, To, true>), grid, dim3(kDecThreads), 0, s,
                        static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
@@ -184,6 +198,11 @@ hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* 
                        static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
                        static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv,
                        d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int qk = 2 * d.hk * d.dk;
+  hipLaunchKernelGGL(decode_qk_shift_kernel<T>, dim3((qk + 255) / 256, b), dim3(256), 0, s,
+                     static_cast<const T*>(x), static_cast<T*>(conv_state), qk, d.cc);
   return hipGetLastError();
 }
 
