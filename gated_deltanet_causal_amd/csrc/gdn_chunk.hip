@@ -89,28 +89,6 @@ __device__ __forceinline__ f32x4_t mma(typename Ops<F32>::F a, typename Ops<F32>
   else return mfma_bf16(a, b, c);
 }
 
-// hi/lo fragment pair of an fp32 matrix row segment m[idx][k0 .. k0+E-1] (k contiguous).
-template <bool F32>
-__device__ __forceinline__ void frag_split_f32(const float* m, int pitch, int idx0, int k0,
-                                               typename Ops<F32>::F& hi, typename Ops<F32>::F& lo) {
-  const int l = threadIdx.x % kWave;
-  const float* p = m + (idx0 + (l & 15)) * pitch + k0 + Ops<F32>::kEpl * (l >> 4);
-  if constexpr (F32) {
-    hi = *p;
-    lo = 0.0f;
-  } else {
-    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      __bf16 h0, l0, h1, l1;
-      split_bf16(a[e], h0, l0);
-      split_bf16(b[e], h1, l1);
-      hi[e] = h0; lo[e] = l0; hi[4 + e] = h1; lo[4 + e] = l1;
-    }
-  }
-}
-
 // Store the four accumulator rows of a lane (rows t0+4(l/16)+r, column c) transposed:
 // mt[c][t0 + 4(l/16) + r] for r = 0..3, as hi/lo bf16 (or one fp32 array).
 template <bool F32>
@@ -209,38 +187,6 @@ __device__ __forceinline__ void load_rows(typename Ops<F32>::E* dst, int pitch, 
   }
 }
 
-
-// Number of (row tile, k step) fragment slots of a lower-triangular 64x64
-// operand in lane layout: k steps up to the diagonal of each 16-row tile.
-template <bool F32> struct Tri;
-template <> struct Tri<false> {            // bf16: k step 32 -> 1,1,2,2 steps
-  static constexpr int kSlots = 6;
-  __device__ static constexpr int slot(int mt, int ks) { return mt < 2 ? mt : 2 + 2 * (mt - 2) + ks; }
-};
-template <> struct Tri<true> {             // fp32: k step 4 -> 4,8,12,16 steps
-  static constexpr int kSlots = 40;
-  __device__ static constexpr int slot(int mt, int ks) { return 2 * mt * (mt + 1) + ks; }
-};
-
-// All of this lane's fragments of a triangular operand record (hi and lo).
-template <bool F32>
-__device__ __forceinline__ void load_tri_frags(const uint8_t* src, int lane, typename Ops<F32>::F* fh,
-                                               typename Ops<F32>::F* fl) {
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int ks = 0; ks * Ops<F32>::kKs <= 16 * mt + 15; ++ks) {
-      const int sl = Tri<F32>::slot(mt, ks);
-      if constexpr (F32) {
-        fh[sl] = reinterpret_cast<const float*>(src)[(mt * 16 + ks) * kWave + lane];
-      } else {
-        const int f = mt * 2 + ks;
-        fh[sl] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
-        fl[sl] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
-      }
-    }
-  }
-}
 
 // 64 x 32 value tile (rows past L zero) as fp32 into LDS, 16-byte loads.
 template <typename Tin>
@@ -343,74 +289,6 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
   __syncthreads();
 }
 
-
-// Register staging of one chunk's bf16 K, Q, V rows and its vectors, so the
-// next chunk's global loads are in flight while the current chunk computes.
-// Piece maps: K = 2 x (8 columns of a row pair), consecutive lanes on
-// consecutive row pairs; Q = 4 x 16 bytes of a row; V = 16 bytes of a row's
-// 32-column tile; one vector element.
-struct ChunkStage {
-  u32x4_t k0[2], k1[2], q[4], v;
-  float vec;
-};
-
-__device__ __forceinline__ void stage_issue(ChunkStage& cs, const uint16_t* k, const uint16_t* q,
-                                            int64_t qk_stride, const uint16_t* v, int64_t v_stride,
-                                            const float* vec, int L) {
-  const int tid = threadIdx.x;
-  const u32x4_t z = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + i * kThreads;
-    const int t = 2 * (p % (kC / 2)), j0 = 8 * (p / (kC / 2));
-    cs.k0[i] = t < L ? *reinterpret_cast<const u32x4_t*>(k + (int64_t)t * qk_stride + j0) : z;
-    cs.k1[i] = t + 1 < L ? *reinterpret_cast<const u32x4_t*>(k + (int64_t)(t + 1) * qk_stride + j0) : z;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + i * kThreads;
-    const int t = p / (kD / 8), j0 = 8 * (p % (kD / 8));
-    cs.q[i] = t < L ? *reinterpret_cast<const u32x4_t*>(q + (int64_t)t * qk_stride + j0) : z;
-  }
-  {
-    const int t = tid / (kTile / 8), i0 = 8 * (tid % (kTile / 8));
-    cs.v = t < L ? *reinterpret_cast<const u32x4_t*>(v + (int64_t)t * v_stride + i0) : z;
-  }
-  cs.vec = tid < 3 * kC + 1 ? vec[tid] : 0.0f;
-}
-
-__device__ __forceinline__ void stage_commit(const ChunkStage& cs, uint16_t* sK, int pitch, uint16_t* sKt,
-                                             int tpitch, uint16_t* sQ, float* sV, int vpitch, float* s_vec) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = tid + i * kThreads;
-    const int t = 2 * (p % (kC / 2)), j0 = 8 * (p / (kC / 2));
-    *reinterpret_cast<u32x4_t*>(sK + t * pitch + j0) = cs.k0[i];
-    *reinterpret_cast<u32x4_t*>(sK + (t + 1) * pitch + j0) = cs.k1[i];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t a = (cs.k0[i][e / 2] >> (16 * (e % 2))) & 0xffffu;
-      const uint32_t b = (cs.k1[i][e / 2] >> (16 * (e % 2))) & 0xffffu;
-      *reinterpret_cast<uint32_t*>(sKt + (j0 + e) * tpitch + t) = a | (b << 16);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = tid + i * kThreads;
-    const int t = p / (kD / 8), j0 = 8 * (p % (kD / 8));
-    *reinterpret_cast<u32x4_t*>(sQ + t * pitch + j0) = cs.q[i];
-  }
-  {
-    const int t = tid / (kTile / 8), i0 = 8 * (tid % (kTile / 8));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sV[t * vpitch + i0 + 2 * e] = __uint_as_float(cs.v[e] << 16);
-      sV[t * vpitch + i0 + 2 * e + 1] = __uint_as_float(cs.v[e] & 0xffff0000u);
-    }
-  }
-  if (tid < 3 * kC + 1) s_vec[tid] = cs.vec;
-}
 
 // ---------------------------------------------------------------------------
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
@@ -574,8 +452,105 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
 // ---------------------------------------------------------------------------
 // spine: per (sequence, value head, dv tile), sequential over chunks
 // ---------------------------------------------------------------------------
+constexpr int kSpineThreads = 512;   // 8 waves, two per SIMD
+
+// Register staging of one chunk's inputs: K and Q rows, the V tile, the chunk
+// record (Tt and Pt fragments, vectors).  Issued while the previous chunk
+// computes, committed to LDS at the top of the chunk.
+template <bool F32> struct Stage;
+template <> struct Stage<false> {      // bf16 rows
+  u32x4_t k0, k1, q[2], v, f[4];
+  float vec;
+};
+template <> struct Stage<true> {       // fp32 rows
+  u32x4_t k[4], q[4], v, f[4];
+  float vec;
+};
+
+template <bool F32, typename Tin>
+__device__ __forceinline__ void stage_issue(Stage<F32>& sg, const Tin* k, const Tin* q, int64_t qk_stride,
+                                            const Tin* v, int64_t v_stride, const uint8_t* rec, int L) {
+  const int tid = threadIdx.x;
+  const u32x4_t z = {0u, 0u, 0u, 0u};
+  auto row16 = [&](const Tin* base, int64_t stride, int t, int col) -> u32x4_t {
+    return t < L ? *reinterpret_cast<const u32x4_t*>(base + (int64_t)t * stride + col) : z;
+  };
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + i * kSpineThreads;            // 64 rows x 32 pieces of 4 floats
+      sg.k[i] = row16(k, qk_stride, p / 32, 4 * (p % 32));
+      sg.q[i] = row16(q, qk_stride, p / 32, 4 * (p % 32));
+    }
+    sg.v = row16(v, v_stride, tid / 8, 4 * (tid % 8));  // 64 rows x 8 pieces
+  } else {
+    {
+      const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));   // row pair x 8 columns
+      sg.k0 = row16(k, qk_stride, t, j0);
+      sg.k1 = row16(k, qk_stride, t + 1, j0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + i * kSpineThreads;            // 64 rows x 16 pieces of 8
+      sg.q[i] = row16(q, qk_stride, p / 16, 8 * (p % 16));
+    }
+    sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sg.f[i] = reinterpret_cast<const u32x4_t*>(rec)[tid + i * kSpineThreads];
+  sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+}
+
+template <bool F32>
+__device__ __forceinline__ void stage_commit(const Stage<F32>& sg, typename Ops<F32>::E* sK,
+                                             typename Ops<F32>::E* sKt, typename Ops<F32>::E* sQ, int pitch,
+                                             int tpitch, float* sV, int vpitch, uint8_t* sF, float* s_vec) {
+  const int tid = threadIdx.x;
+  if constexpr (F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = tid + i * kSpineThreads;
+      *reinterpret_cast<u32x4_t*>(sK + (p / 32) * pitch + 4 * (p % 32)) = sg.k[i];
+      *reinterpret_cast<u32x4_t*>(sQ + (p / 32) * pitch + 4 * (p % 32)) = sg.q[i];
+    }
+    const int t = tid / 8, i0 = 4 * (tid % 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sV[t * vpitch + i0 + e] = __uint_as_float(sg.v[e]);
+  } else {
+    {
+      const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
+      *reinterpret_cast<u32x4_t*>(sK + t * pitch + j0) = sg.k0;
+      *reinterpret_cast<u32x4_t*>(sK + (t + 1) * pitch + j0) = sg.k1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // columns j0+2e (low halves) and j0+2e+1 (high halves) of rows t, t+1
+        *reinterpret_cast<uint32_t*>(sKt + (j0 + 2 * e) * tpitch + t) =
+            __builtin_amdgcn_perm(sg.k1[e], sg.k0[e], 0x05040100u);
+        *reinterpret_cast<uint32_t*>(sKt + (j0 + 2 * e + 1) * tpitch + t) =
+            __builtin_amdgcn_perm(sg.k1[e], sg.k0[e], 0x07060302u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int p = tid + i * kSpineThreads;
+      *reinterpret_cast<u32x4_t*>(sQ + (p / 16) * pitch + 8 * (p % 16)) = sg.q[i];
+    }
+    if (tid < kC * 4) {
+      const int t = tid / 4, i0 = 8 * (tid % 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sV[t * vpitch + i0 + 2 * e] = __uint_as_float(sg.v[e] << 16);
+        sV[t * vpitch + i0 + 2 * e + 1] = __uint_as_float(sg.v[e] & 0xffff0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4_t*>(sF)[tid + i * kSpineThreads] = sg.f[i];
+  if (tid < 3 * kC + 1) s_vec[tid] = sg.vec;
+}
+
 template <bool F32, typename Tin, typename To>
-__global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
+__global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     const Tin* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
@@ -583,18 +558,21 @@ __global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
-  constexpr int kPitch = kD + O::kPadK;          // K, Q rows
+  constexpr int kPitch = kD + O::kPadK;          // K, Q and state rows
   constexpr int kTP = kC + O::kPadK;             // transposed [i][t] tiles
-  constexpr int kSP = kD + 4;                    // fp32 state pitch
   constexpr int kVP = kTile + 1;                 // fp32 V tile pitch
   __shared__ __attribute__((aligned(16))) E sK[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sQ[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sKt[F32 ? 1 : kD * kTP];
-  __shared__ __attribute__((aligned(16))) float sS[kTile * kSP];
+  // The fp32 state tile lives in the waves' MFMA accumulators across chunks;
+  // LDS holds it as the B operand of product 1, split into bf16 hi / lo
+  // (fp32 on the fp32 path), row-major [i][j].
+  __shared__ __attribute__((aligned(16))) E sSh[kTile * kPitch], sSl[F32 ? 1 : kTile * kPitch];
   __shared__ float sV[kC * kVP];
   __shared__ __attribute__((aligned(16))) E sRh[kTile * kTP], sRl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
+  __shared__ __attribute__((aligned(16))) uint8_t sF[2 * kFragBytes];   // Tt | Pt fragments
   __shared__ float s_vec[3 * kC + 4];
 
   // Block -> (sequence, key head) group and member (value head of the group,
@@ -618,185 +596,181 @@ __global__ __launch_bounds__(kThreads) void chunk_spine_kernel(
   const uint8_t* recs = ws + records_offset(n_seq);
   const int seq_beg = cu[n], seq_end = cu[n + 1];
   const int chunk0 = first[n];
+  auto rec_of = [&](int cidx) { return recs + ((size_t)cidx * hv + h) * kRecBytes; };
 
-  float* s_out = final_state ? final_state + (((int64_t)n * hv + h) * kD + i0) * kD : nullptr;
+  // Roles.  Wave w owns token row tile mt = w % 4 and dv half hf = w / 4 of
+  // Y, Z, R, Vnew and O.  For the state update it owns the transposed state
+  // tiles S^T[16 nj ..][si ..], nj = 2 (w / 2) + {0, 1}, si = 16 (w % 2): a lane
+  // holds S[si + l%16][16 nj + 4 (l/16) .. +3], four consecutive key columns.
+  const int mt = wave & 3, hf = wave >> 2;
+  const int si = 16 * (wave & 1);
+  const int nj0 = 2 * (wave >> 1);
+  const int nks = F32 ? 4 * (mt + 1) : 1 + (mt >> 1);   // k steps up to the diagonal
+  constexpr int kMaxKs = F32 ? 16 : 2;
+
+  f32x4_t sacc[2];
+  auto store_state_lds = [&]() {
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      const int off = (si + (lane & 15)) * kPitch + 16 * (nj0 + q2) + 4 * (lane >> 4);
+      if constexpr (F32) {
+        *reinterpret_cast<f32x4_t*>(sSh + off) = sacc[q2];
+      } else {
+        uint32_t hp[2], lp[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          __bf16 h0, l0, h1, l1;
+          split_bf16(sacc[q2][2 * e], h0, l0);
+          split_bf16(sacc[q2][2 * e + 1], h1, l1);
+          hp[e] = __builtin_bit_cast(uint16_t, h0) | (uint32_t(__builtin_bit_cast(uint16_t, h1)) << 16);
+          lp[e] = __builtin_bit_cast(uint16_t, l0) | (uint32_t(__builtin_bit_cast(uint16_t, l1)) << 16);
+        }
+        *reinterpret_cast<uint2*>(sSh + off) = make_uint2(hp[0], hp[1]);
+        *reinterpret_cast<uint2*>(sSl + off) = make_uint2(lp[0], lp[1]);
+      }
+    }
+  };
   {
     const float* s_in = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0) * kD : nullptr;
-    for (int p = tid; p < kTile * kD / 4; p += kThreads) {
-      const int i = p / (kD / 4), j = (p % (kD / 4)) * 4;
-      f32x4_t val = {0.f, 0.f, 0.f, 0.f};
-      if (s_in) val = *reinterpret_cast<const f32x4_t*>(s_in + i * kD + j);
-      *reinterpret_cast<f32x4_t*>(sS + i * kSP + j) = val;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2) {
+      sacc[q2] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (s_in)
+        sacc[q2] = *reinterpret_cast<const f32x4_t*>(s_in + (si + (lane & 15)) * kD + 16 * (nj0 + q2) + 4 * (lane >> 4));
     }
+    store_state_lds();
   }
 
-  // product roles: waves 0,1 own Y / R / Vnew for dv sub-tile (wave & 1);
-  // waves 2,3 own Z / O for the same sub-tiles; all four share the state update.
-  const int sub = wave & 1;
-  const bool y_role = wave < 2;
-
-  // bf16 inputs: chunk c+1's K / Q / V / vectors are loaded into registers
-  // while chunk c computes (ChunkStage); fp32 inputs stage synchronously.
-  [[maybe_unused]] ChunkStage stage;
-  auto chunk_ptrs = [&](int t0c, int cidx, const Tin*& kp, const Tin*& qp, const Tin*& vp, const float*& vecp) {
-    kp = k + (int64_t)t0c * qk_stride + kh * kD;
-    qp = q + (int64_t)t0c * qk_stride + kh * kD;
-    vp = v + (int64_t)t0c * v_stride + h * kD + i0;
-    vecp = reinterpret_cast<const float*>(recs + ((size_t)cidx * hv + h) * kRecBytes + 2 * kFragBytes);
+  Stage<F32> stage;
+  auto issue = [&](int t0c, int cidx) {
+    stage_issue<F32>(stage, k + (int64_t)t0c * qk_stride + kh * kD, q + (int64_t)t0c * qk_stride + kh * kD,
+                     qk_stride, v + (int64_t)t0c * v_stride + h * kD + i0, v_stride, rec_of(cidx),
+                     min(kC, seq_end - t0c));
   };
-  if constexpr (!F32) {
-    if (seq_beg < seq_end) {
-      const Tin *kp, *qp, *vp;
-      const float* vecp;
-      chunk_ptrs(seq_beg, chunk0, kp, qp, vp, vecp);
-      stage_issue(stage, kp, qp, qk_stride, vp, v_stride, vecp, min(kC, seq_end - seq_beg));
-    }
-  }
+  if (seq_beg < seq_end) issue(seq_beg, chunk0);
+
   for (int t0 = seq_beg, c = chunk0; t0 < seq_end; t0 += kC, ++c) {
     const int L = min(kC, seq_end - t0);
-    const uint8_t* rec = recs + ((size_t)c * hv + h) * kRecBytes;
-    // this wave's triangular operand (Tt for waves 0,1, Pt for waves 2,3):
-    // issued first, in flight while K / Q / V are committed and product 1 runs
-    F fh[Tri<F32>::kSlots], fl[Tri<F32>::kSlots];
-    load_tri_frags<F32>(rec + (y_role ? 0 : kFragBytes), lane, fh, fl);
-    __syncthreads();   // previous chunk finished with sK / sQ / sV / tiles
-    if constexpr (F32) {
-      load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-      load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-      load_values(sV, kVP, v + (int64_t)t0 * v_stride + h * kD + i0, v_stride, L);
-      if (tid < 3 * kC + 1) s_vec[tid] = reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid];
-    } else {
-      stage_commit(stage, sK, kPitch, sKt, kTP, sQ, sV, kVP, s_vec);
-      if (t0 + kC < seq_end) {
-        const Tin *kp, *qp, *vp;
-        const float* vecp;
-        chunk_ptrs(t0 + kC, c + 1, kp, qp, vp, vecp);
-        stage_issue(stage, kp, qp, qk_stride, vp, v_stride, vecp, min(kC, seq_end - t0 - kC));
-      }
-    }
+    __syncthreads();   // the previous chunk is done with every LDS tile
+    stage_commit<F32>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sF, s_vec);
+    if (t0 + kC < seq_end) issue(t0 + kC, c + 1);
     __syncthreads();
 
-    // ---- Y = K S0^T (waves 0,1) and Z = Q S0^T (waves 2,3): 64 x 16 each ----
-    f32x4_t acc[4];
+    // ---- Y = K S0^T and Z = Q S0^T: rows of tile mt, columns of half hf ----
+    f32x4_t accY = {0.f, 0.f, 0.f, 0.f}, accZ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < kD; ks += O::kKs) {
+      const F ak = frag<F32>(sK, kPitch, 16 * mt, ks);
+      const F aq = frag<F32>(sQ, kPitch, 16 * mt, ks);
+      const F bh = frag<F32>(sSh, kPitch, 16 * hf, ks);
+      accY = mma<F32>(ak, bh, accY);
+      accZ = mma<F32>(aq, bh, accZ);
+      if constexpr (!F32) {
+        const F bl = frag<F32>(sSl, kPitch, 16 * hf, ks);
+        accY = mma<F32>(ak, bl, accY);
+        accZ = mma<F32>(aq, bl, accZ);
+      }
+    }
+    // R = V - a_t Y, stored transposed [i][t] as hi/lo
     {
-      const E* a_src = y_role ? sK : sQ;
-      for (int ks = 0; ks < kD; ks += O::kKs) {
-        F bh, bl;
-        frag_split_f32<F32>(sS, kSP, 16 * sub, ks, bh, bl);
+      f32x4_t rv;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) {
-          const F a = frag<F32>(a_src, kPitch, 16 * mt, ks);
-          acc[mt] = mma<F32>(a, bh, acc[mt]);
-          if constexpr (!F32) acc[mt] = mma<F32>(a, bl, acc[mt]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * mt + 4 * (lane >> 4) + e;
+        rv[e] = sV[t * kVP + 16 * hf + (lane & 15)] - s_vec[t] * accY[e];
       }
-    }
-    if (y_role) {
-      // R = V - a_t Y, stored transposed [i][t] as hi/lo
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4_t rv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * (lane >> 4) + e;
-          rv[e] = sV[t * kVP + 16 * sub + (lane & 15)] - s_vec[t] * acc[mt][e];
-        }
-        store_acc_transposed<F32>(sRh, sRl, kTP, 16 * sub, 16 * mt, rv);
-      }
+      store_acc_transposed<F32>(sRh, sRl, kTP, 16 * hf, 16 * mt, rv);
     }
     __syncthreads();
 
-    // ---- Vnew = Tt R (waves 0,1) ----
-    if (y_role) {
+    // ---- Vnew = Tt R (row tile mt, half hf); W = c_t Vnew ----
+    {
+      f32x4_t vn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        f32x4_t vn = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks * O::kKs <= 16 * mt + 15; ++ks) {
-          const int sl = Tri<F32>::slot(mt, ks);
-          const F bh = frag<F32>(sRh, kTP, 16 * sub, ks * O::kKs);
-          vn = mma<F32>(fh[sl], bh, vn);
-          if constexpr (!F32) {
-            const F bl = frag<F32>(sRl, kTP, 16 * sub, ks * O::kKs);
-            vn = mma<F32>(fh[sl], bl, vn);
-            vn = mma<F32>(fl[sl], bh, vn);
+      for (int ks = 0; ks < kMaxKs; ++ks) {
+        if (ks < nks) {
+          const F bh = frag<F32>(sRh, kTP, 16 * hf, ks * O::kKs);
+          if constexpr (F32) {
+            vn = mma<F32>(reinterpret_cast<const float*>(sF)[(mt * 16 + ks) * kWave + lane], bh, vn);
+          } else {
+            const int f = mt * 2 + ks;
+            const F th = load_bf16x8(reinterpret_cast<const uint16_t*>(sF + ((f * 2 + 0) * kWave + lane) * 16));
+            const F tl = load_bf16x8(reinterpret_cast<const uint16_t*>(sF + ((f * 2 + 1) * kWave + lane) * 16));
+            const F bl = frag<F32>(sRl, kTP, 16 * hf, ks * O::kKs);
+            vn = mma<F32>(th, bh, vn);
+            vn = mma<F32>(th, bl, vn);
+            vn = mma<F32>(tl, bh, vn);
           }
         }
-        store_acc_transposed<F32>(sNh, sNl, kTP, 16 * sub, 16 * mt, vn);
-        f32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[e];
-        store_acc_transposed<F32>(sWh, sWl, kTP, 16 * sub, 16 * mt, w);
       }
+      store_acc_transposed<F32>(sNh, sNl, kTP, 16 * hf, 16 * mt, vn);
+      f32x4_t w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[e];
+      store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, w);
     }
     __syncthreads();
 
-    // ---- O = b_t Z + Pt Vnew (waves 2,3) ----
-    if (!y_role) {
+    // ---- O = b_t Z + Pt Vnew (row tile mt, half hf) ----
+    {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
+      for (int e = 0; e < 4; ++e) accZ[e] *= s_vec[kC + 16 * mt + 4 * (lane >> 4) + e];
+      const uint8_t* pf = sF + kFragBytes;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[mt][e] *= s_vec[kC + 16 * mt + 4 * (lane >> 4) + e];
-#pragma unroll
-        for (int ks = 0; ks * O::kKs <= 16 * mt + 15; ++ks) {
-          const int sl = Tri<F32>::slot(mt, ks);
-          const F bh = frag<F32>(sNh, kTP, 16 * sub, ks * O::kKs);
-          acc[mt] = mma<F32>(fh[sl], bh, acc[mt]);
-          if constexpr (!F32) {
-            const F bl = frag<F32>(sNl, kTP, 16 * sub, ks * O::kKs);
-            acc[mt] = mma<F32>(fh[sl], bl, acc[mt]);
-            acc[mt] = mma<F32>(fl[sl], bh, acc[mt]);
+      for (int ks = 0; ks < kMaxKs; ++ks) {
+        if (ks < nks) {
+          const F bh = frag<F32>(sNh, kTP, 16 * hf, ks * O::kKs);
+          if constexpr (F32) {
+            accZ = mma<F32>(reinterpret_cast<const float*>(pf)[(mt * 16 + ks) * kWave + lane], bh, accZ);
+          } else {
+            const int f = mt * 2 + ks;
+            const F ph = load_bf16x8(reinterpret_cast<const uint16_t*>(pf + ((f * 2 + 0) * kWave + lane) * 16));
+            const F pl = load_bf16x8(reinterpret_cast<const uint16_t*>(pf + ((f * 2 + 1) * kWave + lane) * 16));
+            const F bl = frag<F32>(sNl, kTP, 16 * hf, ks * O::kKs);
+            accZ = mma<F32>(ph, bh, accZ);
+            accZ = mma<F32>(ph, bl, accZ);
+            accZ = mma<F32>(pl, bh, accZ);
           }
         }
+      }
+      To* orow = out + ((int64_t)t0 * hv + h) * kD + i0 + 16 * hf + (lane & 15);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = 16 * mt + 4 * (lane >> 4) + e;
-          if (t < L) st(out + ((int64_t)(t0 + t) * hv + h) * kD + i0 + 16 * sub + (lane & 15), acc[mt][e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * mt + 4 * (lane >> 4) + e;
+        if (t < L) st(orow + (int64_t)t * hv * kD, accZ[e]);
       }
     }
 
-    // ---- S <- d S + W^T K, W = c_t Vnew  (all waves: rows 16*sub.., 4 column tiles) ----
+    // ---- S^T <- d S^T + K^T W on this wave's two tiles, then its LDS copy ----
     {
       const float d = s_vec[3 * kC];
-      const int nj0 = (wave >> 1) * 4;
-      f32x4_t sacc[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = 16 * (nj0 + q4) + (lane & 15);
+      for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[q4][e] = d * sS[(16 * sub + 4 * (lane >> 4) + e) * kSP + j];
-      }
+        for (int e = 0; e < 4; ++e) sacc[q2][e] *= d;
+#pragma unroll
       for (int ks = 0; ks < kC; ks += O::kKs) {
-        const F ah = frag<F32>(sWh, kTP, 16 * sub, ks);
-        F al;
-        if constexpr (!F32) al = frag<F32>(sWl, kTP, 16 * sub, ks);
+        const F bh = frag<F32>(sWh, kTP, si, ks);
+        F bl;
+        if constexpr (!F32) bl = frag<F32>(sWl, kTP, si, ks);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          F b;
-          if constexpr (F32) b = sK[(ks + (lane >> 4)) * kPitch + 16 * (nj0 + q4) + (lane & 15)];
-          else b = frag<F32>(sKt, kTP, 16 * (nj0 + q4), ks);
-          sacc[q4] = mma<F32>(ah, b, sacc[q4]);
-          if constexpr (!F32) sacc[q4] = mma<F32>(al, b, sacc[q4]);
+        for (int q2 = 0; q2 < 2; ++q2) {
+          F a;
+          if constexpr (F32) a = sK[(ks + (lane >> 4)) * kPitch + 16 * (nj0 + q2) + (lane & 15)];
+          else a = frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks);
+          sacc[q2] = mma<F32>(a, bh, sacc[q2]);
+          if constexpr (!F32) sacc[q2] = mma<F32>(a, bl, sacc[q2]);
         }
       }
-      __syncthreads();   // all reads of the old state (Y/Z and the d*S term) are done
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = 16 * (nj0 + q4) + (lane & 15);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sS[(16 * sub + 4 * (lane >> 4) + e) * kSP + j] = sacc[q4][e];
-      }
+      // every wave's product 1 read the old copy before the Vnew barrier
+      store_state_lds();
     }
   }
-  __syncthreads();
-  if (s_out) {
-    for (int p = tid; p < kTile * kD / 4; p += kThreads) {
-      const int i = p / (kD / 4), j = (p % (kD / 4)) * 4;
-      *reinterpret_cast<f32x4_t*>(s_out + i * kD + j) = *reinterpret_cast<const f32x4_t*>(sS + i * kSP + j);
-    }
+  if (final_state) {
+    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0) * kD;
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+      *reinterpret_cast<f32x4_t*>(s_out + (si + (lane & 15)) * kD + 16 * (nj0 + q2) + 4 * (lane >> 4)) = sacc[q2];
   }
 }
 
@@ -820,7 +794,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   const int groups = n * d.hk;
   const int members = (d.hv / d.hk) * (kD / kTile);
   const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-  hipLaunchKernelGGL((chunk_spine_kernel<F32, Tin, To>), dim3(blocks), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((chunk_spine_kernel<F32, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
                      static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride,
                      static_cast<const Tin*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                      static_cast<To*>(out), final_state);
