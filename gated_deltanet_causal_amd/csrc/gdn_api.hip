@@ -149,14 +149,13 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
-  if (d.per_channel) return GDN_ERR_UNSUPPORTED;
   if (N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
   if (!cu_dev) return GDN_ERR_INVALID_ARG;
   if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID_ARG;
   const int64_t vec = in_dtype == GDN_BF16 ? 8 : 4;   // elements per 16-byte load
   if (qk_stride < (int64_t)d.hk * d.dk || v_stride < (int64_t)d.hv * d.dv) return GDN_ERR_INVALID_ARG;
   if (qk_stride % vec || v_stride % vec) return GDN_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g))) return GDN_ERR_INVALID_ARG;
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return GDN_ERR_INVALID_ARG;
   st = check_seqlens(cu_host, N, T);

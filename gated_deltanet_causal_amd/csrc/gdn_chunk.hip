@@ -290,6 +290,234 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 }
 
 
+
+// Shared tail of the intra kernels: T = (I + A)^-1 from sA, then Tt = T diag(beta)
+// and Pt (sP) written to the record in MFMA A-operand lane layout, masked to
+// the lower triangle (hi/lo bf16 fragment pairs, or fp32).  All threads.
+template <bool F32, int kAP>
+__device__ __forceinline__ void write_operands(const float* sA, const float* sP, float* sT, float* sM,
+                                               const float* s_beta, uint8_t* rec) {
+  const int tid = threadIdx.x;
+  unit_lower_inverse<kAP>(sA, sT, sM);
+  for (int which = 0; which < 2; ++which) {
+    const float* src = which == 0 ? sT : sP;
+    const bool scale_cols = which == 0;
+    uint8_t* dst = rec + which * kFragBytes;
+    if constexpr (F32) {
+      // fragment (mt, ks): lane l holds src[16mt + l%16][4ks + l/16]
+      for (int p = tid; p < 16 * 4 * kWave; p += kThreads) {
+        const int l = p % kWave, f = p / kWave;   // f = mt * 16 + ks
+        const int mt = f / 16, ks = f % 16;
+        const int r = 16 * mt + (l & 15), kk = 4 * ks + (l >> 4);
+        reinterpret_cast<float*>(dst)[p] = kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
+      }
+    } else {
+      // fragment (mt, ks, term): lane l holds src[16mt + l%16][32ks + 8(l/16) + e]
+      for (int p = tid; p < 8 * kWave; p += kThreads) {
+        const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
+        const int mt = f / 2, ks = f % 2;
+        const int r = 16 * mt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
+        bf16x8_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = (k0 + e) <= r ? src[r * kAP + k0 + e] * (scale_cols ? s_beta[k0 + e] : 1.0f) : 0.0f;
+          __bf16 a, b;
+          split_bf16(v, a, b);
+          hi[e] = a;
+          lo[e] = b;
+        }
+        *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 0) * kWave + l) * 16) = hi;
+        *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 1) * kWave + l) * 16) = lo;
+      }
+    }
+  }
+}
+
+// Operand fragment of X[row][c] = raw[row][c] * rs[row] * exp(sgn * (gam[row][c] - ref[c]))
+// (ref = 0 when null), rows row0.., columns k0.. in the operand lane layout, split into
+// hi/lo bf16 (fp32: hi only).  raw k-contiguous (pitch), gam fp32 (gpitch).
+template <bool F32>
+__device__ __forceinline__ void decayed_frag(const typename Ops<F32>::E* raw, int pitch, const float* gam,
+                                             int gpitch, const float* ref, const float* rs, int row0, int k0,
+                                             float sgn, typename Ops<F32>::F& hi, typename Ops<F32>::F& lo) {
+  const int l = threadIdx.x % kWave;
+  const int r = row0 + (l & 15);
+  const int c0 = k0 + Ops<F32>::kEpl * (l >> 4);
+  const float s = rs[r];
+  if constexpr (F32) {
+    const float e = gam[r * gpitch + c0] - (ref ? ref[c0] : 0.0f);
+    hi = raw[r * pitch + c0] * s * __expf(sgn * e);
+    lo = 0.0f;
+  } else {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(raw + r * pitch + c0);
+    const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0);
+    const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0 + 4);
+    f32x4_t f0 = {0.f, 0.f, 0.f, 0.f}, f1 = {0.f, 0.f, 0.f, 0.f};
+    if (ref) {
+      f0 = *reinterpret_cast<const f32x4_t*>(ref + c0);
+      f1 = *reinterpret_cast<const f32x4_t*>(ref + c0 + 4);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float kv = (e & 1) ? __uint_as_float(u[e / 2] & 0xffff0000u) : __uint_as_float(u[e / 2] << 16);
+      const float ge = e < 4 ? g0[e] - f0[e] : g1[e - 4] - f1[e - 4];
+      __bf16 a, b;
+      split_bf16(kv * s * __expf(sgn * ge), a, b);
+      hi[e] = a;
+      lo[e] = b;
+    }
+  }
+}
+
+// product with both operands split: hi*hi + hi*lo + lo*hi (fp32: one exact product)
+template <bool F32>
+__device__ __forceinline__ f32x4_t mma3(typename Ops<F32>::F ah, typename Ops<F32>::F al,
+                                        typename Ops<F32>::F bh, typename Ops<F32>::F bl, f32x4_t c) {
+  c = mma<F32>(ah, bh, c);
+  if constexpr (!F32) {
+    c = mma<F32>(ah, bl, c);
+    c = mma<F32>(al, bh, c);
+  }
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// intra, per-key-channel decay: per (chunk, value head).  With gam[r][c] the
+// within-chunk cumulative log decay of channel c and a reference token b in
+// the middle of the chunk,
+//   A[r][j]  = beta_r sum_c (khat_r[c] e^{gam_r[c]-gam_b[c]}) (khat_j[c] e^{gam_b[c]-gam_j[c]})   j < r
+//   Pt[r][j] =        sum_c (qtil_r[c] e^{gam_r[c]-gam_b[c]}) (khat_j[c] e^{gam_b[c]-gam_j[c]})   j <= r
+// so every factor is e^{(sum of at most half a chunk of log decays)}; the
+// operands are formed in registers from raw K / Q and gam, split hi/lo.
+// ---------------------------------------------------------------------------
+template <bool F32, typename Tin>
+__global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
+    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
+  using O = Ops<F32>;
+  using E = typename O::E;
+  using F = typename O::F;
+  constexpr int kPitch = kD + O::kPadK;
+  constexpr int kGP = kD + 4;        // gam pitch (fp32)
+  constexpr int kAP = kC + 1;
+  constexpr int kPhase1 = 2 * kC * kPitch * (int)sizeof(E) + kC * kGP * (int)sizeof(float);
+  constexpr int kScratchBytes = 3 * kC * kAP * (int)sizeof(float);
+  __shared__ __attribute__((aligned(16))) uint8_t s_pool[kPhase1 > kScratchBytes ? kPhase1 : kScratchBytes];
+  E* sK = reinterpret_cast<E*>(s_pool);
+  E* sQ = sK + kC * kPitch;
+  float* sGam = reinterpret_cast<float*>(s_pool + 2 * kC * kPitch * sizeof(E));
+  float* sA = reinterpret_cast<float*>(s_pool);
+  float* sP = sA + kC * kAP;
+  float* sT = sP + kC * kAP;
+  __shared__ float sM[3 * 16 * 17];
+  __shared__ float s_rk[kC], s_rq[kC], s_beta[kC];
+  __shared__ __attribute__((aligned(16))) float s_ref[kD];
+  __shared__ float s_tot[kD];
+
+  const int32_t* first = reinterpret_cast<const int32_t*>(ws);
+  const int c = blockIdx.x;
+  const int h = blockIdx.y;
+  const int kh = h / (hv / hk);
+  const int tid = threadIdx.x, wave = tid / kWave;
+  const int n = chunk_sequence(first, n_seq, c);
+  const int t0 = cu[n] + (c - first[n]) * kC;
+  const int L = min(kC, cu[n + 1] - t0);
+
+  load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
+  load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
+  for (int p = tid; p < kC * kD / 4; p += kThreads) {
+    const int r = p / (kD / 4), c4 = 4 * (p % (kD / 4));
+    f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
+    if (r < L) gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)(t0 + r) * hv + h) * kD + c4);
+    *reinterpret_cast<f32x4_t*>(sGam + r * kGP + c4) = gv;
+  }
+  if (tid < kC) s_beta[tid] = tid < L ? beta[(int64_t)(t0 + tid) * hv + h] : 0.0f;
+  __syncthreads();
+
+  {  // row norms: 4 threads per row
+    const int r = tid / 4, part = tid % 4;
+    float sk = 0.f, sq = 0.f;
+    for (int e = 0; e < 32; ++e) {
+      float kv, qv;
+      if constexpr (F32) { kv = sK[r * kPitch + part * 32 + e]; qv = sQ[r * kPitch + part * 32 + e]; }
+      else { kv = bf16_bits_to_f32(sK[r * kPitch + part * 32 + e]); qv = bf16_bits_to_f32(sQ[r * kPitch + part * 32 + e]); }
+      sk = fmaf(kv, kv, sk);
+      sq = fmaf(qv, qv, sq);
+    }
+    sk = group_sum<4>(sk);
+    sq = group_sum<4>(sq);
+    if (part == 0) {
+      s_rk[r] = r < L ? 1.0f / sqrtf(sk + l2_eps) : 0.0f;
+      s_rq[r] = r < L ? q_scale / sqrtf(sq + l2_eps) : 0.0f;
+    }
+  }
+  {  // per-channel cumulative sum over the chunk: thread (channel, half of the rows)
+    const int ch = tid % kD, half = tid / kD;
+    float v[kC / 2];
+#pragma unroll
+    for (int r = 0; r < kC / 2; ++r) v[r] = sGam[(half * (kC / 2) + r) * kGP + ch];
+#pragma unroll
+    for (int r = 1; r < kC / 2; ++r) v[r] += v[r - 1];
+    if (half == 0) s_tot[ch] = v[kC / 2 - 1];
+    __syncthreads();
+    const float off = half ? s_tot[ch] : 0.0f;
+#pragma unroll
+    for (int r = 0; r < kC / 2; ++r) sGam[(half * (kC / 2) + r) * kGP + ch] = v[r] + off;
+  }
+  __syncthreads();
+  const int b_ref = (L - 1) / 2;
+  if (tid < kD) s_ref[tid] = sGam[b_ref * kGP + tid];
+  __syncthreads();
+
+  // decayed Gram tiles of row tile `wave`: G~ = Ka Kb^T, H~ = Qa Kb^T
+  f32x4_t accG[4], accH[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    accG[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    accH[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int ks = 0; ks < kD; ks += O::kKs) {
+    F kah, kal, qah, qal;
+    decayed_frag<F32>(sK, kPitch, sGam, kGP, s_ref, s_rk, 16 * wave, ks, 1.0f, kah, kal);
+    decayed_frag<F32>(sQ, kPitch, sGam, kGP, s_ref, s_rq, 16 * wave, ks, 1.0f, qah, qal);
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt <= wave) {
+        F bh, bl;
+        decayed_frag<F32>(sK, kPitch, sGam, kGP, s_ref, s_rk, 16 * nt, ks, -1.0f, bh, bl);
+        accG[nt] = mma3<F32>(kah, kal, bh, bl, accG[nt]);
+        accH[nt] = mma3<F32>(qah, qal, bh, bl, accH[nt]);
+      }
+    }
+  }
+  __syncthreads();   // the pool's K / Q / gam are dead from here on
+  {
+    const int lane = tid % kWave;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      if (nt <= wave) {
+        const int j = 16 * nt + (lane & 15);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * wave + 4 * (lane >> 4) + e;
+          sA[r * kAP + j] = j < r ? s_beta[r] * accG[nt][e] : 0.0f;
+          sP[r * kAP + j] = j <= r ? accH[nt][e] : 0.0f;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
+  write_operands<F32, kAP>(sA, sP, sT, sM, s_beta, rec);
+  // vectors for the spine: rk, rq
+  if (tid < kC) {
+    float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
+    vec[tid] = s_rk[tid];
+    vec[kC + tid] = s_rq[tid];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
 // ---------------------------------------------------------------------------
@@ -399,43 +627,9 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     __syncthreads();
 
     // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
-    unit_lower_inverse<kAP>(sA, sT, sM);
-
-    // write Tt and Pt in A-operand lane layout, masked to the lower triangle
     uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
-    for (int which = 0; which < 2; ++which) {
-      const float* src = which == 0 ? sT : sP;
-      const bool scale_cols = which == 0;
-      uint8_t* dst = rec + which * kFragBytes;
-      if constexpr (F32) {
-        // fragment (mt, ks): lane l holds src[16mt + l%16][4ks + l/16]
-        for (int p = tid; p < 16 * 4 * kWave; p += kThreads) {
-          const int l = p % kWave, f = p / kWave;   // f = mt * 16 + ks
-          const int mt = f / 16, ks = f % 16;
-          const int r = 16 * mt + (l & 15), kk = 4 * ks + (l >> 4);
-          reinterpret_cast<float*>(dst)[p] =
-              kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
-        }
-      } else {
-        // fragment (mt, ks, term): lane l holds src[16mt + l%16][32ks + 8(l/16) + e]
-        for (int p = tid; p < 8 * kWave; p += kThreads) {
-          const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
-          const int mt = f / 2, ks = f % 2;
-          const int r = 16 * mt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
-          bf16x8_t hi, lo;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = (k0 + e) <= r ? src[r * kAP + k0 + e] * (scale_cols ? s_beta[k0 + e] : 1.0f) : 0.0f;
-            __bf16 a, b;
-            split_bf16(v, a, b);
-            hi[e] = a;
-            lo[e] = b;
-          }
-          *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 0) * kWave + l) * 16) = hi;
-          *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 1) * kWave + l) * 16) = lo;
-        }
-      }
-    }
+    write_operands<F32, kAP>(sA, sP, sT, sM, s_beta, rec);
+
     // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
     if (tid < kC) {
       float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
@@ -455,21 +649,19 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
 constexpr int kSpineThreads = 512;   // 8 waves, two per SIMD
 
 // Register staging of one chunk's inputs: K and Q rows, the V tile, the chunk
-// record (Tt and Pt fragments, vectors).  Issued while the previous chunk
-// computes, committed to LDS at the top of the chunk.
-template <bool F32> struct Stage;
-template <> struct Stage<false> {      // bf16 rows
-  u32x4_t k0, k1, q[2], v, f[4];
-  float vec;
-};
-template <> struct Stage<true> {       // fp32 rows
-  u32x4_t k[4], q[4], v, f[4];
-  float vec;
+// record (Tt and Pt fragments and vectors; per-key-channel decay: rk, rq and
+// the chunk's log decays g instead of the fragments, which each wave then
+// loads itself).  Issued while the previous chunk computes, committed to LDS
+// at the top of the chunk.
+template <bool F32, bool kPC> struct Stage {
+  u32x4_t k[F32 ? 4 : 2], q[F32 ? 4 : 2], v, f[kPC ? 1 : 4];
+  float vec, gv[kPC ? 16 : 1];
 };
 
-template <bool F32, typename Tin>
-__device__ __forceinline__ void stage_issue(Stage<F32>& sg, const Tin* k, const Tin* q, int64_t qk_stride,
-                                            const Tin* v, int64_t v_stride, const uint8_t* rec, int L) {
+template <bool F32, bool kPC, typename Tin>
+__device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, const Tin* q, int64_t qk_stride,
+                                            const Tin* v, int64_t v_stride, const float* g, int hv,
+                                            const uint8_t* rec, int L) {
   const int tid = threadIdx.x;
   const u32x4_t z = {0u, 0u, 0u, 0u};
   auto row16 = [&](const Tin* base, int64_t stride, int t, int col) -> u32x4_t {
@@ -486,8 +678,8 @@ __device__ __forceinline__ void stage_issue(Stage<F32>& sg, const Tin* k, const 
   } else {
     {
       const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));   // row pair x 8 columns
-      sg.k0 = row16(k, qk_stride, t, j0);
-      sg.k1 = row16(k, qk_stride, t + 1, j0);
+      sg.k[0] = row16(k, qk_stride, t, j0);
+      sg.k[1] = row16(k, qk_stride, t + 1, j0);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -496,15 +688,24 @@ __device__ __forceinline__ void stage_issue(Stage<F32>& sg, const Tin* k, const 
     }
     sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
   }
+  if constexpr (kPC) {
+    // channel tid/4, rows 16 (tid%4) .. +15 of the chunk
+    const int ch = tid / 4, r0 = 16 * (tid % 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) sg.f[i] = reinterpret_cast<const u32x4_t*>(rec)[tid + i * kSpineThreads];
-  sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+    for (int r = 0; r < 16; ++r) sg.gv[r] = r0 + r < L ? g[((int64_t)(r0 + r) * hv) * kD + ch] : 0.0f;
+    sg.vec = tid < 2 * kC ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sg.f[i] = reinterpret_cast<const u32x4_t*>(rec)[tid + i * kSpineThreads];
+    sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+  }
 }
 
-template <bool F32>
-__device__ __forceinline__ void stage_commit(const Stage<F32>& sg, typename Ops<F32>::E* sK,
+template <bool F32, bool kPC>
+__device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename Ops<F32>::E* sK,
                                              typename Ops<F32>::E* sKt, typename Ops<F32>::E* sQ, int pitch,
-                                             int tpitch, float* sV, int vpitch, uint8_t* sF, float* s_vec) {
+                                             int tpitch, float* sV, int vpitch, uint8_t* sF, float* sGam,
+                                             int gpitch, float* s_vec) {
   const int tid = threadIdx.x;
   if constexpr (F32) {
 #pragma unroll
@@ -519,15 +720,15 @@ __device__ __forceinline__ void stage_commit(const Stage<F32>& sg, typename Ops<
   } else {
     {
       const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
-      *reinterpret_cast<u32x4_t*>(sK + t * pitch + j0) = sg.k0;
-      *reinterpret_cast<u32x4_t*>(sK + (t + 1) * pitch + j0) = sg.k1;
+      *reinterpret_cast<u32x4_t*>(sK + t * pitch + j0) = sg.k[0];
+      *reinterpret_cast<u32x4_t*>(sK + (t + 1) * pitch + j0) = sg.k[1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // columns j0+2e (low halves) and j0+2e+1 (high halves) of rows t, t+1
         *reinterpret_cast<uint32_t*>(sKt + (j0 + 2 * e) * tpitch + t) =
-            __builtin_amdgcn_perm(sg.k1[e], sg.k0[e], 0x05040100u);
+            __builtin_amdgcn_perm(sg.k[1][e], sg.k[0][e], 0x05040100u);
         *reinterpret_cast<uint32_t*>(sKt + (j0 + 2 * e + 1) * tpitch + t) =
-            __builtin_amdgcn_perm(sg.k1[e], sg.k0[e], 0x07060302u);
+            __builtin_amdgcn_perm(sg.k[1][e], sg.k[0][e], 0x07060302u);
       }
     }
 #pragma unroll
@@ -544,23 +745,44 @@ __device__ __forceinline__ void stage_commit(const Stage<F32>& sg, typename Ops<
       }
     }
   }
+  if constexpr (kPC) {
+    // cumulative log decay per channel: prefix over this thread's 16 rows, then
+    // over the four row blocks of the channel (adjacent lanes)
+    const int ch = tid / 4, part = tid % 4;
+    float run[16];
+    run[0] = sg.gv[0];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4_t*>(sF)[tid + i * kSpineThreads] = sg.f[i];
-  if (tid < 3 * kC + 1) s_vec[tid] = sg.vec;
+    for (int r = 1; r < 16; ++r) run[r] = run[r - 1] + sg.gv[r];
+    float incl = run[15];
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) {
+      const float up = __shfl_up(incl, o, 4);
+      if (part >= o) incl += up;
+    }
+    const float excl = incl - run[15];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sGam[(16 * part + r) * gpitch + ch] = run[r] + excl;
+    if (tid < 2 * kC) s_vec[tid] = sg.vec;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4_t*>(sF)[tid + i * kSpineThreads] = sg.f[i];
+    if (tid < 3 * kC + 1) s_vec[tid] = sg.vec;
+  }
 }
 
-template <bool F32, typename Tin, typename To>
+template <bool F32, bool kPC, typename Tin, typename To>
 __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
-    const Tin* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
-    const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
-    To* __restrict__ out, float* final_state) {
+    const Tin* __restrict__ v, int64_t v_stride, const float* __restrict__ g,
+    const float* __restrict__ init_state, const int32_t* __restrict__ cu, int n_seq, int hk, int hv,
+    const uint8_t* __restrict__ ws, To* __restrict__ out, float* final_state) {
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
   constexpr int kPitch = kD + O::kPadK;          // K, Q and state rows
   constexpr int kTP = kC + O::kPadK;             // transposed [i][t] tiles
   constexpr int kVP = kTile + 1;                 // fp32 V tile pitch
+  constexpr int kGP = kD + 4;                    // per-channel log decay pitch
   __shared__ __attribute__((aligned(16))) E sK[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sQ[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sKt[F32 ? 1 : kD * kTP];
@@ -572,8 +794,9 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sRh[kTile * kTP], sRl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
-  __shared__ __attribute__((aligned(16))) uint8_t sF[2 * kFragBytes];   // Tt | Pt fragments
-  __shared__ float s_vec[3 * kC + 4];
+  __shared__ __attribute__((aligned(16))) uint8_t sF[kPC ? 16 : 2 * kFragBytes];   // Tt | Pt fragments
+  __shared__ __attribute__((aligned(16))) float sGam[kPC ? kC * kGP : 1];
+  __shared__ __attribute__((aligned(16))) float s_vec[3 * kC + 4];
 
   // Block -> (sequence, key head) group and member (value head of the group,
   // dv tile).  All members of a group share the key head's K/Q tiles, so they
@@ -608,6 +831,39 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   const int nks = F32 ? 4 * (mt + 1) : 1 + (mt >> 1);   // k steps up to the diagonal
   constexpr int kMaxKs = F32 ? 16 : 2;
 
+  // per-key-channel decay: each wave keeps its row tile of Tt / Pt in registers
+  // (loaded one chunk ahead) instead of staging the record in LDS
+  [[maybe_unused]] F th[kPC ? kMaxKs : 1], tl[kPC ? kMaxKs : 1], ph[kPC ? kMaxKs : 1], pl[kPC ? kMaxKs : 1];
+  auto load_row_frags = [&](const uint8_t* src, F* fh, F* fl) {
+#pragma unroll
+    for (int ks = 0; ks < kMaxKs; ++ks) {
+      if (ks < nks) {
+        if constexpr (F32) {
+          fh[ks] = reinterpret_cast<const float*>(src)[(mt * 16 + ks) * kWave + lane];
+        } else {
+          const int f = mt * 2 + ks;
+          fh[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
+          fl[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
+        }
+      }
+    }
+  };
+  // fragment of Tt (which = 0) or Pt (1), row tile mt, k step ks
+  auto tri_frag = [&](int which, int ks, F& fh, F& fl) {
+    if constexpr (kPC) {
+      fh = which == 0 ? th[ks] : ph[ks];
+      fl = which == 0 ? tl[ks] : pl[ks];
+    } else if constexpr (F32) {
+      fh = reinterpret_cast<const float*>(sF + which * kFragBytes)[(mt * 16 + ks) * kWave + lane];
+      fl = 0.0f;
+    } else {
+      const int f = mt * 2 + ks;
+      const uint8_t* base = sF + which * kFragBytes;
+      fh = load_bf16x8(reinterpret_cast<const uint16_t*>(base + ((f * 2 + 0) * kWave + lane) * 16));
+      fl = load_bf16x8(reinterpret_cast<const uint16_t*>(base + ((f * 2 + 1) * kWave + lane) * 16));
+    }
+  };
+
   f32x4_t sacc[2];
   auto store_state_lds = [&]() {
 #pragma unroll
@@ -641,97 +897,110 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     store_state_lds();
   }
 
-  Stage<F32> stage;
+  Stage<F32, kPC> stage;
   auto issue = [&](int t0c, int cidx) {
-    stage_issue<F32>(stage, k + (int64_t)t0c * qk_stride + kh * kD, q + (int64_t)t0c * qk_stride + kh * kD,
-                     qk_stride, v + (int64_t)t0c * v_stride + h * kD + i0, v_stride, rec_of(cidx),
-                     min(kC, seq_end - t0c));
+    stage_issue<F32, kPC>(stage, k + (int64_t)t0c * qk_stride + kh * kD, q + (int64_t)t0c * qk_stride + kh * kD,
+                          qk_stride, v + (int64_t)t0c * v_stride + h * kD + i0, v_stride,
+                          kPC ? g + ((int64_t)t0c * hv + h) * kD : nullptr, hv, rec_of(cidx),
+                          min(kC, seq_end - t0c));
   };
-  if (seq_beg < seq_end) issue(seq_beg, chunk0);
+  if (seq_beg < seq_end) {
+    issue(seq_beg, chunk0);
+    if constexpr (kPC) {
+      load_row_frags(rec_of(chunk0), th, tl);
+      load_row_frags(rec_of(chunk0) + kFragBytes, ph, pl);
+    }
+  }
 
   for (int t0 = seq_beg, c = chunk0; t0 < seq_end; t0 += kC, ++c) {
     const int L = min(kC, seq_end - t0);
+    const bool more = t0 + kC < seq_end;
     __syncthreads();   // the previous chunk is done with every LDS tile
-    stage_commit<F32>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sF, s_vec);
-    if (t0 + kC < seq_end) issue(t0 + kC, c + 1);
+    stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sF, sGam, kGP, s_vec);
+    if (more) issue(t0 + kC, c + 1);
     __syncthreads();
 
     // ---- Y = K S0^T and Z = Q S0^T: rows of tile mt, columns of half hf ----
+    // (per-key-channel decay: Y = (khat e^gam) S0^T, Z = (qtil e^gam) S0^T)
     f32x4_t accY = {0.f, 0.f, 0.f, 0.f}, accZ = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
+#pragma unroll 4
     for (int ks = 0; ks < kD; ks += O::kKs) {
-      const F ak = frag<F32>(sK, kPitch, 16 * mt, ks);
-      const F aq = frag<F32>(sQ, kPitch, 16 * mt, ks);
       const F bh = frag<F32>(sSh, kPitch, 16 * hf, ks);
-      accY = mma<F32>(ak, bh, accY);
-      accZ = mma<F32>(aq, bh, accZ);
-      if constexpr (!F32) {
-        const F bl = frag<F32>(sSl, kPitch, 16 * hf, ks);
-        accY = mma<F32>(ak, bl, accY);
-        accZ = mma<F32>(aq, bl, accZ);
+      F bl{};
+      if constexpr (!F32) bl = frag<F32>(sSl, kPitch, 16 * hf, ks);
+      if constexpr (kPC) {
+        F kh_, kl_, qh_, ql_;
+        decayed_frag<F32>(sK, kPitch, sGam, kGP, nullptr, s_vec, 16 * mt, ks, 1.0f, kh_, kl_);
+        decayed_frag<F32>(sQ, kPitch, sGam, kGP, nullptr, s_vec + kC, 16 * mt, ks, 1.0f, qh_, ql_);
+        accY = mma3<F32>(kh_, kl_, bh, bl, accY);
+        accZ = mma3<F32>(qh_, ql_, bh, bl, accZ);
+      } else {
+        const F ak = frag<F32>(sK, kPitch, 16 * mt, ks);
+        const F aq = frag<F32>(sQ, kPitch, 16 * mt, ks);
+        accY = mma<F32>(ak, bh, accY);
+        accZ = mma<F32>(aq, bh, accZ);
+        if constexpr (!F32) {
+          accY = mma<F32>(ak, bl, accY);
+          accZ = mma<F32>(aq, bl, accZ);
+        }
       }
     }
-    // R = V - a_t Y, stored transposed [i][t] as hi/lo
+    // R = V - a_t Y (per-key-channel decay: R = V - Y), stored transposed [i][t] as hi/lo
     {
       f32x4_t rv;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * mt + 4 * (lane >> 4) + e;
-        rv[e] = sV[t * kVP + 16 * hf + (lane & 15)] - s_vec[t] * accY[e];
+        rv[e] = sV[t * kVP + 16 * hf + (lane & 15)] - (kPC ? 1.0f : s_vec[t]) * accY[e];
       }
       store_acc_transposed<F32>(sRh, sRl, kTP, 16 * hf, 16 * mt, rv);
     }
     __syncthreads();
 
-    // ---- Vnew = Tt R (row tile mt, half hf); W = c_t Vnew ----
+    // ---- Vnew = Tt R (row tile mt, half hf); W = c_t Vnew (per-key-channel: W = Vnew) ----
     {
       f32x4_t vn = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kMaxKs; ++ks) {
         if (ks < nks) {
+          F th_, tl_, bl{};
+          tri_frag(0, ks, th_, tl_);
           const F bh = frag<F32>(sRh, kTP, 16 * hf, ks * O::kKs);
-          if constexpr (F32) {
-            vn = mma<F32>(reinterpret_cast<const float*>(sF)[(mt * 16 + ks) * kWave + lane], bh, vn);
-          } else {
-            const int f = mt * 2 + ks;
-            const F th = load_bf16x8(reinterpret_cast<const uint16_t*>(sF + ((f * 2 + 0) * kWave + lane) * 16));
-            const F tl = load_bf16x8(reinterpret_cast<const uint16_t*>(sF + ((f * 2 + 1) * kWave + lane) * 16));
-            const F bl = frag<F32>(sRl, kTP, 16 * hf, ks * O::kKs);
-            vn = mma<F32>(th, bh, vn);
-            vn = mma<F32>(th, bl, vn);
-            vn = mma<F32>(tl, bh, vn);
-          }
+          if constexpr (!F32) bl = frag<F32>(sRl, kTP, 16 * hf, ks * O::kKs);
+          vn = mma3<F32>(th_, tl_, bh, bl, vn);
         }
       }
       store_acc_transposed<F32>(sNh, sNl, kTP, 16 * hf, 16 * mt, vn);
-      f32x4_t w;
+      if constexpr (kPC) {
+        store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, vn);
+        if (more) load_row_frags(rec_of(c + 1), th, tl);   // next chunk's Tt rows
+      } else {
+        f32x4_t w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[e];
-      store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, w);
+        for (int e = 0; e < 4; ++e) w[e] = s_vec[2 * kC + 16 * mt + 4 * (lane >> 4) + e] * vn[e];
+        store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, w);
+      }
     }
     __syncthreads();
 
     // ---- O = b_t Z + Pt Vnew (row tile mt, half hf) ----
     {
+      if constexpr (!kPC) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) accZ[e] *= s_vec[kC + 16 * mt + 4 * (lane >> 4) + e];
-      const uint8_t* pf = sF + kFragBytes;
+        for (int e = 0; e < 4; ++e) accZ[e] *= s_vec[kC + 16 * mt + 4 * (lane >> 4) + e];
+      }
 #pragma unroll
       for (int ks = 0; ks < kMaxKs; ++ks) {
         if (ks < nks) {
+          F ph_, pl_, bl{};
+          tri_frag(1, ks, ph_, pl_);
           const F bh = frag<F32>(sNh, kTP, 16 * hf, ks * O::kKs);
-          if constexpr (F32) {
-            accZ = mma<F32>(reinterpret_cast<const float*>(pf)[(mt * 16 + ks) * kWave + lane], bh, accZ);
-          } else {
-            const int f = mt * 2 + ks;
-            const F ph = load_bf16x8(reinterpret_cast<const uint16_t*>(pf + ((f * 2 + 0) * kWave + lane) * 16));
-            const F pl = load_bf16x8(reinterpret_cast<const uint16_t*>(pf + ((f * 2 + 1) * kWave + lane) * 16));
-            const F bl = frag<F32>(sNl, kTP, 16 * hf, ks * O::kKs);
-            accZ = mma<F32>(ph, bh, accZ);
-            accZ = mma<F32>(ph, bl, accZ);
-            accZ = mma<F32>(pl, bh, accZ);
-          }
+          if constexpr (!F32) bl = frag<F32>(sNl, kTP, 16 * hf, ks * O::kKs);
+          accZ = mma3<F32>(ph_, pl_, bh, bl, accZ);
         }
+      }
+      if constexpr (kPC) {
+        if (more) load_row_frags(rec_of(c + 1) + kFragBytes, ph, pl);   // next chunk's Pt rows
       }
       To* orow = out + ((int64_t)t0 * hv + h) * kD + i0 + 16 * hf + (lane & 15);
 #pragma unroll
@@ -742,24 +1011,57 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     }
 
     // ---- S^T <- d S^T + K^T W on this wave's two tiles, then its LDS copy ----
+    // (per-key-channel decay: column j decays by e^{gam_L[j]} and the key rows
+    //  enter as khat_t e^{gam_L - gam_t})
     {
-      const float d = s_vec[3 * kC];
+      if constexpr (kPC) {
 #pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
+        for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[q2][e] *= d;
+          for (int e = 0; e < 4; ++e)
+            sacc[q2][e] *= __expf(sGam[(L - 1) * kGP + 16 * (nj0 + q2) + 4 * (lane >> 4) + e]);
+      } else {
+        const float d = s_vec[3 * kC];
 #pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[q2][e] *= d;
+      }
+#pragma unroll 2
       for (int ks = 0; ks < kC; ks += O::kKs) {
         const F bh = frag<F32>(sWh, kTP, si, ks);
-        F bl;
+        F bl{};
         if constexpr (!F32) bl = frag<F32>(sWl, kTP, si, ks);
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
-          F a;
-          if constexpr (F32) a = sK[(ks + (lane >> 4)) * kPitch + 16 * (nj0 + q2) + (lane & 15)];
-          else a = frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks);
-          sacc[q2] = mma<F32>(a, bh, sacc[q2]);
-          if constexpr (!F32) sacc[q2] = mma<F32>(a, bl, sacc[q2]);
+          const int j = 16 * (nj0 + q2) + (lane & 15);
+          if constexpr (kPC) {
+            // A[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam_t[j]}, t = ks + E (l/16) + e
+            F ah, al;
+            const int tb = ks + O::kEpl * (lane >> 4);
+            const float gl = sGam[(L - 1) * kGP + j];
+            if constexpr (F32) {
+              ah = sK[tb * kPitch + j] * s_vec[tb] * __expf(gl - sGam[tb * kGP + j]);
+              al = 0.0f;
+            } else {
+              const u32x4_t u = *reinterpret_cast<const u32x4_t*>(sKt + j * kTP + tb);
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float kv = (e & 1) ? __uint_as_float(u[e / 2] & 0xffff0000u) : __uint_as_float(u[e / 2] << 16);
+                __bf16 a_, b_;
+                split_bf16(kv * s_vec[tb + e] * __expf(gl - sGam[(tb + e) * kGP + j]), a_, b_);
+                ah[e] = a_;
+                al[e] = b_;
+              }
+            }
+            sacc[q2] = mma3<F32>(ah, al, bh, bl, sacc[q2]);
+          } else {
+            F a;
+            if constexpr (F32) a = sK[(ks + (lane >> 4)) * kPitch + j];
+            else a = frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks);
+            sacc[q2] = mma<F32>(a, bh, sacc[q2]);
+            if constexpr (!F32) sacc[q2] = mma<F32>(a, bl, sacc[q2]);
+          }
         }
       }
       // every wave's product 1 read the old copy before the Vnew barrier
@@ -774,7 +1076,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   }
 }
 
-template <bool F32, typename Tin, typename To>
+template <bool F32, bool kPC, typename Tin, typename To>
 hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_stride, const void* v,
                       int64_t v_stride, const float* g, const float* beta, const float* init_state,
                       const int32_t* cu_dev, int n, int total_chunks, void* out,
@@ -785,20 +1087,37 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (total_chunks > 0) {
-    hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
-                       static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
-                       cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
+    if constexpr (kPC)
+      hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
+                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
+                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
+    else
+      hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
+                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
+                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int groups = n * d.hk;
   const int members = (d.hv / d.hk) * (kD / kTile);
   const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-  hipLaunchKernelGGL((chunk_spine_kernel<F32, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
+  hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
                      static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride,
-                     static_cast<const Tin*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
+                     static_cast<const Tin*>(v), v_stride, g, init_state, cu_dev, n, d.hk, d.hv, w,
                      static_cast<To*>(out), final_state);
   return hipGetLastError();
+}
+
+template <bool kPC>
+hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+                          int64_t qk_stride, const void* v, int64_t v_stride, const float* g,
+                          const float* beta, const float* init_state, const int32_t* cu_dev, int n,
+                          int total, void* out, float* final_state, void* ws, hipStream_t s) {
+  if (in_bf16)
+    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
+                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
+  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
+                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
 }
 
 }  // namespace
@@ -819,11 +1138,9 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
   if (n == 0) return hipSuccess;
   int total = 0;
   for (int i = 0; i < n; ++i) total += (cu_host[i + 1] - cu_host[i] + kC - 1) / kC;
-  if (in_bf16)
-    return out_bf16 ? chunk_impl<false, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
-                    : chunk_impl<false, uint16_t, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
-  return out_bf16 ? chunk_impl<true, float, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
-                  : chunk_impl<true, float, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
+  return d.per_channel
+             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
+             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
 }
 
 }  // namespace gdn

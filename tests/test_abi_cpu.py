@@ -129,7 +129,7 @@ def test_chunk_prefill_argument_checks(lib):
     assert call() == gdn.GDN_ERR_WORKSPACE                                  # zero-size workspace
     assert call(ws=None, wsb=1 << 30) == gdn.GDN_ERR_WORKSPACE
     assert call(qks=100) == gdn.GDN_ERR_INVALID_ARG
-    assert call(cfg=_cfg(decay_per_key_channel=1)) == gdn.GDN_ERR_UNSUPPORTED
+    assert call(cfg=_cfg(decay_per_key_channel=1)) == gdn.GDN_ERR_WORKSPACE     # supported; workspace checked
 
 
 def test_decode_and_norm_argument_checks(lib):

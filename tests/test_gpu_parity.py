@@ -368,3 +368,79 @@ def test_negative_controls(orc, tmp_path):
     bad = orc.gated_rmsnorm(np.concatenate([o_a, o_b]), d["z"], d["norm_w"])
     assert worst_ratio(out[:64], bad[:64], TOL_BF16) <= 1.0, "dropped-carry control: head must match"
     assert worst_ratio(out[64:], bad[64:], TOL_BF16) >= 10, "dropped-carry control did not fail"
+
+
+# ---------------------------------------------------------------------------
+# per-key-channel decay (g [T, Hv, dk])
+# ---------------------------------------------------------------------------
+
+def _run_chunk(d, cfg, bf16=True, out_dtype=torch.float32):
+    return gdn.chunk_prefill(dev(d["q"], bf16), dev(d["k"], bf16), dev(d["v"], bf16), dev(d["g"]),
+                             dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                             initial_state=None if d["state_in"] is None else dev(d["state_in"]),
+                             out_dtype=out_dtype, cfg=cfg)
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 129])
+@pytest.mark.parametrize("hk,hv", [(16, 48), (4, 4)], ids=["ratio3", "ratio1"])
+def test_chunk_prefill_per_channel_bf16(orc, T, hk, hv):
+    geo = gi.Geometry(hk=hk, hv=hv)
+    d = gi.gen_qkv(300 + T, [T], geo, per_channel=True)
+    cfg = gdn.config(num_k_heads=hk, num_v_heads=hv, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"per-channel out T={T} {hk}/{hv}")
+    check(host(fs), s_ref, TOL_BF16, f"per-channel state T={T} {hk}/{hv}")
+
+
+@pytest.mark.parametrize("T", [65, 130])
+def test_chunk_prefill_per_channel_fp32(orc, T):
+    geo = gi.Geometry(hk=2, hv=6)
+    d = gi.gen_qkv(400 + T, [T], geo, bf16=False, per_channel=True)
+    cfg = gdn.config(num_k_heads=2, num_v_heads=6, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg, bf16=False)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_F32, f"per-channel fp32 out T={T}")
+    check(host(fs), s_ref, TOL_F32, f"per-channel fp32 state T={T}")
+
+
+def test_chunk_prefill_per_channel_varlen(orc):
+    geo = gi.Geometry(hk=4, hv=8)
+    d = gi.gen_qkv(450, [70, 0, 1, 64, 200], geo, per_channel=True)
+    cfg = gdn.config(num_k_heads=4, num_v_heads=8, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "per-channel varlen out", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, "per-channel varlen state")
+
+
+def test_per_channel_with_equal_channels_matches_scalar_decay():
+    """A per-key-channel decay equal across channels runs the same recurrence as the
+    scalar-decay path: the two GPU paths agree to the tolerance."""
+    d = gi.gen_qkv(460, [150])
+    o1, s1 = _run_chunk(d, gdn.config())
+    dc = dict(d)
+    dc["g"] = np.repeat(d["g"][:, :, None], gi.DK, axis=2)
+    o2, s2 = _run_chunk(dc, gdn.config(decay_per_key_channel=1))
+    torch.cuda.synchronize()
+    check(host(o2), host(o1), TOL_BF16, "per-channel == scalar out")
+    check(host(s2), host(s1), TOL_BF16, "per-channel == scalar state")
+
+
+def test_kda_h64_s16384_full_size_sampled(orc):
+    """The long-context per-key-channel workload: 64 heads (no repeat), 16384 tokens, bf16,
+    random initial state; heads 0, 31 and 63 compared with the token-by-token oracle."""
+    geo = gi.Geometry(hk=64, hv=64)
+    d = gi.gen_qkv(1005, [16384], geo, per_channel=True)
+    cfg = gdn.config(num_k_heads=64, num_v_heads=64, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg)
+    torch.cuda.synchronize()
+    heads = [0, 31, 63]
+    o_ref, s_ref = orc.delta_rule(d["q"][:, heads], d["k"][:, heads], d["v"][:, heads], d["g"][:, heads],
+                                  d["beta"][:, heads], d["cu"], d["state_in"][:, heads])
+    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 out (3 heads)")
+    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 state (3 heads)")
+    assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
