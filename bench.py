@@ -1,20 +1,25 @@
 """Benchmark of the GDN sublayer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|decode|prefill|varlen|kda]
+                    [--no-cpu-baseline] [--calibration-copy]
 
-Headline (``value``): the fused decode step of 64 sequences x 1 token, bf16
-activations, fp32 state [64, 48, 128, 128] updated in place -> state-updates/s
-(one update = one sequence-token across all 48 value heads).  Three state sets
-(604 MB) are rotated so the 201 MB state never sits in the 256 MB Infinity
-Cache between steps.
+Headline (``value``, ``ms_per_step``, ``roofline``): the fused decode step of
+64 sequences x 1 token (bf16 activations, fp32 state [64, 48, 128, 128]
+updated in place) in state-updates/s; one update = one sequence-token across
+all 48 value heads.  Three state sets (604 MB) rotate so the 201 MB state
+never sits in the 256 MB Infinity Cache between steps.
 
-Also measured in the same run and reported under ``prefill``: the 4096-token
-prefill (conv -> chunk-wise delta rule -> gated norm, bf16 inputs, random fp32
-initial state) in tokens/s.
+Also measured in the same run (``workloads``):
+  prefill_s4096_bf16  one 4096-token sequence, conv -> chunk -> gated norm, random initial state
+  varlen8_33k_bf16    8 packed sequences (63, 64, 65 + five lengths up to 8192), same pipeline
+  kda_h64_s16384_bf16 per-key-channel decay, 64 heads, 16384 tokens, the chunk call alone
+each in tokens/s with its whole-path roofline fraction (algorithmic HBM bytes / time / 8 TB/s).
 
-Every timed launch is a library call on torch's current stream, timed with
-events on that stream.  ``cpu_baseline`` runs the fp64 oracle (test
-infrastructure) on the host cores over a bounded sample of the same workload.
+Every launch is a library call on torch's current stream (the stream the
+library enqueues on), timed with events on that stream.  ``cpu_baseline``
+runs the fp64 oracle (test infrastructure) on the host cores over a bounded
+sample of the same workload.  ``--calibration-copy`` only runs 256 MiB device
+copies (the known-size reference for the HBM traffic counters).
 """
 from __future__ import annotations
 
@@ -34,17 +39,20 @@ import gated_deltanet_causal_amd as gdn  # noqa: E402
 import gdn_inputs as gi  # noqa: E402
 
 HK, HV, D = gi.HK, gi.HV, gi.DK
+CC = gi.conv_channels()
 PEAK_HBM_GBS = 8000.0
 METRIC = "GDN prefill tokens/s + decode state-updates/s; % MFMA / HBM roofline"
+STATE_BYTES = HV * D * D * 4          # one sequence's fp32 state, 48 heads
 
-# Algorithmic bytes of one decode sequence-update (each input / output moved once):
-# state read + write, conv state read + write, x, z, g, beta, out.
-DECODE_BYTES_PER_UPDATE = (2 * HV * D * D * 4 + 2 * 3 * gi.conv_channels() * 2 + gi.conv_channels() * 2
-                           + HV * D * 2 + 2 * HV * 4 + HV * D * 2)
-# Algorithmic bytes of one prefill token through conv -> chunk -> norm, fused minimum:
-# x, z, g, beta in; out (bf16) out.  The 2 x 3 MiB per-sequence state is added per call.
-PREFILL_BYTES_PER_TOKEN = gi.conv_channels() * 2 + HV * D * 2 + 2 * HV * 4 + HV * D * 2
-STATE_BYTES = HV * D * D * 4
+# Algorithmic bytes (each input / output moved once):
+# decode, per sequence-update: state read + write, conv state read + write, x, z, g, beta, out
+DECODE_BYTES_PER_UPDATE = 2 * STATE_BYTES + 2 * 3 * CC * 2 + CC * 2 + HV * D * 2 + 2 * HV * 4 + HV * D * 2
+# prefill pipeline, per token: x, z, g, beta in; gated output out (bf16); plus 2 states per sequence
+PREFILL_BYTES_PER_TOKEN = CC * 2 + HV * D * 2 + 2 * HV * 4 + HV * D * 2
+# per-key-channel chunk call, 64 heads, per token: q, k, v, g [64,128] fp32, beta, out (bf16)
+KDA_H = 64
+KDA_BYTES_PER_TOKEN = 3 * KDA_H * D * 2 + KDA_H * D * 4 + KDA_H * 4 + KDA_H * D * 2
+KDA_STATE_BYTES = KDA_H * D * D * 4
 
 
 def t_dev(a, bf16=False):
@@ -52,9 +60,9 @@ def t_dev(a, bf16=False):
     return x.to(torch.bfloat16) if bf16 else x
 
 
-def time_launches(fn, n_sets, steps, warmup):
+def time_calls(fn, n_sets, steps, warmup):
     """Run fn(i) warmup + steps times; time the steps with events on the current stream.
-    Returns (total_ms, per-launch ms list)."""
+    Returns (mean ms, per-step ms list)."""
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
@@ -65,8 +73,28 @@ def time_launches(fn, n_sets, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[-1]), per
+    return evs[0].elapsed_time(evs[-1]) / steps, per
 
+
+# HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
+# copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
+DECODE_TRAFFIC_BYTES = 207.8e6 + 206.3e6
+PREFILL_S4096_TRAFFIC_BYTES = 474.5e6 + 341.1e6
+
+
+def roofline(bytes_alg, ms, traffic=None):
+    achieved = bytes_alg / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
+
+
+def oracle_threads():
+    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
 
 def bench_decode(steps, warmup, batch=64):
     d = gi.gen_decode(1002, batch)
@@ -81,51 +109,9 @@ def bench_decode(steps, warmup, batch=64):
     def step(i):
         gdn.decode_step(x, w, convs[i], g, beta, z, nw, states[i], out=out, cfg=cfg)
 
-    total_ms, per = time_launches(step, n_sets, steps, warmup)
-    ms = total_ms / steps
-    achieved = DECODE_BYTES_PER_UPDATE * batch / (ms * 1e-3) / 1e9
-    return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3), achieved_gbs=achieved)
-
-
-def bench_prefill(steps, warmup, T=4096):
-    d = gi.gen_prefill(1003, [T], bf16=True, init_state=True)
-    cfg = gdn.config()
-    cu_np = d["cu"]
-    cu = torch.from_numpy(cu_np).cuda()
-    x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
-                            t_dev(d["z"], True), t_dev(d["norm_w"]))
-    s_in = t_dev(d["state_in"])
-    s_out = torch.empty_like(s_in)
-    y = torch.empty((T, gi.conv_channels()), dtype=torch.bfloat16, device="cuda")
-    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
-    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
-    ws = torch.empty(gdn.chunk_prefill_workspace_size(1, T, cfg), dtype=torch.uint8, device="cuda")
-    marks = {}
-
-    def step(_):
-        gdn.conv1d_prefill(x, w, cu, cu_host=cu_np, y=y, cfg=cfg)
-        gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], g, beta, cu,
-                          cu_host=cu_np, initial_state=s_in, out=o, final_state=s_out, workspace=ws, cfg=cfg)
-        gdn.gated_rmsnorm(o, z, nw, out=out, cfg=cfg)
-
-    total_ms, per = time_launches(step, 1, steps, warmup)
-    ms = total_ms / steps
-    # one instrumented pass: time of each library call
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    evs[0].record()
-    gdn.conv1d_prefill(x, w, cu, cu_host=cu_np, y=y, cfg=cfg)
-    evs[1].record()
-    gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], g, beta, cu,
-                      cu_host=cu_np, initial_state=s_in, out=o, final_state=s_out, workspace=ws, cfg=cfg)
-    evs[2].record()
-    gdn.gated_rmsnorm(o, z, nw, out=out, cfg=cfg)
-    evs[3].record()
-    torch.cuda.synchronize()
-    marks = dict(conv_ms=evs[0].elapsed_time(evs[1]), chunk_ms=evs[1].elapsed_time(evs[2]),
-                 norm_ms=evs[2].elapsed_time(evs[3]))
-    bytes_alg = PREFILL_BYTES_PER_TOKEN * T + 2 * STATE_BYTES
-    return dict(ms=ms, per=per, tokens_per_s=T / (ms * 1e-3), achieved_gbs=bytes_alg / (ms * 1e-3) / 1e9,
-                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, **marks)
+    ms, per = time_calls(step, n_sets, steps, warmup)
+    return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3),
+                roofline=roofline(DECODE_BYTES_PER_UPDATE * batch, ms, DECODE_TRAFFIC_BYTES))
 
 
 def cpu_baseline_decode(target_s=10.0):
@@ -139,24 +125,137 @@ def cpu_baseline_decode(target_s=10.0):
                                        Hk=HK, Hv=HV, dk=D, dv=D)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= target_s or reps >= 200:
+        if el >= target_s or reps >= 400:
             break
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=64 * reps / el, unit="state-updates/s", cores=threads, kind="oracle",
-                sample=f"{reps} decode steps of the 64-sequence batch, fp64, {el:.1f} s")
+    return dict(value=64 * reps / el, unit="state-updates/s", cores=oracle_threads(), kind="oracle",
+                sample=f"{reps} fused decode steps of the 64-sequence batch, fp64, {el:.1f} s")
 
 
-def cpu_baseline_prefill(tokens=512):
+# ---------------------------------------------------------------------------
+# prefill pipelines (conv -> chunk -> gated norm)
+# ---------------------------------------------------------------------------
+
+def bench_pipeline(lengths, seed, steps, warmup):
+    d = gi.gen_prefill(seed, lengths, bf16=True, init_state=True)
+    cfg = gdn.config()
+    T, N = int(sum(lengths)), len(lengths)
+    cu_np = d["cu"]
+    cu = torch.from_numpy(cu_np).cuda()
+    x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
+                            t_dev(d["z"], True), t_dev(d["norm_w"]))
+    s_in = t_dev(d["state_in"])
+    s_out = torch.empty_like(s_in)
+    y = torch.empty((T, CC), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.chunk_prefill_workspace_size(N, T, cfg), dtype=torch.uint8, device="cuda")
+
+    def conv():
+        gdn.conv1d_prefill(x, w, cu, cu_host=cu_np, y=y, cfg=cfg)
+
+    def chunk():
+        gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], g, beta, cu,
+                          cu_host=cu_np, initial_state=s_in, out=o, final_state=s_out, workspace=ws, cfg=cfg)
+
+    def norm():
+        gdn.gated_rmsnorm(o, z, nw, out=out, cfg=cfg)
+
+    def step(_):
+        conv()
+        chunk()
+        norm()
+
+    ms, per = time_calls(step, 1, steps, warmup)
+    # per-call split over a few instrumented passes
+    split = {"conv_ms": 0.0, "chunk_ms": 0.0, "norm_ms": 0.0}
+    reps = 3
+    for _ in range(reps):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        evs[0].record()
+        conv()
+        evs[1].record()
+        chunk()
+        evs[2].record()
+        norm()
+        evs[3].record()
+        torch.cuda.synchronize()
+        for i, key in enumerate(split):
+            split[key] += evs[i].elapsed_time(evs[i + 1]) / reps
+    bytes_alg = PREFILL_BYTES_PER_TOKEN * T + 2 * STATE_BYTES * N
+    traffic = PREFILL_S4096_TRAFFIC_BYTES if lengths == [4096] else None
+    return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, traffic),
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, **split)
+
+
+def cpu_baseline_pipeline(lengths, seed, max_tokens):
+    """The oracle over the first sequences of the workload, up to max_tokens tokens."""
     import oracle
     orc = oracle.Oracle()
-    d = gi.gen_prefill(1003, [tokens], bf16=True, init_state=True)
+    take, total = [], 0
+    for n in lengths:
+        if total + n > max_tokens:
+            take.append(max_tokens - total)
+            break
+        take.append(n)
+        total += n
+    take = [n for n in take if n > 0]
+    d = gi.gen_prefill(seed, take, bf16=True, init_state=True)
     t0 = time.perf_counter()
     orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"], Hk=HK, Hv=HV, dk=D, dv=D,
                 state_in=d["state_in"], round_y_bf16=True)
     el = time.perf_counter() - t0
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return dict(value=tokens / el, unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"first {tokens} tokens of the 4096-token prefill, all 48 heads, fp64, {el:.1f} s")
+    T = int(sum(take))
+    return dict(value=T / el, unit="tokens/s", cores=oracle_threads(), kind="oracle",
+                sample=f"{T} tokens (sequence lengths {take}) of the workload, all 48 heads, fp64, {el:.1f} s")
+
+
+# ---------------------------------------------------------------------------
+# per-key-channel decay, chunk call alone
+# ---------------------------------------------------------------------------
+
+def bench_kda(steps, warmup, T=16384):
+    geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
+    d = gi.gen_qkv(1005, [T], geo, per_channel=True)
+    cfg = gdn.config(num_k_heads=KDA_H, num_v_heads=KDA_H, decay_per_key_channel=1)
+    cu_np = d["cu"]
+    cu = torch.from_numpy(cu_np).cuda()
+    q, k, v = t_dev(d["q"], True), t_dev(d["k"], True), t_dev(d["v"], True)
+    g, beta, s_in = t_dev(d["g"]), t_dev(d["beta"]), t_dev(d["state_in"])
+    del d
+    s_out = torch.empty_like(s_in)
+    out = torch.empty((T, KDA_H, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.chunk_prefill_workspace_size(1, T, cfg), dtype=torch.uint8, device="cuda")
+
+    def step(_):
+        gdn.chunk_prefill(q, k, v, g, beta, cu, cu_host=cu_np, initial_state=s_in, out=out, final_state=s_out,
+                          workspace=ws, cfg=cfg)
+
+    ms, per = time_calls(step, 1, steps, warmup)
+    bytes_alg = KDA_BYTES_PER_TOKEN * T + 2 * KDA_STATE_BYTES
+    return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms),
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3)
+
+
+def cpu_baseline_kda(tokens=2048):
+    import oracle
+    orc = oracle.Oracle()
+    geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
+    d = gi.gen_qkv(1005, [tokens], geo, per_channel=True)
+    t0 = time.perf_counter()
+    orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    el = time.perf_counter() - t0
+    return dict(value=tokens / el, unit="tokens/s", cores=oracle_threads(), kind="oracle",
+                sample=f"first {tokens} tokens of the 16384-token per-key-channel workload, 64 heads, fp64, "
+                       f"{el:.1f} s")
+
+
+def calibration_copy(steps):
+    n = 256 * 1024 * 1024 // 4
+    a = torch.randn(n, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(steps):
+        b.copy_(a)
+    torch.cuda.synchronize()
 
 
 def main():
@@ -164,45 +263,72 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "varlen", "kda"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
               f"multi-GPU path)", file=sys.stderr)
         sys.exit(2)
-    dec = bench_decode(args.steps, args.warmup)
-    pre = bench_prefill(max(10, args.steps // 10), max(3, args.warmup // 4))
-    per = np.array(dec["per"])
-    line = {
-        "metric": METRIC,
-        "value": dec["updates_per_s"],
-        "unit": "state-updates/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": dec["ms"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "decode_b64_bf16", "batch": 64, "k_heads": HK, "v_heads": HV, "head_dim": D,
-                   "activations": "bf16", "state": "f32 [64,48,128,128] x3 rotated"},
-        "p10_ms": float(np.percentile(per, 10)),
-        "p90_ms": float(np.percentile(per, 90)),
-        "head_updates_per_s": dec["updates_per_s"] * HV,
-        "roofline": {"bound": "hbm", "achieved": dec["achieved_gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": dec["achieved_gbs"] / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "decode_step_kernel", "bytes_per_update": DECODE_BYTES_PER_UPDATE},
-        "prefill": {"workload": "prefill_s4096_bf16", "tokens_per_s": pre["tokens_per_s"], "ms": pre["ms"],
-                    "conv_ms": pre["conv_ms"], "chunk_ms": pre["chunk_ms"], "norm_ms": pre["norm_ms"],
-                    "roofline": {"bound": "hbm", "achieved": pre["achieved_gbs"], "peak": PEAK_HBM_GBS,
-                                 "unit": "GB/s", "frac": pre["achieved_gbs"] / PEAK_HBM_GBS,
-                                 "roofline_ms": pre["roofline_ms"]}},
-    }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_decode()
-        line["prefill"]["cpu_baseline"] = cpu_baseline_prefill()
+    if args.calibration_copy:
+        calibration_copy(args.steps)
+        print(json.dumps({"calibration_copy_bytes": 2 * 256 * 1024 * 1024, "copies": args.steps}))
+        return
+    wl = args.workload
+    cpu = not args.no_cpu_baseline
+    small_steps, small_warm = max(5, args.steps // 10), max(2, args.warmup // 4)
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    workloads = {}
+    if wl in ("all", "decode"):
+        dec = bench_decode(args.steps, args.warmup)
+        per = np.array(dec["per"])
+        line.update({
+            "value": dec["updates_per_s"], "unit": "state-updates/s", "ms_per_step": dec["ms"],
+            "dtype": "f32",
+            "config": {"workload": "decode_b64_bf16", "batch": 64, "k_heads": HK, "v_heads": HV, "head_dim": D,
+                       "activations": "bf16", "state": "f32 [64,48,128,128], 3 sets rotated"},
+            "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
+            "head_updates_per_s": dec["updates_per_s"] * HV,
+            "roofline": dict(dec["roofline"], kernel="decode_step_kernel (one launch per step)",
+                             bytes_per_update=DECODE_BYTES_PER_UPDATE),
+        })
+        if cpu:
+            line["cpu_baseline"] = cpu_baseline_decode()
+    if wl in ("all", "prefill"):
+        pre = bench_pipeline([4096], 1003, small_steps, small_warm)
+        workloads["prefill_s4096_bf16"] = dict(
+            metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], conv_ms=pre["conv_ms"],
+            chunk_ms=pre["chunk_ms"], norm_ms=pre["norm_ms"], roofline=pre["roofline"],
+            roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate")
+        if cpu:
+            workloads["prefill_s4096_bf16"]["cpu_baseline"] = cpu_baseline_pipeline([4096], 1003, 4096)
+    if wl in ("all", "varlen"):
+        lengths, _ = gi.varlen_lengths()
+        var = bench_pipeline(lengths, 1004, small_steps, small_warm)
+        workloads["varlen8_33k_bf16"] = dict(
+            metric="tokens/s", value=var["tokens_per_s"], ms=var["ms"], tokens=var["tokens"], lengths=lengths,
+            conv_ms=var["conv_ms"], chunk_ms=var["chunk_ms"], norm_ms=var["norm_ms"], roofline=var["roofline"],
+            roofline_ms=var["roofline_ms"])
+        if cpu:
+            workloads["varlen8_33k_bf16"]["cpu_baseline"] = cpu_baseline_pipeline(lengths, 1004, 4096)
+    if wl in ("all", "kda"):
+        kda = bench_kda(max(3, args.steps // 40), 1)
+        workloads["kda_h64_s16384_bf16"] = dict(
+            metric="tokens/s", value=kda["tokens_per_s"], ms=kda["ms"], roofline=kda["roofline"],
+            roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
+        if cpu:
+            workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
+    if wl != "decode" and "value" not in line:
+        # a single prefill-side workload was requested: it is the headline
+        name, obj = next(iter(workloads.items()))
+        line.update({"value": obj["value"], "unit": "tokens/s", "ms_per_step": obj["ms"], "dtype": "bf16",
+                     "config": {"workload": name}, "roofline": obj["roofline"]})
+        if "cpu_baseline" in obj:
+            line["cpu_baseline"] = obj["cpu_baseline"]
+    if workloads:
+        line["workloads"] = workloads
     print(json.dumps(line))
 
 

@@ -201,6 +201,7 @@ gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dty
   if (st != GDN_OK) return st;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (B < 0 || B > 65535 * 64) return GDN_ERR_INVALID_ARG;
+  if (d.hv / d.hk > 4) return GDN_ERR_UNSUPPORTED;   // one workgroup holds a key head's value heads
   if (B > 0 && (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out))
     return GDN_ERR_INVALID_ARG;
   if (B > 0 && (!aligned16(conv_w) || !aligned16(state) || (d.per_channel && !aligned16(g))))

@@ -19,29 +19,28 @@
 //     o   = S' qtil = r + u (khat . qtil)
 // so S is read once and written once.
 //
-// Work split: one workgroup per (sequence, value head), 256 threads, so a
-// 64-sequence batch is 3072 equal workgroups (three full rounds at four
-// resident workgroups per CU).  The 64 KiB state of the head is spread as
+// Work split: one workgroup per (sequence, key head) with one 256-thread group
+// per value head of that key head (768 threads for the pages' ratio of 3), so
+// a 64-sequence batch is 1024 equal workgroups (four full rounds at one per
+// CU).  The workgroup owns the key head's q/k conv channels and its value
+// heads' v channels, so each conv-state element has exactly one writer and is
+// shifted in place.  Within a group, the 64 KiB state of the head is spread as
 // 16 rows x one float4 per thread; a wavefront loads two full 512-byte rows
-// per instruction.  Each workgroup computes its key head's q/k conv outputs
-// from the OLD conv state without writing it (three value heads read the same
-// channels), and owns its value channels' conv state, which it shifts in
-// place.  A second, tiny kernel launched behind it on the same stream shifts
-// the q/k conv-state rows once all readers are done.
+// per instruction.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
 namespace gdn {
 namespace {
 
-constexpr int kDecThreads = 256;
+constexpr int kGroup = 256;             // threads per value head
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
 constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
 constexpr int kRedPitch = 33;           // padded pitch of the row-sum exchange
 
-// Conv of one channel for one token: y = act(w . (s0, s1, s2, x)).  With kShift
-// the channel's state rows become (s1, s2, x).
-template <bool kShift, typename T>
+// Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); the
+// channel's state rows become (s1, s2, x).
+template <typename T>
 __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_w, T* cs_row,
                                               int c, int cc, int act) {
   T* p = cs_row + c;
@@ -52,32 +51,32 @@ __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_
   y = fmaf(w[1], s1, y);
   y = fmaf(w[2], s2, y);
   y = fmaf(w[3], xv, y);
-  if constexpr (kShift) {
-    st(p, s1);
-    st(p + cc, s2);
-    st(p + 2 * cc, xv);
-  }
+  st(p, s1);
+  st(p + cc, s2);
+  st(p + 2 * cc, xv);
   return act ? y * sigmoidf_(y) : y;
 }
 
-template <typename T, typename To, bool kPerChannel>
-__global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
+template <typename T, typename To, bool kPerChannel, int kRatio>
+__global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
     const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
     int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
-  const int b = blockIdx.x / hv;
-  const int h = blockIdx.x % hv;
-  const int kh = h / (hv / hk);
+  const int b = blockIdx.x / hk;
+  const int kh = blockIdx.x % hk;
   const int tid = threadIdx.x;
-  const int wave = tid / kWave;
+  const int hh = tid / kGroup;            // value head within the key head
+  const int h = kh * kRatio + hh;
+  const int gt = tid % kGroup;            // thread within the value head's group
+  const int gwave = gt / kWave;
   const int lane = tid % kWave;
-  const int cg = tid % 32;          // column group: columns 4cg .. 4cg+3
-  const int rg = tid / 32;          // row group: rows rg + 8m
+  const int cg = gt % 32;                 // column group: columns 4cg .. 4cg+3
+  const int rg = gt / 32;                 // row group: rows rg + 8m
 
-  __shared__ float s_q[kD], s_k[kD], s_v[kD], s_u[kD];
-  __shared__ float s_red[2][kD][kRedPitch];
-  __shared__ float s_scal[8];
+  __shared__ float s_q[kD], s_k[kD], s_scal[4];
+  __shared__ float s_v[kRatio][kD], s_u[kRatio][kD], s_nrm[kRatio][2];
+  __shared__ float s_red[kRatio][2][kD][kRedPitch];
 
   // issue the state loads first; the conv and norms below overlap their latency.
   // The state is streamed once per step (no reuse), so its loads and stores are
@@ -90,22 +89,23 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
 
   const T* x_row = x + (int64_t)b * cc;
   T* cs_row = conv_state + (int64_t)b * 3 * cc;
-  {
+  if (tid < 2 * kD) {   // the key head's q and k channels
     const int c = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
-    const float y = conv_channel<false>(x_row, conv_w, cs_row, c, cc, act);
+    const float y = conv_channel(x_row, conv_w, cs_row, c, cc, act);
     if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
-    if (tid < kD) s_v[tid] = conv_channel<true>(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + tid, cc, act);
   }
+  if (gt < kD) s_v[hh][gt] = conv_channel(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + gt, cc, act);
   __syncthreads();
-  if (wave < 2) {
-    const float* src = wave == 0 ? s_q : s_k;
+  if (tid < 2 * kWave) {
+    const int w = tid / kWave;
+    const float* src = w == 0 ? s_q : s_k;
     const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
     const float ss = wave_sum(a0 * a0 + a1 * a1);
-    if (lane == 0) s_scal[wave] = 1.0f / sqrtf(ss + l2_eps);
+    if (lane == 0) s_scal[w] = 1.0f / sqrtf(ss + l2_eps);
   }
   __syncthreads();
   const float rq = s_scal[0] * q_scale, rk = s_scal[1];
-  if (wave == 0) {
+  if (tid < kWave) {
     const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]);
     if (lane == 0) s_scal[2] = kq * rq * rk;
   }
@@ -133,77 +133,68 @@ __global__ __launch_bounds__(kDecThreads) void decode_step_kernel(
       pk = fmaf(sreg[m][e], kcol[e], pk);
       pq = fmaf(sreg[m][e], qcol[e], pq);
     }
-    s_red[0][rg + 8 * m][cg] = pk;
-    s_red[1][rg + 8 * m][cg] = pq;
+    s_red[hh][0][rg + 8 * m][cg] = pk;
+    s_red[hh][1][rg + 8 * m][cg] = pq;
   }
   __syncthreads();
 
   // rows: u = beta (v - p), o = r + u (khat . qtil), then the gated norm
-  if (tid < kD) {
+  float o = 0.0f;
+  if (gt < kD) {
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll 8
-    for (int j = 0; j < 32; ++j) { pk += s_red[0][tid][j]; pq += s_red[1][tid][j]; }
-    const float u = beta[(int64_t)b * hv + h] * (s_v[tid] - pk);
-    s_u[tid] = u;
-    const float o = fmaf(u, s_scal[2], pq);
+    for (int j = 0; j < 32; ++j) { pk += s_red[hh][0][gt][j]; pq += s_red[hh][1][gt][j]; }
+    const float u = beta[(int64_t)b * hv + h] * (s_v[hh][gt] - pk);
+    s_u[hh][gt] = u;
+    o = fmaf(u, s_scal[2], pq);
     const float ss = wave_sum(o * o);
-    if (lane == 0) s_scal[4 + wave] = ss;
-    s_v[tid] = o;
+    if (lane == 0) s_nrm[hh][gwave] = ss;
   }
   __syncthreads();
-  if (tid < kD) {
-    const float r = rsqrtf((s_scal[4] + s_scal[5]) * (1.0f / kD) + rms_eps);
-    const int64_t off = ((int64_t)b * hv + h) * kD + tid;
-    st(out + off, s_v[tid] * r * norm_w[tid] * sigmoidf_(ld(z + off)));
+  if (gt < kD) {
+    const float r = rsqrtf((s_nrm[hh][0] + s_nrm[hh][1]) * (1.0f / kD) + rms_eps);
+    const int64_t off = ((int64_t)b * hv + h) * kD + gt;
+    st(out + off, o * r * norm_w[gt] * sigmoidf_(ld(z + off)));
   }
 
   // write the updated state: S' = Sd + u khat^T
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m) {
-    const float u = s_u[rg + 8 * m];
+    const float u = s_u[hh][rg + 8 * m];
 #pragma unroll
     for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
     __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
   }
 }
 
-// Shift the q/k conv-state rows (s0, s1, s2) <- (s1, s2, x) for every sequence,
-// after every value head has read the old rows.
-template <typename T>
-__global__ __launch_bounds__(256) void decode_qk_shift_kernel(const T* __restrict__ x,
-                                                               T* __restrict__ conv_state,
-                                                               int qk_channels, int cc) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int b = blockIdx.y;
-  if (c >= qk_channels) return;
-  T* p = conv_state + (int64_t)b * 3 * cc + c;
-  const T s1 = p[cc], s2 = p[2 * cc], xv = x[(int64_t)b * cc + c];
-  p[0] = s1;
-  p[cc] = s2;
-  p[2 * cc] = xv;
+template <typename T, typename To, bool kPC>
+hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void* conv_state,
+                        const float* g, const float* beta, const void* z, const float* norm_w,
+                        float* state, void* out, int b, hipStream_t s) {
+  const int ratio = d.hv / d.hk;
+  dim3 grid(b * d.hk);
+#define GDN_DECODE_LAUNCH(R)                                                                      \
+  hipLaunchKernelGGL((decode_step_kernel<T, To, kPC, R>), grid, dim3(kGroup * (R)), 0, s,         \
+                     static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,      \
+                     static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv, \
+                     d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps)
+  switch (ratio) {
+    case 1: GDN_DECODE_LAUNCH(1); break;
+    case 2: GDN_DECODE_LAUNCH(2); break;
+    case 3: GDN_DECODE_LAUNCH(3); break;
+    case 4: GDN_DECODE_LAUNCH(4); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef GDN_DECODE_LAUNCH
+  return hipGetLastError();
 }
 
 template <typename T, typename To>
 hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                        const float* g, const float* beta, const void* z, const float* norm_w,
                        float* state, void* out, int b, hipStream_t s) {
-  dim3 grid(b * d.hv);
-  if (d.per_channel)
-    hipLaunchKernelGGL((decode_step_kernel<T, To, true>), grid, dim3(kDecThreads), 0, s,
-                       static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
-                       static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv,
-                       d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
-  else
-    hipLaunchKernelGGL((decode_step_kernel<T, To, false>), grid, dim3(kDecThreads), 0, s,
-                       static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,
-                       static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv,
-                       d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int qk = 2 * d.hk * d.dk;
-  hipLaunchKernelGGL(decode_qk_shift_kernel<T>, dim3((qk + 255) / 256, b), dim3(256), 0, s,
-                     static_cast<const T*>(x), static_cast<T*>(conv_state), qk, d.cc);
-  return hipGetLastError();
+  return d.per_channel ? decode_ratio<T, To, true>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
+                       : decode_ratio<T, To, false>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
 }
 
 }  // namespace

@@ -182,6 +182,7 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
  *   z            [B][Hv][dv];  norm_w fp32 [dv]
  *   state        fp32 [B][Hv][dv][dk], updated in place
  *   out          [B][Hv][dv]
+ * Requires Hv / Hk <= 4 (GDN_ERR_UNSUPPORTED otherwise).
  */
 gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
                              const void* x, const float* conv_w, void* conv_state, const float* g,

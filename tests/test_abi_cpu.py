@@ -156,3 +156,10 @@ def test_empty_calls_launch_nothing(lib):
                                None, None, None, None, 0, None) == 0
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_F32, gdn.GDN_F32, None, None, None,
                                  None, 0, None) == 0
+
+
+def test_decode_rejects_more_than_four_value_heads_per_key_head(lib):
+    cfg = _cfg(num_k_heads=8, num_v_heads=48)
+    got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, 4, None)
+    assert got == gdn.GDN_ERR_UNSUPPORTED
