@@ -65,7 +65,10 @@ template <> struct Ops<false> {
   using E = uint16_t;            // storage element in LDS (bf16 bits)
   using F = bf16x8_t;            // MFMA operand fragment
   static constexpr int kEpl = 8, kKs = 32;
-  static constexpr int kPadK = 8;     // row padding (elements) of k-contiguous LDS tiles
+  // row padding (elements) of k-contiguous LDS tiles: 32 bytes, so that the
+  // 16-byte fragment reads of 16 rows (128 or 256 bytes per row) hit distinct
+  // banks; a 16-byte pad makes those reads two-way bank conflicted
+  static constexpr int kPadK = 16;
 };
 template <> struct Ops<true> {
   using E = float;
@@ -835,16 +838,17 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   // (loaded one chunk ahead) instead of staging the record in LDS
   [[maybe_unused]] F th[kPC ? kMaxKs : 1], tl[kPC ? kMaxKs : 1], ph[kPC ? kMaxKs : 1], pl[kPC ? kMaxKs : 1];
   auto load_row_frags = [&](const uint8_t* src, F* fh, F* fl) {
+    // every k step is loaded (those past the diagonal are in the record and
+    // unused) so that the count of loads in flight is the same on every wave
+    // and the compiler's waits for them stay exact
 #pragma unroll
     for (int ks = 0; ks < kMaxKs; ++ks) {
-      if (ks < nks) {
-        if constexpr (F32) {
-          fh[ks] = reinterpret_cast<const float*>(src)[(mt * 16 + ks) * kWave + lane];
-        } else {
-          const int f = mt * 2 + ks;
-          fh[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
-          fl[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
-        }
+      if constexpr (F32) {
+        fh[ks] = reinterpret_cast<const float*>(src)[(mt * 16 + ks) * kWave + lane];
+      } else {
+        const int f = mt * 2 + ks;
+        fh[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 0) * kWave + lane) * 16);
+        fl[ks] = *reinterpret_cast<const bf16x8_t*>(src + ((size_t)(f * 2 + 1) * kWave + lane) * 16);
       }
     }
   };
@@ -973,7 +977,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
       store_acc_transposed<F32>(sNh, sNl, kTP, 16 * hf, 16 * mt, vn);
       if constexpr (kPC) {
         store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, vn);
-        if (more) load_row_frags(rec_of(c + 1), th, tl);   // next chunk's Tt rows
+        load_row_frags(rec_of(more ? c + 1 : c), th, tl);   // next chunk's Tt rows (unconditional: exact waits)
       } else {
         f32x4_t w;
 #pragma unroll
@@ -1000,7 +1004,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
         }
       }
       if constexpr (kPC) {
-        if (more) load_row_frags(rec_of(c + 1) + kFragBytes, ph, pl);   // next chunk's Pt rows
+        load_row_frags(rec_of(more ? c + 1 : c) + kFragBytes, ph, pl);   // next chunk's Pt rows
       }
       To* orow = out + ((int64_t)t0 * hv + h) * kD + i0 + 16 * hf + (lane & 15);
 #pragma unroll
