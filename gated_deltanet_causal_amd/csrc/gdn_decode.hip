@@ -21,12 +21,15 @@
 //
 // Work split: one workgroup per (sequence, key head) with one 256-thread group
 // per value head of that key head (768 threads for the pages' ratio of 3), so
-// a 64-sequence batch is 1024 equal workgroups (four full rounds at one per
-// CU).  The workgroup owns the key head's q/k conv channels and its value
-// heads' v channels, so each conv-state element has exactly one writer and is
-// shifted in place.  Within a group, the 64 KiB state of the head is spread as
-// 16 rows x one float4 per thread; a wavefront loads two full 512-byte rows
-// per instruction.
+// a 64-sequence batch is 1024 equal workgroups.  The workgroup owns the key
+// head's q/k conv channels and its value heads' v channels, so each conv-state
+// element has exactly one writer and is shifted in place.  Within a group, the
+// 64 KiB state of the head is spread as 16 rows x one float4 per thread; a
+// wavefront loads two full 512-byte rows per instruction.  Rows are
+// independent: each row's two dot products are reduced across the 32 lanes
+// that hold it (DPP and a swizzle, no LDS), and the row is updated and stored
+// as soon as its loads land.  The small LDS footprint lets two workgroups share
+// a CU, so one streams its state while the other computes.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -36,7 +39,22 @@ namespace {
 constexpr int kGroup = 256;             // threads per value head
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
 constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
-constexpr int kRedPitch = 33;           // padded pitch of the row-sum exchange
+constexpr int kWindow = 8;              // state rows in flight per thread
+
+// Sum over the 32 lanes holding one state row (aligned halves of the wave):
+// quad_perm swaps for lane distance 1 and 2, the half-row and row mirrors for
+// 4 and 8, and a swizzle exchanging lane i with i ^ 16 for the last step.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row32_sum(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);   // row_half_mirror
+  v = dpp_add<0x140>(v);   // row_mirror
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
 
 // Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); the
 // channel's state rows become (s1, s2, x).
@@ -58,7 +76,7 @@ __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_
 }
 
 template <typename T, typename To, bool kPerChannel, int kRatio>
-__global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
+__global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
     const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
@@ -74,18 +92,22 @@ __global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
   const int cg = gt % 32;                 // column group: columns 4cg .. 4cg+3
   const int rg = gt / 32;                 // row group: rows rg + 8m
 
-  __shared__ float s_q[kD], s_k[kD], s_scal[4];
-  __shared__ float s_v[kRatio][kD], s_u[kRatio][kD], s_nrm[kRatio][2];
-  __shared__ float s_red[kRatio][2][kD][kRedPitch];
+  __shared__ float s_q[kD], s_k[kD], s_scal[2];
+  __shared__ float s_v[kRatio][kD], s_o[kRatio][kD], s_nrm[kRatio][2];
 
   // issue the state loads first; the conv and norms below overlap their latency.
   // The state is streamed once per step (no reuse), so its loads and stores are
   // non-temporal.
+  // A window of kWindow rows is in flight: the first rows are issued here and
+  // each processed row issues the load of the row kWindow after it, which keeps
+  // the registers of two workgroups per CU within the register file.
   float* S = state + ((int64_t)b * hv + h) * kD * kD;
+  auto load_row = [&](int m) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  };
   f32x4_t sreg[kRowsPerThread];
 #pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m)
-    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  for (int m = 0; m < kWindow; ++m) sreg[m] = load_row(m);
 
   const T* x_row = x + (int64_t)b * cc;
   T* cs_row = conv_state + (int64_t)b * 3 * cc;
@@ -105,10 +127,8 @@ __global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
   }
   __syncthreads();
   const float rq = s_scal[0] * q_scale, rk = s_scal[1];
-  if (tid < kWave) {
-    const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]);
-    if (lane == 0) s_scal[2] = kq * rq * rk;
-  }
+  // khat . qtil, computed by every wave (no exchange needed)
+  const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
   // this thread's normalised key / query columns and decay factors
   float kcol[4], qcol[4], a[4];
 #pragma unroll
@@ -123,9 +143,14 @@ __global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
     for (int e = 0; e < 4; ++e) a[e] = av;
   }
 
-  // decay, then the two row sums over this thread's four columns
+  // per row: decay, the two dot products reduced over the row's 32 lanes,
+  // u = beta (v - p), o = r + u (khat . qtil), then the row is updated and
+  // written back: S' = Sd + u khat^T
+  const float bt = beta[(int64_t)b * hv + h];
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m) {
+    if (m + kWindow < kRowsPerThread) sreg[m + kWindow] = load_row(m + kWindow);
+    const int row = rg + 8 * m;
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -133,37 +158,28 @@ __global__ __launch_bounds__(kGroup * kRatio) void decode_step_kernel(
       pk = fmaf(sreg[m][e], kcol[e], pk);
       pq = fmaf(sreg[m][e], qcol[e], pq);
     }
-    s_red[hh][0][rg + 8 * m][cg] = pk;
-    s_red[hh][1][rg + 8 * m][cg] = pq;
+    pk = row32_sum(pk);
+    pq = row32_sum(pq);
+    const float u = bt * (s_v[hh][row] - pk);
+    if (cg == 0) s_o[hh][row] = fmaf(u, kq, pq);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + row * kD + 4 * cg));
   }
   __syncthreads();
 
-  // rows: u = beta (v - p), o = r + u (khat . qtil), then the gated norm
-  float o = 0.0f;
+  // the sigmoid gated RMSNorm of the head's 128 outputs
   if (gt < kD) {
-    float pk = 0.0f, pq = 0.0f;
-#pragma unroll 8
-    for (int j = 0; j < 32; ++j) { pk += s_red[hh][0][gt][j]; pq += s_red[hh][1][gt][j]; }
-    const float u = beta[(int64_t)b * hv + h] * (s_v[hh][gt] - pk);
-    s_u[hh][gt] = u;
-    o = fmaf(u, s_scal[2], pq);
+    const float o = s_o[hh][gt];
     const float ss = wave_sum(o * o);
     if (lane == 0) s_nrm[hh][gwave] = ss;
   }
   __syncthreads();
   if (gt < kD) {
+    const float o = s_o[hh][gt];
     const float r = rsqrtf((s_nrm[hh][0] + s_nrm[hh][1]) * (1.0f / kD) + rms_eps);
     const int64_t off = ((int64_t)b * hv + h) * kD + gt;
     st(out + off, o * r * norm_w[gt] * sigmoidf_(ld(z + off)));
-  }
-
-  // write the updated state: S' = Sd + u khat^T
-#pragma unroll
-  for (int m = 0; m < kRowsPerThread; ++m) {
-    const float u = s_u[hh][rg + 8 * m];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
-    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
   }
 }
 
