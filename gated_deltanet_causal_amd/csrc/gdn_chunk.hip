@@ -37,6 +37,7 @@
 // accurate to ~2^-16 relative with fp32 accumulation.  The fp32 input path
 // uses fp32 MFMA instead.
 #include <algorithm>
+#include <type_traits>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -652,16 +653,20 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
 constexpr int kSpineThreads = 512;   // 8 waves, two per SIMD
 
 // Register staging of one chunk's inputs: K and Q rows, the V tile, the chunk
-// record (Tt and Pt fragments and vectors; per-key-channel decay: rk, rq and
-// the chunk's log decays g instead of the fragments, which each wave then
-// loads itself).  Issued while the previous chunk computes, committed to LDS
-// at the top of the chunk.
+// vectors (per-key-channel decay: rk, rq and the chunk's log decays g).  Issued
+// while the previous chunk computes, committed to LDS at the top of the chunk.
+// The Tt / Pt fragments do not pass through here: each wave loads its own row
+// tile of them straight into registers.
 template <bool F32, bool kPC> struct Stage {
-  u32x4_t k[F32 ? 4 : 2], q[F32 ? 4 : 2], v, f[kPC ? 1 : 4];
+  u32x4_t k[F32 ? 4 : 2], q[F32 ? 4 : 2], v;
   float vec, gv[kPC ? 16 : 1];
 };
 
-template <bool F32, bool kPC, typename Tin>
+// Loads are issued in parts (kParts: bit 0 K and Q, bit 1 V and the vectors,
+// bit 2 the per-key-channel log decays), at different points of the chunk:
+// the texture units take in about 64 bytes per clock per CU, and a wave
+// stalls at a load while they are full.
+template <int kParts, bool F32, bool kPC, typename Tin>
 __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, const Tin* q, int64_t qk_stride,
                                             const Tin* v, int64_t v_stride, const float* g, int hv,
                                             const uint8_t* rec, int L) {
@@ -670,15 +675,14 @@ __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, c
   auto row16 = [&](const Tin* base, int64_t stride, int t, int col) -> u32x4_t {
     return t < L ? *reinterpret_cast<const u32x4_t*>(base + (int64_t)t * stride + col) : z;
   };
-  if constexpr (F32) {
+  if constexpr ((kParts & 1) && F32) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int p = tid + i * kSpineThreads;            // 64 rows x 32 pieces of 4 floats
       sg.k[i] = row16(k, qk_stride, p / 32, 4 * (p % 32));
       sg.q[i] = row16(q, qk_stride, p / 32, 4 * (p % 32));
     }
-    sg.v = row16(v, v_stride, tid / 8, 4 * (tid % 8));  // 64 rows x 8 pieces
-  } else {
+  } else if constexpr (kParts & 1) {
     {
       const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));   // row pair x 8 columns
       sg.k[0] = row16(k, qk_stride, t, j0);
@@ -689,25 +693,25 @@ __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, c
       const int p = tid + i * kSpineThreads;            // 64 rows x 16 pieces of 8
       sg.q[i] = row16(q, qk_stride, p / 16, 8 * (p % 16));
     }
-    sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
   }
-  if constexpr (kPC) {
+  if constexpr (kParts & 2) {
+    if constexpr (F32) sg.v = row16(v, v_stride, tid / 8, 4 * (tid % 8));  // 64 rows x 8 pieces
+    else sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
+    if constexpr (kPC) sg.vec = tid < 2 * kC ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+    else sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+  }
+  if constexpr ((kParts & 4) && kPC) {
     // channel tid/4, rows 16 (tid%4) .. +15 of the chunk
     const int ch = tid / 4, r0 = 16 * (tid % 4);
 #pragma unroll
     for (int r = 0; r < 16; ++r) sg.gv[r] = r0 + r < L ? g[((int64_t)(r0 + r) * hv) * kD + ch] : 0.0f;
-    sg.vec = tid < 2 * kC ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) sg.f[i] = reinterpret_cast<const u32x4_t*>(rec)[tid + i * kSpineThreads];
-    sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
   }
 }
 
 template <bool F32, bool kPC>
 __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename Ops<F32>::E* sK,
                                              typename Ops<F32>::E* sKt, typename Ops<F32>::E* sQ, int pitch,
-                                             int tpitch, float* sV, int vpitch, uint8_t* sF, float* sGam,
+                                             int tpitch, float* sV, int vpitch, float* sGam,
                                              int gpitch, float* s_vec) {
   const int tid = threadIdx.x;
   if constexpr (F32) {
@@ -767,8 +771,6 @@ __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename
     for (int r = 0; r < 16; ++r) sGam[(16 * part + r) * gpitch + ch] = run[r] + excl;
     if (tid < 2 * kC) s_vec[tid] = sg.vec;
   } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) reinterpret_cast<u32x4_t*>(sF)[tid + i * kSpineThreads] = sg.f[i];
     if (tid < 3 * kC + 1) s_vec[tid] = sg.vec;
   }
 }
@@ -797,7 +799,6 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sRh[kTile * kTP], sRl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
-  __shared__ __attribute__((aligned(16))) uint8_t sF[kPC ? 16 : 2 * kFragBytes];   // Tt | Pt fragments
   __shared__ __attribute__((aligned(16))) float sGam[kPC ? kC * kGP : 1];
   __shared__ __attribute__((aligned(16))) float s_vec[3 * kC + 4];
 
@@ -834,9 +835,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   const int nks = F32 ? 4 * (mt + 1) : 1 + (mt >> 1);   // k steps up to the diagonal
   constexpr int kMaxKs = F32 ? 16 : 2;
 
-  // per-key-channel decay: each wave keeps its row tile of Tt / Pt in registers
-  // (loaded one chunk ahead) instead of staging the record in LDS
-  [[maybe_unused]] F th[kPC ? kMaxKs : 1], tl[kPC ? kMaxKs : 1], ph[kPC ? kMaxKs : 1], pl[kPC ? kMaxKs : 1];
+  // Each wave keeps its row tile of Tt / Pt in registers, loaded from the
+  // record one chunk ahead (right after its use in this chunk), so the record
+  // never passes through LDS and its loads drain behind the compute.
+  [[maybe_unused]] F th[kMaxKs], tl[kMaxKs], ph[kMaxKs], pl[kMaxKs];
   auto load_row_frags = [&](const uint8_t* src, F* fh, F* fl) {
     // every k step is loaded (those past the diagonal are in the record and
     // unused) so that the count of loads in flight is the same on every wave
@@ -854,18 +856,9 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   };
   // fragment of Tt (which = 0) or Pt (1), row tile mt, k step ks
   auto tri_frag = [&](int which, int ks, F& fh, F& fl) {
-    if constexpr (kPC) {
-      fh = which == 0 ? th[ks] : ph[ks];
-      fl = which == 0 ? tl[ks] : pl[ks];
-    } else if constexpr (F32) {
-      fh = reinterpret_cast<const float*>(sF + which * kFragBytes)[(mt * 16 + ks) * kWave + lane];
-      fl = 0.0f;
-    } else {
-      const int f = mt * 2 + ks;
-      const uint8_t* base = sF + which * kFragBytes;
-      fh = load_bf16x8(reinterpret_cast<const uint16_t*>(base + ((f * 2 + 0) * kWave + lane) * 16));
-      fl = load_bf16x8(reinterpret_cast<const uint16_t*>(base + ((f * 2 + 1) * kWave + lane) * 16));
-    }
+    fh = which == 0 ? th[ks] : ph[ks];
+    if constexpr (F32) fl = 0.0f;
+    else fl = which == 0 ? tl[ks] : pl[ks];
   };
 
   f32x4_t sacc[2];
@@ -902,26 +895,24 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   }
 
   Stage<F32, kPC> stage;
-  auto issue = [&](int t0c, int cidx) {
-    stage_issue<F32, kPC>(stage, k + (int64_t)t0c * qk_stride + kh * kD, q + (int64_t)t0c * qk_stride + kh * kD,
-                          qk_stride, v + (int64_t)t0c * v_stride + h * kD + i0, v_stride,
-                          kPC ? g + ((int64_t)t0c * hv + h) * kD : nullptr, hv, rec_of(cidx),
-                          min(kC, seq_end - t0c));
+  auto issue = [&](auto parts, int t0c, int cidx) {
+    stage_issue<decltype(parts)::value, F32, kPC>(
+        stage, k + (int64_t)t0c * qk_stride + kh * kD, q + (int64_t)t0c * qk_stride + kh * kD, qk_stride,
+        v + (int64_t)t0c * v_stride + h * kD + i0, v_stride, kPC ? g + ((int64_t)t0c * hv + h) * kD : nullptr,
+        hv, rec_of(cidx), min(kC, seq_end - t0c));
   };
   if (seq_beg < seq_end) {
-    issue(seq_beg, chunk0);
-    if constexpr (kPC) {
-      load_row_frags(rec_of(chunk0), th, tl);
-      load_row_frags(rec_of(chunk0) + kFragBytes, ph, pl);
-    }
+    issue(std::integral_constant<int, 7>{}, seq_beg, chunk0);
+    load_row_frags(rec_of(chunk0), th, tl);
+    load_row_frags(rec_of(chunk0) + kFragBytes, ph, pl);
   }
 
   for (int t0 = seq_beg, c = chunk0; t0 < seq_end; t0 += kC, ++c) {
     const int L = min(kC, seq_end - t0);
     const bool more = t0 + kC < seq_end;
     __syncthreads();   // the previous chunk is done with every LDS tile
-    stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sF, sGam, kGP, s_vec);
-    if (more) issue(t0 + kC, c + 1);
+    stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec);
+    if (more) issue(std::integral_constant<int, 3>{}, t0 + kC, c + 1);   // K, Q, V, vectors
     __syncthreads();
 
     // ---- Y = K S0^T and Z = Q S0^T: rows of tile mt, columns of half hf ----
@@ -949,6 +940,9 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
         }
       }
     }
+    if constexpr (kPC) {
+      if (more) issue(std::integral_constant<int, 4>{}, t0 + kC, c + 1);   // the next chunk's log decays
+    }
     // R = V - a_t Y (per-key-channel decay: R = V - Y), stored transposed [i][t] as hi/lo
     {
       f32x4_t rv;
@@ -975,9 +969,9 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
         }
       }
       store_acc_transposed<F32>(sNh, sNl, kTP, 16 * hf, 16 * mt, vn);
+      load_row_frags(rec_of(more ? c + 1 : c), th, tl);   // next chunk's Tt rows (unconditional: exact waits)
       if constexpr (kPC) {
         store_acc_transposed<F32>(sWh, sWl, kTP, 16 * hf, 16 * mt, vn);
-        load_row_frags(rec_of(more ? c + 1 : c), th, tl);   // next chunk's Tt rows (unconditional: exact waits)
       } else {
         f32x4_t w;
 #pragma unroll
@@ -1003,9 +997,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
           accZ = mma3<F32>(ph_, pl_, bh, bl, accZ);
         }
       }
-      if constexpr (kPC) {
-        load_row_frags(rec_of(more ? c + 1 : c) + kFragBytes, ph, pl);   // next chunk's Pt rows
-      }
+      load_row_frags(rec_of(more ? c + 1 : c) + kFragBytes, ph, pl);   // next chunk's Pt rows
       To* orow = out + ((int64_t)t0 * hv + h) * kD + i0 + 16 * hf + (lane & 15);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
