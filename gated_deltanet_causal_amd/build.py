@@ -28,6 +28,10 @@ FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # no packed fp32 (v_pk_*_f32) instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: on gfx950 independent MFMAs whose
+    # accumulators live in AGPRs issue at ~46 cycles each when eight chains
+    # alternate, against ~17 in VGPRs (measured on MI355X)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

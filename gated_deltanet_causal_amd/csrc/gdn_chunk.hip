@@ -53,6 +53,11 @@ constexpr size_t kFragBytes = 16384;           // one 64x64 operand in lane layo
 constexpr size_t kRecBytes = 2 * kFragBytes + 1024;  // Tt, Pt, vectors
 constexpr int kSortMax = 4096;                 // longest-first order up to this many sequences
 constexpr int kXcds = 8;                       // XCDs; workgroups are dealt to them round-robin
+#ifndef GDN_WAVE_SPINE_WAVES
+#define GDN_WAVE_SPINE_WAVES 4
+#endif
+constexpr int kWaveSpineWaves = GDN_WAVE_SPINE_WAVES;   // waves per register-resident spine workgroup
+constexpr int kWaveSpineMinBlocks = 256;                 // ... used from this many workgroups (one per CU)
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -125,6 +130,17 @@ __device__ __forceinline__ int chunk_sequence(const int32_t* first, int n_seq, i
     if (first[mid] <= c) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Paired-tile k order.  The 32 k slots of a bf16 MFMA are (g, e): lane group
+// g = l/16 and operand element e < 8.  Slot (g, e) of k step ks stands for
+// index 32 ks + 16 (e/4) + 4 g + e%4, which is exactly where two vertically
+// adjacent 16x16 accumulator tiles (rows 32 ks .. +15 and +16 .. +31) keep
+// their rows in lane l (rows 4g .. 4g+3 of each).  A pair of accumulator tiles
+// is therefore a B operand as it stands, and an A operand only needs its
+// columns in the same order.
+__host__ __device__ constexpr int pair_k(int ks, int g, int e) {
+  return 32 * ks + 16 * (e >> 2) + 4 * g + (e & 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,8 +313,11 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 
 // Shared tail of the intra kernels: T = (I + A)^-1 from sA, then Tt = T diag(beta)
 // and Pt (sP) written to the record in MFMA A-operand lane layout, masked to
-// the lower triangle (hi/lo bf16 fragment pairs, or fp32).  All threads.
-template <bool F32, int kAP>
+// the lower triangle (hi/lo bf16 fragment pairs, or fp32).  kPairK selects the
+// paired-tile k order of the register-resident spine (element e of lane l in
+// k step ks holds column pair_k(ks, l/16, e)) instead of the plain order
+// (column 32 ks + 8 (l/16) + e).  All threads.
+template <bool F32, int kAP, bool kPairK = false>
 __device__ __forceinline__ void write_operands(const float* sA, const float* sP, float* sT, float* sM,
                                                const float* s_beta, uint8_t* rec) {
   const int tid = threadIdx.x;
@@ -320,11 +339,12 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
       for (int p = tid; p < 8 * kWave; p += kThreads) {
         const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
         const int mt = f / 2, ks = f % 2;
-        const int r = 16 * mt + (l & 15), k0 = 32 * ks + 8 * (l >> 4);
+        const int r = 16 * mt + (l & 15);
         bf16x8_t hi, lo;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float v = (k0 + e) <= r ? src[r * kAP + k0 + e] * (scale_cols ? s_beta[k0 + e] : 1.0f) : 0.0f;
+          const int kk = kPairK ? pair_k(ks, l >> 4, e) : 32 * ks + 8 * (l >> 4) + e;
+          const float v = kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
           __bf16 a, b;
           split_bf16(v, a, b);
           hi[e] = a;
@@ -525,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
 // ---------------------------------------------------------------------------
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
 // ---------------------------------------------------------------------------
-template <bool F32, typename Tin>
+template <bool F32, typename Tin, bool kPairK>
 __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -632,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
 
     // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
     uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
-    write_operands<F32, kAP>(sA, sP, sT, sM, s_beta, rec);
+    write_operands<F32, kAP, kPairK>(sA, sP, sT, sM, s_beta, rec);
 
     // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
     if (tid < kC) {
@@ -1072,12 +1092,453 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// spine, register-resident form (bf16 inputs, scalar decay).
+//
+// One wave owns 16 value rows i of a head's state, for all 128 key columns and
+// all 64 tokens of a chunk, so every product of the chunk step is wave-local:
+//   Y, Z   = K S0^T, Q S0^T          (A: K / Q rows from LDS, B: the state)
+//   R      = V - a Y
+//   Vnew   = Tt R                     (A: Tt from the record, B: R)
+//   O      = b Z + Pt Vnew            (A: Pt, B: Vnew)
+//   S^T   <- d S^T + K^T (c Vnew)     (A: K^T by transposing LDS reads, B: c Vnew)
+// The state is held as eight 16x16 accumulator tiles of S^T (key rows j, value
+// columns i).  In the paired-tile k order every B operand above is a pair of
+// accumulator tiles of the previous product, split into bf16 hi + lo in
+// registers: nothing but the chunk's shared inputs passes through LDS.  K and Q
+// are stored in LDS with each 32-column block in paired-tile order, so an A
+// fragment is one 16-byte read.  A workgroup is kNW waves (16 kNW value rows of
+// one head) sharing the chunk's K, Q, V and vectors, double-buffered in LDS
+// and staged through registers one chunk ahead; Tt and Pt go straight from the
+// record into each wave's registers, also one chunk ahead.  One barrier per
+// chunk.
+// ---------------------------------------------------------------------------
+constexpr int kWP = kD + 16;   // K / Q row pitch in LDS (bf16 elements): 288 bytes
+
+// LDS column of logical column j of a K / Q row (paired-tile order per 32 columns)
+__device__ __forceinline__ int wave_col(int j) {
+  return (j & ~31) + 8 * ((j >> 2) & 3) + 4 * ((j >> 4) & 1) + (j & 3);
+}
+
+// Two fp32 values -> their bf16 hi parts and bf16 lo parts (x = hi + lo up to
+// 2^-17 relative), each pair packed in one dword: three VALU ops per value.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hp, uint32_t& lp) {
+  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  const float ha = __uint_as_float(hp << 16), hb = __uint_as_float(hp & 0xffff0000u);
+  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
+}
+
+// two accumulator tiles -> one B operand in paired-tile k order, as hi and lo
+__device__ __forceinline__ void split_pair(const f32x4_t& a, const f32x4_t& b, bf16x8_t& hi, bf16x8_t& lo) {
+  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+  split2(a[0], a[1], h0, l0);
+  split2(a[2], a[3], h1, l1);
+  split2(b[0], b[1], h2, l2);
+  split2(b[2], b[3], h3, l3);
+  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h2, h3});
+  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{l0, l1, l2, l3});
+}
+
+// 4 bf16 of a transposing LDS read: within each 16-lane group, lane 4r + q
+// supplies the address of row r, columns 4q .. 4q+3 of a 4 x 16 block, and
+// lane j receives column j, rows 0..3.
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4s_t lds_read_tr4(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(p));
+}
+__device__ __forceinline__ bf16x8_t lds_read_tr8(const uint16_t* p, int second) {
+  const v4s_t a = lds_read_tr4(p), b = lds_read_tr4(p + second);
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Raw buffer access: a descriptor with a uniform base and a byte range, and
+// 32-bit per-lane offsets.  Loads past the range return zero and stores past
+// it are dropped, which is how the spine handles a chunk's rows past the end
+// of its sequence.  Offsets that the range check must see are always in the
+// per-lane offset (the scalar offset is used only for accesses known to be in
+// range).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4_t v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4_t v, uint16_t*) {
+  const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t));
+  const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t));
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, r, voff, 0, 0);
+}
+
+template <int kNW>
+struct WaveSpineCfg {
+  static constexpr int kThreadsW = kNW * kWave;
+  static constexpr int kRows = 16 * kNW;                  // value rows per workgroup
+  static constexpr int kVP = kRows + 8;                   // V row pitch (bf16)
+  // one LDS slot (bytes): K | Q | V (bf16) | Tt, Pt fragments | chunk vectors
+  static constexpr int kOffQ = kC * kWP * 2;
+  static constexpr int kOffV = 2 * kOffQ;
+  static constexpr int kOffTri = kOffV + kC * kVP * 2;
+  static constexpr int kTriFrags = 24;                    // (Tt, Pt) x 6 fragments x (hi, lo), 1 KB each
+  static constexpr int kOffVec = kOffTri + kTriFrags * 1024;
+  static constexpr int kSlotBytes = kOffVec + 1024;
+  static constexpr int kPiecesKQ = kC * kD / 8 / kThreadsW;    // 16-byte pieces of K (and Q) per thread
+  static constexpr int kPiecesV = kC * kRows / 8 / kThreadsW;  // ... of V: 2
+  static constexpr int kPiecesTri = kTriFrags * kWave / kThreadsW;
+};
+
+// Tt / Pt fragments (mt, ks) with ks <= mt / 2 (the rest of the 64 x 64 is zero)
+constexpr int kNF = 6;
+__host__ __device__ constexpr int frag_mt(int x) { return x < 4 ? x : x - 2; }     // 0 1 2 3 2 3
+__host__ __device__ constexpr int frag_ks(int x) { return x < 4 ? 0 : 1; }         // 0 0 0 0 1 1
+
+template <int kNW, typename To>
+__global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
+    const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
+    const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
+    To* __restrict__ out, float* final_state) {
+  using Cf = WaveSpineCfg<kNW>;
+  constexpr int kT = Cf::kThreadsW;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_in[2][Cf::kSlotBytes];
+
+  // block -> (sequence, key head) group and member (value head, row block);
+  // the members of a group get block ids congruent mod kXcds (one XCD, one L2)
+  const int ratio = hv / hk;
+  const int blocks_per_head = kD / Cf::kRows;
+  const int members = ratio * blocks_per_head;
+  const int xcd = blockIdx.x % kXcds;
+  const int rest = blockIdx.x / kXcds;
+  const int grp = (rest / members) * kXcds + xcd;
+  if (grp >= n_seq * hk) return;
+  const int member = rest % members;
+  const int32_t* first = reinterpret_cast<const int32_t*>(ws);
+  const int32_t* order = first + n_seq + 1;
+  const int n = order[grp / hk];
+  const int kh = grp % hk;
+  const int h = kh * ratio + member / blocks_per_head;
+  const int i0 = (member % blocks_per_head) * Cf::kRows;     // first value row of the workgroup
+  const int tid = threadIdx.x, lane = tid % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int iw = 16 * wave;                                  // the wave's rows within the block
+  const int g = lane >> 4, m = lane & 15;
+  const uint8_t* recs = ws + records_offset(n_seq);
+  const int seq_beg = cu[n], seq_end = cu[n + 1];
+  const int chunk0 = first[n];
+  const int n_chunks = (seq_end - seq_beg + kC - 1) / kC;
+  auto rec_of = [&](int cidx) { return recs + ((size_t)cidx * hv + h) * kRecBytes; };
+
+  // ---- staging of a chunk's inputs through registers ----
+  // The loads for chunk cl+1 are issued in pieces between the MFMAs of chunk
+  // cl's first products, and written to the other LDS slot in pieces between
+  // its last products, so neither the texture path nor LDS sees a burst.  Per
+  // chunk a descriptor covers its rows: rows past the end of the sequence load
+  // as zeros, and a chunk past the end of the sequence has an empty range (no
+  // access at all).
+  u32x4_t st_k[Cf::kPiecesKQ], st_q[Cf::kPiecesKQ], st_v[Cf::kPiecesV], st_tri[Cf::kPiecesTri], st_vec;
+  constexpr int kLoads = 2 * Cf::kPiecesKQ + Cf::kPiecesV + Cf::kPiecesTri + 1;
+  const uint32_t qk_row = (uint32_t)qk_stride * 2, v_row = (uint32_t)v_stride * 2;
+  const uint32_t off_kq = (uint32_t)(tid >> 4) * qk_row + 16 * (tid & 15);
+  const uint32_t off_v = (uint32_t)(tid / (Cf::kRows / 8)) * v_row + 16 * (tid % (Cf::kRows / 8));
+  struct Rsrc { __amdgpu_buffer_rsrc_t k, q, v, r; };
+  auto chunk_rsrc = [&](int cl) {   // local chunk index cl (may be past the end)
+    const int t0 = seq_beg + cl * kC;
+    const bool in = cl < n_chunks;
+    const uint32_t L = in ? (uint32_t)min(kC, seq_end - t0) : 0u;
+    Rsrc r;
+    r.k = make_rsrc(k + (int64_t)t0 * qk_stride + kh * kD, L * qk_row);
+    r.q = make_rsrc(q + (int64_t)t0 * qk_stride + kh * kD, L * qk_row);
+    r.v = make_rsrc(v + (int64_t)t0 * v_stride + h * kD + i0, L * v_row);
+    r.r = make_rsrc(rec_of(chunk0 + (in ? cl : 0)), in ? (uint32_t)kRecBytes : 0u);
+    return r;
+  };
+  auto load_piece = [&](const Rsrc& r, int i) {   // i < kLoads, a compile-time constant after unrolling
+    if (i < Cf::kPiecesKQ) {
+      st_k[i] = buf_load16(r.k, off_kq + (uint32_t)i * (kT / 16) * qk_row, 0);
+    } else if (i < 2 * Cf::kPiecesKQ) {
+      const int j = i - Cf::kPiecesKQ;
+      st_q[j] = buf_load16(r.q, off_kq + (uint32_t)j * (kT / 16) * qk_row, 0);
+    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
+      const int j = i - 2 * Cf::kPiecesKQ;
+      st_v[j] = buf_load16(r.v, off_v + (uint32_t)j * (kT / (Cf::kRows / 8)) * v_row, 0);
+    } else if (i < kLoads - 1) {
+      // slot fragment f = record fragment (Tt then Pt, x, hi / lo)
+      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      const int f = (tid + j * kT) / kWave;                 // uniform per wave
+      const int which = f / 12, x = (f % 12) / 2, hl = f % 2;
+      const int rf = 2 * (2 * frag_mt(x) + frag_ks(x)) + hl;
+      st_tri[j] = buf_load16(r.r, 16 * lane, (uint32_t)(which * kFragBytes + rf * 1024));
+    } else {
+      st_vec = buf_load16(r.r, 16 * (tid % kC), (uint32_t)(2 * kFragBytes));
+    }
+  };
+  auto commit_piece = [&](int slot, int i) {
+    uint8_t* base = s_in[slot];
+    if (i < 2 * Cf::kPiecesKQ) {
+      const int j = i % Cf::kPiecesKQ;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(base + (i < Cf::kPiecesKQ ? 0 : Cf::kOffQ));
+      const u32x4_t& val = i < Cf::kPiecesKQ ? st_k[j] : st_q[j];
+      const int p = tid + j * kT, r = p >> 4, c8 = 8 * (p & 15);
+      // logical columns c8 .. c8+3 and c8+4 .. c8+7 land as two 8-byte runs
+      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8)) = make_uint2(val[0], val[1]);
+      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8 + 4)) = make_uint2(val[2], val[3]);
+    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
+      const int j = i - 2 * Cf::kPiecesKQ;
+      const int p = tid + j * kT, r = p / (Cf::kRows / 8), c8 = 8 * (p % (Cf::kRows / 8));
+      *reinterpret_cast<u32x4_t*>(base + Cf::kOffV + 2 * (r * Cf::kVP + c8)) = st_v[j];
+    } else if (i < kLoads - 1) {
+      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * (tid + j * kT)) = st_tri[j];
+    } else if (tid < kC) {
+      reinterpret_cast<u32x4_t*>(base + Cf::kOffVec)[tid] = st_vec;
+    }
+  };
+
+  // ---- the state: S^T tiles jt = 0..7, lane holds S[i0 + iw + m][16 jt + 4 g + e] ----
+  f32x4_t sst[8];
+  {
+    const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD : nullptr;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+      sst[jt] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + 16 * jt + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (n_chunks > 0) {
+    const Rsrc r0 = chunk_rsrc(0);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_piece(r0, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) commit_piece(0, i);
+  }
+  // Let every load issued so far land here, once: otherwise the compiler's
+  // wait for the initial state (first used at the top of the chunk loop) is
+  // placed inside the loop and drains all prefetches on every chunk.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t orow = (uint32_t)(hv * kD * sizeof(To));
+  for (int cl = 0; cl < n_chunks; ++cl) {
+    const int slot = cl & 1;
+    const int t0 = seq_beg + cl * kC;
+    const int L = min(kC, seq_end - t0);
+    const uint8_t* base = s_in[slot];
+    const uint16_t* sk = reinterpret_cast<const uint16_t*>(base);
+    const uint16_t* sq = reinterpret_cast<const uint16_t*>(base + Cf::kOffQ);
+    const uint16_t* sv = reinterpret_cast<const uint16_t*>(base + Cf::kOffV);
+    const uint8_t* tri = base + Cf::kOffTri;
+    const float* vec = reinterpret_cast<const float*>(base + Cf::kOffVec);
+    auto tri_frag = [&](int which, int x, int hl) {
+      return load_bf16x8(reinterpret_cast<const uint16_t*>(tri + (which * 12 + 2 * x + hl) * 1024 + 16 * lane));
+    };
+
+    // LDS operands of the first k step of Y / Z, the V tile, the vectors
+    bf16x8_t fk[4], fq[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int off = (16 * mt + m) * kWP + 8 * g;
+      fk[mt] = load_bf16x8(sk + off);
+      fq[mt] = load_bf16x8(sq + off);
+    }
+    v4s_t vv[4];
+    f32x4_t va[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      vv[mt] = lds_read_tr4(sv + (16 * mt + 4 * g + (m >> 2)) * Cf::kVP + iw + 4 * (m & 3));
+      va[mt] = *reinterpret_cast<const f32x4_t*>(vec + 16 * mt + 4 * g);
+    }
+
+    // state as B operands (and, for Z^T = S Q^T, as A operands): k step ks = key tiles 2ks, 2ks+1
+    bf16x8_t sbh[4], sbl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) split_pair(sst[2 * ks], sst[2 * ks + 1], sbh[ks], sbl[ks]);
+
+    // ---- Y = K S0^T (rows t, columns i) and Z^T = S0 Q^T (rows i, columns t) ----
+    f32x4_t y[4], zt[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) y[mt] = zt[mt] = zero4;
+    // the next chunk's loads go out between these MFMAs, two per group of four
+    const Rsrc rn = chunk_rsrc(cl + 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8_t nk[4], nq[4];
+      if (ks < 3) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          const int off = (16 * mt + m) * kWP + 32 * (ks + 1) + 8 * g;
+          nk[mt] = load_bf16x8(sk + off);
+          nq[mt] = load_bf16x8(sq + off);
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        constexpr int kPer = (kLoads + 15) / 16;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int i = (4 * ks + mt) * kPer + u;
+          if (i < kLoads) load_piece(rn, i);
+        }
+        y[mt] = mfma_bf16(fk[mt], sbh[ks], y[mt]);
+        zt[mt] = mfma_bf16(sbh[ks], fq[mt], zt[mt]);
+        y[mt] = mfma_bf16(fk[mt], sbl[ks], y[mt]);
+        zt[mt] = mfma_bf16(sbl[ks], fq[mt], zt[mt]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (ks < 3) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) { fk[mt] = nk[mt]; fq[mt] = nq[mt]; }
+      }
+    }
+
+    // ---- R = V - a Y (accumulator layout: rows 16 mt + 4 g + e, column iw + m) ----
+    bf16x8_t rbh[2], rbl[2];
+    {
+      f32x4_t r[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) r[mt][e] = bf16_bits_to_f32((uint16_t)vv[mt][e]) - va[mt][e] * y[mt][e];
+      split_pair(r[0], r[1], rbh[0], rbl[0]);
+      split_pair(r[2], r[3], rbh[1], rbl[1]);
+    }
+
+    // K^T operands of the state update's first k step (transposing reads):
+    // A[j][slot (g, e)] = K[pair_k(ks, g, e)][16 jt + j]
+    bf16x8_t kt[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+      kt[jt] = lds_read_tr8(sk + (4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
+
+    // ---- Vnew = Tt R ----
+    f32x4_t vn[4];
+    {
+      bf16x8_t th[kNF], tl[kNF];
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) { th[x] = tri_frag(0, x, 0); tl[x] = tri_frag(0, x, 1); }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) vn[mt] = zero4;
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(th[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(th[x], rbl[frag_ks(x)], vn[frag_mt(x)]);
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(tl[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
+    }
+
+    bf16x8_t nbh[2], nbl[2], wbh[2], wbl[2];
+    split_pair(vn[0], vn[1], nbh[0], nbl[0]);
+    split_pair(vn[2], vn[3], nbh[1], nbl[1]);
+    {
+      f32x4_t w[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4_t c = *reinterpret_cast<const f32x4_t*>(vec + 2 * kC + 16 * mt + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[mt][e] = c[e] * vn[mt][e];
+      }
+      split_pair(w[0], w[1], wbh[0], wbl[0]);
+      split_pair(w[2], w[3], wbh[1], wbl[1]);
+    }
+
+    // The next chunk's inputs go to the other LDS slot in pieces between the
+    // remaining MFMAs (22 groups: U first half, O^T, U second half).
+    constexpr int kCPer = (kLoads + 21) / 22;
+    auto commit_group = [&](int grp_idx) {
+#pragma unroll
+      for (int uu = 0; uu < kCPer; ++uu) {
+        const int i = grp_idx * kCPer + uu;
+        if (i < kLoads) commit_piece(slot ^ 1, i);
+      }
+    };
+
+    // ---- U = K^T W (the state update without the decay) ----
+    f32x4_t u[8];
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      commit_group(jt);
+      u[jt] = mfma_bf16(kt[jt], wbh[0], zero4);
+      u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt)
+      kt[jt] = lds_read_tr8(sk + (32 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
+
+    // ---- O^T = Z^T diag(b) + Vnew^T Pt^T (rows i, columns t: A = Vnew pairs, B = Pt fragments) ----
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const float b = vec[kC + 16 * mt + m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
+    }
+    {
+      bf16x8_t ph[kNF], pl[kNF];
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) {
+        commit_group(8 + x);
+        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+        zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) {
+      commit_group(14 + jt);
+      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
+      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- S <- d S + U ----
+    {
+      const float d = vec[3 * kC];
+#pragma unroll
+      for (int jt = 0; jt < 8; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sst[jt][e] = fmaf(d, sst[jt][e], u[jt][e]);
+    }
+
+    // ---- the output: lane (g, m) of tile mt holds O[16 mt + m][iw + 4 g .. +3] ----
+    {
+      // rows past the end of the sequence fall outside the descriptor
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + ((int64_t)t0 * hv + h) * kD + i0 + iw, (uint32_t)L * orow);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
+    }
+    __syncthreads();
+  }
+
+  if (final_state) {
+    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD;
+#pragma unroll
+    for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4_t*>(s_out + 16 * jt + 4 * g) = sst[jt];
+  }
+}
+
 template <bool F32, bool kPC, typename Tin, typename To>
 hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_stride, const void* v,
                       int64_t v_stride, const float* g, const float* beta, const float* init_state,
                       const int32_t* cu_dev, int n, int total_chunks, void* out,
                       float* final_state, void* ws, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
+  // bf16 inputs with scalar decay: the register-resident spine (16 value rows
+  // per wave, 64 per workgroup) once it has enough workgroups to fill the
+  // chip; with fewer sequences the 8-wave, 32-row spine spreads one sequence
+  // over twice as many CUs and is faster.
+  constexpr int kNW = kWaveSpineWaves;
+  const int wave_blocks = n * d.hv * (kD / (16 * kNW));
+  const bool wave_spine = !F32 && !kPC && wave_blocks >= kWaveSpineMinBlocks;
   hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
                      reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
   hipError_t e = hipGetLastError();
@@ -1087,20 +1548,33 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
+    else if (!F32 && wave_spine)
+      hipLaunchKernelGGL((chunk_intra_kernel<false, uint16_t, true>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride, g, beta,
+                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     else
-      hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
+      hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, false>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int groups = n * d.hk;
-  const int members = (d.hv / d.hk) * (kD / kTile);
-  const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-  hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
-                     static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride,
-                     static_cast<const Tin*>(v), v_stride, g, init_state, cu_dev, n, d.hk, d.hv, w,
-                     static_cast<To*>(out), final_state);
+  if (!F32 && wave_spine) {
+    const int members = (d.hv / d.hk) * (kD / (16 * kNW));
+    const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<kNW, To>), dim3(blocks), dim3(kNW * kWave), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                       static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
+                       static_cast<To*>(out), final_state);
+  } else {
+    const int members = (d.hv / d.hk) * (kD / kTile);
+    const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
+    hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
+                       static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride,
+                       static_cast<const Tin*>(v), v_stride, g, init_state, cu_dev, n, d.hk, d.hv, w,
+                       static_cast<To*>(out), final_state);
+  }
   return hipGetLastError();
 }
 

@@ -225,6 +225,23 @@ def test_chunk_prefill_bf16_boundary_lengths(orc, T):
     check(host(fs), s_ref, TOL_BF16, f"chunk state T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["out_f32", "out_bf16"])
+def test_chunk_prefill_bf16_boundary_lengths_batched(orc, T, out_dtype):
+    """Three sequences per call: with 48 value heads that is enough workgroups for the
+    register-resident spine (one sequence alone runs the 8-wave spine)."""
+    lengths = [T, max(T - 1, 0), T + 1]
+    d = gi.gen_qkv(300 + T, lengths)
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                              initial_state=dev(d["state_in"]), out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    stored = out_dtype == torch.bfloat16
+    check(host(o), o_ref, TOL_BF16, f"batched chunk out {lengths}", stored_bf16=stored)
+    check(host(fs), s_ref, TOL_BF16, f"batched chunk state {lengths}")
+
+
 @pytest.mark.parametrize("T", [1, 64, 129])
 def test_chunk_prefill_fp32_boundary_lengths(orc, T):
     d = gi.gen_qkv(200 + T, [T], bf16=False)
