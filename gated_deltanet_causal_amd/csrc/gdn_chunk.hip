@@ -269,17 +269,19 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
     float tc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) tc[m] = (4 * m + part == c) ? 1.0f : 0.0f;
+    // A's row r, columns 4m + part, read up front (independent of the recurrence)
+    float ar[16][4];
+#pragma unroll
+    for (int r = 1; r < 16; ++r)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) ar[r][m] = (4 * m < r && 4 * m + part < r) ? Ab[r * kAP + 4 * m + part] : 0.0f;
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
       float acc = 0.0f;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (4 * m < r) {
-          const float a = Ab[r * kAP + 4 * m + part];
-          acc = fmaf(4 * m + part < r ? a : 0.0f, tc[m], acc);
-        }
-      }
-      acc = group_sum<4>(acc);
+      for (int m = 0; m < 4; ++m)
+        if (4 * m < r) acc = fmaf(ar[r][m], tc[m], acc);
+      acc = quad_sum(acc);
       if (r > c && (r & 3) == part) tc[r >> 2] = -acc;
     }
     float* Tb = sT + 16 * b * kAP + 16 * b;
@@ -335,23 +337,31 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
         reinterpret_cast<float*>(dst)[p] = kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
       }
     } else {
-      // fragment (mt, ks, term): lane l holds src[16mt + l%16][32ks + 8(l/16) + e]
-      for (int p = tid; p < 8 * kWave; p += kThreads) {
+      // fragment (mt, ks, term): lane l holds src[16mt + l%16][kk(e)], kk(e) = pair_k(ks, l/16, e)
+      // (paired-tile order) or 32ks + 8(l/16) + e; entries above the diagonal are zero.
+      // All loads are issued unconditionally (the upper part of sT is never
+      // written; the select drops those values).
+#pragma unroll
+      for (int it = 0; it < 8 * kWave / kThreads; ++it) {
+        const int p = tid + it * kThreads;
         const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
         const int mt = f / 2, ks = f % 2;
         const int r = 16 * mt + (l & 15);
-        bf16x8_t hi, lo;
+        float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int kk = kPairK ? pair_k(ks, l >> 4, e) : 32 * ks + 8 * (l >> 4) + e;
-          const float v = kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
-          __bf16 a, b;
-          split_bf16(v, a, b);
-          hi[e] = a;
-          lo[e] = b;
+          v[e] = src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f);
         }
-        *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 0) * kWave + l) * 16) = hi;
-        *reinterpret_cast<bf16x8_t*>(dst + ((size_t)(f * 2 + 1) * kWave + l) * 16) = lo;
+        uint32_t hp[4], lp[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int k0 = kPairK ? pair_k(ks, l >> 4, e) : 32 * ks + 8 * (l >> 4) + e;
+          const int k1 = kPairK ? pair_k(ks, l >> 4, e + 1) : k0 + 1;
+          split2(k0 <= r ? v[e] : 0.0f, k1 <= r ? v[e + 1] : 0.0f, hp[e / 2], lp[e / 2]);
+        }
+        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 0) * kWave + l) * 16) = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
+        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 1) * kWave + l) * 16) = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
       }
     }
   }
@@ -565,7 +575,8 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   float* sP = sA + kC * kAP;
   float* sT = sP + kC * kAP;
   __shared__ float sM[3 * 16 * 17];
-  __shared__ float s_rk[kC], s_rq[kC], s_gam[kC], s_beta[kC];
+  __shared__ __attribute__((aligned(16))) float s_rk[kC], s_rq[kC];
+  __shared__ __attribute__((aligned(16))) float s_gam[2][kC], s_beta[2][kC];   // per value head, double-buffered
 
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int c = blockIdx.x;
@@ -576,23 +587,73 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   const int L = min(kC, cu[n + 1] - t0);
   const int ratio = hv / hk;
 
-  load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-  load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
+  // cumulative log decay and beta of value head kh * ratio + hh (padded tokens
+  // decay by 1 and have beta 0), by wave 0: lane = token
+  auto gb_load = [&](int hh, float& gv, float& bv) {
+    const int h = kh * ratio + hh;
+    gv = lane < L ? g[(int64_t)(t0 + lane) * hv + h] : 0.0f;
+    bv = lane < L ? beta[(int64_t)(t0 + lane) * hv + h] : 0.0f;
+  };
+  auto gb_store = [&](int buf, float gv, float bv) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const float up = __shfl_up(gv, o, kWave);
+      if (lane >= o) gv += up;
+    }
+    s_gam[buf][lane] = gv;
+    s_beta[buf][lane] = bv;
+  };
+  float gv_next = 0.f, bv_next = 0.f;
+  if (wave == 0) gb_load(0, gv_next, bv_next);
+
+  // K and Q rows: all loads issued before the first store (rows past L read as zero)
+  {
+    constexpr int kPer = 16 / sizeof(Tin);
+    constexpr int kIt = kC * kD / kPer / kThreads;
+    u32x4_t rk_[kIt], rq_[kIt];
+    const Tin* kb = k + (int64_t)t0 * qk_stride + kh * kD;
+    const Tin* qb = q + (int64_t)t0 * qk_stride + kh * kD;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / kPer), c = (p % (kD / kPer)) * kPer;
+      const int rr = min(r, L - 1);
+      rk_[it] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)rr * qk_stride + c);
+      rq_[it] = *reinterpret_cast<const u32x4_t*>(qb + (int64_t)rr * qk_stride + c);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / kPer), c = (p % (kD / kPer)) * kPer;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(sK + r * kPitch + c) = r < L ? rk_[it] : z;
+      *reinterpret_cast<u32x4_t*>(sQ + r * kPitch + c) = r < L ? rq_[it] : z;
+    }
+  }
+  if (wave == 0) gb_store(0, gv_next, bv_next);
   __syncthreads();
 
-  // row norms: 4 threads per row, 32 elements each
+  // row norms: 4 threads per row, 32 elements each (16-byte reads)
   {
     const int r = tid / 4, part = tid % 4;
     float sk = 0.f, sq = 0.f;
-    for (int e = 0; e < 32; ++e) {
-      float kv, qv;
-      if constexpr (F32) { kv = sK[r * kPitch + part * 32 + e]; qv = sQ[r * kPitch + part * 32 + e]; }
-      else { kv = bf16_bits_to_f32(sK[r * kPitch + part * 32 + e]); qv = bf16_bits_to_f32(sQ[r * kPitch + part * 32 + e]); }
-      sk = fmaf(kv, kv, sk);
-      sq = fmaf(qv, qv, sq);
+#pragma unroll
+    for (int e4 = 0; e4 < 32; e4 += 16 / (int)sizeof(E)) {
+      const u32x4_t ku = *reinterpret_cast<const u32x4_t*>(sK + r * kPitch + part * 32 + e4);
+      const u32x4_t qu = *reinterpret_cast<const u32x4_t*>(sQ + r * kPitch + part * 32 + e4);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if constexpr (F32) {
+          sk = fmaf(__uint_as_float(ku[w]), __uint_as_float(ku[w]), sk);
+          sq = fmaf(__uint_as_float(qu[w]), __uint_as_float(qu[w]), sq);
+        } else {
+          const float k0 = __uint_as_float(ku[w] << 16), k1 = __uint_as_float(ku[w] & 0xffff0000u);
+          const float q0 = __uint_as_float(qu[w] << 16), q1 = __uint_as_float(qu[w] & 0xffff0000u);
+          sk = fmaf(k0, k0, fmaf(k1, k1, sk));
+          sq = fmaf(q0, q0, fmaf(q1, q1, sq));
+        }
+      }
     }
-    sk = group_sum<4>(sk);
-    sq = group_sum<4>(sq);
+    sk = quad_sum(sk);
+    sq = quad_sum(sq);
     if (part == 0) {
       s_rk[r] = r < L ? 1.0f / sqrtf(sk + l2_eps) : 0.0f;
       s_rq[r] = r < L ? q_scale / sqrtf(sq + l2_eps) : 0.0f;
@@ -619,32 +680,36 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     }
   }
 
+  __syncthreads();   // every wave's Gram tiles are in registers: the K / Q LDS becomes scratch
+
   for (int hh = 0; hh < ratio; ++hh) {
     const int h = kh * ratio + hh;
-    // cumulative log decay within the chunk (padded tokens decay by 1, beta 0)
-    if (wave == 0) {
-      float gv = lane < L ? g[(int64_t)(t0 + lane) * hv + h] : 0.0f;
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        const float up = __shfl_up(gv, o, kWave);
-        if (lane >= o) gv += up;
-      }
-      s_gam[lane] = gv;
-      s_beta[lane] = lane < L ? beta[(int64_t)(t0 + lane) * hv + h] : 0.0f;
-    }
-    __syncthreads();
+    const int buf = hh & 1;
+    if (wave == 0 && hh + 1 < ratio) gb_load(hh + 1, gv_next, bv_next);   // lands during this head
+    const float* gam = s_gam[buf];
+    const float* bet = s_beta[buf];
 
     // A (strictly lower) and Pt (lower incl. diagonal) from the Gram tiles
+    {
+      const int r0 = 16 * wave + 4 * (lane >> 4);
+      const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gam + r0);
+      const f32x4_t br = *reinterpret_cast<const f32x4_t*>(bet + r0);
+      const f32x4_t rkr = *reinterpret_cast<const f32x4_t*>(s_rk + r0);
+      const f32x4_t rqr = *reinterpret_cast<const f32x4_t*>(s_rq + r0);
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (nt <= wave) {
-        const int j = 16 * nt + (lane & 15);
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt <= wave) {
+          const int j = 16 * nt + (lane & 15);
+          const float gj = gam[j], rkj = s_rk[j];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * wave + 4 * (lane >> 4) + e;
-          const float dec = __expf(s_gam[r] - s_gam[j]);
-          sA[r * kAP + j] = j < r ? s_beta[r] * dec * s_rk[r] * s_rk[j] * accG[nt][e] : 0.0f;
-          sP[r * kAP + j] = j <= r ? s_rq[r] * s_rk[j] * dec * accH[nt][e] : 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = r0 + e;
+            const float dec = __expf(gr[e] - gj);
+            const float a = br[e] * dec * rkr[e] * rkj * accG[nt][e];
+            const float pv = rqr[e] * rkj * dec * accH[nt][e];
+            sA[r * kAP + j] = j < r ? a : 0.0f;
+            sP[r * kAP + j] = j <= r ? pv : 0.0f;
+          }
         }
       }
     }
@@ -652,18 +717,19 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
 
     // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
     uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
-    write_operands<F32, kAP, kPairK>(sA, sP, sT, sM, s_beta, rec);
+    write_operands<F32, kAP, kPairK>(sA, sP, sT, sM, bet, rec);
 
     // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
     if (tid < kC) {
       float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
-      const float gl = s_gam[kC - 1];
-      vec[tid] = __expf(s_gam[tid]) * s_rk[tid];
-      vec[kC + tid] = s_rq[tid] * __expf(s_gam[tid]);
-      vec[2 * kC + tid] = s_rk[tid] * __expf(gl - s_gam[tid]);
+      const float gl = gam[kC - 1];
+      vec[tid] = __expf(gam[tid]) * s_rk[tid];
+      vec[kC + tid] = s_rq[tid] * __expf(gam[tid]);
+      vec[2 * kC + tid] = s_rk[tid] * __expf(gl - gam[tid]);
       if (tid == 0) vec[3 * kC] = __expf(gl);
     }
-    __syncthreads();   // sA, sP, s_gam, s_beta are rewritten for the next value head
+    if (wave == 0 && hh + 1 < ratio) gb_store(buf ^ 1, gv_next, bv_next);
+    __syncthreads();   // sA, sP and this head's decay buffer are rewritten next
   }
 }
 
@@ -1118,16 +1184,6 @@ constexpr int kWP = kD + 16;   // K / Q row pitch in LDS (bf16 elements): 288 by
 // LDS column of logical column j of a K / Q row (paired-tile order per 32 columns)
 __device__ __forceinline__ int wave_col(int j) {
   return (j & ~31) + 8 * ((j >> 2) & 3) + 4 * ((j >> 4) & 1) + (j & 3);
-}
-
-// Two fp32 values -> their bf16 hi parts and bf16 lo parts (x = hi + lo up to
-// 2^-17 relative), each pair packed in one dword: three VALU ops per value.
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split2(float a, float b, uint32_t& hp, uint32_t& lp) {
-  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
-  const float ha = __uint_as_float(hp << 16), hb = __uint_as_float(hp & 0xffff0000u);
-  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
 }
 
 // two accumulator tiles -> one B operand in paired-tile k order, as hi and lo

@@ -49,6 +49,16 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = static_cast<__bf16>(x - static_cast<float>(hi));
 }
 
+// Two fp32 values -> their bf16 hi parts and bf16 lo parts (x = hi + lo up to
+// 2^-17 relative), each pair packed in one dword: three VALU ops per value.
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hp, uint32_t& lp) {
+  hp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+  const float ha = __uint_as_float(hp << 16), hb = __uint_as_float(hp & 0xffff0000u);
+  lp = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a - ha, b - hb}, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // MFMA 16x16 output tiles.  Accumulator layout (both instructions): lane l
 // holds C[4*(l/16) + r][l%16] in element r (r = 0..3).  Operand layout: lane l
@@ -85,6 +95,14 @@ template <int width>
 __device__ __forceinline__ float group_sum(float v) {
 #pragma unroll
   for (int o = width / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Sum over aligned groups of 4 lanes with DPP quad permutes (no LDS crossbar).
+__device__ __forceinline__ float quad_sum(float v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
   return v;
 }
 
