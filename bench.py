@@ -62,10 +62,19 @@ def t_dev(a, bf16=False):
 
 def time_calls(fn, n_sets, steps, warmup):
     """Run fn(i) warmup + steps times; time the steps with events on the current stream.
-    Returns (mean ms, per-step ms list)."""
+    Returns (mean ms, per-step ms list).  The mean comes from one event pair around all
+    steps (nothing recorded between launches); the per-step times from a second pass
+    with an event after every step."""
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i % n_sets)
+    e1.record()
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) / steps
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
@@ -73,7 +82,7 @@ def time_calls(fn, n_sets, steps, warmup):
         evs[i + 1].record()
     torch.cuda.synchronize()
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-    return evs[0].elapsed_time(evs[-1]) / steps, per
+    return mean, per
 
 
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size

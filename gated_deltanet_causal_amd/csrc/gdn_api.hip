@@ -182,6 +182,8 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
   if (!valid_dtype(o_dtype) || !valid_dtype(z_dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (rows < 0) return GDN_ERR_INVALID_ARG;
   if (rows > 0 && (!o || !z || !w || !out)) return GDN_ERR_INVALID_ARG;
+  if (rows > 0 && (!aligned16(o) || !aligned16(z) || !aligned16(w) || !aligned16(out)))
+    return GDN_ERR_INVALID_ARG;
   if (out != o && rows > 0) {
     const size_t n = (size_t)rows * d.hv * d.dv;
     if (overlaps(out, n * dsize(out_dtype), o, n * dsize(o_dtype))) return GDN_ERR_INVALID_ARG;

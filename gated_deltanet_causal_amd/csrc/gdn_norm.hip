@@ -8,9 +8,11 @@
 //
 //   out[i] = o[i] * rsqrt(mean_i o^2 + eps) * w[i] * sigmoid(z[i])
 //
-// One wavefront per vector of dv = 128: each lane owns two adjacent elements
-// (one 8-byte fp32 or 4-byte bf16 access, coalesced across the wave).  Pure
-// streaming: HBM-bound.
+// Sixteen lanes per vector of dv = 128: each lane owns eight adjacent elements
+// (16- or 32-byte accesses, coalesced across the wave), a wave covers four
+// vectors per step and takes two steps at once so each lane keeps two sets of
+// loads in flight.  The sum of squares is reduced inside each 16-lane row with
+// DPP.  Pure streaming: HBM-bound.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -18,23 +20,89 @@ namespace gdn {
 namespace {
 
 constexpr int kNormThreads = 256;
-constexpr int kVecPerBlock = kNormThreads / kWave;
+constexpr int kVecPerWaveStep = kWave / 16;                   // 4
+constexpr int kSteps = 2;                                     // vector groups per wave
+constexpr int kVecPerBlock = kNormThreads / kWave * kVecPerWaveStep * kSteps;   // 32
+
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  } else {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4_t u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * i], v[2 * i + 1]}, bf16x2_t));
+    *reinterpret_cast<u32x4_t*>(p) = u;
+  } else {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(p + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+// Sum over each row of 16 lanes (quad sums, then rotations by 4 and 8 lanes).
+__device__ __forceinline__ float row16_sum(float v) {
+  v = quad_sum(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+  return v;
+}
 
 template <typename Ti, typename Tz, typename To>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     const Ti* o, const Tz* __restrict__ z, const float* __restrict__ w, To* out,
     int64_t vectors, float eps) {
-  const int lane = threadIdx.x % kWave;
-  const int64_t vec = (int64_t)blockIdx.x * kVecPerBlock + threadIdx.x / kWave;
-  if (vec >= vectors) return;
-  const int64_t base = vec * 128 + 2 * lane;
-  const float o0 = ld(o + base), o1 = ld(o + base + 1);
-  const float ss = wave_sum(o0 * o0 + o1 * o1);
-  const float r = rsqrtf(ss * (1.0f / 128.0f) + eps);
-  const float y0 = o0 * r * w[2 * lane] * sigmoidf_(ld(z + base));
-  const float y1 = o1 * r * w[2 * lane + 1] * sigmoidf_(ld(z + base + 1));
-  st(out + base, y0);
-  st(out + base + 1, y1);
+  const int lane = threadIdx.x % kWave, q = lane & 15;
+  const int64_t first = (int64_t)blockIdx.x * kVecPerBlock +
+                        (threadIdx.x / kWave) * kVecPerWaveStep * kSteps + (lane >> 4);
+  float wv[8];
+  {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(w + 8 * q);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(w + 8 * q + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { wv[i] = a[i]; wv[4 + i] = b[i]; }
+  }
+  // vectors handled by this lane's row: first, first + 4 (rows of 16 lanes are
+  // all active or all inactive, so the row reduction never reads an idle lane)
+  float ov[kSteps][8], zv[kSteps][8];
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t vec = first + s * kVecPerWaveStep;
+    if (vec < vectors) {
+      ld8(o + vec * 128 + 8 * q, ov[s]);
+      ld8(z + vec * 128 + 8 * q, zv[s]);
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < kSteps; ++s) {
+    const int64_t vec = first + s * kVecPerWaveStep;
+    if (vec < vectors) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss = fmaf(ov[s][i], ov[s][i], ss);
+      ss = row16_sum(ss);
+      const float r = rsqrtf(ss * (1.0f / 128.0f) + eps);
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = ov[s][i] * r * wv[i] * sigmoidf_(zv[s][i]);
+      st8(out + vec * 128 + 8 * q, y);
+    }
+  }
 }
 
 template <typename Ti, typename Tz, typename To>

@@ -161,7 +161,8 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
  *     out[i] = o[i] * rsqrt(mean(o^2) + rms_eps) * w[i] * sigmoid(z[i])
  *   o     [rows][Hv][dv] in o_dtype;  z [rows][Hv][dv] in z_dtype
  *   w     fp32 [dv], shared by every head;  out [rows][Hv][dv] in out_dtype
- * out may equal o when o_dtype == out_dtype.
+ * out may equal o when o_dtype == out_dtype.  o, z, w and out are 16-byte
+ * aligned (GDN_ERR_INVALID_ARG otherwise).
  */
 gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn_dtype_t z_dtype,
                                gdn_dtype_t out_dtype, const void* o, const void* z,

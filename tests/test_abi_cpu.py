@@ -146,6 +146,10 @@ def test_decode_and_norm_argument_checks(lib):
     got = lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_F32, FAKE, FAKE, FAKE,
                                 ctypes.c_void_p(0x10000 + 256), 4, None)
     assert got == gdn.GDN_ERR_INVALID_ARG                                  # partial overlap
+    far = ctypes.c_void_p(0x40000000)
+    got = lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_BF16,
+                                ctypes.c_void_p(0x10000 + 8), FAKE, FAKE, far, 4, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                  # o not 16-byte aligned
 
 
 def test_empty_calls_launch_nothing(lib):
