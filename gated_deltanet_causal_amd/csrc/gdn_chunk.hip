@@ -54,7 +54,7 @@ constexpr size_t kRecBytes = 2 * kFragBytes + 1024;  // Tt, Pt, vectors
 constexpr int kSortMax = 4096;                 // longest-first order up to this many sequences
 constexpr int kXcds = 8;                       // XCDs; workgroups are dealt to them round-robin
 #ifndef GDN_WAVE_SPINE_WAVES
-#define GDN_WAVE_SPINE_WAVES 4
+#define GDN_WAVE_SPINE_WAVES 8
 #endif
 constexpr int kWaveSpineWaves = GDN_WAVE_SPINE_WAVES;   // waves per register-resident spine workgroup
 constexpr int kWaveSpineMinBlocks = 256;                 // ... used from this many workgroups (one per CU)
@@ -1589,9 +1589,10 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
                       float* final_state, void* ws, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   // bf16 inputs with scalar decay: the register-resident spine (16 value rows
-  // per wave, 64 per workgroup) once it has enough workgroups to fill the
-  // chip; with fewer sequences the 8-wave, 32-row spine spreads one sequence
-  // over twice as many CUs and is faster.
+  // per wave, a whole value head per workgroup, two waves per SIMD so one
+  // wave's VALU work overlaps the other's MFMAs) once it has a workgroup for
+  // every CU; with fewer sequences the 8-wave, 32-row spine spreads them over
+  // four times as many CUs and is faster.
   constexpr int kNW = kWaveSpineWaves;
   const int wave_blocks = n * d.hv * (kD / (16 * kNW));
   const bool wave_spine = !F32 && !kPC && wave_blocks >= kWaveSpineMinBlocks;

@@ -228,9 +228,9 @@ def test_chunk_prefill_bf16_boundary_lengths(orc, T):
 @pytest.mark.parametrize("T", [1, 63, 64, 65, 127, 128, 129])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16], ids=["out_f32", "out_bf16"])
 def test_chunk_prefill_bf16_boundary_lengths_batched(orc, T, out_dtype):
-    """Three sequences per call: with 48 value heads that is enough workgroups for the
-    register-resident spine (one sequence alone runs the 8-wave spine)."""
-    lengths = [T, max(T - 1, 0), T + 1]
+    """Six sequences per call: with 48 value heads that is a workgroup per CU, so the
+    register-resident spine runs (a single sequence runs the 8-wave, 32-row spine)."""
+    lengths = [T, max(T - 1, 0), T + 1, T, T + 1, max(T - 1, 0)]
     d = gi.gen_qkv(300 + T, lengths)
     o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
                               dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
