@@ -53,11 +53,11 @@ constexpr size_t kFragBytes = 16384;           // one 64x64 operand in lane layo
 constexpr size_t kRecBytes = 2 * kFragBytes + 1024;  // Tt, Pt, vectors
 constexpr int kSortMax = 4096;                 // longest-first order up to this many sequences
 constexpr int kXcds = 8;                       // XCDs; workgroups are dealt to them round-robin
-#ifndef GDN_WAVE_SPINE_WAVES
-#define GDN_WAVE_SPINE_WAVES 8
-#endif
-constexpr int kWaveSpineWaves = GDN_WAVE_SPINE_WAVES;   // waves per register-resident spine workgroup
-constexpr int kWaveSpineMinBlocks = 256;                 // ... used from this many workgroups (one per CU)
+// Spine kernels (the sequential walk over a sequence's chunks)
+constexpr int kSpineLds = 0;    // 8 waves per 32 value rows, intermediates through LDS (fp32, per key channel)
+constexpr int kSpineWave = 1;   // register-resident, a value head per workgroup
+constexpr int kSpinePair = 2;   // register-resident, two waves per 16 value rows (key halves)
+constexpr int kWaveSpineMinBlocks = 256;   // value heads x sequences from which kSpineWave is used
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1232,10 +1232,12 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t vo
   __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{lo, hi}, r, voff, 0, 0);
 }
 
-template <int kNW>
-struct WaveSpineCfg {
-  static constexpr int kThreadsW = kNW * kWave;
-  static constexpr int kRows = 16 * kNW;                  // value rows per workgroup
+// Workgroup shape of the register-resident spines: kThreadsT threads sharing
+// one chunk's inputs for kRowsT value rows of one head.
+template <int kThreadsT, int kRowsT>
+struct SpineCfg {
+  static constexpr int kThreadsW = kThreadsT;
+  static constexpr int kRows = kRowsT;                    // value rows per workgroup
   static constexpr int kVP = kRows + 8;                   // V row pitch (bf16)
   // one LDS slot (bytes): K | Q | V (bf16) | Tt, Pt fragments | chunk vectors
   static constexpr int kOffQ = kC * kWP * 2;
@@ -1245,8 +1247,11 @@ struct WaveSpineCfg {
   static constexpr int kOffVec = kOffTri + kTriFrags * 1024;
   static constexpr int kSlotBytes = kOffVec + 1024;
   static constexpr int kPiecesKQ = kC * kD / 8 / kThreadsW;    // 16-byte pieces of K (and Q) per thread
-  static constexpr int kPiecesV = kC * kRows / 8 / kThreadsW;  // ... of V: 2
+  static constexpr int kPiecesV = kC * kRows / 8 / kThreadsW;  // ... of V
   static constexpr int kPiecesTri = kTriFrags * kWave / kThreadsW;
+  static constexpr int kLoads = 2 * kPiecesKQ + kPiecesV + kPiecesTri + 1;   // + the vectors
+  static_assert(kPiecesKQ * kThreadsW == kC * kD / 8 && kPiecesV * kThreadsW == kC * kRows / 8 &&
+                kPiecesTri * kThreadsW == kTriFrags * kWave, "pieces must divide evenly over the threads");
 };
 
 // Tt / Pt fragments (mt, ks) with ks <= mt / 2 (the rest of the 64 x 64 is zero)
@@ -1254,15 +1259,107 @@ constexpr int kNF = 6;
 __host__ __device__ constexpr int frag_mt(int x) { return x < 4 ? x : x - 2; }     // 0 1 2 3 2 3
 __host__ __device__ constexpr int frag_ks(int x) { return x < 4 ? 0 : 1; }         // 0 0 0 0 1 1
 
-template <int kNW, typename To>
+// One chunk's inputs (K and Q rows, the workgroup's V columns, the Tt / Pt
+// fragments and the chunk vectors of its record) staged through registers into
+// an LDS slot, one 16-byte piece per call so the loads and the LDS writes can
+// be spread between MFMAs.  Per chunk a buffer descriptor covers its rows:
+// rows past the end of the sequence load as zeros, and a chunk past the end of
+// the sequence has an empty range (no access at all).
+template <typename Cf>
+struct ChunkStage {
+  u32x4_t k[Cf::kPiecesKQ], q[Cf::kPiecesKQ], v[Cf::kPiecesV], tri[Cf::kPiecesTri], vec;
+  struct Rsrc { __amdgpu_buffer_rsrc_t k, q, v, r; };
+  const uint16_t *kp, *qp, *vp;      // key head / value head / value row base of row 0
+  int64_t qk_stride, v_stride;
+  const uint8_t* rec0;               // the sequence's first record of this value head
+  size_t rec_step;                   // bytes between the records of consecutive chunks
+  int seq_beg, seq_end, n_chunks, tid;
+  uint32_t qk_row, v_row, off_kq, off_v;
+
+  __device__ void init() {
+    qk_row = (uint32_t)qk_stride * 2;
+    v_row = (uint32_t)v_stride * 2;
+    off_kq = (uint32_t)(tid >> 4) * qk_row + 16 * (tid & 15);
+    off_v = (uint32_t)(tid / (Cf::kRows / 8)) * v_row + 16 * (tid % (Cf::kRows / 8));
+  }
+  __device__ Rsrc rsrc(int cl) const {   // local chunk index cl (may be past the end)
+    const int t0 = seq_beg + cl * kC;
+    const bool in = cl < n_chunks;
+    const uint32_t L = in ? (uint32_t)min(kC, seq_end - t0) : 0u;
+    Rsrc r;
+    r.k = make_rsrc(kp + (int64_t)t0 * qk_stride, L * qk_row);
+    r.q = make_rsrc(qp + (int64_t)t0 * qk_stride, L * qk_row);
+    r.v = make_rsrc(vp + (int64_t)t0 * v_stride, L * v_row);
+    r.r = make_rsrc(rec0 + (in ? cl : 0) * rec_step, in ? (uint32_t)kRecBytes : 0u);
+    return r;
+  }
+  __device__ void load(const Rsrc& r, int i) {   // i < kLoads, a compile-time constant after unrolling
+    constexpr int kT = Cf::kThreadsW;
+    if (i < Cf::kPiecesKQ) {
+      k[i] = buf_load16(r.k, off_kq + (uint32_t)i * (kT / 16) * qk_row, 0);
+    } else if (i < 2 * Cf::kPiecesKQ) {
+      const int j = i - Cf::kPiecesKQ;
+      q[j] = buf_load16(r.q, off_kq + (uint32_t)j * (kT / 16) * qk_row, 0);
+    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
+      const int j = i - 2 * Cf::kPiecesKQ;
+      v[j] = buf_load16(r.v, off_v + (uint32_t)j * (kT / (Cf::kRows / 8)) * v_row, 0);
+    } else if (i < Cf::kLoads - 1) {
+      // slot fragment f = record fragment (Tt then Pt, x, hi / lo)
+      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      const int f = (tid + j * kT) / kWave;                 // uniform per wave
+      const int which = f / 12, x = (f % 12) / 2, hl = f % 2;
+      const int rf = 2 * (2 * frag_mt(x) + frag_ks(x)) + hl;
+      tri[j] = buf_load16(r.r, 16 * (tid % kWave), (uint32_t)(which * kFragBytes + rf * 1024));
+    } else {
+      vec = buf_load16(r.r, 16 * (tid % kC), (uint32_t)(2 * kFragBytes));
+    }
+  }
+  __device__ void commit(uint8_t* base, int i) const {
+    constexpr int kT = Cf::kThreadsW;
+    if (i < 2 * Cf::kPiecesKQ) {
+      const int j = i % Cf::kPiecesKQ;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(base + (i < Cf::kPiecesKQ ? 0 : Cf::kOffQ));
+      const u32x4_t& val = i < Cf::kPiecesKQ ? k[j] : q[j];
+      const int p = tid + j * kT, r = p >> 4, c8 = 8 * (p & 15);
+      // logical columns c8 .. c8+3 and c8+4 .. c8+7 land as two 8-byte runs
+      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8)) = make_uint2(val[0], val[1]);
+      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8 + 4)) = make_uint2(val[2], val[3]);
+    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
+      const int j = i - 2 * Cf::kPiecesKQ;
+      const int p = tid + j * kT, r = p / (Cf::kRows / 8), c8 = 8 * (p % (Cf::kRows / 8));
+      *reinterpret_cast<u32x4_t*>(base + Cf::kOffV + 2 * (r * Cf::kVP + c8)) = v[j];
+    } else if (i < Cf::kLoads - 1) {
+      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * (tid + j * kT)) = tri[j];
+    } else if (tid < kC) {
+      reinterpret_cast<u32x4_t*>(base + Cf::kOffVec)[tid] = vec;
+    }
+  }
+};
+
+// Register-resident spine.  kNW waves per workgroup; kSplit waves share each
+// block of 16 value rows, wave `half` of a block owning key columns
+// [128 half / kSplit, 128 (half + 1) / kSplit) of its state:
+//   kSplit = 1: a wave holds all 128 key columns of its 16 rows (every product
+//               of the chunk step is wave-local);
+//   kSplit = 2: Y = K S0^T and Z^T = S0 Q^T are summed over the two halves
+//               through LDS once per chunk; both waves then form R, Vnew and W
+//               (shared work), each updates its own half of the state and
+//               writes two of the four 16-token tiles of the output.  The
+//               chain that carries the state from chunk to chunk is half as
+//               long per wave, which is what a single sequence waits on.
+template <int kNW, int kSplit, typename To>
 __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
     const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
     To* __restrict__ out, float* final_state) {
-  using Cf = WaveSpineCfg<kNW>;
-  constexpr int kT = Cf::kThreadsW;
+  using Cf = SpineCfg<kNW * kWave, 16 * kNW / kSplit>;
+  constexpr int kKS = 4 / kSplit;                 // 32-key steps of a wave's state
+  constexpr int kJT = 8 / kSplit;                 // 16-key tiles of a wave's state
+  constexpr int kExch = kSplit == 2 ? kNW * 6 * 1024 : 16;   // per wave: Y and two Z^T partial tiles
   __shared__ __attribute__((aligned(1024))) uint8_t s_in[2][Cf::kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t s_ex[kExch];
 
   // block -> (sequence, key head) group and member (value head, row block);
   // the members of a group get block ids congruent mod kXcds (one XCD, one L2)
@@ -1282,95 +1379,46 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
   const int i0 = (member % blocks_per_head) * Cf::kRows;     // first value row of the workgroup
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int iw = 16 * wave;                                  // the wave's rows within the block
+  const int half = wave % kSplit;                            // key half (kSplit = 2)
+  const int iw = 16 * (wave / kSplit);                       // the wave's rows within the block
+  const int jh = half * (kD / kSplit);                       // the wave's first key column
   const int g = lane >> 4, m = lane & 15;
-  const uint8_t* recs = ws + records_offset(n_seq);
   const int seq_beg = cu[n], seq_end = cu[n + 1];
-  const int chunk0 = first[n];
   const int n_chunks = (seq_end - seq_beg + kC - 1) / kC;
-  auto rec_of = [&](int cidx) { return recs + ((size_t)cidx * hv + h) * kRecBytes; };
 
-  // ---- staging of a chunk's inputs through registers ----
-  // The loads for chunk cl+1 are issued in pieces between the MFMAs of chunk
-  // cl's first products, and written to the other LDS slot in pieces between
-  // its last products, so neither the texture path nor LDS sees a burst.  Per
-  // chunk a descriptor covers its rows: rows past the end of the sequence load
-  // as zeros, and a chunk past the end of the sequence has an empty range (no
-  // access at all).
-  u32x4_t st_k[Cf::kPiecesKQ], st_q[Cf::kPiecesKQ], st_v[Cf::kPiecesV], st_tri[Cf::kPiecesTri], st_vec;
-  constexpr int kLoads = 2 * Cf::kPiecesKQ + Cf::kPiecesV + Cf::kPiecesTri + 1;
-  const uint32_t qk_row = (uint32_t)qk_stride * 2, v_row = (uint32_t)v_stride * 2;
-  const uint32_t off_kq = (uint32_t)(tid >> 4) * qk_row + 16 * (tid & 15);
-  const uint32_t off_v = (uint32_t)(tid / (Cf::kRows / 8)) * v_row + 16 * (tid % (Cf::kRows / 8));
-  struct Rsrc { __amdgpu_buffer_rsrc_t k, q, v, r; };
-  auto chunk_rsrc = [&](int cl) {   // local chunk index cl (may be past the end)
-    const int t0 = seq_beg + cl * kC;
-    const bool in = cl < n_chunks;
-    const uint32_t L = in ? (uint32_t)min(kC, seq_end - t0) : 0u;
-    Rsrc r;
-    r.k = make_rsrc(k + (int64_t)t0 * qk_stride + kh * kD, L * qk_row);
-    r.q = make_rsrc(q + (int64_t)t0 * qk_stride + kh * kD, L * qk_row);
-    r.v = make_rsrc(v + (int64_t)t0 * v_stride + h * kD + i0, L * v_row);
-    r.r = make_rsrc(rec_of(chunk0 + (in ? cl : 0)), in ? (uint32_t)kRecBytes : 0u);
-    return r;
-  };
-  auto load_piece = [&](const Rsrc& r, int i) {   // i < kLoads, a compile-time constant after unrolling
-    if (i < Cf::kPiecesKQ) {
-      st_k[i] = buf_load16(r.k, off_kq + (uint32_t)i * (kT / 16) * qk_row, 0);
-    } else if (i < 2 * Cf::kPiecesKQ) {
-      const int j = i - Cf::kPiecesKQ;
-      st_q[j] = buf_load16(r.q, off_kq + (uint32_t)j * (kT / 16) * qk_row, 0);
-    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
-      const int j = i - 2 * Cf::kPiecesKQ;
-      st_v[j] = buf_load16(r.v, off_v + (uint32_t)j * (kT / (Cf::kRows / 8)) * v_row, 0);
-    } else if (i < kLoads - 1) {
-      // slot fragment f = record fragment (Tt then Pt, x, hi / lo)
-      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
-      const int f = (tid + j * kT) / kWave;                 // uniform per wave
-      const int which = f / 12, x = (f % 12) / 2, hl = f % 2;
-      const int rf = 2 * (2 * frag_mt(x) + frag_ks(x)) + hl;
-      st_tri[j] = buf_load16(r.r, 16 * lane, (uint32_t)(which * kFragBytes + rf * 1024));
-    } else {
-      st_vec = buf_load16(r.r, 16 * (tid % kC), (uint32_t)(2 * kFragBytes));
-    }
-  };
-  auto commit_piece = [&](int slot, int i) {
-    uint8_t* base = s_in[slot];
-    if (i < 2 * Cf::kPiecesKQ) {
-      const int j = i % Cf::kPiecesKQ;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(base + (i < Cf::kPiecesKQ ? 0 : Cf::kOffQ));
-      const u32x4_t& val = i < Cf::kPiecesKQ ? st_k[j] : st_q[j];
-      const int p = tid + j * kT, r = p >> 4, c8 = 8 * (p & 15);
-      // logical columns c8 .. c8+3 and c8+4 .. c8+7 land as two 8-byte runs
-      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8)) = make_uint2(val[0], val[1]);
-      *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8 + 4)) = make_uint2(val[2], val[3]);
-    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
-      const int j = i - 2 * Cf::kPiecesKQ;
-      const int p = tid + j * kT, r = p / (Cf::kRows / 8), c8 = 8 * (p % (Cf::kRows / 8));
-      *reinterpret_cast<u32x4_t*>(base + Cf::kOffV + 2 * (r * Cf::kVP + c8)) = st_v[j];
-    } else if (i < kLoads - 1) {
-      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
-      *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * (tid + j * kT)) = st_tri[j];
-    } else if (tid < kC) {
-      reinterpret_cast<u32x4_t*>(base + Cf::kOffVec)[tid] = st_vec;
-    }
-  };
+  ChunkStage<Cf> stage;
+  stage.kp = k + kh * kD;
+  stage.qp = q + kh * kD;
+  stage.vp = v + h * kD + i0;
+  stage.qk_stride = qk_stride;
+  stage.v_stride = v_stride;
+  stage.rec0 = ws + records_offset(n_seq) + ((size_t)first[n] * hv + h) * kRecBytes;
+  stage.rec_step = (size_t)hv * kRecBytes;
+  stage.seq_beg = seq_beg;
+  stage.seq_end = seq_end;
+  stage.n_chunks = n_chunks;
+  stage.tid = tid;
+  stage.init();
+  constexpr int kLoads = Cf::kLoads;
 
-  // ---- the state: S^T tiles jt = 0..7, lane holds S[i0 + iw + m][16 jt + 4 g + e] ----
-  f32x4_t sst[8];
+  // output tiles of this wave: all four, or (kSplit = 2) mt = half and half + 2
+  auto owns_mt = [&](int mt) { return kSplit == 1 || (mt & 1) == half; };
+
+  // ---- the state: S^T tiles, lane holds S[i0 + iw + m][jh + 16 jt + 4 g + e], jt < kJT ----
+  f32x4_t sst[kJT];
   {
-    const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD : nullptr;
+    const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh : nullptr;
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
+    for (int jt = 0; jt < kJT; ++jt)
       sst[jt] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + 16 * jt + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
   if (n_chunks > 0) {
-    const Rsrc r0 = chunk_rsrc(0);
+    const auto r0 = stage.rsrc(0);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_piece(r0, i);
+    for (int i = 0; i < kLoads; ++i) stage.load(r0, i);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) commit_piece(0, i);
+    for (int i = 0; i < kLoads; ++i) stage.commit(s_in[0], i);
   }
   // Let every load issued so far land here, once: otherwise the compiler's
   // wait for the initial state (first used at the top of the chunk loop) is
@@ -1398,7 +1446,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     bf16x8_t fk[4], fq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int off = (16 * mt + m) * kWP + 8 * g;
+      const int off = (16 * mt + m) * kWP + jh + 8 * g;
       fk[mt] = load_bf16x8(sk + off);
       fq[mt] = load_bf16x8(sq + off);
     }
@@ -1411,34 +1459,34 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     }
 
     // state as B operands (and, for Z^T = S Q^T, as A operands): k step ks = key tiles 2ks, 2ks+1
-    bf16x8_t sbh[4], sbl[4];
+    bf16x8_t sbh[kKS], sbl[kKS];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) split_pair(sst[2 * ks], sst[2 * ks + 1], sbh[ks], sbl[ks]);
+    for (int ks = 0; ks < kKS; ++ks) split_pair(sst[2 * ks], sst[2 * ks + 1], sbh[ks], sbl[ks]);
 
-    // ---- Y = K S0^T (rows t, columns i) and Z^T = S0 Q^T (rows i, columns t) ----
+    // ---- Y = K S0^T (rows t, columns i) and Z^T = S0 Q^T (rows i, columns t), over this wave's keys ----
     f32x4_t y[4], zt[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) y[mt] = zt[mt] = zero4;
-    // the next chunk's loads go out between these MFMAs, two per group of four
-    const Rsrc rn = chunk_rsrc(cl + 1);
+    // the next chunk's loads go out between these MFMAs
+    const auto rn = stage.rsrc(cl + 1);
+    constexpr int kLPer = (kLoads + 4 * kKS - 1) / (4 * kKS);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+    for (int ks = 0; ks < kKS; ++ks) {
       bf16x8_t nk[4], nq[4];
-      if (ks < 3) {
+      if (ks + 1 < kKS) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int off = (16 * mt + m) * kWP + 32 * (ks + 1) + 8 * g;
+          const int off = (16 * mt + m) * kWP + jh + 32 * (ks + 1) + 8 * g;
           nk[mt] = load_bf16x8(sk + off);
           nq[mt] = load_bf16x8(sq + off);
         }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        constexpr int kPer = (kLoads + 15) / 16;
 #pragma unroll
-        for (int u = 0; u < kPer; ++u) {
-          const int i = (4 * ks + mt) * kPer + u;
-          if (i < kLoads) load_piece(rn, i);
+        for (int u = 0; u < kLPer; ++u) {
+          const int i = (4 * ks + mt) * kLPer + u;
+          if (i < kLoads) stage.load(rn, i);
         }
         y[mt] = mfma_bf16(fk[mt], sbh[ks], y[mt]);
         zt[mt] = mfma_bf16(sbh[ks], fq[mt], zt[mt]);
@@ -1446,10 +1494,25 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
         zt[mt] = mfma_bf16(sbl[ks], fq[mt], zt[mt]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (ks < 3) {
+      if (ks + 1 < kKS) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) { fk[mt] = nk[mt]; fq[mt] = nq[mt]; }
       }
+    }
+
+    if constexpr (kSplit == 2) {
+      // sum the two key halves: Y for all four token tiles, Z^T for the partner's tiles
+      f32x4_t* mine = reinterpret_cast<f32x4_t*>(s_ex + wave * 6 * 1024) + lane;
+      const f32x4_t* other = reinterpret_cast<const f32x4_t*>(s_ex + (wave ^ 1) * 6 * 1024) + lane;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) mine[mt * kWave] = y[mt];
+      mine[4 * kWave] = zt[1 - half];
+      mine[5 * kWave] = zt[3 - half];
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) y[mt] += other[mt * kWave];
+      zt[half] += other[4 * kWave];
+      zt[half + 2] += other[5 * kWave];
     }
 
     // ---- R = V - a Y (accumulator layout: rows 16 mt + 4 g + e, column iw + m) ----
@@ -1464,12 +1527,12 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
       split_pair(r[2], r[3], rbh[1], rbl[1]);
     }
 
-    // K^T operands of the state update's first k step (transposing reads):
-    // A[j][slot (g, e)] = K[pair_k(ks, g, e)][16 jt + j]
-    bf16x8_t kt[8];
+    // K^T operands of the state update's first k step (transposing reads), this wave's key tiles:
+    // A[j][slot (g, e)] = K[pair_k(ks, g, e)][jh + 16 jt + j]
+    bf16x8_t kt[kJT];
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-      kt[jt] = lds_read_tr8(sk + (4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
+    for (int jt = 0; jt < kJT; ++jt)
+      kt[jt] = lds_read_tr8(sk + (4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
 
     // ---- Vnew = Tt R ----
     f32x4_t vn[4];
@@ -1503,53 +1566,61 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     }
 
     // The next chunk's inputs go to the other LDS slot in pieces between the
-    // remaining MFMAs (22 groups: U first half, O^T, U second half).
-    constexpr int kCPer = (kLoads + 21) / 22;
+    // remaining MFMAs (groups: U first half, O^T, U second half).
+    constexpr int kCGroups = 2 * kJT + kNF;
+    constexpr int kCPer = (kLoads + kCGroups - 1) / kCGroups;
     auto commit_group = [&](int grp_idx) {
 #pragma unroll
       for (int uu = 0; uu < kCPer; ++uu) {
         const int i = grp_idx * kCPer + uu;
-        if (i < kLoads) commit_piece(slot ^ 1, i);
+        if (i < kLoads) stage.commit(s_in[slot ^ 1], i);
       }
     };
 
-    // ---- U = K^T W (the state update without the decay) ----
-    f32x4_t u[8];
+    // ---- U = K^T W on this wave's key tiles (the state update without the decay) ----
+    f32x4_t u[kJT];
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
+    for (int jt = 0; jt < kJT; ++jt) {
       commit_group(jt);
       u[jt] = mfma_bf16(kt[jt], wbh[0], zero4);
       u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt)
-      kt[jt] = lds_read_tr8(sk + (32 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
+    for (int jt = 0; jt < kJT; ++jt)
+      kt[jt] = lds_read_tr8(sk + (32 + 4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
 
-    // ---- O^T = Z^T diag(b) + Vnew^T Pt^T (rows i, columns t: A = Vnew pairs, B = Pt fragments) ----
+    // ---- O^T = Z^T diag(b) + Vnew^T Pt^T on this wave's token tiles ----
+    // (rows i, columns t: A = Vnew pairs, B = Pt fragments)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const float b = vec[kC + 16 * mt + m];
+      if (owns_mt(mt)) {
+        const float b = vec[kC + 16 * mt + m];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
+        for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
+      }
     }
     {
       bf16x8_t ph[kNF], pl[kNF];
 #pragma unroll
-      for (int x = 0; x < kNF; ++x) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+      for (int x = 0; x < kNF; ++x) {
+        if (owns_mt(frag_mt(x))) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+      }
 #pragma unroll
       for (int x = 0; x < kNF; ++x) {
-        commit_group(8 + x);
-        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-        zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
+        commit_group(kJT + x);
+        if (owns_mt(frag_mt(x))) {
+          zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+          zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+          zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
 
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) {
-      commit_group(14 + jt);
+    for (int jt = 0; jt < kJT; ++jt) {
+      commit_group(kJT + kNF + jt);
       u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
       u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
       __builtin_amdgcn_sched_barrier(0);
@@ -1559,7 +1630,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     {
       const float d = vec[3 * kC];
 #pragma unroll
-      for (int jt = 0; jt < 8; ++jt)
+      for (int jt = 0; jt < kJT; ++jt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) sst[jt][e] = fmaf(d, sst[jt][e], u[jt][e]);
     }
@@ -1570,15 +1641,15 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + ((int64_t)t0 * hv + h) * kD + i0 + iw, (uint32_t)L * orow);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
+        if (owns_mt(mt)) buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
     }
     __syncthreads();
   }
 
   if (final_state) {
-    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD;
+    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh;
 #pragma unroll
-    for (int jt = 0; jt < 8; ++jt) *reinterpret_cast<f32x4_t*>(s_out + 16 * jt + 4 * g) = sst[jt];
+    for (int jt = 0; jt < kJT; ++jt) *reinterpret_cast<f32x4_t*>(s_out + 16 * jt + 4 * g) = sst[jt];
   }
 }
 
@@ -1588,14 +1659,14 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
                       const int32_t* cu_dev, int n, int total_chunks, void* out,
                       float* final_state, void* ws, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  // bf16 inputs with scalar decay: the register-resident spine (16 value rows
-  // per wave, a whole value head per workgroup, two waves per SIMD so one
-  // wave's VALU work overlaps the other's MFMAs) once it has a workgroup for
-  // every CU; with fewer sequences the 8-wave, 32-row spine spreads them over
-  // four times as many CUs and is faster.
-  constexpr int kNW = kWaveSpineWaves;
-  const int wave_blocks = n * d.hv * (kD / (16 * kNW));
-  const bool wave_spine = !F32 && !kPC && wave_blocks >= kWaveSpineMinBlocks;
+  // bf16 inputs with scalar decay run a register-resident spine: a whole
+  // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
+  // work overlaps the other's MFMAs) once there is a workgroup for every CU;
+  // for fewer sequences the key-split form (two waves per 16 value rows, four
+  // waves and 32 rows per workgroup) spreads them over eight times as many
+  // workgroups and halves each wave's serial work per chunk.
+  const int head_blocks = n * d.hv;
+  const int spine = F32 || kPC ? kSpineLds : (head_blocks >= kWaveSpineMinBlocks ? kSpineWave : kSpinePair);
   hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
                      reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
   hipError_t e = hipGetLastError();
@@ -1605,26 +1676,29 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
-    else if (!F32 && wave_spine)
-      hipLaunchKernelGGL((chunk_intra_kernel<false, uint16_t, true>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride, g, beta,
-                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
-    else
-      hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, false>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
+    else   // bf16: records in the paired-tile k order of the register-resident spines
+      hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, !F32>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int groups = n * d.hk;
-  if (!F32 && wave_spine) {
-    const int members = (d.hv / d.hk) * (kD / (16 * kNW));
+  if (!F32 && spine == kSpineWave) {
+    const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<kNW, To>), dim3(blocks), dim3(kNW * kWave), 0, s,
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, To>), dim3(blocks), dim3(8 * kWave), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state);
-  } else {
+  } else if (!F32 && spine == kSpinePair) {
+    const int members = (d.hv / d.hk) * (kD / 32);
+    const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<4, 2, To>), dim3(blocks), dim3(4 * kWave), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                       static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
+                       static_cast<To*>(out), final_state);
+  } else if constexpr (F32 || kPC) {
     const int members = (d.hv / d.hk) * (kD / kTile);
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
