@@ -38,6 +38,7 @@
 // uses fp32 MFMA instead.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "gdn_device.h"
 #include "gdn_launch.h"
@@ -58,6 +59,10 @@ constexpr int kSpineLds = 0;    // 8 waves per 32 value rows, intermediates thro
 constexpr int kSpineWave = 1;   // register-resident, a value head per workgroup
 constexpr int kSpinePair = 2;   // register-resident, two waves per 16 value rows (key halves)
 constexpr int kWaveSpineMinBlocks = 256;   // value heads x sequences from which kSpineWave is used
+#ifndef GDN_PAIR_LOADERS
+#define GDN_PAIR_LOADERS 2
+#endif
+constexpr int kPairLoaders = GDN_PAIR_LOADERS;   // loader waves of the key-split spine
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1309,11 +1314,20 @@ struct ChunkStage {
       const int f = (tid + j * kT) / kWave;                 // uniform per wave
       const int which = f / 12, x = (f % 12) / 2, hl = f % 2;
       const int rf = 2 * (2 * frag_mt(x) + frag_ks(x)) + hl;
-      tri[j] = buf_load16(r.r, 16 * (tid % kWave), (uint32_t)(which * kFragBytes + rf * 1024));
+      tri[j] = buf_load16(r.r, 16 * (tid % kWave) + (uint32_t)(which * kFragBytes + rf * 1024), 0);
     } else {
-      vec = buf_load16(r.r, 16 * (tid % kC), (uint32_t)(2 * kFragBytes));
+      vec = buf_load16(r.r, 16 * (tid % kC) + (uint32_t)(2 * kFragBytes), 0);
     }
   }
+  // every piece, with each index a compile-time constant (so the staging
+  // registers are never indexed at run time)
+  template <int... I>
+  __device__ void load_seq(const Rsrc& r, std::integer_sequence<int, I...>) { (load(r, I), ...); }
+  template <int... I>
+  __device__ void commit_seq(uint8_t* base, std::integer_sequence<int, I...>) const { (commit(base, I), ...); }
+  __device__ void load_all(const Rsrc& r) { load_seq(r, std::make_integer_sequence<int, Cf::kLoads>{}); }
+  __device__ void commit_all(uint8_t* base) const { commit_seq(base, std::make_integer_sequence<int, Cf::kLoads>{}); }
+
   __device__ void commit(uint8_t* base, int i) const {
     constexpr int kT = Cf::kThreadsW;
     if (i < 2 * Cf::kPiecesKQ) {
@@ -1348,13 +1362,18 @@ struct ChunkStage {
 //               writes two of the four 16-token tiles of the output.  The
 //               chain that carries the state from chunk to chunk is half as
 //               long per wave, which is what a single sequence waits on.
-template <int kNW, int kSplit, typename To>
-__global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
+// kLoaders > 0 adds that many loader waves: they stage chunk cl+1 into the other
+// LDS slot while the kNW compute waves work on chunk cl, so the compute waves
+// never wait at the texture path; without them the compute waves stage in
+// pieces between their MFMAs.
+template <int kNW, int kSplit, int kLoaders, typename To>
+__global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
     const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
     To* __restrict__ out, float* final_state) {
   using Cf = SpineCfg<kNW * kWave, 16 * kNW / kSplit>;
+  using StageCf = SpineCfg<(kLoaders > 0 ? kLoaders : kNW) * kWave, Cf::kRows>;   // same LDS layout
   constexpr int kKS = 4 / kSplit;                 // 32-key steps of a wave's state
   constexpr int kJT = 8 / kSplit;                 // 16-key tiles of a wave's state
   constexpr int kExch = kSplit == 2 ? kNW * 6 * 1024 : 16;   // per wave: Y and two Z^T partial tiles
@@ -1386,7 +1405,8 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
   const int seq_beg = cu[n], seq_end = cu[n + 1];
   const int n_chunks = (seq_end - seq_beg + kC - 1) / kC;
 
-  ChunkStage<Cf> stage;
+  const bool loader = kLoaders > 0 && wave >= kNW;
+  ChunkStage<StageCf> stage;
   stage.kp = k + kh * kD;
   stage.qp = q + kh * kD;
   stage.vp = v + h * kD + i0;
@@ -1397,28 +1417,25 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
   stage.seq_beg = seq_beg;
   stage.seq_end = seq_end;
   stage.n_chunks = n_chunks;
-  stage.tid = tid;
+  stage.tid = kLoaders > 0 ? tid - kNW * kWave : tid;
   stage.init();
-  constexpr int kLoads = Cf::kLoads;
+  constexpr int kLoads = StageCf::kLoads;
 
   // output tiles of this wave: all four, or (kSplit = 2) mt = half and half + 2
   auto owns_mt = [&](int mt) { return kSplit == 1 || (mt & 1) == half; };
 
   // ---- the state: S^T tiles, lane holds S[i0 + iw + m][jh + 16 jt + 4 g + e], jt < kJT ----
   f32x4_t sst[kJT];
-  {
+  if (!loader) {
     const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh : nullptr;
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt)
       sst[jt] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + 16 * jt + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (n_chunks > 0) {
-    const auto r0 = stage.rsrc(0);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) stage.load(r0, i);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) stage.commit(s_in[0], i);
+  if (n_chunks > 0 && (kLoaders == 0 || loader)) {
+    stage.load_all(stage.rsrc(0));
+    stage.commit_all(s_in[0]);
   }
   // Let every load issued so far land here, once: otherwise the compiler's
   // wait for the initial state (first used at the top of the chunk loop) is
@@ -1430,6 +1447,15 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
   const uint32_t orow = (uint32_t)(hv * kD * sizeof(To));
   for (int cl = 0; cl < n_chunks; ++cl) {
     const int slot = cl & 1;
+    if (loader) {
+      // stage chunk cl+1 into the other slot (free since the last barrier),
+      // meeting the compute waves at each of their barriers
+      stage.load_all(stage.rsrc(cl + 1));
+      if constexpr (kSplit == 2) __syncthreads();
+      stage.commit_all(s_in[slot ^ 1]);
+      __syncthreads();
+      continue;
+    }
     const int t0 = seq_beg + cl * kC;
     const int L = min(kC, seq_end - t0);
     const uint8_t* base = s_in[slot];
@@ -1467,7 +1493,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     f32x4_t y[4], zt[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) y[mt] = zt[mt] = zero4;
-    // the next chunk's loads go out between these MFMAs
+    // without loader waves the next chunk's loads go out between these MFMAs
     const auto rn = stage.rsrc(cl + 1);
     constexpr int kLPer = (kLoads + 4 * kKS - 1) / (4 * kKS);
 #pragma unroll
@@ -1483,16 +1509,18 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
+        if constexpr (kLoaders == 0) {
 #pragma unroll
-        for (int u = 0; u < kLPer; ++u) {
-          const int i = (4 * ks + mt) * kLPer + u;
-          if (i < kLoads) stage.load(rn, i);
+          for (int u = 0; u < kLPer; ++u) {
+            const int i = (4 * ks + mt) * kLPer + u;
+            if (i < kLoads) stage.load(rn, i);
+          }
         }
         y[mt] = mfma_bf16(fk[mt], sbh[ks], y[mt]);
         zt[mt] = mfma_bf16(sbh[ks], fq[mt], zt[mt]);
         y[mt] = mfma_bf16(fk[mt], sbl[ks], y[mt]);
         zt[mt] = mfma_bf16(sbl[ks], fq[mt], zt[mt]);
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
       if (ks + 1 < kKS) {
 #pragma unroll
@@ -1570,10 +1598,12 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     constexpr int kCGroups = 2 * kJT + kNF;
     constexpr int kCPer = (kLoads + kCGroups - 1) / kCGroups;
     auto commit_group = [&](int grp_idx) {
+      if constexpr (kLoaders == 0) {
 #pragma unroll
-      for (int uu = 0; uu < kCPer; ++uu) {
-        const int i = grp_idx * kCPer + uu;
-        if (i < kLoads) stage.commit(s_in[slot ^ 1], i);
+        for (int uu = 0; uu < kCPer; ++uu) {
+          const int i = grp_idx * kCPer + uu;
+          if (i < kLoads) stage.commit(s_in[slot ^ 1], i);
+        }
       }
     };
 
@@ -1584,7 +1614,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
       commit_group(jt);
       u[jt] = mfma_bf16(kt[jt], wbh[0], zero4);
       u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt)
@@ -1614,7 +1644,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
           zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
           zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
     }
 
@@ -1623,7 +1653,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
       commit_group(kJT + kNF + jt);
       u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
       u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- S <- d S + U ----
@@ -1646,7 +1676,7 @@ __global__ __launch_bounds__(kNW * kWave) void chunk_spine_wave_kernel(
     __syncthreads();
   }
 
-  if (final_state) {
+  if (final_state && !loader) {
     float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh;
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) *reinterpret_cast<f32x4_t*>(s_out + 16 * jt + 4 * g) = sst[jt];
@@ -1687,14 +1717,15 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   if (!F32 && spine == kSpineWave) {
     const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, To>), dim3(blocks), dim3(8 * kWave), 0, s,
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state);
   } else if (!F32 && spine == kSpinePair) {
     const int members = (d.hv / d.hk) * (kD / 32);
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<4, 2, To>), dim3(blocks), dim3(4 * kWave), 0, s,
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<4, 2, kPairLoaders, To>), dim3(blocks),
+                       dim3((4 + kPairLoaders) * kWave), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state);
