@@ -87,8 +87,10 @@ def time_calls(fn, n_sets, steps, warmup):
 
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
-DECODE_TRAFFIC_BYTES = 207.8e6 + 206.3e6
-PREFILL_S4096_TRAFFIC_BYTES = 474.5e6 + 341.1e6
+DECODE_TRAFFIC_BYTES = 207.8e6 + 206.0e6
+PREFILL_S4096_TRAFFIC_BYTES = 455.6e6 + 341.1e6
+VARLEN_TRAFFIC_BYTES = 3817.9e6 + 2751.6e6
+KDA_TRAFFIC_BYTES = 3019.3e6 + 817.9e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
@@ -191,7 +193,8 @@ def bench_pipeline(lengths, seed, steps, warmup):
         for i, key in enumerate(split):
             split[key] += evs[i].elapsed_time(evs[i + 1]) / reps
     bytes_alg = PREFILL_BYTES_PER_TOKEN * T + 2 * STATE_BYTES * N
-    traffic = PREFILL_S4096_TRAFFIC_BYTES if lengths == [4096] else None
+    traffic = {(4096,): PREFILL_S4096_TRAFFIC_BYTES,
+               tuple(gi.varlen_lengths()[0]): VARLEN_TRAFFIC_BYTES}.get(tuple(lengths))
     return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, traffic),
                 roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, **split)
 
@@ -241,7 +244,7 @@ def bench_kda(steps, warmup, T=16384):
 
     ms, per = time_calls(step, 1, steps, warmup)
     bytes_alg = KDA_BYTES_PER_TOKEN * T + 2 * KDA_STATE_BYTES
-    return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms),
+    return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, KDA_TRAFFIC_BYTES),
                 roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3)
 
 
