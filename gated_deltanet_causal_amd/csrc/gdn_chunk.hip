@@ -1528,6 +1528,29 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       }
     }
 
+    // LDS operands of the later products: Tt, Pt (this wave's token tiles) and
+    // K^T for the state update (transposing reads: A[j][slot (g, e)] =
+    // K[k0 + pair_k(0, g, e)][jh + 16 jt + j]).  With the key split (half the
+    // key tiles per wave) there are registers to issue each a phase early, Tt
+    // and the first K^T step before the exchange so they land during it.
+    constexpr bool kEarly = kSplit == 2;
+    bf16x8_t th[kNF], tl[kNF], ph[kNF], pl[kNF], kt[kJT], kt2[kEarly ? kJT : 1];
+    auto read_tt = [&]() {
+#pragma unroll
+      for (int x = 0; x < kNF; ++x) { th[x] = tri_frag(0, x, 0); tl[x] = tri_frag(0, x, 1); }
+    };
+    auto read_pt = [&]() {
+#pragma unroll
+      for (int x = 0; x < kNF; ++x)
+        if (owns_mt(frag_mt(x))) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+    };
+    auto read_kt = [&](int k0, bf16x8_t* dst) {
+#pragma unroll
+      for (int jt = 0; jt < kJT; ++jt)
+        dst[jt] = lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
+    };
+    if constexpr (kEarly) { read_tt(); read_kt(0, kt); }
+
     if constexpr (kSplit == 2) {
       // sum the two key halves: Y for all four token tiles, Z^T for the partner's tiles
       f32x4_t* mine = reinterpret_cast<f32x4_t*>(s_ex + wave * 6 * 1024) + lane;
@@ -1555,19 +1578,11 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       split_pair(r[2], r[3], rbh[1], rbl[1]);
     }
 
-    // K^T operands of the state update's first k step (transposing reads), this wave's key tiles:
-    // A[j][slot (g, e)] = K[pair_k(ks, g, e)][jh + 16 jt + j]
-    bf16x8_t kt[kJT];
-#pragma unroll
-    for (int jt = 0; jt < kJT; ++jt)
-      kt[jt] = lds_read_tr8(sk + (4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
+    if constexpr (!kEarly) { read_kt(0, kt); read_tt(); }
 
     // ---- Vnew = Tt R ----
     f32x4_t vn[4];
     {
-      bf16x8_t th[kNF], tl[kNF];
-#pragma unroll
-      for (int x = 0; x < kNF; ++x) { th[x] = tri_frag(0, x, 0); tl[x] = tri_frag(0, x, 1); }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) vn[mt] = zero4;
 #pragma unroll
@@ -1577,6 +1592,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
       for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(tl[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
     }
+
+    if constexpr (kEarly) { read_pt(); read_kt(32, kt2); }
 
     bf16x8_t nbh[2], nbl[2], wbh[2], wbl[2];
     split_pair(vn[0], vn[1], nbh[0], nbl[0]);
@@ -1616,9 +1633,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
-#pragma unroll
-    for (int jt = 0; jt < kJT; ++jt)
-      kt[jt] = lds_read_tr8(sk + (32 + 4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
+    if constexpr (!kEarly) { read_kt(32, kt); read_pt(); }   // the second k step reuses kt
 
     // ---- O^T = Z^T diag(b) + Vnew^T Pt^T on this wave's token tiles ----
     // (rows i, columns t: A = Vnew pairs, B = Pt fragments)
@@ -1631,11 +1646,6 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       }
     }
     {
-      bf16x8_t ph[kNF], pl[kNF];
-#pragma unroll
-      for (int x = 0; x < kNF; ++x) {
-        if (owns_mt(frag_mt(x))) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
-      }
 #pragma unroll
       for (int x = 0; x < kNF; ++x) {
         commit_group(kJT + x);
@@ -1651,8 +1661,9 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) {
       commit_group(kJT + kNF + jt);
-      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
-      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
+      const bf16x8_t a2 = kEarly ? kt2[kEarly ? jt : 0] : kt[jt];
+      u[jt] = mfma_bf16(a2, wbh[1], u[jt]);
+      u[jt] = mfma_bf16(a2, wbl[1], u[jt]);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 
