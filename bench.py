@@ -10,8 +10,9 @@ all 48 value heads.  Three state sets (604 MB) rotate so the 201 MB state
 never sits in the 256 MB Infinity Cache between steps.
 
 Also measured in the same run (``workloads``):
-  prefill_s4096_bf16  one 4096-token sequence, conv -> chunk -> gated norm, random initial state
-  varlen8_33k_bf16    8 packed sequences (63, 64, 65 + five lengths up to 8192), same pipeline
+  prefill_s4096_bf16  one 4096-token sequence, conv -> chunk -> gated norm in one gdn_prefill call,
+                      random initial state
+  varlen8_33k_bf16    8 packed sequences (63, 64, 65 + five lengths up to 8192), same call
   kda_h64_s16384_bf16 per-key-channel decay, 64 heads, 16384 tokens, the chunk call alone
 each in tokens/s with its whole-path roofline fraction (algorithmic HBM bytes / time / 8 TB/s).
 
@@ -88,8 +89,8 @@ def time_calls(fn, n_sets, steps, warmup):
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 207.8e6 + 206.0e6
-PREFILL_S4096_TRAFFIC_BYTES = 455.6e6 + 341.1e6
-VARLEN_TRAFFIC_BYTES = 3817.9e6 + 2751.6e6
+PREFILL_S4096_TRAFFIC_BYTES = None     # the one-call prefill: not yet measured
+VARLEN_TRAFFIC_BYTES = None
 KDA_TRAFFIC_BYTES = 3019.3e6 + 817.9e6
 
 
@@ -147,6 +148,8 @@ def cpu_baseline_decode(target_s=10.0):
 # ---------------------------------------------------------------------------
 
 def bench_pipeline(lengths, seed, steps, warmup):
+    """A step is one gdn_prefill call (conv -> chunk -> gated norm).  The same work as three
+    separate calls (conv, chunk with an fp32 output, norm) is timed per call for the split."""
     d = gi.gen_prefill(seed, lengths, bf16=True, init_state=True)
     cfg = gdn.config()
     T, N = int(sum(lengths)), len(lengths)
@@ -160,6 +163,11 @@ def bench_pipeline(lengths, seed, steps, warmup):
     o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
     out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gdn.chunk_prefill_workspace_size(N, T, cfg), dtype=torch.uint8, device="cuda")
+    ws_one = torch.empty(gdn.prefill_workspace_size(N, T, torch.bfloat16, cfg), dtype=torch.uint8, device="cuda")
+
+    def one_call(_):
+        gdn.prefill(x, w, cu, g, beta, z, nw, cu_host=cu_np, initial_state=s_in, out=out, final_state=s_out,
+                    workspace=ws_one, cfg=cfg)
 
     def conv():
         gdn.conv1d_prefill(x, w, cu, cu_host=cu_np, y=y, cfg=cfg)
@@ -171,13 +179,8 @@ def bench_pipeline(lengths, seed, steps, warmup):
     def norm():
         gdn.gated_rmsnorm(o, z, nw, out=out, cfg=cfg)
 
-    def step(_):
-        conv()
-        chunk()
-        norm()
-
-    ms, per = time_calls(step, 1, steps, warmup)
-    # per-call split over a few instrumented passes
+    ms, per = time_calls(one_call, 1, steps, warmup)
+    # the separate calls, each timed, over a few passes
     split = {"conv_ms": 0.0, "chunk_ms": 0.0, "norm_ms": 0.0}
     reps = 3
     for _ in range(reps):
@@ -196,7 +199,7 @@ def bench_pipeline(lengths, seed, steps, warmup):
     traffic = {(4096,): PREFILL_S4096_TRAFFIC_BYTES,
                tuple(gi.varlen_lengths()[0]): VARLEN_TRAFFIC_BYTES}.get(tuple(lengths))
     return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, traffic),
-                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, **split)
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, separate_calls=split)
 
 
 def cpu_baseline_pipeline(lengths, seed, max_tokens):
@@ -311,8 +314,8 @@ def main():
     if wl in ("all", "prefill"):
         pre = bench_pipeline([4096], 1003, small_steps, small_warm)
         workloads["prefill_s4096_bf16"] = dict(
-            metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], conv_ms=pre["conv_ms"],
-            chunk_ms=pre["chunk_ms"], norm_ms=pre["norm_ms"], roofline=pre["roofline"],
+            metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], call="gdn_prefill",
+            separate_calls=pre["separate_calls"], roofline=pre["roofline"],
             roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate")
         if cpu:
             workloads["prefill_s4096_bf16"]["cpu_baseline"] = cpu_baseline_pipeline([4096], 1003, 4096)
@@ -321,7 +324,7 @@ def main():
         var = bench_pipeline(lengths, 1004, small_steps, small_warm)
         workloads["varlen8_33k_bf16"] = dict(
             metric="tokens/s", value=var["tokens_per_s"], ms=var["ms"], tokens=var["tokens"], lengths=lengths,
-            conv_ms=var["conv_ms"], chunk_ms=var["chunk_ms"], norm_ms=var["norm_ms"], roofline=var["roofline"],
+            call="gdn_prefill", separate_calls=var["separate_calls"], roofline=var["roofline"],
             roofline_ms=var["roofline_ms"])
         if cpu:
             workloads["varlen8_33k_bf16"]["cpu_baseline"] = cpu_baseline_pipeline(lengths, 1004, 4096)

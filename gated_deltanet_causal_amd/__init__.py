@@ -27,7 +27,7 @@ GDN_F32, GDN_BF16 = 0, 1
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_conv1d_prefill",
            "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
-           "gdn_gated_rmsnorm", "gdn_decode_step")
+           "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step")
 
 
 class GDNError(RuntimeError):
@@ -74,6 +74,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "gdn_chunk_prefill": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp,
                                i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([cfgp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, vp], ctypes.c_int),
+        "gdn_prefill_workspace_size": ([cfgp, ctypes.c_int, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "gdn_prefill": ([cfgp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                         i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "gdn_decode_step": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp],
                             ctypes.c_int),
     }
@@ -224,6 +227,49 @@ def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,
         ctypes.byref(cfg), _dtype(o), _dtype(z), _dtype(out), _ptr(o), _ptr(z), _ptr(w), _ptr(out),
         rows, _stream()))
     return out
+
+
+def prefill_workspace_size(N: int, T: int, dtype: torch.dtype = torch.bfloat16,
+                           cfg: Optional[GDNConfig] = None) -> int:
+    cfg = cfg or config()
+    out = ctypes.c_size_t(0)
+    code = GDN_BF16 if dtype == torch.bfloat16 else GDN_F32
+    _check("gdn_prefill_workspace_size",
+           load_library().gdn_prefill_workspace_size(ctypes.byref(cfg), code, N, T, ctypes.byref(out)))
+    return out.value
+
+
+def prefill(x: torch.Tensor, conv_w: torch.Tensor, cu: torch.Tensor, g: torch.Tensor,
+            beta: torch.Tensor, z: torch.Tensor, norm_w: torch.Tensor, *, cu_host=None,
+            conv_state_in: Optional[torch.Tensor] = None,
+            conv_state_out: Optional[torch.Tensor] = None,
+            initial_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+            final_state: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+            workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+    """The whole sublayer prefill (conv -> chunk-wise delta rule -> gated norm) over packed
+    sequences; x [T, Cc] (row stride free).  Returns (out [T, Hv, dv], final_state)."""
+    cfg = cfg or config()
+    T = x.shape[0]
+    N = cu.numel() - 1
+    if out is None:
+        out = torch.empty((T, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype,
+                          device=x.device)
+    if final_state is None:
+        final_state = torch.empty((N, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim),
+                                  dtype=torch.float32, device=x.device)
+    for t in (g, beta, z, out):
+        if not t.is_contiguous():
+            raise ValueError("prefill g, beta, z and out must be contiguous")
+    if workspace is None:
+        workspace = torch.empty(prefill_workspace_size(N, T, x.dtype, cfg), dtype=torch.uint8,
+                                device=x.device)
+    hc = _cu_host(cu, cu_host)
+    _check("gdn_prefill", load_library().gdn_prefill(
+        ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _row_stride(x), _ptr(conv_w),
+        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
+        _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out, final_state
 
 
 def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: torch.Tensor,

@@ -53,6 +53,22 @@ gdn_status_t check_seqlens(const int32_t* cu_host, int32_t n, int32_t t) {
 
 gdn_status_t hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ERR_HIP; }
 
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// gdn_prefill workspace: the conv output [T][Cc] | the chunk workspace | the
+// fp32 pre-norm output [T][Hv][dv] when the chunk kernels do not apply the norm
+struct PrefillWs {
+  size_t y, chunk, o, total;
+};
+PrefillWs prefill_ws(const Dims& d, bool bf16, int32_t n, int32_t t) {
+  PrefillWs w;
+  w.y = 0;
+  w.chunk = round256((size_t)t * d.cc * (bf16 ? 2 : 4));
+  w.o = w.chunk + round256(gdn::chunk_workspace_bytes(d, n, t));
+  w.total = w.o + (gdn::chunk_fuses_norm(d, bf16, n) ? 0 : (size_t)t * d.hv * d.dv * sizeof(float));
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,7 +186,83 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
   return hip_status(gdn::launch_chunk_prefill(d, in_dtype == GDN_BF16, out_dtype == GDN_BF16, q, k,
                                               qk_stride, v, v_stride, g, beta, initial_state,
                                               cu_dev, cu_host, N, T, out, final_state, ws,
-                                              ws_bytes, static_cast<hipStream_t>(stream)));
+                                              ws_bytes, nullptr, nullptr,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_prefill_workspace_size(const gdn_config_t* cfg, gdn_dtype_t dtype, int32_t N,
+                                        int32_t T, size_t* bytes) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+  if (!bytes || N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
+  *bytes = prefill_ws(d, dtype == GDN_BF16, N, T).total;
+  return GDN_OK;
+}
+
+gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                         const void* x, int64_t x_stride, const float* conv_w,
+                         const void* conv_state_in, void* conv_state_out, const float* g,
+                         const float* beta, const void* z, const float* norm_w,
+                         const float* initial_state, const int32_t* cu_dev, const int32_t* cu_host,
+                         int32_t N, int32_t T, void* out, float* final_state, void* ws,
+                         size_t ws_bytes, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
+  if (N < 0 || T < 0 || !cu_dev || !conv_w) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !g || !beta || !z || !norm_w || !out)) return GDN_ERR_INVALID_ARG;
+  if (x_stride < d.cc || x_stride % 8) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(x) || !aligned16(conv_w) || !aligned16(g) || !aligned16(z) ||
+                !aligned16(norm_w) || !aligned16(out)))
+    return GDN_ERR_INVALID_ARG;
+  if ((conv_state_in && !aligned16(conv_state_in)) || (initial_state && !aligned16(initial_state)) ||
+      (final_state && !aligned16(final_state)))
+    return GDN_ERR_INVALID_ARG;
+  st = check_seqlens(cu_host, N, T);
+  if (st != GDN_OK) return st;
+  if ((size_t)N * d.hk > (size_t)1 << 24) return GDN_ERR_INVALID_ARG;
+  const bool bf16 = dtype == GDN_BF16;
+  const PrefillWs wl = prefill_ws(d, bf16, N, T);
+  if (N > 0 && (!ws || ws_bytes < wl.total || !aligned16(ws))) return GDN_ERR_WORKSPACE;
+  const size_t es = dsize(dtype);
+  const size_t out_bytes = (size_t)T * d.hv * d.dv * dsize(out_dtype);
+  const size_t state_bytes = (size_t)N * d.hv * d.dv * d.dk * sizeof(float);
+  const size_t x_bytes = T > 0 ? ((size_t)(T - 1) * x_stride + d.cc) * es : 0;
+  const size_t z_bytes = (size_t)T * d.hv * d.dv * es;
+  if (overlaps(out, out_bytes, ws, wl.total) || overlaps(out, out_bytes, x, x_bytes) ||
+      overlaps(out, out_bytes, z, z_bytes) || overlaps(final_state, state_bytes, ws, wl.total) ||
+      overlaps(ws, wl.total, x, x_bytes) || overlaps(ws, wl.total, z, z_bytes) ||
+      overlaps(conv_state_out, (size_t)N * 3 * d.cc * es, ws, wl.total))
+    return GDN_ERR_INVALID_ARG;
+  if (N == 0) return GDN_OK;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  void* y = w8 + wl.y;
+  hipError_t e = gdn::launch_conv1d_prefill(d, bf16, x, x_stride, conv_w, conv_state_in,
+                                            conv_state_out, y, d.cc, cu_dev, N, T, s);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  // q | k | v are column blocks of the conv output rows
+  const size_t kq = (size_t)d.hk * d.dk * es;
+  const void* q = y;
+  const void* k = static_cast<uint8_t*>(y) + kq;
+  const void* v = static_cast<uint8_t*>(y) + 2 * kq;
+  if (gdn::chunk_fuses_norm(d, bf16, N)) {
+    // bf16 here: the gate comes in the activations' dtype
+    return hip_status(gdn::launch_chunk_prefill(d, bf16, out_dtype == GDN_BF16, q, k, d.cc, v, d.cc,
+                                                g, beta, initial_state, cu_dev, cu_host, N, T, out,
+                                                final_state, w8 + wl.chunk, wl.o - wl.chunk,
+                                                static_cast<const uint16_t*>(z), norm_w, s));
+  }
+  float* o = reinterpret_cast<float*>(w8 + wl.o);
+  e = gdn::launch_chunk_prefill(d, bf16, false, q, k, d.cc, v, d.cc, g, beta, initial_state, cu_dev,
+                                cu_host, N, T, o, final_state, w8 + wl.chunk, wl.o - wl.chunk,
+                                nullptr, nullptr, s);
+  if (e != hipSuccess) return GDN_ERR_HIP;
+  return hip_status(gdn::launch_gated_rmsnorm(d, false, bf16, out_dtype == GDN_BF16, o, z, norm_w,
+                                              out, T, s));
 }
 
 gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn_dtype_t z_dtype,

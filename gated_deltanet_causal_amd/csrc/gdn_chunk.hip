@@ -1366,17 +1366,30 @@ struct ChunkStage {
 // LDS slot while the kNW compute waves work on chunk cl, so the compute waves
 // never wait at the texture path; without them the compute waves stage in
 // pieces between their MFMAs.
-template <int kNW, int kSplit, int kLoaders, typename To>
+// kNorm (a whole value head per workgroup) applies the sigmoid-gated RMSNorm
+// to each chunk's output before it is stored: per token, each wave's partial
+// sum of squares over its 16 value columns meets the others' in LDS at the
+// chunk's barrier, so the pre-norm output never goes to memory.
+struct FusedNorm {
+  const uint16_t* z;   // bf16 gate [T][Hv][dv], or null when the norm is not fused
+  const float* w;      // [dv]
+  float eps;
+};
+
+template <int kNW, int kSplit, int kLoaders, typename To, bool kNorm = false>
 __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
     const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
-    To* __restrict__ out, float* final_state) {
+    To* __restrict__ out, float* final_state, FusedNorm nrm) {
   using Cf = SpineCfg<kNW * kWave, 16 * kNW / kSplit>;
   using StageCf = SpineCfg<(kLoaders > 0 ? kLoaders : kNW) * kWave, Cf::kRows>;   // same LDS layout
+  static_assert(!kNorm || (kSplit == 1 && kNW * 16 == kD), "the fused norm needs a whole value head per workgroup");
   constexpr int kKS = 4 / kSplit;                 // 32-key steps of a wave's state
   constexpr int kJT = 8 / kSplit;                 // 16-key tiles of a wave's state
-  constexpr int kExch = kSplit == 2 ? kNW * 6 * 1024 : 16;   // per wave: Y and two Z^T partial tiles
+  // kSplit = 2: per wave Y and two Z^T partial tiles; kNorm: per chunk parity,
+  // token and wave a partial sum of squares
+  constexpr int kExch = kSplit == 2 ? kNW * 6 * 1024 : (kNorm ? 2 * kC * kNW * 4 : 16);
   __shared__ __attribute__((aligned(1024))) uint8_t s_in[2][Cf::kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_ex[kExch];
 
@@ -1426,6 +1439,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 
   // ---- the state: S^T tiles, lane holds S[i0 + iw + m][jh + 16 jt + 4 g + e], jt < kJT ----
   f32x4_t sst[kJT];
+  f32x4_t nw = {0.f, 0.f, 0.f, 0.f};   // norm weights of the lane's output columns iw + 4 g .. +3
+  if constexpr (kNorm) nw = *reinterpret_cast<const f32x4_t*>(nrm.w + iw + 4 * g);
   if (!loader) {
     const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh : nullptr;
 #pragma unroll
@@ -1467,6 +1482,16 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     auto tri_frag = [&](int which, int x, int hl) {
       return load_bf16x8(reinterpret_cast<const uint16_t*>(tri + (which * 12 + 2 * x + hl) * 1024 + 16 * lane));
     };
+    // gate inputs of this chunk's outputs (tokens 16 mt + m, columns iw + 4 g .. +3),
+    // issued now so they land during the chunk
+    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+    u32x2_t zr[4];
+    if constexpr (kNorm) {
+      const __amdgpu_buffer_rsrc_t rz = make_rsrc(nrm.z + ((int64_t)t0 * hv + h) * kD + iw, (uint32_t)L * hv * kD * 2);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+        zr[mt] = __builtin_amdgcn_raw_buffer_load_b64(rz, (16 * mt + m) * (uint32_t)(hv * kD * 2) + 8 * g, 0, 0);
+    }
 
     // LDS operands of the first k step of Y / Z, the V tile, the vectors
     bf16x8_t fk[4], fq[4];
@@ -1677,14 +1702,49 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     }
 
     // ---- the output: lane (g, m) of tile mt holds O[16 mt + m][iw + 4 g .. +3] ----
-    {
-      // rows past the end of the sequence fall outside the descriptor
-      const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + ((int64_t)t0 * hv + h) * kD + i0 + iw, (uint32_t)L * orow);
+    // (rows past the end of the sequence fall outside the descriptor)
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(out + ((int64_t)t0 * hv + h) * kD + i0 + iw, (uint32_t)L * orow);
+    float* s_ss = reinterpret_cast<float*>(s_ex) + slot * kC * kNW;   // [token][wave]
+    if constexpr (kNorm) {
+      // this wave's sum of squares per token: the lane's four columns, then the
+      // four lane groups holding the same token
+      float ss[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        ss[mt] = zt[mt][0] * zt[mt][0] + zt[mt][1] * zt[mt][1] + zt[mt][2] * zt[mt][2] + zt[mt][3] * zt[mt][3];
+        ss[mt] += __shfl_xor(ss[mt], 16, kWave);
+        ss[mt] += __shfl_xor(ss[mt], 32, kWave);
+      }
+      s_ss[(16 * g + m) * kNW + wave] = g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3];
+      // w * sigmoid(z), folded into the output tiles; sigmoid as 1 / (1 + 2^(-z log2 e))
+      // with the hardware exp2 and reciprocal (each within 1 ulp)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const float zf[4] = {__uint_as_float(zr[mt][0] << 16), __uint_as_float(zr[mt][0] & 0xffff0000u),
+                             __uint_as_float(zr[mt][1] << 16), __uint_as_float(zr[mt][1] & 0xffff0000u)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          zt[mt][e] *= nw[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * zf[e]));
+      }
+    } else {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
         if (owns_mt(mt)) buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
     }
     __syncthreads();
+    if constexpr (kNorm) {
+      // every wave's partial sums are in: scale by rsqrt(mean o^2 + eps) and store
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const f32x4_t* p = reinterpret_cast<const f32x4_t*>(s_ss + (16 * mt + m) * kNW);
+        const f32x4_t a = p[0], b = p[1];
+        const float tot = ((a[0] + a[1]) + (a[2] + a[3])) + ((b[0] + b[1]) + (b[2] + b[3]));
+        const float r = rsqrtf(tot * (1.0f / kD) + nrm.eps);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zt[mt][e] *= r;
+        buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
+      }
+    }
   }
 
   if (final_state && !loader) {
@@ -1694,11 +1754,16 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   }
 }
 
+int chunk_spine_kind(const Dims& d, bool in_bf16, int n) {
+  if (!in_bf16 || d.per_channel) return kSpineLds;
+  return n * d.hv >= kWaveSpineMinBlocks ? kSpineWave : kSpinePair;
+}
+
 template <bool F32, bool kPC, typename Tin, typename To>
 hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_stride, const void* v,
                       int64_t v_stride, const float* g, const float* beta, const float* init_state,
                       const int32_t* cu_dev, int n, int total_chunks, void* out,
-                      float* final_state, void* ws, hipStream_t s) {
+                      float* final_state, void* ws, const FusedNorm& nrm, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   // bf16 inputs with scalar decay run a register-resident spine: a whole
   // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
@@ -1706,8 +1771,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   // for fewer sequences the key-split form (two waves per 16 value rows, four
   // waves and 32 rows per workgroup) spreads them over eight times as many
   // workgroups and halves each wave's serial work per chunk.
-  const int head_blocks = n * d.hv;
-  const int spine = F32 || kPC ? kSpineLds : (head_blocks >= kWaveSpineMinBlocks ? kSpineWave : kSpinePair);
+  const int spine = chunk_spine_kind(d, !F32, n);
   hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
                      reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
   hipError_t e = hipGetLastError();
@@ -1728,10 +1792,16 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   if (!F32 && spine == kSpineWave) {
     const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
-                       static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
-                       static_cast<To*>(out), final_state);
+    if (nrm.z)
+      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                         static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
+                         static_cast<To*>(out), final_state, nrm);
+    else
+      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                         static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
+                         static_cast<To*>(out), final_state, nrm);
   } else if (!F32 && spine == kSpinePair) {
     const int members = (d.hv / d.hk) * (kD / 32);
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
@@ -1739,7 +1809,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
                        dim3((4 + kPairLoaders) * kWave), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
-                       static_cast<To*>(out), final_state);
+                       static_cast<To*>(out), final_state, nrm);
   } else if constexpr (F32 || kPC) {
     const int members = (d.hv / d.hk) * (kD / kTile);
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
@@ -1755,15 +1825,20 @@ template <bool kPC>
 hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                           int64_t qk_stride, const void* v, int64_t v_stride, const float* g,
                           const float* beta, const float* init_state, const int32_t* cu_dev, int n,
-                          int total, void* out, float* final_state, void* ws, hipStream_t s) {
+                          int total, void* out, float* final_state, void* ws, const FusedNorm& nrm,
+                          hipStream_t s) {
   if (in_bf16)
-    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
-                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
-  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
-                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
+    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace
+
+bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n) {
+  return chunk_spine_kind(d, in_bf16, n) == kSpineWave;
+}
 
 size_t chunk_workspace_bytes(const Dims& d, int n, int t) {
   const size_t max_chunks = (size_t)t / kC + (size_t)n;
@@ -1775,15 +1850,18 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
                                 int64_t v_stride, const float* g, const float* beta,
                                 const float* init_state, const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
-                                float* final_state, void* ws, size_t ws_bytes, hipStream_t s) {
+                                float* final_state, void* ws, size_t ws_bytes,
+                                const uint16_t* norm_z, const float* norm_w, hipStream_t s) {
   (void)t;
   (void)ws_bytes;
   if (n == 0) return hipSuccess;
+  if (norm_z && !chunk_fuses_norm(d, in_bf16, n)) return hipErrorInvalidValue;
   int total = 0;
   for (int i = 0; i < n; ++i) total += (cu_host[i + 1] - cu_host[i] + kC - 1) / kC;
+  const FusedNorm nrm{norm_z, norm_w, d.rms_eps};
   return d.per_channel
-             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s)
-             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, s);
+             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace gdn

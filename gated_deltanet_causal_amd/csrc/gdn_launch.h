@@ -34,11 +34,18 @@ hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const voi
 
 // Chunk prefill.  Workspace layout is private to gdn_chunk.hip.
 size_t chunk_workspace_bytes(const Dims& d, int n, int t);
+// Whether the chunk prefill for n sequences can apply the gated norm to its
+// output itself (norm_z / norm_w of launch_chunk_prefill); the answer depends
+// only on the geometry, the input dtype and n.
+bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n);
+// norm_z (bf16 [T][Hv][dv]) and norm_w non-null: out receives the gated norm
+// of the chunk output (requires chunk_fuses_norm).
 hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
                                 const void* k, int64_t qk_stride, const void* v,
                                 int64_t v_stride, const float* g, const float* beta,
                                 const float* init_state, const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
-                                float* final_state, void* ws, size_t ws_bytes, hipStream_t s);
+                                float* final_state, void* ws, size_t ws_bytes,
+                                const uint16_t* norm_z, const float* norm_w, hipStream_t s);
 
 }  // namespace gdn

@@ -168,6 +168,45 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
                                gdn_dtype_t out_dtype, const void* o, const void* z,
                                const float* w, void* out, int64_t rows, gdn_stream_t stream);
 
+/* Bytes of device workspace gdn_prefill needs for N sequences and T tokens
+ * in total with activations of `dtype`.  Host only; pure. */
+gdn_status_t gdn_prefill_workspace_size(const gdn_config_t* cfg, gdn_dtype_t dtype, int32_t N,
+                                        int32_t T, size_t* bytes);
+
+/*
+ * The whole sublayer prefill over N packed sequences (the golden PR's
+ * Consumer section: conv, then the chunked delta rule, then the gated norm):
+ * gdn_conv1d_prefill over x, q | k | v taken from the conv output rows,
+ * gdn_chunk_prefill, and gdn_gated_rmsnorm of its output, with the same
+ * arithmetic as those calls made in that order (the pre-norm output is kept
+ * in fp32).  Where the geometry allows, the chunk kernels apply the gated norm
+ * to each chunk's output themselves and the pre-norm output is never stored.
+ *   dtype            dtype of x, the conv states and z
+ *   out_dtype        dtype of out
+ *   x                [T][Cc] raw projected rows, row stride x_stride (>= Cc,
+ *                    a multiple of 8)
+ *   conv_w           fp32 [Cc][4]
+ *   conv_state_in    [N][3][Cc] or NULL (zero);  conv_state_out [N][3][Cc] or
+ *                    NULL, may equal conv_state_in
+ *   g, beta          as for gdn_chunk_prefill
+ *   z                [T][Hv][dv] gate;  norm_w fp32 [dv]
+ *   initial_state    fp32 [N][Hv][dv][dk] or NULL;  final_state the same or
+ *                    NULL, may equal initial_state
+ *   cu_dev, cu_host  as for gdn_conv1d_prefill
+ *   out              [T][Hv][dv]
+ *   ws, ws_bytes     device workspace of at least
+ *                    gdn_prefill_workspace_size(cfg, dtype, N, T) bytes; it
+ *                    must not overlap x, z, out or the states
+ * x, conv_w, g, z, norm_w, out and the workspace are 16-byte aligned.
+ */
+gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                         const void* x, int64_t x_stride, const float* conv_w,
+                         const void* conv_state_in, void* conv_state_out, const float* g,
+                         const float* beta, const void* z, const float* norm_w,
+                         const float* initial_state, const int32_t* cu_dev, const int32_t* cu_host,
+                         int32_t N, int32_t T, void* out, float* final_state, void* ws,
+                         size_t ws_bytes, gdn_stream_t stream);
+
 /*
  * One fused decode step for B sequences (the TDD ledger's scalar recurrence
  * with fused output gate; the Qwen3SsmLayer conv + recurrence + norm decode

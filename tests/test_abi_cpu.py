@@ -167,3 +167,50 @@ def test_decode_rejects_more_than_four_value_heads_per_key_head(lib):
     got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, FAKE, FAKE, 4, None)
     assert got == gdn.GDN_ERR_UNSUPPORTED
+
+
+def _prefill_ws(lib, n, t, dtype=gdn.GDN_BF16, cfg=None):
+    s = ctypes.c_size_t()
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(cfg or _cfg()), dtype, n, t, ctypes.byref(s)) == 0
+    return s.value
+
+
+def test_prefill_workspace_holds_the_prenorm_output_only_when_unfused(lib):
+    """Six or more sequences of 48 value heads (bf16, scalar decay) apply the norm inside the
+    chunk kernels: no fp32 pre-norm buffer.  Fewer, fp32 or per-key-channel decay keep it."""
+    T = 4096
+    o_bytes = T * 48 * 128 * 4
+    fused, unfused = _prefill_ws(lib, 6, T), _prefill_ws(lib, 5, T)
+
+    def chunk_ws(n):
+        s = ctypes.c_size_t()
+        assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(_cfg()), n, T, ctypes.byref(s)) == 0
+        return s.value
+    assert abs((unfused - fused) - (o_bytes - (chunk_ws(6) - chunk_ws(5)))) <= 512
+    assert _prefill_ws(lib, 6, T, gdn.GDN_F32) - fused >= o_bytes + T * 10240 * 2 - 4096
+    assert _prefill_ws(lib, 6, T, cfg=_cfg(decay_per_key_channel=1)) > fused + o_bytes - 4096
+    assert _prefill_ws(lib, 1, T) > _prefill_ws(lib, 1, T // 2)
+
+
+def test_prefill_argument_checks(lib):
+    cfg = _cfg()
+    hc = (ctypes.c_int32 * 2)(0, 64)
+    need = _prefill_ws(lib, 1, 64)
+
+    def call(**kw):
+        return lib.gdn_prefill(
+            ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, kw.get("x", FAKE), kw.get("xs", 10240), FAKE,
+            None, None, FAKE, FAKE, kw.get("z", ctypes.c_void_p(0x2000000)), FAKE, None, FAKE, hc, 1, 64,
+            ctypes.c_void_p(0x4000000), None, kw.get("ws", ctypes.c_void_p(0x8000000)), kw.get("wsb", need),
+            None)
+    assert call(wsb=0) == gdn.GDN_ERR_WORKSPACE
+    assert call(ws=None) == gdn.GDN_ERR_WORKSPACE
+    assert call(wsb=need - 1) == gdn.GDN_ERR_WORKSPACE
+    assert call(z=None) == gdn.GDN_ERR_INVALID_ARG
+    assert call(z=ctypes.c_void_p(0x2000000 + 8)) == gdn.GDN_ERR_INVALID_ARG     # z not 16-byte aligned
+    assert call(xs=10244) == gdn.GDN_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(0x10000 + 4096)) == gdn.GDN_ERR_INVALID_ARG  # workspace overlaps x
+    assert call(ws=ctypes.c_void_p(0x4000000)) == gdn.GDN_ERR_INVALID_ARG       # workspace overlaps out
+    assert lib.gdn_prefill(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, None, 10240, FAKE, None, None,
+                           None, None, None, None, None, FAKE, (ctypes.c_int32 * 1)(0), 0, 0, None, None,
+                           None, 0, None) == 0                                   # nothing to do

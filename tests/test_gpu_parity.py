@@ -317,6 +317,98 @@ def test_varlen_32k_full_size_sampled(orc):
 
 
 # ---------------------------------------------------------------------------
+# the whole prefill in one call (gdn_prefill)
+# ---------------------------------------------------------------------------
+
+def _prefill_gpu(d, bf16, out_dtype):
+    """gdn_prefill on the generated inputs; conv state and recurrent state carried in."""
+    x = dev(d["x"], bf16)
+    N = len(d["cu"]) - 1
+    cs_in = None if d["conv_state_in"] is None else dev(d["conv_state_in"], bf16)
+    cs_out = torch.empty((N, 3, x.shape[1]), dtype=x.dtype, device=x.device)
+    s_in = None if d["state_in"] is None else dev(d["state_in"])
+    out, fs = gdn.prefill(x, dev(d["conv_w"]), dev_i32(d["cu"]), dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], bf16), dev(d["norm_w"]), cu_host=d["cu"], conv_state_in=cs_in,
+                          conv_state_out=cs_out, initial_state=s_in, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return out, fs, cs_out
+
+
+def _prefill_ref(orc, d, bf16):
+    out, _, s, cso, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                    Hk=HK, Hv=HV, dk=D, dv=D, conv_state_in=d["conv_state_in"],
+                                    state_in=d["state_in"], round_y_bf16=bf16)
+    return out, s, cso
+
+
+@pytest.mark.parametrize("lengths", [[200], [64, 63, 65, 64, 65, 63], [129, 0, 1, 63, 64, 65, 7]],
+                         ids=["one_seq", "six_seqs", "seven_with_empty"])
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["out_bf16", "out_f32"])
+def test_prefill_entry_bf16(orc, lengths, out_dtype):
+    """conv -> chunk -> gated norm in one call, bf16 activations, carried conv and recurrent
+    state.  One sequence runs the key-split spine and a separate norm; six or more sequences
+    of 48 value heads run the whole-head spine with the norm applied in its epilogue."""
+    d = gi.gen_prefill(500 + sum(lengths), lengths, bf16=True, conv_state=True)
+    out, fs, cso = _prefill_gpu(d, True, out_dtype)
+    out_ref, s_ref, cso_ref = _prefill_ref(orc, d, True)
+    check(host(out), out_ref, TOL_BF16, f"prefill out {lengths}", stored_bf16=out_dtype == torch.bfloat16)
+    check(host(fs), s_ref, TOL_BF16, f"prefill state {lengths}")
+    assert np.array_equal(host(cso), cso_ref), "conv state out: the last three inputs, copied"
+
+
+def test_prefill_entry_fp32_s80(orc):
+    """The 80-token fp32 case through the one-call prefill, at the fp32 bound."""
+    d = gi.gen_prefill(1001, [80], bf16=False, conv_state=True)
+    out, fs, cso = _prefill_gpu(d, False, torch.float32)
+    out_ref, s_ref, cso_ref = _prefill_ref(orc, d, False)
+    check(host(out), out_ref, TOL_F32, "S=80 fp32 prefill out")
+    check(host(fs), s_ref, TOL_F32, "S=80 fp32 prefill state")
+    assert np.array_equal(host(cso), cso_ref)
+
+
+def test_prefill_entry_fused_norm_equals_separate_calls():
+    """The norm in the spine's epilogue against the same chunk output normed by
+    gdn_gated_rmsnorm: only the order of the sum of squares differs."""
+    lengths = [100, 37, 64, 1, 250, 128]
+    d = gi.gen_prefill(77, lengths, bf16=True, conv_state=True)
+    out, fs, _ = _prefill_gpu(d, True, torch.float32)
+    cu = dev_i32(d["cu"])
+    y = gdn.conv1d_prefill(dev(d["x"], True), dev(d["conv_w"]), cu, cu_host=d["cu"],
+                           conv_state_in=dev(d["conv_state_in"], True))
+    q, k, v = y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:]
+    o, fs2 = gdn.chunk_prefill(q, k, v, dev(d["g"]), dev(d["beta"]), cu, cu_host=d["cu"],
+                               initial_state=dev(d["state_in"]), out_dtype=torch.float32)
+    out2 = gdn.gated_rmsnorm(o, dev(d["z"], True), dev(d["norm_w"]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check(host(out), host(out2), TOL_F32, "fused norm vs separate norm")
+    assert torch.equal(fs, fs2), "the final state does not depend on the norm"
+
+
+def test_prefill_entry_varlen_full_size_sampled(orc):
+    """The ~32k-token varlen workload through the one-call prefill (eight sequences: the
+    norm runs in the spine's epilogue); the value heads of key head 5 compared with the
+    oracle's conv -> delta rule -> norm over every token."""
+    lengths, _ = gi.varlen_lengths()
+    d = gi.gen_prefill(1005, lengths, bf16=True, conv_state=True)
+    out, fs, cso = _prefill_gpu(d, True, torch.bfloat16)
+    kh, ratio = 5, HV // HK
+    vheads = [kh * ratio + r for r in range(ratio)]
+    cols = np.concatenate([np.arange(kh * D, (kh + 1) * D), np.arange((HK + kh) * D, (HK + kh + 1) * D)] +
+                          [np.arange(2 * HK * D + h * D, 2 * HK * D + (h + 1) * D) for h in vheads])
+    y, cso_ref = orc.conv1d(d["x"][:, cols], d["conv_w"][cols], d["cu"], d["conv_state_in"][:, :, cols])
+    y = oracle.round_bf16(y)
+    T = y.shape[0]
+    o_ref, s_ref = orc.delta_rule(y[:, :D].reshape(T, 1, D), y[:, D: 2 * D].reshape(T, 1, D),
+                                  y[:, 2 * D:].reshape(T, ratio, D), d["g"][:, vheads], d["beta"][:, vheads],
+                                  d["cu"], d["state_in"][:, vheads])
+    out_ref = orc.gated_rmsnorm(o_ref, d["z"][:, vheads], d["norm_w"])
+    check(host(out)[:, vheads], out_ref, TOL_BF16, f"varlen prefill out {lengths}", stored_bf16=True)
+    check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen prefill state")
+    assert np.array_equal(host(cso)[:, :, cols], cso_ref)
+    assert np.all(np.isfinite(host(out))), "non-finite output in unsampled heads"
+
+
+# ---------------------------------------------------------------------------
 # composition and negative controls
 # ---------------------------------------------------------------------------
 
