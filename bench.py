@@ -14,7 +14,9 @@ Also measured in the same run (``workloads``):
                       random initial state
   varlen8_33k_bf16    8 packed sequences (63, 64, 65 + five lengths up to 8192), same call
   kda_h64_s16384_bf16 per-key-channel decay, 64 heads, 16384 tokens, the chunk call alone
-each in tokens/s with its whole-path roofline fraction (algorithmic HBM bytes / time / 8 TB/s).
+  kda_decode_b64_h64_bf16  the per-key-channel decode step, 64 sequences x 64 heads
+each in tokens/s (state-updates/s for the decode) with its roofline fraction (algorithmic HBM
+bytes / time / 8 TB/s).
 
 Every launch is a library call on torch's current stream (the stream the
 library enqueues on), timed with events on that stream.  ``cpu_baseline``
@@ -54,6 +56,11 @@ PREFILL_BYTES_PER_TOKEN = CC * 2 + HV * D * 2 + 2 * HV * 4 + HV * D * 2
 KDA_H = 64
 KDA_BYTES_PER_TOKEN = 3 * KDA_H * D * 2 + KDA_H * D * 4 + KDA_H * 4 + KDA_H * D * 2
 KDA_STATE_BYTES = KDA_H * D * D * 4
+# per-key-channel decode at 64 heads, per sequence-update: state read + write, conv state read + write,
+# x, z, g [64,128] fp32, beta, out
+KDA_CC = 3 * KDA_H * D
+KDA_DECODE_BYTES_PER_UPDATE = (2 * KDA_STATE_BYTES + 2 * 3 * KDA_CC * 2 + KDA_CC * 2 + KDA_H * D * 2 +
+                               KDA_H * D * 4 + KDA_H * 4 + KDA_H * D * 2)
 
 
 def t_dev(a, bf16=False):
@@ -108,22 +115,30 @@ def oracle_threads():
 # decode
 # ---------------------------------------------------------------------------
 
-def bench_decode(steps, warmup, batch=64):
-    d = gi.gen_decode(1002, batch)
-    cfg = gdn.config()
+def bench_decode(steps, warmup, batch=64, per_channel=False):
+    """64 sequences of one token; per_channel: the per-key-channel decode at 64 heads (ratio 1)."""
+    if per_channel:
+        geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
+        d = gi.gen_decode(1006, batch, geo, per_channel=True)
+        cfg = gdn.config(num_k_heads=KDA_H, num_v_heads=KDA_H, decay_per_key_channel=1)
+        hv, bytes_per, traffic = KDA_H, KDA_DECODE_BYTES_PER_UPDATE, None
+    else:
+        d = gi.gen_decode(1002, batch)
+        cfg = gdn.config()
+        hv, bytes_per, traffic = HV, DECODE_BYTES_PER_UPDATE, DECODE_TRAFFIC_BYTES
     n_sets = 3
     x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
                             t_dev(d["z"], True), t_dev(d["norm_w"]))
     states = [t_dev(d["state"]) for _ in range(n_sets)]
     convs = [t_dev(d["conv_state"], True) for _ in range(n_sets)]
-    out = torch.empty((batch, HV, D), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((batch, hv, D), dtype=torch.bfloat16, device="cuda")
 
     def step(i):
         gdn.decode_step(x, w, convs[i], g, beta, z, nw, states[i], out=out, cfg=cfg)
 
     ms, per = time_calls(step, n_sets, steps, warmup)
     return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3),
-                roofline=roofline(DECODE_BYTES_PER_UPDATE * batch, ms, DECODE_TRAFFIC_BYTES))
+                roofline=roofline(bytes_per * batch, ms, traffic))
 
 
 def cpu_baseline_decode(target_s=10.0):
@@ -278,7 +293,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="all", choices=["all", "decode", "prefill", "varlen", "kda"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
@@ -335,10 +351,16 @@ def main():
             roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
+    if wl in ("all", "kda_decode"):
+        kdd = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), per_channel=True)
+        workloads["kda_decode_b64_h64_bf16"] = dict(
+            metric="state-updates/s", value=kdd["updates_per_s"], ms=kdd["ms"], roofline=kdd["roofline"],
+            bytes_per_update=KDA_DECODE_BYTES_PER_UPDATE,
+            call="gdn_decode_step, decay per key channel, 64 heads, state f32 [64,64,128,128], 3 sets rotated")
     if wl != "decode" and "value" not in line:
         # a single prefill-side workload was requested: it is the headline
         name, obj = next(iter(workloads.items()))
-        line.update({"value": obj["value"], "unit": "tokens/s", "ms_per_step": obj["ms"], "dtype": "bf16",
+        line.update({"value": obj["value"], "unit": obj["metric"], "ms_per_step": obj["ms"], "dtype": "bf16",
                      "config": {"workload": name}, "roofline": obj["roofline"]})
         if "cpu_baseline" in obj:
             line["cpu_baseline"] = obj["cpu_baseline"]

@@ -187,6 +187,27 @@ def test_decode_step_f32_two_steps(orc, per_channel):
         assert np.allclose(host(cs), cs_ref, rtol=0, atol=0)
 
 
+def test_decode_step_per_channel_h64_bf16_two_steps(orc):
+    """The per-key-channel (KDA) decode at the long-context geometry: 64 heads, no repeat,
+    g [B, 64, 128], bf16 activations, 64 sequences; two steps with the states carried."""
+    geo = gi.Geometry(hk=64, hv=64)
+    d = gi.gen_decode(1006, 64, geo, per_channel=True)
+    cfg = gdn.config(num_k_heads=64, num_v_heads=64, decay_per_key_channel=1)
+    cs, st = dev(d["conv_state"], True), dev(d["state"])
+    cs_ref, st_ref = d["conv_state"], d["state"]
+    rng = np.random.default_rng(6)
+    for step in range(2):
+        x = d["x"] if step == 0 else gi.bf16_round(rng.standard_normal(d["x"].shape, dtype=np.float32))
+        out = gdn.decode_step(dev(x, True), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]),
+                              dev(d["z"], True), dev(d["norm_w"]), st, out_dtype=torch.bfloat16, cfg=cfg)
+        torch.cuda.synchronize()
+        o_ref, cs_ref, st_ref = orc.decode_step(x, d["conv_w"], cs_ref, d["g"], d["beta"], d["z"], d["norm_w"],
+                                                st_ref, Hk=64, Hv=64, dk=D, dv=D)
+        check(host(out), o_ref, TOL_BF16, f"KDA decode out step {step}", stored_bf16=True)
+        check(host(st), st_ref, TOL_BF16, f"KDA decode state step {step}")
+        assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
+
+
 # ---------------------------------------------------------------------------
 # chunk prefill
 # ---------------------------------------------------------------------------
