@@ -50,9 +50,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.gdn_oracle_gated_rmsnorm.argtypes = [dp, dp, dp, i64, i32, dbl, dp]
     lib.gdn_oracle_decode_step.argtypes = [i32, i32, i32, i32, i32, i32, dbl, dbl, dbl, i32,
                                            dp, dp, dp, dp, dp, dp, dp, dp, dp]
+    lib.gdn_oracle_gates.argtypes = [dp, dp, dp, dp, i64, i32, dp, dp]
     for name in ("gdn_oracle_conv1d", "gdn_oracle_conv1d_step", "gdn_oracle_delta_rule",
                  "gdn_oracle_delta_rule_chunked", "gdn_oracle_gated_rmsnorm",
-                 "gdn_oracle_decode_step"):
+                 "gdn_oracle_decode_step", "gdn_oracle_gates"):
         getattr(lib, name).restype = None
     return lib
 
@@ -150,6 +151,19 @@ class Oracle:
         else:
             self.lib.gdn_oracle_delta_rule_chunked(*args, int(chunk), _ptr(o), _ptr(so))
         return o, so
+
+    # -- gates from the a / b projections ------------------------------------
+    def gates(self, a, b, A_log, dt_bias) -> Tuple[np.ndarray, np.ndarray]:
+        """a, b [..., Hv]; A_log, dt_bias [Hv] -> (g, beta) [..., Hv]:
+        g = -exp(A_log) softplus(a + dt_bias), beta = sigmoid(b)."""
+        a, b, A_log, dt_bias = _f64(a), _f64(b), _f64(A_log), _f64(dt_bias)
+        Hv = A_log.shape[0]
+        assert a.shape == b.shape and a.shape[-1] == Hv and dt_bias.shape == (Hv,)
+        g = np.empty_like(a)
+        beta = np.empty_like(b)
+        self.lib.gdn_oracle_gates(_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias), a.size // Hv, Hv,
+                                  _ptr(g), _ptr(beta))
+        return g, beta
 
     # -- gated norm (a9) ----------------------------------------------------
     def gated_rmsnorm(self, o, z, w, eps: float = 1e-6) -> np.ndarray:

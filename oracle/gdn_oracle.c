@@ -334,6 +334,31 @@ void gdn_oracle_delta_rule_chunked(int32_t Hk, int32_t Hv, int32_t dk, int32_t d
 }
 
 /*
+ * Gate derivation from the a / b projections.  The pages name the step (the
+ * TDD ledger's GDN alpha/beta transform kernels; the golden PR's prepare stage
+ * "derives the raw g/beta" from in_proj_a / in_proj_b outputs with the layer's
+ * A_log and dt_bias vectors, which its fixture does not store) but do not
+ * print the formula.  Reading: A_log is the log of a positive per-head decay
+ * rate and dt_bias a per-head bias of the a projection, so per token t and
+ * value head h
+ *     g[t][h]    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *     beta[t][h] = sigmoid(b[t][h])
+ * with softplus(x) = log(1 + exp(x)) (evaluated as x + log1p(exp(-x)) for
+ * x > 0, the same function without overflow).  a, b, g, beta are [rows][Hv].
+ */
+static double softplus(double x) { return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+void gdn_oracle_gates(const double* a, const double* b, const double* A_log, const double* dt_bias,
+                      int64_t rows, int32_t Hv, double* g, double* beta) {
+  for (int64_t t = 0; t < rows; ++t) {
+    for (int32_t h = 0; h < Hv; ++h) {
+      g[t * Hv + h] = -exp(A_log[h]) * softplus(a[t * Hv + h] + dt_bias[h]);
+      beta[t * Hv + h] = sigmoid(b[t * Hv + h]);
+    }
+  }
+}
+
+/*
  * Gated RMSNorm with the sigmoid gate [GOLDEN Summary, Negative controls and
  * code review: rsqrt(variance + eps), sigmoid not SiLU].  Over each of the
  * `vectors` rows of length d:

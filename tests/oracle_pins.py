@@ -16,7 +16,10 @@ Kinds of pin used (none re-types the oracle's own loops):
   * invariants: chunked WY arm == token arm, split calls == one call, decode
     steps == prefill, per-channel decay with equal channels == scalar decay,
     linearity in v, packed varlen == separate sequences;
-  * geometry printed by the golden PR (tests/golden/golden_pr_geometry.txt).
+  * geometry printed by the golden PR (tests/golden/golden_pr_geometry.txt);
+  * gates from the a / b projections: closed forms of softplus and the sigmoid at
+    ln-rational points, the identities softplus(x) - softplus(-x) = x and
+    sigmoid(x) + sigmoid(-x) = 1, and the far tails.
 """
 from __future__ import annotations
 
@@ -441,6 +444,47 @@ def pin_decode_equals_prefill(orc):
 # ---------------------------------------------------------------------------
 # geometry the golden PR prints
 # ---------------------------------------------------------------------------
+
+# ---------------------------------------------------------------------------
+# gates from the a / b projections
+# ---------------------------------------------------------------------------
+
+def pin_gates_closed_forms(orc):
+    """Points where softplus and the sigmoid have closed forms: softplus(0) = ln 2,
+    softplus(ln 3) = ln 4, softplus(-ln 3) = ln(4/3); sigmoid(0) = 1/2, sigmoid(+-ln 3) =
+    3/4, 1/4.  Head 1 has A_log = ln 5 (g scales by 5), head 2 has dt_bias = ln 3 (it
+    shifts a), so a dropped exp, a dropped or negated bias and a sign slip each miss."""
+    ln3 = math.log(3.0)
+    A_log = np.array([0.0, math.log(5.0), 0.0])
+    dt_bias = np.array([0.0, 0.0, ln3])
+    a = np.array([[0.0, ln3, -2.0 * ln3]])
+    b = np.array([[0.0, ln3, -ln3]])
+    g, beta = orc.gates(a, b, A_log, dt_bias)
+    _close(g, [[-math.log(2.0), -5.0 * math.log(4.0), -math.log(4.0 / 3.0)]], 1e-14, "g closed forms")
+    _close(beta, [[0.5, 0.75, 0.25]], 1e-14, "beta closed forms")
+
+
+def pin_gates_identities_and_tails(orc):
+    """softplus(x) - softplus(-x) = x and sigmoid(x) + sigmoid(-x) = 1 on random points;
+    far tails: softplus(40) = 40 + e^-40, softplus(-40) = e^-40 (relative), so a ReLU or
+    an exp in place of softplus fails; g <= 0 everywhere and heads are not mixed up."""
+    rng = np.random.default_rng(23)
+    Hv = 4
+    A_log = rng.uniform(0.0, 2.7, Hv)
+    dt_bias = rng.uniform(-4.0, 1.0, Hv)
+    x = rng.standard_normal((9, Hv)) * 3.0
+    g_pos, b_pos = orc.gates(x - dt_bias, x, A_log, dt_bias)
+    g_neg, b_neg = orc.gates(-x - dt_bias, -x, A_log, dt_bias)
+    A = np.exp(A_log)
+    _close((g_neg - g_pos) / A, x, 1e-13, "softplus(x) - softplus(-x) = x")
+    _close(b_pos + b_neg, np.ones_like(x), 1e-14, "sigmoid(x) + sigmoid(-x) = 1")
+    assert np.all(g_pos <= 0.0) and np.all(g_neg <= 0.0), "g must be a log decay (<= 0)"
+    tail = np.array([[40.0, -40.0, 0.0, 0.0]])
+    g, _ = orc.gates(tail - dt_bias, np.zeros((1, Hv)), A_log, dt_bias)
+    assert abs(g[0, 0] / -(A[0] * (40.0 + math.exp(-40.0))) - 1.0) < 1e-14, "softplus(40)"
+    assert abs(g[0, 1] / -(A[1] * math.exp(-40.0)) - 1.0) < 1e-12, "softplus(-40) = e^-40 (relative)"
+    _close(g[0, 2:], -A[2:] * math.log(2.0), 1e-14, "per-head A at softplus(0)")
+
 
 def read_golden_geometry():
     cases = {}

@@ -53,6 +53,20 @@ MUTANTS = [
      "exp(gam[(int64_t)j * dk + c] - gam[(int64_t)r * dk + c]);"),
     ("chunk_output_exclusive", "for (int32_t j = 0; j <= r; ++j) {", "for (int32_t j = 0; j < r; ++j) {"),
     ("chunk_factorised_decay_sign", "exp(gl - gam[(int64_t)j * dk + c]);", "exp(gam[(int64_t)j * dk + c] - gl);"),
+    ("gate_sign", "g[t * Hv + h] = -exp(A_log[h])", "g[t * Hv + h] = exp(A_log[h])"),
+    ("gate_A_not_exponentiated", "g[t * Hv + h] = -exp(A_log[h]) * softplus", "g[t * Hv + h] = -A_log[h] * softplus"),
+    ("gate_dt_bias_dropped", "softplus(a[t * Hv + h] + dt_bias[h])", "softplus(a[t * Hv + h])"),
+    ("gate_dt_bias_negated", "softplus(a[t * Hv + h] + dt_bias[h])", "softplus(a[t * Hv + h] - dt_bias[h])"),
+    ("gate_relu_for_softplus", "return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+     "return x > 0.0 ? x : 0.0;"),
+    ("gate_softplus_branch_sign", "return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));",
+     "return x > 0.0 ? x - log1p(exp(-x)) : log1p(exp(x));"),
+    ("gate_exp_for_softplus", "return x > 0.0 ? x + log1p(exp(-x)) : log1p(exp(x));", "return exp(x);"),
+    ("gate_beta_silu", "beta[t * Hv + h] = sigmoid(b[t * Hv + h]);",
+     "beta[t * Hv + h] = b[t * Hv + h] * sigmoid(b[t * Hv + h]);"),
+    ("gate_beta_sign", "beta[t * Hv + h] = sigmoid(b[t * Hv + h]);", "beta[t * Hv + h] = sigmoid(-b[t * Hv + h]);"),
+    ("gate_head_index", "-exp(A_log[h]) * softplus(a[t * Hv + h] + dt_bias[h])",
+     "-exp(A_log[0]) * softplus(a[t * Hv + h] + dt_bias[h])"),
     ("decode_skips_conv_state_update", "gdn_oracle_conv1d_step(x, B, Cc, conv_w, conv_state, act, y);",
      "{ double* tmp = (double*)malloc(sizeof(double) * B * 3 * Cc); "
      "memcpy(tmp, conv_state, sizeof(double) * B * 3 * Cc); "
