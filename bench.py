@@ -15,6 +15,7 @@ Also measured in the same run (``workloads``):
   varlen8_33k_bf16    8 packed sequences (63, 64, 65 + five lengths up to 8192), same call
   kda_h64_s16384_bf16 per-key-channel decay, 64 heads, 16384 tokens, the chunk call alone
   kda_decode_b64_h64_bf16  the per-key-channel decode step, 64 sequences x 64 heads
+  decode_b64_ab_bf16  the decode step with g, beta derived from the a / b projections
 each in tokens/s (state-updates/s for the decode) with its roofline fraction (algorithmic HBM
 bytes / time / 8 TB/s).
 
@@ -115,8 +116,9 @@ def oracle_threads():
 # decode
 # ---------------------------------------------------------------------------
 
-def bench_decode(steps, warmup, batch=64, per_channel=False):
-    """64 sequences of one token; per_channel: the per-key-channel decode at 64 heads (ratio 1)."""
+def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False):
+    """64 sequences of one token; per_channel: the per-key-channel decode at 64 heads (ratio 1);
+    derived_gates: g and beta derived in the kernel from the a / b projections (gdn_decode_step_ab)."""
     if per_channel:
         geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
         d = gi.gen_decode(1006, batch, geo, per_channel=True)
@@ -126,6 +128,11 @@ def bench_decode(steps, warmup, batch=64, per_channel=False):
         d = gi.gen_decode(1002, batch)
         cfg = gdn.config()
         hv, bytes_per, traffic = HV, DECODE_BYTES_PER_UPDATE, DECODE_TRAFFIC_BYTES
+    ab = None
+    if derived_gates:
+        r = gi.gen_gate_projections(1102, batch)
+        ab = (t_dev(r["a"], True), t_dev(r["b"], True), t_dev(r["A_log"]), t_dev(r["dt_bias"]))
+        bytes_per, traffic = bytes_per - 2 * hv * 4 + 2 * hv * 2, None   # a, b bf16 in place of g, beta fp32
     n_sets = 3
     x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
                             t_dev(d["z"], True), t_dev(d["norm_w"]))
@@ -134,7 +141,10 @@ def bench_decode(steps, warmup, batch=64, per_channel=False):
     out = torch.empty((batch, hv, D), dtype=torch.bfloat16, device="cuda")
 
     def step(i):
-        gdn.decode_step(x, w, convs[i], g, beta, z, nw, states[i], out=out, cfg=cfg)
+        if ab is None:
+            gdn.decode_step(x, w, convs[i], g, beta, z, nw, states[i], out=out, cfg=cfg)
+        else:
+            gdn.decode_step(x, w, convs[i], None, None, z, nw, states[i], out=out, cfg=cfg, ab=ab)
 
     ms, per = time_calls(step, n_sets, steps, warmup)
     return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3),
@@ -294,7 +304,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode"])
+                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode", "decode_ab"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
@@ -351,6 +361,11 @@ def main():
             roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
+    if wl in ("all", "decode_ab"):
+        dab = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), derived_gates=True)
+        workloads["decode_b64_ab_bf16"] = dict(
+            metric="state-updates/s", value=dab["updates_per_s"], ms=dab["ms"], roofline=dab["roofline"],
+            call="gdn_decode_step_ab: g, beta derived in the kernel from the a / b projections")
     if wl in ("all", "kda_decode"):
         kdd = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), per_channel=True)
         workloads["kda_decode_b64_h64_bf16"] = dict(

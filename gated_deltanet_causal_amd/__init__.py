@@ -27,7 +27,8 @@ GDN_F32, GDN_BF16 = 0, 1
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_conv1d_prefill",
            "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
-           "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill", "gdn_decode_step")
+           "gdn_chunk_prefill_ab", "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill",
+           "gdn_prefill_ab", "gdn_decode_step", "gdn_decode_step_ab")
 
 
 class GDNError(RuntimeError):
@@ -79,6 +80,12 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                          i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "gdn_decode_step": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp],
                             ctypes.c_int),
+        "gdn_chunk_prefill_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp, vp,
+                                  vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_prefill_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                            vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_decode_step_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
+                                vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -182,13 +189,28 @@ def chunk_prefill_workspace_size(N: int, T: int, cfg: Optional[GDNConfig] = None
     return out.value
 
 
-def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
-                  beta: torch.Tensor, cu: torch.Tensor, *, cu_host=None,
+def _gate_args(g, beta, ab):
+    """(g, beta) given, or ab = (a, b, A_log, dt_bias) from which the kernels derive them."""
+    if ab is None:
+        return [_ptr(g), _ptr(beta)], False
+    if g is not None or beta is not None:
+        raise ValueError("pass either g and beta or ab=(a, b, A_log, dt_bias)")
+    a, b, A_log, dt_bias = ab
+    for t in (a, b, A_log, dt_bias):
+        if not t.is_contiguous():
+            raise ValueError("a, b, A_log and dt_bias must be contiguous")
+    return [_ptr(a), _ptr(b), _ptr(A_log), _ptr(dt_bias)], True
+
+
+def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor],
+                  beta: Optional[torch.Tensor], cu: torch.Tensor, *, cu_host=None,
                   initial_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                  workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+                  workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None, ab=None):
     """Chunk-wise gated delta rule; q, k [T, Hk*dk] (or [T, Hk, dk]), v [T, Hv*dv], views with
-    a shared row stride allowed.  Returns (out [T, Hv, dv], final_state [N, Hv, dv, dk])."""
+    a shared row stride allowed.  Gates: g, beta, or (g = beta = None) ab = (a, b, A_log,
+    dt_bias) with a, b [T, Hv] in q's dtype (gdn_chunk_prefill_ab).
+    Returns (out [T, Hv, dv], final_state [N, Hv, dv, dk])."""
     cfg = cfg or config()
     T = q.shape[0]
     N = cu.numel() - 1
@@ -205,9 +227,11 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     hc = _cu_host(cu, cu_host)
-    _check("gdn_chunk_prefill", load_library().gdn_chunk_prefill(
+    gates, derived = _gate_args(g, beta, ab)
+    name = "gdn_chunk_prefill_ab" if derived else "gdn_chunk_prefill"
+    _check(name, getattr(load_library(), name)(
         ctypes.byref(cfg), _dtype(q), _dtype(out), _ptr(q), _ptr(k), qs, _ptr(v), _row_stride(v),
-        _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state),
+        *gates, _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
     return out, final_state
 
@@ -239,15 +263,16 @@ def prefill_workspace_size(N: int, T: int, dtype: torch.dtype = torch.bfloat16,
     return out.value
 
 
-def prefill(x: torch.Tensor, conv_w: torch.Tensor, cu: torch.Tensor, g: torch.Tensor,
-            beta: torch.Tensor, z: torch.Tensor, norm_w: torch.Tensor, *, cu_host=None,
+def prefill(x: torch.Tensor, conv_w: torch.Tensor, cu: torch.Tensor, g: Optional[torch.Tensor],
+            beta: Optional[torch.Tensor], z: torch.Tensor, norm_w: torch.Tensor, *, cu_host=None,
             conv_state_in: Optional[torch.Tensor] = None,
             conv_state_out: Optional[torch.Tensor] = None,
             initial_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
             final_state: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-            workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+            workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None, ab=None):
     """The whole sublayer prefill (conv -> chunk-wise delta rule -> gated norm) over packed
-    sequences; x [T, Cc] (row stride free).  Returns (out [T, Hv, dv], final_state)."""
+    sequences; x [T, Cc] (row stride free).  Gates: g, beta, or ab = (a, b, A_log, dt_bias)
+    (gdn_prefill_ab).  Returns (out [T, Hv, dv], final_state)."""
     cfg = cfg or config()
     T = x.shape[0]
     N = cu.numel() - 1
@@ -258,35 +283,41 @@ def prefill(x: torch.Tensor, conv_w: torch.Tensor, cu: torch.Tensor, g: torch.Te
         final_state = torch.empty((N, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim),
                                   dtype=torch.float32, device=x.device)
     for t in (g, beta, z, out):
-        if not t.is_contiguous():
+        if t is not None and not t.is_contiguous():
             raise ValueError("prefill g, beta, z and out must be contiguous")
     if workspace is None:
         workspace = torch.empty(prefill_workspace_size(N, T, x.dtype, cfg), dtype=torch.uint8,
                                 device=x.device)
     hc = _cu_host(cu, cu_host)
-    _check("gdn_prefill", load_library().gdn_prefill(
+    gates, derived = _gate_args(g, beta, ab)
+    name = "gdn_prefill_ab" if derived else "gdn_prefill"
+    _check(name, getattr(load_library(), name)(
         ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _row_stride(x), _ptr(conv_w),
-        _ptr(conv_state_in), _ptr(conv_state_out), _ptr(g), _ptr(beta), _ptr(z), _ptr(norm_w),
+        _ptr(conv_state_in), _ptr(conv_state_out), *gates, _ptr(z), _ptr(norm_w),
         _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state), _ptr(workspace),
         workspace.numel() * workspace.element_size(), _stream()))
     return out, final_state
 
 
-def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: torch.Tensor,
-                beta: torch.Tensor, z: torch.Tensor, norm_w: torch.Tensor, state: torch.Tensor, *,
+def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: Optional[torch.Tensor],
+                beta: Optional[torch.Tensor], z: torch.Tensor, norm_w: torch.Tensor, state: torch.Tensor, *,
                 out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-                cfg: Optional[GDNConfig] = None) -> torch.Tensor:
-    """One fused decode step; conv_state and state are updated in place.  Returns out [B, Hv, dv]."""
+                cfg: Optional[GDNConfig] = None, ab=None) -> torch.Tensor:
+    """One fused decode step; conv_state and state are updated in place.  Gates: g, beta, or
+    ab = (a, b, A_log, dt_bias) with a, b [B, Hv] in x's dtype (gdn_decode_step_ab).
+    Returns out [B, Hv, dv]."""
     cfg = cfg or config()
     B = x.shape[0]
     if out is None:
         out = torch.empty((B, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype, device=x.device)
     for t in (x, conv_state, g, beta, z, state, out):
-        if not t.is_contiguous():
+        if t is not None and not t.is_contiguous():
             raise ValueError("decode_step tensors must be contiguous")
-    _check("gdn_decode_step", load_library().gdn_decode_step(
-        ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(g),
-        _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, _stream()))
+    gates, derived = _gate_args(g, beta, ab)
+    name = "gdn_decode_step_ab" if derived else "gdn_decode_step"
+    _check(name, getattr(load_library(), name)(
+        ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), *gates,
+        _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, _stream()))
     return out
 
 

@@ -55,6 +55,25 @@ gdn_status_t hip_status(hipError_t e) { return e == hipSuccess ? GDN_OK : GDN_ER
 
 size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+// The gates of a call: fp32 g / beta (g 16-byte aligned, it is read as vectors
+// with per-key-channel decay), or the a / b projections with A_log and dt_bias
+// (scalar decay only).
+gdn_status_t check_gates(const Dims& d, const gdn::Gates& gt, bool any_rows) {
+  if (gt.a || gt.b || gt.A_log || gt.dt_bias) {
+    if (d.per_channel) return GDN_ERR_UNSUPPORTED;
+    if (any_rows && (!gt.a || !gt.b || !gt.A_log || !gt.dt_bias)) return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+  }
+  if (any_rows && (!gt.g || !gt.beta)) return GDN_ERR_INVALID_ARG;
+  if (any_rows && !aligned16(gt.g)) return GDN_ERR_INVALID_ARG;
+  return GDN_OK;
+}
+
+gdn::Gates given_gates(const float* g, const float* beta) { return gdn::Gates{g, beta, nullptr, nullptr, nullptr, nullptr}; }
+gdn::Gates derived_gates(const void* a, const void* b, const float* A_log, const float* dt_bias) {
+  return gdn::Gates{nullptr, nullptr, a, b, A_log, dt_bias};
+}
+
 // gdn_prefill workspace: the conv output [T][Cc] | the chunk workspace | the
 // fp32 pre-norm output [T][Hv][dv] when the chunk kernels do not apply the norm
 struct PrefillWs {
@@ -154,24 +173,26 @@ gdn_status_t gdn_chunk_prefill_workspace_size(const gdn_config_t* cfg, int32_t N
   return GDN_OK;
 }
 
-gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
-                               gdn_dtype_t out_dtype, const void* q, const void* k,
-                               int64_t qk_stride, const void* v, int64_t v_stride,
-                               const float* g, const float* beta, const float* initial_state,
-                               const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
-                               int32_t T, void* out, float* final_state, void* ws,
-                               size_t ws_bytes, gdn_stream_t stream) {
+static gdn_status_t chunk_prefill_checked(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                                          gdn_dtype_t out_dtype, const void* q, const void* k,
+                                          int64_t qk_stride, const void* v, int64_t v_stride,
+                                          const gdn::Gates& gt, const float* initial_state,
+                                          const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                          int32_t T, void* out, float* final_state, void* ws,
+                                          size_t ws_bytes, gdn_stream_t stream) {
   Dims d;
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
   if (!valid_dtype(in_dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
   if (!cu_dev) return GDN_ERR_INVALID_ARG;
-  if (T > 0 && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_INVALID_ARG;
+  st = check_gates(d, gt, T > 0);
+  if (st != GDN_OK) return st;
+  if (T > 0 && (!q || !k || !v || !out)) return GDN_ERR_INVALID_ARG;
   const int64_t vec = in_dtype == GDN_BF16 ? 8 : 4;   // elements per 16-byte load
   if (qk_stride < (int64_t)d.hk * d.dk || v_stride < (int64_t)d.hv * d.dv) return GDN_ERR_INVALID_ARG;
   if (qk_stride % vec || v_stride % vec) return GDN_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g))) return GDN_ERR_INVALID_ARG;
+  if (T > 0 && (!aligned16(q) || !aligned16(k) || !aligned16(v))) return GDN_ERR_INVALID_ARG;
   if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)))
     return GDN_ERR_INVALID_ARG;
   st = check_seqlens(cu_host, N, T);
@@ -184,7 +205,7 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
   if (overlaps(out, out_bytes, ws, need) || overlaps(final_state, state_bytes, ws, need))
     return GDN_ERR_INVALID_ARG;
   return hip_status(gdn::launch_chunk_prefill(d, in_dtype == GDN_BF16, out_dtype == GDN_BF16, q, k,
-                                              qk_stride, v, v_stride, g, beta, initial_state,
+                                              qk_stride, v, v_stride, gt, initial_state,
                                               cu_dev, cu_host, N, T, out, final_state, ws,
                                               ws_bytes, nullptr, nullptr,
                                               static_cast<hipStream_t>(stream)));
@@ -201,22 +222,24 @@ gdn_status_t gdn_prefill_workspace_size(const gdn_config_t* cfg, gdn_dtype_t dty
   return GDN_OK;
 }
 
-gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
-                         const void* x, int64_t x_stride, const float* conv_w,
-                         const void* conv_state_in, void* conv_state_out, const float* g,
-                         const float* beta, const void* z, const float* norm_w,
-                         const float* initial_state, const int32_t* cu_dev, const int32_t* cu_host,
-                         int32_t N, int32_t T, void* out, float* final_state, void* ws,
-                         size_t ws_bytes, gdn_stream_t stream) {
+static gdn_status_t prefill_checked(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                    const void* x, int64_t x_stride, const float* conv_w,
+                                    const void* conv_state_in, void* conv_state_out, const gdn::Gates& gt,
+                                    const void* z, const float* norm_w, const float* initial_state,
+                                    const int32_t* cu_dev, const int32_t* cu_host, int32_t N, int32_t T,
+                                    void* out, float* final_state, void* ws, size_t ws_bytes,
+                                    gdn_stream_t stream) {
   Dims d;
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (N < 0 || T < 0 || !cu_dev || !conv_w) return GDN_ERR_INVALID_ARG;
-  if (T > 0 && (!x || !g || !beta || !z || !norm_w || !out)) return GDN_ERR_INVALID_ARG;
+  st = check_gates(d, gt, T > 0);
+  if (st != GDN_OK) return st;
+  if (T > 0 && (!x || !z || !norm_w || !out)) return GDN_ERR_INVALID_ARG;
   if (x_stride < d.cc || x_stride % 8) return GDN_ERR_INVALID_ARG;
-  if (T > 0 && (!aligned16(x) || !aligned16(conv_w) || !aligned16(g) || !aligned16(z) ||
-                !aligned16(norm_w) || !aligned16(out)))
+  if (T > 0 && (!aligned16(x) || !aligned16(conv_w) || !aligned16(z) || !aligned16(norm_w) ||
+                !aligned16(out)))
     return GDN_ERR_INVALID_ARG;
   if ((conv_state_in && !aligned16(conv_state_in)) || (initial_state && !aligned16(initial_state)) ||
       (final_state && !aligned16(final_state)))
@@ -252,12 +275,12 @@ gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t
   if (gdn::chunk_fuses_norm(d, bf16, N)) {
     // bf16 here: the gate comes in the activations' dtype
     return hip_status(gdn::launch_chunk_prefill(d, bf16, out_dtype == GDN_BF16, q, k, d.cc, v, d.cc,
-                                                g, beta, initial_state, cu_dev, cu_host, N, T, out,
+                                                gt, initial_state, cu_dev, cu_host, N, T, out,
                                                 final_state, w8 + wl.chunk, wl.o - wl.chunk,
                                                 static_cast<const uint16_t*>(z), norm_w, s));
   }
   float* o = reinterpret_cast<float*>(w8 + wl.o);
-  e = gdn::launch_chunk_prefill(d, bf16, false, q, k, d.cc, v, d.cc, g, beta, initial_state, cu_dev,
+  e = gdn::launch_chunk_prefill(d, bf16, false, q, k, d.cc, v, d.cc, gt, initial_state, cu_dev,
                                 cu_host, N, T, o, final_state, w8 + wl.chunk, wl.o - wl.chunk,
                                 nullptr, nullptr, s);
   if (e != hipSuccess) return GDN_ERR_HIP;
@@ -286,23 +309,90 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
                                               static_cast<hipStream_t>(stream)));
 }
 
-gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
-                             const void* x, const float* conv_w, void* conv_state, const float* g,
-                             const float* beta, const void* z, const float* norm_w, float* state,
-                             void* out, int32_t B, gdn_stream_t stream) {
+static gdn_status_t decode_step_checked(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                        const void* x, const float* conv_w, void* conv_state,
+                                        const gdn::Gates& gt, const void* z, const float* norm_w,
+                                        float* state, void* out, int32_t B, gdn_stream_t stream) {
   Dims d;
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (B < 0 || B > 65535 * 64) return GDN_ERR_INVALID_ARG;
   if (d.hv / d.hk > 4) return GDN_ERR_UNSUPPORTED;   // one workgroup holds a key head's value heads
-  if (B > 0 && (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out))
+  st = check_gates(d, gt, B > 0);
+  if (st != GDN_OK) return st;
+  if (B > 0 && (!x || !conv_w || !conv_state || !z || !norm_w || !state || !out))
     return GDN_ERR_INVALID_ARG;
-  if (B > 0 && (!aligned16(conv_w) || !aligned16(state) || (d.per_channel && !aligned16(g))))
-    return GDN_ERR_INVALID_ARG;
+  if (B > 0 && (!aligned16(conv_w) || !aligned16(state))) return GDN_ERR_INVALID_ARG;
   return hip_status(gdn::launch_decode_step(d, dtype == GDN_BF16, out_dtype == GDN_BF16, x, conv_w,
-                                            conv_state, g, beta, z, norm_w, state, out, B,
+                                            conv_state, gt, z, norm_w, state, out, B,
                                             static_cast<hipStream_t>(stream)));
+}
+
+
+gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                               gdn_dtype_t out_dtype, const void* q, const void* k,
+                               int64_t qk_stride, const void* v, int64_t v_stride,
+                               const float* g, const float* beta, const float* initial_state,
+                               const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                               int32_t T, void* out, float* final_state, void* ws,
+                               size_t ws_bytes, gdn_stream_t stream) {
+  return chunk_prefill_checked(cfg, in_dtype, out_dtype, q, k, qk_stride, v, v_stride, given_gates(g, beta),
+                               initial_state, cu_dev, cu_host, N, T, out, final_state, ws, ws_bytes, stream);
+}
+
+gdn_status_t gdn_chunk_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                                  gdn_dtype_t out_dtype, const void* q, const void* k,
+                                  int64_t qk_stride, const void* v, int64_t v_stride,
+                                  const void* a, const void* b, const float* A_log,
+                                  const float* dt_bias, const float* initial_state,
+                                  const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                  int32_t T, void* out, float* final_state, void* ws,
+                                  size_t ws_bytes, gdn_stream_t stream) {
+  return chunk_prefill_checked(cfg, in_dtype, out_dtype, q, k, qk_stride, v, v_stride,
+                               derived_gates(a, b, A_log, dt_bias), initial_state, cu_dev, cu_host, N, T,
+                               out, final_state, ws, ws_bytes, stream);
+}
+
+gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                         const void* x, int64_t x_stride, const float* conv_w,
+                         const void* conv_state_in, void* conv_state_out, const float* g,
+                         const float* beta, const void* z, const float* norm_w,
+                         const float* initial_state, const int32_t* cu_dev, const int32_t* cu_host,
+                         int32_t N, int32_t T, void* out, float* final_state, void* ws,
+                         size_t ws_bytes, gdn_stream_t stream) {
+  return prefill_checked(cfg, dtype, out_dtype, x, x_stride, conv_w, conv_state_in, conv_state_out,
+                         given_gates(g, beta), z, norm_w, initial_state, cu_dev, cu_host, N, T, out,
+                         final_state, ws, ws_bytes, stream);
+}
+
+gdn_status_t gdn_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                            const void* x, int64_t x_stride, const float* conv_w,
+                            const void* conv_state_in, void* conv_state_out, const void* a,
+                            const void* b, const float* A_log, const float* dt_bias, const void* z,
+                            const float* norm_w, const float* initial_state, const int32_t* cu_dev,
+                            const int32_t* cu_host, int32_t N, int32_t T, void* out,
+                            float* final_state, void* ws, size_t ws_bytes, gdn_stream_t stream) {
+  return prefill_checked(cfg, dtype, out_dtype, x, x_stride, conv_w, conv_state_in, conv_state_out,
+                         derived_gates(a, b, A_log, dt_bias), z, norm_w, initial_state, cu_dev, cu_host,
+                         N, T, out, final_state, ws, ws_bytes, stream);
+}
+
+gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                             const void* x, const float* conv_w, void* conv_state, const float* g,
+                             const float* beta, const void* z, const float* norm_w, float* state,
+                             void* out, int32_t B, gdn_stream_t stream) {
+  return decode_step_checked(cfg, dtype, out_dtype, x, conv_w, conv_state, given_gates(g, beta), z, norm_w,
+                             state, out, B, stream);
+}
+
+gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                const void* x, const float* conv_w, void* conv_state, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias,
+                                const void* z, const float* norm_w, float* state, void* out,
+                                int32_t B, gdn_stream_t stream) {
+  return decode_step_checked(cfg, dtype, out_dtype, x, conv_w, conv_state, derived_gates(a, b, A_log, dt_bias),
+                             z, norm_w, state, out, B, stream);
 }
 
 }  // extern "C"

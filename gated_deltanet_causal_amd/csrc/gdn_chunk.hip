@@ -563,7 +563,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
 template <bool F32, typename Tin, bool kPairK>
 __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
-    const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
+    Gates gates, const int32_t* __restrict__ cu,
     int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
   using O = Ops<F32>;
   using E = typename O::E;
@@ -593,11 +593,12 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   const int ratio = hv / hk;
 
   // cumulative log decay and beta of value head kh * ratio + hh (padded tokens
-  // decay by 1 and have beta 0), by wave 0: lane = token
+  // decay by 1 and have beta 0), by wave 0: lane = token.  The gates are given,
+  // or derived here from the a / b projections.
   auto gb_load = [&](int hh, float& gv, float& bv) {
     const int h = kh * ratio + hh;
-    gv = lane < L ? g[(int64_t)(t0 + lane) * hv + h] : 0.0f;
-    bv = lane < L ? beta[(int64_t)(t0 + lane) * hv + h] : 0.0f;
+    gv = bv = 0.0f;
+    if (lane < L) gate_pair<Tin>(gates, t0 + lane, hv, h, gv, bv);
   };
   auto gb_store = [&](int buf, float gv, float bv) {
 #pragma unroll
@@ -1761,7 +1762,7 @@ int chunk_spine_kind(const Dims& d, bool in_bf16, int n) {
 
 template <bool F32, bool kPC, typename Tin, typename To>
 hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_stride, const void* v,
-                      int64_t v_stride, const float* g, const float* beta, const float* init_state,
+                      int64_t v_stride, const Gates& gt, const float* init_state,
                       const int32_t* cu_dev, int n, int total_chunks, void* out,
                       float* final_state, void* ws, const FusedNorm& nrm, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -1779,11 +1780,11 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   if (total_chunks > 0) {
     if constexpr (kPC)
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
-                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
+                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt.g, gt.beta,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     else   // bf16: records in the paired-tile k order of the register-resident spines
       hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, !F32>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
-                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, g, beta,
+                         static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt,
                          cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1815,7 +1816,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
                        static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride,
-                       static_cast<const Tin*>(v), v_stride, g, init_state, cu_dev, n, d.hk, d.hv, w,
+                       static_cast<const Tin*>(v), v_stride, gt.g, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state);
   }
   return hipGetLastError();
@@ -1823,15 +1824,15 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
 
 template <bool kPC>
 hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void* q, const void* k,
-                          int64_t qk_stride, const void* v, int64_t v_stride, const float* g,
-                          const float* beta, const float* init_state, const int32_t* cu_dev, int n,
+                          int64_t qk_stride, const void* v, int64_t v_stride, const Gates& gt,
+                          const float* init_state, const int32_t* cu_dev, int n,
                           int total, void* out, float* final_state, void* ws, const FusedNorm& nrm,
                           hipStream_t s) {
   if (in_bf16)
-    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
-  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace
@@ -1847,8 +1848,8 @@ size_t chunk_workspace_bytes(const Dims& d, int n, int t) {
 
 hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
                                 const void* k, int64_t qk_stride, const void* v,
-                                int64_t v_stride, const float* g, const float* beta,
-                                const float* init_state, const int32_t* cu_dev,
+                                int64_t v_stride, const Gates& gt, const float* init_state,
+                                const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
                                 float* final_state, void* ws, size_t ws_bytes,
                                 const uint16_t* norm_z, const float* norm_w, hipStream_t s) {
@@ -1860,8 +1861,8 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
   for (int i = 0; i < n; ++i) total += (cu_host[i + 1] - cu_host[i] + kC - 1) / kC;
   const FusedNorm nrm{norm_z, norm_w, d.rms_eps};
   return d.per_channel
-             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, g, beta, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
+             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace gdn

@@ -78,7 +78,7 @@ __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_
 template <typename T, typename To, bool kPerChannel, int kRatio>
 __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
-    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
+    Gates gates, const T* __restrict__ z,
     const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
     int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
   const int b = blockIdx.x / hk;
@@ -130,15 +130,18 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   // khat . qtil, computed by every wave (no exchange needed)
   const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
   // this thread's normalised key / query columns and decay factors
-  float kcol[4], qcol[4], a[4];
+  float kcol[4], qcol[4], a[4], bt;
 #pragma unroll
   for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e] * rk; qcol[e] = s_q[4 * cg + e] * rq; }
   if constexpr (kPerChannel) {
-    const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)b * hv + h) * kD + 4 * cg);
+    const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(gates.g + ((int64_t)b * hv + h) * kD + 4 * cg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+    bt = gates.beta[(int64_t)b * hv + h];
   } else {
-    const float av = __expf(g[(int64_t)b * hv + h]);
+    float gs;
+    gate_pair<T>(gates, b, hv, h, gs, bt);   // given, or derived from the a / b projections
+    const float av = __expf(gs);
 #pragma unroll
     for (int e = 0; e < 4; ++e) a[e] = av;
   }
@@ -146,7 +149,6 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   // per row: decay, the two dot products reduced over the row's 32 lanes,
   // u = beta (v - p), o = r + u (khat . qtil), then the row is updated and
   // written back: S' = Sd + u khat^T
-  const float bt = beta[(int64_t)b * hv + h];
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m) {
     if (m + kWindow < kRowsPerThread) sreg[m + kWindow] = load_row(m + kWindow);
@@ -185,13 +187,13 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
 
 template <typename T, typename To, bool kPC>
 hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void* conv_state,
-                        const float* g, const float* beta, const void* z, const float* norm_w,
+                        const Gates& gt, const void* z, const float* norm_w,
                         float* state, void* out, int b, hipStream_t s) {
   const int ratio = d.hv / d.hk;
   dim3 grid(b * d.hk);
 #define GDN_DECODE_LAUNCH(R)                                                                      \
   hipLaunchKernelGGL((decode_step_kernel<T, To, kPC, R>), grid, dim3(kGroup * (R)), 0, s,         \
-                     static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), g, beta,      \
+                     static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,          \
                      static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv, \
                      d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps)
   switch (ratio) {
@@ -207,24 +209,24 @@ hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void*
 
 template <typename T, typename To>
 hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* conv_state,
-                       const float* g, const float* beta, const void* z, const float* norm_w,
+                       const Gates& gt, const void* z, const float* norm_w,
                        float* state, void* out, int b, hipStream_t s) {
-  return d.per_channel ? decode_ratio<T, To, true>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
-                       : decode_ratio<T, To, false>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
+  return d.per_channel ? decode_ratio<T, To, true>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
+                       : decode_ratio<T, To, false>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
-                              const float* conv_w, void* conv_state, const float* g,
-                              const float* beta, const void* z, const float* norm_w,
-                              float* state, void* out, int b, hipStream_t s) {
+                              const float* conv_w, void* conv_state, const Gates& gt,
+                              const void* z, const float* norm_w, float* state, void* out, int b,
+                              hipStream_t s) {
   if (b == 0) return hipSuccess;
   if (bf16)
-    return out_bf16 ? decode_impl<uint16_t, uint16_t>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
-                    : decode_impl<uint16_t, float>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
-  return out_bf16 ? decode_impl<float, uint16_t>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s)
-                  : decode_impl<float, float>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out, b, s);
+    return out_bf16 ? decode_impl<uint16_t, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
+                    : decode_impl<uint16_t, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
+  return out_bf16 ? decode_impl<float, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
+                  : decode_impl<float, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
 }
 
 }  // namespace gdn

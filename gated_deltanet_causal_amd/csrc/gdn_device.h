@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gdn_launch.h"
+
 namespace gdn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -107,5 +109,30 @@ __device__ __forceinline__ float quad_sum(float v) {
 }
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// Gates of one token and value head from the a / b projections (the prepare
+// stage's gate derivation, as read from the golden PR and the TDD ledger's
+// alpha/beta transforms): g = -exp(A_log) softplus(a + dt_bias), beta =
+// sigmoid(b); softplus(x) = log(1 + e^x), as x + log1p(e^-x) for x > 0.
+__device__ __forceinline__ void derive_gates(float a, float b, float A_log, float dt_bias, float& g,
+                                             float& beta) {
+  const float x = a + dt_bias;
+  const float sp = x > 0.0f ? x + log1pf(__expf(-x)) : log1pf(__expf(x));
+  g = -__expf(A_log) * sp;
+  beta = sigmoidf_(b);
+}
+
+// g and beta of row t, value head h (scalar decay)
+template <typename T>
+__device__ __forceinline__ void gate_pair(const Gates& gt, int64_t t, int hv, int h, float& g, float& beta) {
+  const int64_t i = t * hv + h;
+  if (gt.a) {
+    derive_gates(ld(static_cast<const T*>(gt.a) + i), ld(static_cast<const T*>(gt.b) + i), gt.A_log[h],
+                 gt.dt_bias[h], g, beta);
+  } else {
+    g = gt.g[i];
+    beta = gt.beta[i];
+  }
+}
 
 }  // namespace gdn

@@ -8,6 +8,18 @@
 
 namespace gdn {
 
+// Where g and beta of a call come from: fp32 arrays, or (a non-null) derived
+// per element from the a / b projections [rows][Hv] in the activations'
+// dtype with the per-head A_log and dt_bias (scalar decay only).
+struct Gates {
+  const float* g;
+  const float* beta;
+  const void* a;
+  const void* b;
+  const float* A_log;
+  const float* dt_bias;
+};
+
 // Geometry resolved from gdn_config_t.
 struct Dims {
   int hk, hv, dk, dv;
@@ -28,9 +40,9 @@ hipError_t launch_gated_rmsnorm(const Dims& d, bool o_bf16, bool z_bf16, bool ou
                                 const void* o, const void* z, const float* w, void* out,
                                 int64_t rows, hipStream_t s);
 hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
-                              const float* conv_w, void* conv_state, const float* g,
-                              const float* beta, const void* z, const float* norm_w,
-                              float* state, void* out, int b, hipStream_t s);
+                              const float* conv_w, void* conv_state, const Gates& gt,
+                              const void* z, const float* norm_w, float* state, void* out, int b,
+                              hipStream_t s);
 
 // Chunk prefill.  Workspace layout is private to gdn_chunk.hip.
 size_t chunk_workspace_bytes(const Dims& d, int n, int t);
@@ -42,8 +54,7 @@ bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n);
 // of the chunk output (requires chunk_fuses_norm).
 hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
                                 const void* k, int64_t qk_stride, const void* v,
-                                int64_t v_stride, const float* g, const float* beta,
-                                const float* init_state, const int32_t* cu_dev,
+                                int64_t v_stride, const Gates& gt, const float* init_state, const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
                                 float* final_state, void* ws, size_t ws_bytes,
                                 const uint16_t* norm_z, const float* norm_w, hipStream_t s);

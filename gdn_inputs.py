@@ -157,6 +157,20 @@ def gen_decode(seed: int, batch: int, geo: Geometry = Geometry(), *, bf16: bool 
                 state=state)
 
 
+def gen_gate_projections(seed: int, rows: int, hv: int = HV, *, bf16: bool = True) -> Dict[str, np.ndarray]:
+    """Raw gate inputs for ``rows`` tokens (or sequences): the a / b projection outputs
+    a, b [rows, Hv] ~ N(0, 1) (bf16-representable where ``bf16``), and per head
+    A_log = log(U[1, 16]) and dt_bias = log(expm1(U[0.001, 0.1])) (the bias that makes
+    softplus(dt_bias) a step in [0.001, 0.1]), fp32."""
+    rng = np.random.default_rng(seed)
+    act_round = bf16_round if bf16 else (lambda a: a.astype(np.float32))
+    a = act_round(rng.standard_normal((rows, hv), dtype=np.float32))
+    b = act_round(rng.standard_normal((rows, hv), dtype=np.float32))
+    A_log = np.log(rng.uniform(1.0, 16.0, hv)).astype(np.float32)
+    dt_bias = np.log(np.expm1(rng.uniform(0.001, 0.1, hv))).astype(np.float32)
+    return dict(a=a, b=b, A_log=A_log, dt_bias=dt_bias)
+
+
 # The five workloads, by what they are.
 WORKLOADS = {
     "prefill_s80_fp32": dict(lengths=[80], bf16=False, init_state=False, seed=1001),

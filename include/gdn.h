@@ -156,6 +156,30 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
                                size_t ws_bytes, gdn_stream_t stream);
 
 /*
+ * The gates of a call from the a / b projections.  The golden PR's prepare
+ * stage derives the raw g/beta from the in_proj_a / in_proj_b outputs with the
+ * layer's A_log and dt_bias vectors, and the TDD ledger lists the GDN
+ * alpha/beta transform kernels; neither page prints the transform.  This
+ * library reads it as, per token (or sequence) t and value head h,
+ *     g[t][h]    = -exp(A_log[h]) * softplus(a[t][h] + dt_bias[h])
+ *     beta[t][h] = sigmoid(b[t][h]),        softplus(x) = log(1 + exp(x)).
+ * The *_ab calls below take a, b ([rows][Hv], in the activations' dtype) and
+ * A_log, dt_bias (fp32 [Hv]) in place of g and beta and derive the gates
+ * inside their kernels (no g / beta pass).  Scalar decay only:
+ * GDN_ERR_UNSUPPORTED with decay_per_key_channel.
+ */
+
+/* gdn_chunk_prefill with derived gates; a, b [T][Hv] in in_dtype. */
+gdn_status_t gdn_chunk_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                                  gdn_dtype_t out_dtype, const void* q, const void* k,
+                                  int64_t qk_stride, const void* v, int64_t v_stride,
+                                  const void* a, const void* b, const float* A_log,
+                                  const float* dt_bias, const float* initial_state,
+                                  const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                  int32_t T, void* out, float* final_state, void* ws,
+                                  size_t ws_bytes, gdn_stream_t stream);
+
+/*
  * Gated RMSNorm with the sigmoid gate (the golden PR: sigmoid, not SiLU;
  * rsqrt(variance + eps)) over rows * Hv vectors of length dv:
  *     out[i] = o[i] * rsqrt(mean(o^2) + rms_eps) * w[i] * sigmoid(z[i])
@@ -207,6 +231,16 @@ gdn_status_t gdn_prefill(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t
                          int32_t N, int32_t T, void* out, float* final_state, void* ws,
                          size_t ws_bytes, gdn_stream_t stream);
 
+/* gdn_prefill with derived gates; a, b [T][Hv] in dtype.  Workspace as for
+ * gdn_prefill (gdn_prefill_workspace_size). */
+gdn_status_t gdn_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                            const void* x, int64_t x_stride, const float* conv_w,
+                            const void* conv_state_in, void* conv_state_out, const void* a,
+                            const void* b, const float* A_log, const float* dt_bias, const void* z,
+                            const float* norm_w, const float* initial_state, const int32_t* cu_dev,
+                            const int32_t* cu_host, int32_t N, int32_t T, void* out,
+                            float* final_state, void* ws, size_t ws_bytes, gdn_stream_t stream);
+
 /*
  * One fused decode step for B sequences (the TDD ledger's scalar recurrence
  * with fused output gate; the Qwen3SsmLayer conv + recurrence + norm decode
@@ -228,6 +262,13 @@ gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dty
                              const void* x, const float* conv_w, void* conv_state, const float* g,
                              const float* beta, const void* z, const float* norm_w, float* state,
                              void* out, int32_t B, gdn_stream_t stream);
+
+/* gdn_decode_step with derived gates; a, b [B][Hv] in dtype. */
+gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                const void* x, const float* conv_w, void* conv_state, const void* a,
+                                const void* b, const float* A_log, const float* dt_bias,
+                                const void* z, const float* norm_w, float* state, void* out,
+                                int32_t B, gdn_stream_t stream);
 
 #ifdef __cplusplus
 }

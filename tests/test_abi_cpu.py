@@ -214,3 +214,25 @@ def test_prefill_argument_checks(lib):
     assert lib.gdn_prefill(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, None, 10240, FAKE, None, None,
                            None, None, None, None, None, FAKE, (ctypes.c_int32 * 1)(0), 0, 0, None, None,
                            None, 0, None) == 0                                   # nothing to do
+
+
+def test_derived_gate_calls_argument_checks(lib):
+    """The *_ab calls take a, b, A_log, dt_bias in place of g, beta: all four are required,
+    and per-key-channel decay (whose gates the pages do not derive) is unsupported."""
+    cfg, pc = _cfg(), _cfg(decay_per_key_channel=1)
+
+    def decode(c, A_log=FAKE, a=FAKE):
+        return lib.gdn_decode_step_ab(ctypes.byref(c), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, a, FAKE,
+                                      A_log, FAKE, FAKE, FAKE, FAKE, FAKE, 4, None)
+    assert decode(pc) == gdn.GDN_ERR_UNSUPPORTED
+    assert decode(cfg, A_log=None) == gdn.GDN_ERR_INVALID_ARG
+    assert decode(cfg, a=None) == gdn.GDN_ERR_INVALID_ARG
+    hc = (ctypes.c_int32 * 2)(0, 64)
+
+    def chunk(c, dt_bias=FAKE):
+        return lib.gdn_chunk_prefill_ab(ctypes.byref(c), gdn.GDN_BF16, gdn.GDN_F32, FAKE, FAKE, 10240, FAKE,
+                                        10240, FAKE, FAKE, FAKE, dt_bias, None, FAKE, hc, 1, 64,
+                                        ctypes.c_void_p(0x4000000), None, ctypes.c_void_p(0x8000000), 0, None)
+    assert chunk(pc) == gdn.GDN_ERR_UNSUPPORTED
+    assert chunk(cfg, dt_bias=None) == gdn.GDN_ERR_INVALID_ARG
+    assert chunk(cfg) == gdn.GDN_ERR_WORKSPACE          # gates accepted; the workspace is checked next

@@ -430,6 +430,81 @@ def test_prefill_entry_varlen_full_size_sampled(orc):
 
 
 # ---------------------------------------------------------------------------
+# gates derived from the a / b projections (the *_ab calls)
+# ---------------------------------------------------------------------------
+
+def _ab_dev(r, bf16):
+    return (dev(r["a"], bf16), dev(r["b"], bf16), dev(r["A_log"]), dev(r["dt_bias"]))
+
+
+def test_decode_step_ab_batch64_bf16(orc):
+    """The decode workload with the gates derived in the kernel from a, b, A_log, dt_bias."""
+    d = gi.gen_decode(1002, 64)
+    r = gi.gen_gate_projections(1102, 64)
+    cs, st = dev(d["conv_state"], True), dev(d["state"])
+    out = gdn.decode_step(dev(d["x"], True), dev(d["conv_w"]), cs, None, None, dev(d["z"], True),
+                          dev(d["norm_w"]), st, out_dtype=torch.bfloat16, ab=_ab_dev(r, True))
+    torch.cuda.synchronize()
+    g, beta = orc.gates(r["a"], r["b"], r["A_log"], r["dt_bias"])
+    o_ref, cs_ref, st_ref = orc.decode_step(d["x"], d["conv_w"], d["conv_state"], g, beta, d["z"], d["norm_w"],
+                                            d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    check(host(out), o_ref, TOL_BF16, "decode_ab out", stored_bf16=True)
+    check(host(st), st_ref, TOL_BF16, "decode_ab state")
+    assert np.array_equal(host(cs), cs_ref)
+
+
+@pytest.mark.parametrize("lengths", [[1], [65], [129], [64, 63, 65, 1, 129, 7]],
+                         ids=["T1", "T65", "T129", "six_seqs"])
+def test_chunk_prefill_ab_bf16(orc, lengths):
+    d = gi.gen_qkv(700 + sum(lengths), lengths)
+    r = gi.gen_gate_projections(800 + sum(lengths), int(sum(lengths)))
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), None, None,
+                              dev_i32(d["cu"]), cu_host=d["cu"], initial_state=dev(d["state_in"]),
+                              out_dtype=torch.float32, ab=_ab_dev(r, True))
+    torch.cuda.synchronize()
+    g, beta = orc.gates(r["a"], r["b"], r["A_log"], r["dt_bias"])
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], g, beta, d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"chunk_ab out {lengths}")
+    check(host(fs), s_ref, TOL_BF16, f"chunk_ab state {lengths}")
+
+
+def test_chunk_prefill_ab_fp32_s80(orc):
+    """The fp32 path with derived gates, at the fp32 bound."""
+    d = gi.gen_qkv(901, [80], bf16=False)
+    r = gi.gen_gate_projections(902, 80, bf16=False)
+    o, fs = gdn.chunk_prefill(dev(d["q"]), dev(d["k"]), dev(d["v"]), None, None, dev_i32(d["cu"]),
+                              cu_host=d["cu"], initial_state=dev(d["state_in"]), out_dtype=torch.float32,
+                              ab=_ab_dev(r, False))
+    torch.cuda.synchronize()
+    g, beta = orc.gates(r["a"], r["b"], r["A_log"], r["dt_bias"])
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], g, beta, d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_F32, "chunk_ab fp32 out")
+    check(host(fs), s_ref, TOL_F32, "chunk_ab fp32 state")
+
+
+@pytest.mark.parametrize("lengths", [[200], [100, 37, 64, 1, 250, 128]], ids=["one_seq", "six_seqs"])
+def test_prefill_ab_bf16(orc, lengths):
+    """The whole prefill with derived gates (six sequences: the norm in the spine's epilogue)."""
+    d = gi.gen_prefill(1200 + sum(lengths), lengths, bf16=True, conv_state=True)
+    r = gi.gen_gate_projections(1300 + sum(lengths), int(sum(lengths)))
+    x = dev(d["x"], True)
+    N = len(lengths)
+    cs_out = torch.empty((N, 3, x.shape[1]), dtype=x.dtype, device=x.device)
+    out, fs = gdn.prefill(x, dev(d["conv_w"]), dev_i32(d["cu"]), None, None, dev(d["z"], True),
+                          dev(d["norm_w"]), cu_host=d["cu"], conv_state_in=dev(d["conv_state_in"], True),
+                          conv_state_out=cs_out, initial_state=dev(d["state_in"]), out_dtype=torch.bfloat16,
+                          ab=_ab_dev(r, True))
+    torch.cuda.synchronize()
+    g, beta = orc.gates(r["a"], r["b"], r["A_log"], r["dt_bias"])
+    out_ref, _, s_ref, cso_ref, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], g, beta, d["z"], d["norm_w"],
+                                                Hk=HK, Hv=HV, dk=D, dv=D, conv_state_in=d["conv_state_in"],
+                                                state_in=d["state_in"], round_y_bf16=True)
+    check(host(out), out_ref, TOL_BF16, f"prefill_ab out {lengths}", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, f"prefill_ab state {lengths}")
+    assert np.array_equal(host(cs_out), cso_ref)
+
+
+# ---------------------------------------------------------------------------
 # composition and negative controls
 # ---------------------------------------------------------------------------
 
