@@ -193,6 +193,35 @@ class Oracle:
                                         _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(st), _ptr(out))
         return out, cs, st
 
+    # -- speculative verify transaction --------------------------------------
+    def verify(self, x, conv_w, conv_state, g, beta, z, norm_w, state, *, Hk: int, Hv: int,
+               dk: int, dv: int, **kw):
+        """The verify half of a speculative transaction (the TDD ledger's transaction rules:
+        the K verified rows are computed from the prior logical state, which only a commit
+        may change).  x [B,K,Cc]; g, beta [B,K,Hv] (g [B,K,Hv,dk] per channel); z [B,K,Hv,dv].
+        Row t of each sequence is decode step t from (conv_state, state); the inputs are left
+        unchanged.  Returns (out [B,K,Hv,dv], snaps) with snaps[c] = (conv state, state)
+        after the first c rows of every sequence, c = 0..K."""
+        K = np.asarray(x).shape[1]
+        cs, st = _f64(conv_state).copy(), _f64(state).copy()
+        snaps = [(cs, st)]
+        outs = []
+        for t in range(K):
+            o, cs, st = self.decode_step(np.asarray(x)[:, t], conv_w, cs, np.asarray(g)[:, t],
+                                         np.asarray(beta)[:, t], np.asarray(z)[:, t], norm_w, st,
+                                         Hk=Hk, Hv=Hv, dk=dk, dv=dv, **kw)
+            outs.append(o)
+            snaps.append((cs, st))
+        return np.stack(outs, axis=1), snaps
+
+    @staticmethod
+    def commit(snaps, accepted) -> Tuple[np.ndarray, np.ndarray]:
+        """The commit half: sequence b keeps the states after its first accepted[b] rows
+        (0 = abort: the prior states).  Returns (conv state, state)."""
+        cs = np.stack([snaps[int(c)][0][b] for b, c in enumerate(accepted)])
+        st = np.stack([snaps[int(c)][1][b] for b, c in enumerate(accepted)])
+        return cs, st
+
     # -- composition of the whole prefill path ------------------------------
     def prefill(self, x, conv_w, cu, g, beta, z, norm_w, *, Hk: int, Hv: int, dk: int, dv: int,
                 conv_state_in=None, state_in=None, act: int = 1, l2_eps: float = 1e-6,

@@ -441,6 +441,42 @@ def pin_decode_equals_prefill(orc):
     assert np.array_equal(c_state, csT), "decode conv state == prefill conv state"
 
 
+def pin_verify_transaction_equals_prefill(orc):
+    """A verify of K rows per sequence and a commit of c of them reproduce the prefill path
+    over each sequence's first c tokens (outputs for every verified row, and both states),
+    with c = 0 (abort: the prior states bit for bit), a middle prefix and all K rows; the
+    verify leaves its inputs unchanged."""
+    rng = np.random.default_rng(43)
+    Hk, Hv, d, B, K = 2, 6, 8, 3, 4
+    C = 2 * Hk * d + Hv * d
+    x = rng.standard_normal((B, K, C))
+    w = 0.5 * rng.standard_normal((C, 4))
+    cs = rng.standard_normal((B, 3, C))
+    g = -np.logaddexp(0.0, -rng.standard_normal((B, K, Hv)))
+    beta = 1 / (1 + np.exp(-rng.standard_normal((B, K, Hv))))
+    z = rng.standard_normal((B, K, Hv, d))
+    nw = 1 + 0.1 * rng.standard_normal(d)
+    S0 = 0.1 * rng.standard_normal((B, Hv, d, d))
+    cs_keep, S0_keep = cs.copy(), S0.copy()
+    out, snaps = orc.verify(x, w, cs, g, beta, z, nw, S0, Hk=Hk, Hv=Hv, dk=d, dv=d)
+    assert np.array_equal(cs, cs_keep) and np.array_equal(S0, S0_keep), "verify must not touch its inputs"
+    accepted = [0, 2, K]
+    cs_c, st_c = orc.commit(snaps, accepted)
+    for b, c in enumerate(accepted):
+        ref_out, _, ref_s, ref_cs, _ = orc.prefill(x[b], w, [0, K], g[b], beta[b], z[b], nw, Hk=Hk, Hv=Hv,
+                                                   dk=d, dv=d, conv_state_in=cs[b:b + 1], state_in=S0[b:b + 1])
+        _close(out[b], ref_out, 1e-13, f"verified rows of sequence {b}")
+        if c == 0:
+            assert np.array_equal(st_c[b], S0[b]) and np.array_equal(cs_c[b], cs[b]), "abort keeps the prior states"
+            continue
+        _, _, pre_s, pre_cs, _ = orc.prefill(x[b, :c], w, [0, c], g[b, :c], beta[b, :c], z[b, :c], nw, Hk=Hk,
+                                             Hv=Hv, dk=d, dv=d, conv_state_in=cs[b:b + 1], state_in=S0[b:b + 1])
+        _close(st_c[b], pre_s[0], 1e-13, f"committed state, {c} rows")
+        assert np.array_equal(cs_c[b], pre_cs[0]), f"committed conv state, {c} rows"
+        if c == K:
+            _close(st_c[b], ref_s[0], 1e-13, "commit of every row == prefill final state")
+
+
 # ---------------------------------------------------------------------------
 # geometry the golden PR prints
 # ---------------------------------------------------------------------------

@@ -108,3 +108,42 @@ def test_mutant_fails_a_pin(source, tmp_path, name, old, new):
     oracle.compile_oracle(str(src), lib)
     failed = _run_pins(oracle.Oracle(oracle.load(lib)))
     assert failed, f"planted mistake '{name}' passed every pin"
+
+
+# The verify / commit transaction of the oracle is Python composing the C decode step; its
+# plausible slips are planted in subclasses and must fail the transaction pin.
+class _CommitOffByOne(oracle.Oracle):
+    @staticmethod
+    def commit(snaps, accepted):
+        return oracle.Oracle.commit(snaps, [min(int(c) + 1, len(snaps) - 1) for c in accepted])
+
+
+class _CommitKeepsLast(oracle.Oracle):
+    @staticmethod
+    def commit(snaps, accepted):
+        return oracle.Oracle.commit(snaps, [len(snaps) - 1 for _ in accepted])
+
+
+class _VerifyInPlace(oracle.Oracle):
+    def verify(self, x, conv_w, conv_state, g, beta, z, norm_w, state, **kw):
+        out, snaps = super().verify(x, conv_w, conv_state, g, beta, z, norm_w, state, **kw)
+        conv_state[...] = snaps[-1][0]
+        state[...] = snaps[-1][1]
+        return out, snaps
+
+
+class _VerifyRowsFromPriorState(oracle.Oracle):
+    """Every verified row decoded from the prior state (no chaining inside the window)."""
+    def verify(self, x, conv_w, conv_state, g, beta, z, norm_w, state, *, Hk, Hv, dk, dv, **kw):
+        outs = [self.decode_step(x[:, t], conv_w, conv_state, g[:, t], beta[:, t], z[:, t], norm_w, state,
+                                 Hk=Hk, Hv=Hv, dk=dk, dv=dv, **kw) for t in range(x.shape[1])]
+        snaps = [(conv_state.copy(), state.copy())] + [(o[1], o[2]) for o in outs]
+        return __import__("numpy").stack([o[0] for o in outs], axis=1), snaps
+
+
+@pytest.mark.parametrize("mutant", [_CommitOffByOne, _CommitKeepsLast, _VerifyInPlace, _VerifyRowsFromPriorState],
+                         ids=lambda m: m.__name__.strip("_"))
+def test_transaction_mutant_fails_the_pin(mutant):
+    from oracle_pins import pin_verify_transaction_equals_prefill
+    with pytest.raises(AssertionError):
+        pin_verify_transaction_equals_prefill(mutant())
