@@ -16,6 +16,7 @@ Also measured in the same run (``workloads``):
   kda_h64_s16384_bf16 per-key-channel decay, 64 heads, 16384 tokens, the chunk call alone
   kda_decode_b64_h64_bf16  the per-key-channel decode step, 64 sequences x 64 heads
   decode_b64_ab_bf16  the decode step with g, beta derived from the a / b projections
+  verify_k4_b64_bf16  a speculative transaction: verify 4 rows x 64 sequences, commit all 4
 each in tokens/s (state-updates/s for the decode) with its roofline fraction (algorithmic HBM
 bytes / time / 8 TB/s).
 
@@ -149,6 +150,39 @@ def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False
     ms, per = time_calls(step, n_sets, steps, warmup)
     return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3),
                 roofline=roofline(bytes_per * batch, ms, traffic))
+
+
+def bench_verify(steps, warmup, batch=64, K=4):
+    """One speculative transaction per step: gdn_verify of K rows for every sequence, then
+    gdn_verify_commit accepting all K (the commit's largest write)."""
+    steps_in = [gi.gen_decode(2400 + t, batch) for t in range(K)]
+    d = steps_in[0]
+    cfg = gdn.config()
+    x = t_dev(np.stack([st["x"] for st in steps_in], 1), True)
+    g = t_dev(np.stack([st["g"] for st in steps_in], 1))
+    beta = t_dev(np.stack([st["beta"] for st in steps_in], 1))
+    z = t_dev(np.stack([st["z"] for st in steps_in], 1), True)
+    w, nw = t_dev(d["conv_w"]), t_dev(d["norm_w"])
+    n_sets = 3
+    states = [t_dev(d["state"]) for _ in range(n_sets)]
+    convs = [t_dev(d["conv_state"], True) for _ in range(n_sets)]
+    out = torch.empty((batch, K, HV, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.verify_workspace_size(batch, K, cfg), dtype=torch.uint8, device="cuda")
+    accepted = torch.full((batch,), K, dtype=torch.int32, device="cuda")
+
+    def step(i):
+        gdn.verify(x, w, convs[i], g, beta, z, nw, states[i], out=out, workspace=ws, cfg=cfg)
+        gdn.verify_commit(accepted, x, g, convs[i], states[i], ws, cfg=cfg)
+
+    ms, per = time_calls(step, n_sets, steps, warmup)
+    rec = K * (HV * D + HK * D) * 4
+    # per sequence: state read by the verify, read + written by the commit; conv state read
+    # by each and written by the commit; x, z, g, beta and out of the K rows; the records
+    # written and read back
+    per_seq = (3 * STATE_BYTES + 3 * 3 * CC * 2 + K * (2 * CC * 2 + HV * D * 2 + 3 * HV * 4 + HV * D * 2)
+               + 2 * rec)
+    return dict(ms=ms, rows_per_s=batch * K / (ms * 1e-3), roofline=roofline(per_seq * batch, ms, None),
+                bytes_per_transaction=per_seq * batch)
 
 
 def cpu_baseline_decode(target_s=10.0):
@@ -304,7 +338,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode", "decode_ab"])
+                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode", "decode_ab", "verify"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
@@ -361,6 +395,12 @@ def main():
             roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
+    if wl in ("all", "verify"):
+        ver = bench_verify(max(20, args.steps // 4), max(5, args.warmup // 4))
+        workloads["verify_k4_b64_bf16"] = dict(
+            metric="state-updates/s", value=ver["rows_per_s"], ms=ver["ms"], roofline=ver["roofline"],
+            bytes_per_transaction=ver["bytes_per_transaction"],
+            call="gdn_verify (64 sequences x 4 rows) + gdn_verify_commit accepting all 4; one update = one row")
     if wl in ("all", "decode_ab"):
         dab = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), derived_gates=True)
         workloads["decode_b64_ab_bf16"] = dict(

@@ -28,7 +28,8 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_conv1d_prefill",
            "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
            "gdn_chunk_prefill_ab", "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill",
-           "gdn_prefill_ab", "gdn_decode_step", "gdn_decode_step_ab")
+           "gdn_prefill_ab", "gdn_decode_step", "gdn_decode_step_ab", "gdn_verify_workspace_size",
+           "gdn_verify", "gdn_verify_commit")
 
 
 class GDNError(RuntimeError):
@@ -84,6 +85,10 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                   vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "gdn_prefill_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_verify_workspace_size": ([cfgp, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
+        "gdn_verify": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp],
+                       ctypes.c_int),
+        "gdn_verify_commit": ([cfgp, ctypes.c_int, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp], ctypes.c_int),
         "gdn_decode_step_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32,
                                 vp], ctypes.c_int),
     }
@@ -319,6 +324,50 @@ def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
         ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), *gates,
         _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, _stream()))
     return out
+
+
+def verify_workspace_size(B: int, K: int, cfg: Optional[GDNConfig] = None) -> int:
+    cfg = cfg or config()
+    out = ctypes.c_size_t(0)
+    _check("gdn_verify_workspace_size",
+           load_library().gdn_verify_workspace_size(ctypes.byref(cfg), B, K, ctypes.byref(out)))
+    return out.value
+
+
+def verify(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: torch.Tensor,
+           beta: torch.Tensor, z: torch.Tensor, norm_w: torch.Tensor, state: torch.Tensor, *,
+           out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+           workspace: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+    """Verify half of a speculative transaction: x [B, K, Cc], g / beta [B, K, Hv] (g
+    [B, K, Hv, dk] per channel), z [B, K, Hv, dv].  conv_state and state are only read.
+    Returns (out [B, K, Hv, dv], workspace); pass the workspace to verify_commit."""
+    cfg = cfg or config()
+    B, K = x.shape[0], x.shape[1]
+    if out is None:
+        out = torch.empty((B, K, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype, device=x.device)
+    for t in (x, conv_state, g, beta, z, state, out):
+        if not t.is_contiguous():
+            raise ValueError("verify tensors must be contiguous")
+    if workspace is None:
+        workspace = torch.empty(verify_workspace_size(B, K, cfg), dtype=torch.uint8, device=x.device)
+    _check("gdn_verify", load_library().gdn_verify(
+        ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), _ptr(g), _ptr(beta),
+        _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, K, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream()))
+    return out, workspace
+
+
+def verify_commit(accepted: torch.Tensor, x: torch.Tensor, g: torch.Tensor, conv_state: torch.Tensor,
+                  state: torch.Tensor, workspace: torch.Tensor, *, cfg: Optional[GDNConfig] = None) -> None:
+    """Commit half: sequence b advances conv_state and state (in place) by its first
+    clamp(accepted[b], 0, K) verified rows; accepted is an int32 device tensor [B]."""
+    cfg = cfg or config()
+    B, K = x.shape[0], x.shape[1]
+    if accepted.dtype != torch.int32 or accepted.numel() != B:
+        raise ValueError("accepted must be an int32 tensor of one entry per sequence")
+    _check("gdn_verify_commit", load_library().gdn_verify_commit(
+        ctypes.byref(cfg), _dtype(x), _ptr(accepted), _ptr(x), _ptr(g), _ptr(conv_state), _ptr(state), B, K,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
 
 
 def default_q_scale(cfg: GDNConfig) -> float:

@@ -395,4 +395,57 @@ gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_
                              z, norm_w, state, out, B, stream);
 }
 
+gdn_status_t gdn_verify_workspace_size(const gdn_config_t* cfg, int32_t B, int32_t K, size_t* bytes) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!bytes || B < 0 || K < 1 || K > GDN_MAX_VERIFY_ROWS) return GDN_ERR_INVALID_ARG;
+  *bytes = gdn::verify_workspace_bytes(d, B, K);
+  return GDN_OK;
+}
+
+gdn_status_t gdn_verify(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                        const void* x, const float* conv_w, const void* conv_state, const float* g,
+                        const float* beta, const void* z, const float* norm_w, const float* state,
+                        void* out, int32_t B, int32_t K, void* ws, size_t ws_bytes,
+                        gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
+  if (B < 0 || (int64_t)B * d.hv > INT32_MAX || K < 1 || K > GDN_MAX_VERIFY_ROWS) return GDN_ERR_INVALID_ARG;
+  if (B == 0) return GDN_OK;
+  if (!x || !conv_w || !conv_state || !g || !beta || !z || !norm_w || !state || !out) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(conv_w) || !aligned16(state) || (d.per_channel && !aligned16(g))) return GDN_ERR_INVALID_ARG;
+  const size_t need = gdn::verify_workspace_bytes(d, B, K);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return GDN_ERR_WORKSPACE;
+  const size_t state_bytes = (size_t)B * d.hv * d.dv * d.dk * sizeof(float);
+  const size_t out_bytes = (size_t)B * K * d.hv * d.dv * dsize(out_dtype);
+  if (overlaps(out, out_bytes, state, state_bytes) || overlaps(out, out_bytes, ws, need) ||
+      overlaps(ws, need, state, state_bytes))
+    return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_verify(d, dtype == GDN_BF16, out_dtype == GDN_BF16, x, conv_w, conv_state, g,
+                                       beta, z, norm_w, state, out, B, K, ws, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status_t gdn_verify_commit(const gdn_config_t* cfg, gdn_dtype_t dtype, const int32_t* accepted,
+                               const void* x, const float* g, void* conv_state, float* state,
+                               int32_t B, int32_t K, const void* ws, size_t ws_bytes,
+                               gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (!valid_dtype(dtype)) return GDN_ERR_UNSUPPORTED;
+  if (B < 0 || B > 65535 || K < 1 || K > GDN_MAX_VERIFY_ROWS) return GDN_ERR_INVALID_ARG;
+  if (B == 0) return GDN_OK;
+  if (!accepted || !x || !g || !conv_state || !state) return GDN_ERR_INVALID_ARG;
+  if (!aligned16(state) || (d.per_channel && !aligned16(g))) return GDN_ERR_INVALID_ARG;
+  const size_t need = gdn::verify_workspace_bytes(d, B, K);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return GDN_ERR_WORKSPACE;
+  const size_t state_bytes = (size_t)B * d.hv * d.dv * d.dk * sizeof(float);
+  if (overlaps(ws, need, state, state_bytes)) return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_verify_commit(d, dtype == GDN_BF16, accepted, x, g, conv_state, state, B, K, ws,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -41,21 +41,6 @@ constexpr int kD = 128;                 // head_k_dim == head_v_dim
 constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
 constexpr int kWindow = 8;              // state rows in flight per thread
 
-// Sum over the 32 lanes holding one state row (aligned halves of the wave):
-// quad_perm swaps for lane distance 1 and 2, the half-row and row mirrors for
-// 4 and 8, and a swizzle exchanging lane i with i ^ 16 for the last step.
-template <int kCtrl>
-__device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
-}
-__device__ __forceinline__ float row32_sum(float v) {
-  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_add<0x141>(v);   // row_half_mirror
-  v = dpp_add<0x140>(v);   // row_mirror
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
-}
-
 // Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); the
 // channel's state rows become (s1, s2, x).
 template <typename T>

@@ -110,6 +110,21 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Sum over the 32 lanes holding one state row (aligned halves of the wave):
+// quad_perm swaps for lane distance 1 and 2, the half-row and row mirrors for
+// 4 and 8, and a swizzle exchanging lane i with i ^ 16 for the last step.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row32_sum(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);   // row_half_mirror
+  v = dpp_add<0x140>(v);   // row_mirror
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+
 // Gates of one token and value head from the a / b projections (the prepare
 // stage's gate derivation, as read from the golden PR and the TDD ledger's
 // alpha/beta transforms): g = -exp(A_log) softplus(a + dt_bias), beta =

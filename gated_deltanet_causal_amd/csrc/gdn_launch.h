@@ -44,6 +44,18 @@ hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const voi
                               const void* z, const float* norm_w, float* state, void* out, int b,
                               hipStream_t s);
 
+// Speculative verify transaction (gdn_verify.hip).  The workspace holds the
+// per-row update vectors the commit replays: u [b][k][hv][dv] then the
+// normalised keys [b][k][hk][dk], fp32.
+size_t verify_workspace_bytes(const Dims& d, int b, int k);
+hipError_t launch_verify(const Dims& d, bool bf16, bool out_bf16, const void* x, const float* conv_w,
+                         const void* conv_state, const float* g, const float* beta, const void* z,
+                         const float* norm_w, const float* state, void* out, int b, int k, void* ws,
+                         hipStream_t s);
+hipError_t launch_verify_commit(const Dims& d, bool bf16, const int32_t* accepted, const void* x,
+                                const float* g, void* conv_state, float* state, int b, int k,
+                                const void* ws, hipStream_t s);
+
 // Chunk prefill.  Workspace layout is private to gdn_chunk.hip.
 size_t chunk_workspace_bytes(const Dims& d, int n, int t);
 // Whether the chunk prefill for n sequences can apply the gated norm to its

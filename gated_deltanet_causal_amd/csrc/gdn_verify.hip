@@ -1,0 +1,333 @@
+// gdn_verify.hip -- the speculative verify transaction: K rows per sequence
+// decoded from the prior logical state, which only the commit changes.
+//
+// Follows the Qwen3.8 kernel TDD ledger's transaction rules (the verified
+// rows are computed from the prior state; a commit publishes the state after
+// the accepted prefix; abort, error or an unresolved drop leaves the prior
+// state; rejected rows must never be read) and the Qwen3SsmLayer field notes
+// on the WY verify kernels (one kernel for all K rows of a window, the h-state
+// read once, with either per-token rollback snapshots or a write-on-accept
+// twin whose post-verdict fold applies only the accepted rows).  This is the
+// write-on-accept form:
+//
+//   verify  per (sequence, value head) workgroup, the head's state is read
+//           once into registers and carried through the K rows; row
+//           t is exactly the fused decode step (conv from register windows,
+//           L2 / q scale, decay, predict, write, output, gated norm).  Besides
+//           the outputs it records, per row, the update's two vectors: u
+//           ([Hv][dv]) and the normalised key ([Hk][dk]).  The state and the
+//           conv state in memory are not written.
+//   commit  per (sequence, value head): with c = accepted rows, the state is
+//           read, the c rank-one updates S <- S diag(a_t) + u_t khat_t^T are
+//           replayed in the verify's own operation order (so the result is the
+//           state the verify carried after row c, bit for bit) and written;
+//           c = 0 touches nothing.  The conv state takes the last three inputs
+//           of (its rows, x rows 0 .. c-1).
+//
+// HBM per transaction: the state is read twice and written once (2R + 1W),
+// against 1R + KW for per-row snapshots plus a copy at commit.
+#include "gdn_device.h"
+#include "gdn_launch.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kGroup = 256;             // threads per value head
+constexpr int kD = 128;                 // head_k_dim == head_v_dim
+constexpr int kRows = 16;               // state rows per thread: rows rg + 8 m
+
+// One conv window of a channel, carried in registers across the rows (the
+// taps are read again for each row: they stay in cache and keep registers free).
+struct ConvWindow {
+  float s0, s1, s2;
+  // y = act(w . (s0, s1, s2, x)); the window becomes (s1, s2, x).  Same
+  // arithmetic as the decode step's conv.
+  __device__ float step(const float* conv_w, int c, float xv, int act) {
+    const f32x4_t w = *reinterpret_cast<const f32x4_t*>(conv_w + (int64_t)c * 4);
+    float y = w[0] * s0;
+    y = fmaf(w[1], s1, y);
+    y = fmaf(w[2], s2, y);
+    y = fmaf(w[3], xv, y);
+    s0 = s1;
+    s1 = s2;
+    s2 = xv;
+    return act ? y * sigmoidf_(y) : y;
+  }
+};
+
+template <typename T>
+__device__ __forceinline__ ConvWindow load_window(const T* cs_row, int c, int cc) {
+  ConvWindow cw;
+  cw.s0 = ld(cs_row + c);
+  cw.s1 = ld(cs_row + cc + c);
+  cw.s2 = ld(cs_row + 2 * cc + c);
+  return cw;
+}
+
+template <typename T, typename To, bool kPerChannel>
+__global__ __launch_bounds__(kGroup) void verify_kernel(
+    const T* __restrict__ x, const float* __restrict__ conv_w, const T* __restrict__ conv_state,
+    const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
+    const float* __restrict__ norm_w, const float* __restrict__ state, To* __restrict__ out,
+    float* __restrict__ rec_u, float* __restrict__ rec_k, int K, int hk, int hv, int cc, int act,
+    float l2_eps, float q_scale, float rms_eps) {
+  const int b = blockIdx.x / hv;
+  const int h = blockIdx.x % hv;
+  const int kh = h / (hv / hk);           // the key head it reads (repeat-interleave)
+  const int tid = threadIdx.x;
+  const int gt = tid;
+  const int gwave = gt / kWave;
+  const int lane = tid % kWave;
+  const int cg = gt % 32;                 // column group: columns 4cg .. 4cg+3
+  const int rg = gt / 32;                 // row group: rows rg + 8m
+
+  __shared__ float s_q[kD], s_k[kD], s_scal[2];
+  __shared__ float s_v[kD], s_o[kD], s_nrm[2];
+
+  // the head's state, read once and carried through the K rows
+  const float* S = state + ((int64_t)b * hv + h) * kD * kD;
+  f32x4_t sreg[kRows];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m)
+    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+
+  // conv windows: thread i owns q channel i (i < kD) or k channel i - kD of the
+  // key head, and threads below kD also v channel i of the value head.  The
+  // conv state is only read, so the value heads of a key head each redo the
+  // key head's q / k conv (a workgroup per value head).
+  const T* cs_row = conv_state + (int64_t)b * 3 * cc;
+  const int c_qk = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
+  const int c_v = 2 * hk * kD + h * kD + gt;
+  ConvWindow wqk = {}, wv = {};
+  if (tid < 2 * kD) wqk = load_window(cs_row, c_qk, cc);
+  if (gt < kD) wv = load_window(cs_row, c_v, cc);
+
+  // a row's global inputs, fetched one row ahead so their latency overlaps the
+  // previous row's work
+  float xqk_n = 0.0f, xv_n = 0.0f, z_n = 0.0f, bt_n = 0.0f;
+  f32x4_t g_n = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto fetch = [&](int t) {
+    const int64_t row_t = (int64_t)b * K + t;
+    const T* x_row = x + row_t * cc;
+    if (tid < 2 * kD) xqk_n = ld(x_row + c_qk);
+    if (gt < kD) {
+      xv_n = ld(x_row + c_v);
+      z_n = ld(z + (row_t * hv + h) * kD + gt);
+    }
+    if constexpr (kPerChannel) g_n = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 4 * cg);
+    else g_n[0] = g[row_t * hv + h];
+    bt_n = beta[row_t * hv + h];
+  };
+  fetch(0);
+
+  for (int t = 0; t < K; ++t) {
+    const int64_t row_t = (int64_t)b * K + t;   // (sequence, verified row)
+    const float xqk = xqk_n, xv = xv_n, zv = z_n, bt = bt_n;
+    const f32x4_t gv = g_n;
+    if (t + 1 < K) fetch(t + 1);
+    if (tid < 2 * kD) {
+      const float y = wqk.step(conv_w, c_qk, xqk, act);
+      if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
+    }
+    if (gt < kD) s_v[gt] = wv.step(conv_w, c_v, xv, act);
+    __syncthreads();
+    if (tid < 2 * kWave) {
+      const int w = tid / kWave;
+      const float* src = w == 0 ? s_q : s_k;
+      const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
+      const float ss = wave_sum(a0 * a0 + a1 * a1);
+      if (lane == 0) s_scal[w] = 1.0f / sqrtf(ss + l2_eps);
+    }
+    __syncthreads();
+    const float rq = s_scal[0] * q_scale, rk = s_scal[1];
+    const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
+    float kcol[4], qcol[4], a[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e] * rk; qcol[e] = s_q[4 * cg + e] * rq; }
+    if constexpr (kPerChannel) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+    } else {
+      const float av = __expf(gv[0]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = av;
+    }
+    // the normalised key of this row, for the commit's replay
+    if (h % (hv / hk) == 0 && gt < kD) rec_k[(row_t * hk + kh) * kD + gt] = s_k[gt] * rk;
+
+    // per state row: decay, the two dot products, u = beta (v - p),
+    // o = r + u (khat . qtil), S' = Sd + u khat^T (as the decode step)
+    float* u_out = rec_u + (row_t * hv + h) * kD;
+#pragma unroll
+    for (int m = 0; m < kRows; ++m) {
+      const int row = rg + 8 * m;
+      float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sreg[m][e] *= a[e];
+        pk = fmaf(sreg[m][e], kcol[e], pk);
+        pq = fmaf(sreg[m][e], qcol[e], pq);
+      }
+      pk = row32_sum(pk);
+      pq = row32_sum(pq);
+      const float u = bt * (s_v[row] - pk);
+      if (cg == 0) {
+        s_o[row] = fmaf(u, kq, pq);
+        u_out[row] = u;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+    }
+    __syncthreads();
+
+    // the sigmoid gated RMSNorm of the row's 128 outputs per value head
+    if (gt < kD) {
+      const float o = s_o[gt];
+      const float ss = wave_sum(o * o);
+      if (lane == 0) s_nrm[gwave] = ss;
+    }
+    __syncthreads();
+    if (gt < kD) {
+      const float o = s_o[gt];
+      const float r = rsqrtf((s_nrm[0] + s_nrm[1]) * (1.0f / kD) + rms_eps);
+      st(out + (row_t * hv + h) * kD + gt, o * r * norm_w[gt] * sigmoidf_(zv));
+    }
+  }
+}
+
+// Commit of the recurrent state: sequence b keeps its first clamp(accepted[b],
+// 0, K) verified rows.  One workgroup per (sequence, value head).
+template <bool kPerChannel>
+__global__ __launch_bounds__(kGroup) void verify_commit_state_kernel(
+    const int32_t* __restrict__ accepted, const float* __restrict__ g, const float* __restrict__ rec_u,
+    const float* __restrict__ rec_k, float* __restrict__ state, int K, int hk, int hv) {
+  const int b = blockIdx.x / hv;
+  const int h = blockIdx.x % hv;
+  const int kh = h / (hv / hk);
+  const int c = min(max(accepted[b], 0), K);
+  if (c == 0) return;   // abort: the prior state stays
+  const int gt = threadIdx.x;
+  const int cg = gt % 32, rg = gt / 32;
+  float* S = state + ((int64_t)b * hv + h) * kD * kD;
+  f32x4_t sreg[kRows];
+#pragma unroll
+  for (int m = 0; m < kRows; ++m)
+    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  for (int t = 0; t < c; ++t) {
+    const int64_t row_t = (int64_t)b * K + t;
+    float a[4];
+    if constexpr (kPerChannel) {
+      const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 4 * cg);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+    } else {
+      const float av = __expf(g[row_t * hv + h]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[e] = av;
+    }
+    const f32x4_t kcol = *reinterpret_cast<const f32x4_t*>(rec_k + (row_t * hk + kh) * kD + 4 * cg);
+    const float* u_in = rec_u + (row_t * hv + h) * kD;
+#pragma unroll
+    for (int m = 0; m < kRows; ++m) {
+      const float u = u_in[rg + 8 * m];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sreg[m][e] *= a[e];
+        sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kRows; ++m)
+    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+}
+
+// Commit of the conv state: the last three inputs of (the state's rows, x rows
+// 0 .. c-1).  One thread per (sequence, channel).
+template <typename T>
+__global__ __launch_bounds__(kGroup) void verify_commit_conv_kernel(const int32_t* __restrict__ accepted,
+                                                                    const T* __restrict__ x,
+                                                                    T* __restrict__ conv_state, int K,
+                                                                    int cc) {
+  const int b = blockIdx.y;
+  const int ch = blockIdx.x * kGroup + threadIdx.x;
+  if (ch >= cc) return;
+  const int c = min(max(accepted[b], 0), K);
+  if (c == 0) return;
+  T* cs = conv_state + (int64_t)b * 3 * cc + ch;
+  float win[3] = {ld(cs), ld(cs + cc), ld(cs + 2 * cc)};
+  for (int t = 0; t < c; ++t) {
+    win[0] = win[1];
+    win[1] = win[2];
+    win[2] = ld(x + ((int64_t)b * K + t) * cc + ch);
+  }
+  st(cs, win[0]);
+  st(cs + cc, win[1]);
+  st(cs + 2 * cc, win[2]);
+}
+
+template <typename T, typename To, bool kPC>
+hipError_t verify_launch(const Dims& d, const void* x, const float* conv_w, const void* conv_state,
+                         const float* g, const float* beta, const void* z, const float* norm_w,
+                         const float* state, void* out, float* rec_u, float* rec_k, int b, int k,
+                         hipStream_t s) {
+  hipLaunchKernelGGL((verify_kernel<T, To, kPC>), dim3(b * d.hv), dim3(kGroup), 0, s, static_cast<const T*>(x),
+                     conv_w, static_cast<const T*>(conv_state), g, beta, static_cast<const T*>(z), norm_w, state,
+                     static_cast<To*>(out), rec_u, rec_k, k, d.hk, d.hv, d.cc, d.act, d.l2_eps, d.q_scale,
+                     d.rms_eps);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t verify_workspace_bytes(const Dims& d, int b, int k) {
+  return (size_t)b * k * ((size_t)d.hv * d.dv + (size_t)d.hk * d.dk) * sizeof(float);
+}
+
+hipError_t launch_verify(const Dims& d, bool bf16, bool out_bf16, const void* x, const float* conv_w,
+                         const void* conv_state, const float* g, const float* beta, const void* z,
+                         const float* norm_w, const float* state, void* out, int b, int k, void* ws,
+                         hipStream_t s) {
+  if (b == 0) return hipSuccess;
+  float* rec_u = static_cast<float*>(ws);
+  float* rec_k = rec_u + (size_t)b * k * d.hv * d.dv;
+#define GDN_VERIFY_TYPES(T, To)                                                                         \
+  return d.per_channel                                                                                  \
+             ? verify_launch<T, To, true>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out,    \
+                                          rec_u, rec_k, b, k, s)                                      \
+             : verify_launch<T, To, false>(d, x, conv_w, conv_state, g, beta, z, norm_w, state, out,   \
+                                           rec_u, rec_k, b, k, s)
+  if (bf16) {
+    if (out_bf16) { GDN_VERIFY_TYPES(uint16_t, uint16_t); }
+    GDN_VERIFY_TYPES(uint16_t, float);
+  }
+  if (out_bf16) { GDN_VERIFY_TYPES(float, uint16_t); }
+  GDN_VERIFY_TYPES(float, float);
+#undef GDN_VERIFY_TYPES
+}
+
+hipError_t launch_verify_commit(const Dims& d, bool bf16, const int32_t* accepted, const void* x,
+                                const float* g, void* conv_state, float* state, int b, int k,
+                                const void* ws, hipStream_t s) {
+  if (b == 0) return hipSuccess;
+  const float* rec_u = static_cast<const float*>(ws);
+  const float* rec_k = rec_u + (size_t)b * k * d.hv * d.dv;
+  if (d.per_channel)
+    hipLaunchKernelGGL(verify_commit_state_kernel<true>, dim3(b * d.hv), dim3(kGroup), 0, s, accepted, g, rec_u,
+                       rec_k, state, k, d.hk, d.hv);
+  else
+    hipLaunchKernelGGL(verify_commit_state_kernel<false>, dim3(b * d.hv), dim3(kGroup), 0, s, accepted, g, rec_u,
+                       rec_k, state, k, d.hk, d.hv);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 cgrid((d.cc + kGroup - 1) / kGroup, b);
+  if (bf16)
+    hipLaunchKernelGGL(verify_commit_conv_kernel<uint16_t>, cgrid, dim3(kGroup), 0, s, accepted,
+                       static_cast<const uint16_t*>(x), static_cast<uint16_t*>(conv_state), k, d.cc);
+  else
+    hipLaunchKernelGGL(verify_commit_conv_kernel<float>, cgrid, dim3(kGroup), 0, s, accepted,
+                       static_cast<const float*>(x), static_cast<float*>(conv_state), k, d.cc);
+  return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -270,6 +270,54 @@ gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_
                                 const void* z, const float* norm_w, float* state, void* out,
                                 int32_t B, gdn_stream_t stream);
 
+/*
+ * Speculative verify transaction (the Qwen3.8 TDD ledger's transaction rules:
+ * the verified rows are computed from the prior logical state; a commit
+ * publishes only the state after the accepted rows; abort leaves the prior
+ * state; rejected rows are never read.  The Qwen3SsmLayer field notes give
+ * the WY verify kernels of K = 2..17 rows and their write-on-accept twin with
+ * a post-verdict fold, the form built here).  One transaction is one
+ * gdn_verify followed by exactly one gdn_verify_commit on the same workspace
+ * (accepted = 0 everywhere is the abort).
+ */
+#define GDN_MAX_VERIFY_ROWS 64
+
+/* Bytes of workspace a transaction of B sequences x K rows needs.  Host only. */
+gdn_status_t gdn_verify_workspace_size(const gdn_config_t* cfg, int32_t B, int32_t K, size_t* bytes);
+
+/*
+ * Verify: row t of sequence b gets the output decode step t would produce
+ * after rows 0..t-1 of that sequence, starting from (conv_state, state) --
+ * the same arithmetic as gdn_decode_step, row by row.  conv_state and state
+ * are only read.  The workspace receives what the commit replays.
+ *   dtype, out_dtype   as for gdn_decode_step
+ *   x                  [B][K][Cc] raw projected rows (contiguous)
+ *   conv_state         [B][3][Cc];  state fp32 [B][Hv][dv][dk]
+ *   g                  fp32 [B][K][Hv] (or [B][K][Hv][dk]);  beta fp32 [B][K][Hv]
+ *   z                  [B][K][Hv][dv];  norm_w fp32 [dv]
+ *   out                [B][K][Hv][dv]
+ *   K                  1 .. GDN_MAX_VERIFY_ROWS
+ */
+gdn_status_t gdn_verify(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                        const void* x, const float* conv_w, const void* conv_state, const float* g,
+                        const float* beta, const void* z, const float* norm_w, const float* state,
+                        void* out, int32_t B, int32_t K, void* ws, size_t ws_bytes,
+                        gdn_stream_t stream);
+
+/*
+ * Commit: sequence b advances by its first c = clamp(accepted[b], 0, K) rows,
+ * exactly as c decode steps would leave conv_state and state (the recurrent
+ * state is the verify's own value after row c, bit for bit); c = 0 leaves
+ * both untouched.  Reads x and g rows 0..c-1 of each sequence only.
+ *   accepted   DEVICE int32 [B]
+ *   x, g       the verify's (unchanged since)
+ *   conv_state, state   updated in place
+ */
+gdn_status_t gdn_verify_commit(const gdn_config_t* cfg, gdn_dtype_t dtype, const int32_t* accepted,
+                               const void* x, const float* g, void* conv_state, float* state,
+                               int32_t B, int32_t K, const void* ws, size_t ws_bytes,
+                               gdn_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -236,3 +236,25 @@ def test_derived_gate_calls_argument_checks(lib):
     assert chunk(pc) == gdn.GDN_ERR_UNSUPPORTED
     assert chunk(cfg, dt_bias=None) == gdn.GDN_ERR_INVALID_ARG
     assert chunk(cfg) == gdn.GDN_ERR_WORKSPACE          # gates accepted; the workspace is checked next
+
+
+def test_verify_argument_checks(lib):
+    cfg = _cfg()
+    size = ctypes.c_size_t()
+    assert lib.gdn_verify_workspace_size(ctypes.byref(cfg), 64, 4, ctypes.byref(size)) == 0
+    assert size.value == 64 * 4 * (48 * 128 + 16 * 128) * 4
+    assert lib.gdn_verify_workspace_size(ctypes.byref(cfg), 64, 0, ctypes.byref(size)) == gdn.GDN_ERR_INVALID_ARG
+    assert lib.gdn_verify_workspace_size(ctypes.byref(cfg), 64, 65, ctypes.byref(size)) == gdn.GDN_ERR_INVALID_ARG
+
+    def verify(K=4, ws=ctypes.c_void_p(0x8000000), wsb=size.value, state=ctypes.c_void_p(0x4000000)):
+        return lib.gdn_verify(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, state, ctypes.c_void_p(0x2000000), 64, K, ws, wsb, None)
+    assert verify(K=0) == gdn.GDN_ERR_INVALID_ARG
+    assert verify(wsb=size.value - 1) == gdn.GDN_ERR_WORKSPACE
+    assert verify(state=None) == gdn.GDN_ERR_INVALID_ARG
+    assert verify(state=ctypes.c_void_p(0x8000000)) == gdn.GDN_ERR_INVALID_ARG   # state overlaps the workspace
+    got = lib.gdn_verify_commit(ctypes.byref(cfg), gdn.GDN_BF16, None, FAKE, FAKE, FAKE, FAKE, 64, 4,
+                                ctypes.c_void_p(0x8000000), size.value, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                         # accepted missing
+    assert lib.gdn_verify(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, None, None, None, None, None, None, None,
+                          None, None, 0, 4, None, 0, None) == 0                   # nothing to do

@@ -505,6 +505,98 @@ def test_prefill_ab_bf16(orc, lengths):
 
 
 # ---------------------------------------------------------------------------
+# speculative verify transaction (gdn_verify / gdn_verify_commit)
+# ---------------------------------------------------------------------------
+
+def _verify_inputs(seed, B, K, geo=gi.Geometry(), bf16=True, per_channel=False):
+    """K decode-step inputs per sequence, stacked as [B, K, ...]."""
+    steps = [gi.gen_decode(seed + t, B, geo, bf16=bf16, per_channel=per_channel) for t in range(K)]
+    d = dict(steps[0])
+    for key in ("x", "g", "beta", "z"):
+        d[key] = np.stack([st[key] for st in steps], axis=1)
+    return d
+
+
+def _verify_dev(d, bf16):
+    return dict(x=dev(d["x"], bf16), conv_w=dev(d["conv_w"]), cs=dev(d["conv_state"], bf16), g=dev(d["g"]),
+                beta=dev(d["beta"]), z=dev(d["z"], bf16), nw=dev(d["norm_w"]), st=dev(d["state"]))
+
+
+@pytest.mark.parametrize("K", [1, 4], ids=["K1", "K4"])
+def test_verify_commit_equals_decode_steps_bitwise(K):
+    """Verified row t equals decode step t bit for bit, the verify leaves both states as they
+    were, and a commit of c rows leaves exactly the states c decode steps leave (c = 0 .. K,
+    and out-of-range counts clamped)."""
+    B = 8
+    d = _verify_inputs(2100, B, K)
+    t_ = _verify_dev(d, True)
+    cs0, st0 = t_["cs"].clone(), t_["st"].clone()
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(t_["cs"], cs0) and torch.equal(t_["st"], st0), "verify must not write the states"
+    cs_d, st_d = cs0.clone(), st0.clone()
+    snaps = [(cs_d.clone(), st_d.clone())]
+    for t in range(K):
+        o = gdn.decode_step(t_["x"][:, t].contiguous(), t_["conv_w"], cs_d, t_["g"][:, t].contiguous(),
+                            t_["beta"][:, t].contiguous(), t_["z"][:, t].contiguous(), t_["nw"], st_d,
+                            out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(out_v[:, t], o), f"verified row {t} != decode step {t}"
+        snaps.append((cs_d.clone(), st_d.clone()))
+    accepted = [0, 1, K, -3, K + 5, min(2, K), K, 0]
+    gdn.verify_commit(torch.tensor(accepted, dtype=torch.int32, device="cuda"), t_["x"], t_["g"], t_["cs"],
+                      t_["st"], ws)
+    torch.cuda.synchronize()
+    for b, c in enumerate(accepted):
+        c = min(max(c, 0), K)
+        assert torch.equal(t_["st"][b], snaps[c][1][b]), f"sequence {b}: state after commit of {c}"
+        assert torch.equal(t_["cs"][b], snaps[c][0][b]), f"sequence {b}: conv state after commit of {c}"
+
+
+def test_verify_transaction_full_size_poisoned_tail(orc):
+    """64 sequences x 4 verified rows against the oracle's transaction; before the commit the
+    rejected rows of x and g are overwritten with NaN, so a commit that read them would fail."""
+    B, K = 64, 4
+    d = _verify_inputs(2200, B, K)
+    t_ = _verify_dev(d, True)
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.bfloat16)
+    accepted = np.random.default_rng(9).integers(0, K + 1, B)
+    for b, c in enumerate(accepted):
+        t_["x"][b, c:] = float("nan")
+        t_["g"][b, c:] = float("nan")
+    gdn.verify_commit(torch.from_numpy(accepted.astype(np.int32)).cuda(), t_["x"], t_["g"], t_["cs"], t_["st"], ws)
+    torch.cuda.synchronize()
+    out_ref, snaps = orc.verify(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    cs_ref, st_ref = orc.commit(snaps, accepted)
+    check(host(out_v), out_ref, TOL_BF16, "verify rows", stored_bf16=True)
+    check(host(t_["st"]), st_ref, TOL_BF16, "committed state")
+    assert np.array_equal(host(t_["cs"]), cs_ref), "committed conv state must be exact"
+
+
+def test_verify_per_channel_fp32(orc):
+    """Per-key-channel decay on the fp32 path, 3 sequences x 3 rows, at the fp32 bound."""
+    B, K = 3, 3
+    d = _verify_inputs(2300, B, K, bf16=False, per_channel=True)
+    cfg = gdn.config(decay_per_key_channel=1)
+    t_ = _verify_dev(d, False)
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.float32, cfg=cfg)
+    accepted = [3, 1, 0]
+    gdn.verify_commit(torch.tensor(accepted, dtype=torch.int32, device="cuda"), t_["x"], t_["g"], t_["cs"],
+                      t_["st"], ws, cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, snaps = orc.verify(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    cs_ref, st_ref = orc.commit(snaps, accepted)
+    check(host(out_v), out_ref, TOL_F32, "per-channel verify rows")
+    check(host(t_["st"]), st_ref, TOL_F32, "per-channel committed state")
+    assert np.array_equal(host(t_["cs"]), cs_ref)
+
+
+# ---------------------------------------------------------------------------
 # composition and negative controls
 # ---------------------------------------------------------------------------
 
