@@ -17,6 +17,7 @@ Also measured in the same run (``workloads``):
   kda_decode_b64_h64_bf16  the per-key-channel decode step, 64 sequences x 64 heads
   decode_b64_ab_bf16  the decode step with g, beta derived from the a / b projections
   verify_k4_b64_bf16  a speculative transaction: verify 4 rows x 64 sequences, commit all 4
+  decode_b64_h16_bf16 the decode step with the recurrent state stored in fp16
 each in tokens/s (state-updates/s for the decode) with its roofline fraction (algorithmic HBM
 bytes / time / 8 TB/s).
 
@@ -117,7 +118,7 @@ def oracle_threads():
 # decode
 # ---------------------------------------------------------------------------
 
-def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False):
+def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False, state_f16=False):
     """64 sequences of one token; per_channel: the per-key-channel decode at 64 heads (ratio 1);
     derived_gates: g and beta derived in the kernel from the a / b projections (gdn_decode_step_ab)."""
     if per_channel:
@@ -134,10 +135,12 @@ def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False
         r = gi.gen_gate_projections(1102, batch)
         ab = (t_dev(r["a"], True), t_dev(r["b"], True), t_dev(r["A_log"]), t_dev(r["dt_bias"]))
         bytes_per, traffic = bytes_per - 2 * hv * 4 + 2 * hv * 2, None   # a, b bf16 in place of g, beta fp32
+    if state_f16:   # the fp16 state: half the state bytes
+        bytes_per, traffic = bytes_per - hv * D * D * 4, None
     n_sets = 3
     x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
                             t_dev(d["z"], True), t_dev(d["norm_w"]))
-    states = [t_dev(d["state"]) for _ in range(n_sets)]
+    states = [t_dev(d["state"]).to(torch.float16 if state_f16 else torch.float32) for _ in range(n_sets)]
     convs = [t_dev(d["conv_state"], True) for _ in range(n_sets)]
     out = torch.empty((batch, hv, D), dtype=torch.bfloat16, device="cuda")
 
@@ -338,7 +341,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode", "decode_ab", "verify"])
+                    choices=["all", "decode", "prefill", "varlen", "kda", "kda_decode", "decode_ab", "verify",
+                             "decode_h16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
@@ -395,6 +399,11 @@ def main():
             roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
+    if wl in ("all", "decode_h16"):
+        dh = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), state_f16=True)
+        workloads["decode_b64_h16_bf16"] = dict(
+            metric="state-updates/s", value=dh["updates_per_s"], ms=dh["ms"], roofline=dh["roofline"],
+            call="gdn_decode_step_h16: the recurrent state stored in fp16 (rounded once per token)")
     if wl in ("all", "verify"):
         ver = bench_verify(max(20, args.steps // 4), max(5, args.warmup // 4))
         workloads["verify_k4_b64_bf16"] = dict(

@@ -22,14 +22,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_SEQLENS, GDN_ERR_WORKSPACE, GDN_ERR_HIP = range(6)
-GDN_F32, GDN_BF16 = 0, 1
+GDN_F32, GDN_BF16, GDN_F16 = 0, 1, 2
 
 # Every symbol include/gdn.h declares.
 EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_conv1d_prefill",
            "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
            "gdn_chunk_prefill_ab", "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill",
            "gdn_prefill_ab", "gdn_decode_step", "gdn_decode_step_ab", "gdn_verify_workspace_size",
-           "gdn_verify", "gdn_verify_commit")
+           "gdn_verify", "gdn_verify_commit", "gdn_decode_step_h16", "gdn_state_convert")
 
 
 class GDNError(RuntimeError):
@@ -85,6 +85,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                   vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "gdn_prefill_ab": ([cfgp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                             vp, i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_decode_step_h16": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, vp],
+                                ctypes.c_int),
+        "gdn_state_convert": ([vp, ctypes.c_int, vp, ctypes.c_int, i64, vp], ctypes.c_int),
         "gdn_verify_workspace_size": ([cfgp, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
         "gdn_verify": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, sz, vp],
                        ctypes.c_int),
@@ -122,6 +125,8 @@ def _dtype(t: torch.Tensor) -> int:
         return GDN_BF16
     if t.dtype == torch.float32:
         return GDN_F32
+    if t.dtype == torch.float16:
+        return GDN_F16
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -319,11 +324,26 @@ def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
         if t is not None and not t.is_contiguous():
             raise ValueError("decode_step tensors must be contiguous")
     gates, derived = _gate_args(g, beta, ab)
-    name = "gdn_decode_step_ab" if derived else "gdn_decode_step"
+    if state.dtype == torch.float16:
+        if derived:
+            raise ValueError("the fp16-state decode takes g and beta")
+        name = "gdn_decode_step_h16"
+    else:
+        name = "gdn_decode_step_ab" if derived else "gdn_decode_step"
     _check(name, getattr(load_library(), name)(
         ctypes.byref(cfg), _dtype(x), _dtype(out), _ptr(x), _ptr(conv_w), _ptr(conv_state), *gates,
         _ptr(z), _ptr(norm_w), _ptr(state), _ptr(out), B, _stream()))
     return out
+
+
+def state_convert(src: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
+    """A recurrent state widened (fp16 -> fp32) or narrowed (fp32 -> fp16, round to nearest even)."""
+    if not src.is_contiguous():
+        raise ValueError("state_convert needs a contiguous state")
+    dst = torch.empty(src.shape, dtype=dtype, device=src.device)
+    _check("gdn_state_convert", load_library().gdn_state_convert(
+        _ptr(src), _dtype(src), _ptr(dst), _dtype(dst), src.numel(), _stream()))
+    return dst
 
 
 def verify_workspace_size(B: int, K: int, cfg: Optional[GDNConfig] = None) -> int:

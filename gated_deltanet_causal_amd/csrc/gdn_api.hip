@@ -312,7 +312,8 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
 static gdn_status_t decode_step_checked(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
                                         const void* x, const float* conv_w, void* conv_state,
                                         const gdn::Gates& gt, const void* z, const float* norm_w,
-                                        float* state, void* out, int32_t B, gdn_stream_t stream) {
+                                        void* state, bool state_f16, void* out, int32_t B,
+                                        gdn_stream_t stream) {
   Dims d;
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
@@ -325,7 +326,7 @@ static gdn_status_t decode_step_checked(const gdn_config_t* cfg, gdn_dtype_t dty
     return GDN_ERR_INVALID_ARG;
   if (B > 0 && (!aligned16(conv_w) || !aligned16(state))) return GDN_ERR_INVALID_ARG;
   return hip_status(gdn::launch_decode_step(d, dtype == GDN_BF16, out_dtype == GDN_BF16, x, conv_w,
-                                            conv_state, gt, z, norm_w, state, out, B,
+                                            conv_state, gt, z, norm_w, state, state_f16, out, B,
                                             static_cast<hipStream_t>(stream)));
 }
 
@@ -383,7 +384,27 @@ gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dty
                              const float* beta, const void* z, const float* norm_w, float* state,
                              void* out, int32_t B, gdn_stream_t stream) {
   return decode_step_checked(cfg, dtype, out_dtype, x, conv_w, conv_state, given_gates(g, beta), z, norm_w,
-                             state, out, B, stream);
+                             state, false, out, B, stream);
+}
+
+gdn_status_t gdn_decode_step_h16(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                 const void* x, const float* conv_w, void* conv_state, const float* g,
+                                 const float* beta, const void* z, const float* norm_w, void* state,
+                                 void* out, int32_t B, gdn_stream_t stream) {
+  return decode_step_checked(cfg, dtype, out_dtype, x, conv_w, conv_state, given_gates(g, beta), z, norm_w,
+                             state, true, out, B, stream);
+}
+
+gdn_status_t gdn_state_convert(const void* src, gdn_dtype_t src_dtype, void* dst, gdn_dtype_t dst_dtype,
+                               int64_t n, gdn_stream_t stream) {
+  const bool widen = src_dtype == GDN_F16 && dst_dtype == GDN_F32;
+  const bool narrow = src_dtype == GDN_F32 && dst_dtype == GDN_F16;
+  if (!widen && !narrow) return GDN_ERR_UNSUPPORTED;
+  if (n < 0) return GDN_ERR_INVALID_ARG;
+  if (n == 0) return GDN_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return GDN_ERR_INVALID_ARG;
+  if (overlaps(src, (size_t)n * (widen ? 2 : 4), dst, (size_t)n * (widen ? 4 : 2))) return GDN_ERR_INVALID_ARG;
+  return hip_status(gdn::launch_state_convert(src, widen, dst, n, static_cast<hipStream_t>(stream)));
 }
 
 gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
@@ -392,7 +413,7 @@ gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_
                                 const void* z, const float* norm_w, float* state, void* out,
                                 int32_t B, gdn_stream_t stream) {
   return decode_step_checked(cfg, dtype, out_dtype, x, conv_w, conv_state, derived_gates(a, b, A_log, dt_bias),
-                             z, norm_w, state, out, B, stream);
+                             z, norm_w, state, false, out, B, stream);
 }
 
 gdn_status_t gdn_verify_workspace_size(const gdn_config_t* cfg, int32_t B, int32_t K, size_t* bytes) {

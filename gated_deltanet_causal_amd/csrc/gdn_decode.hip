@@ -60,11 +60,11 @@ __device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_
   return act ? y * sigmoidf_(y) : y;
 }
 
-template <typename T, typename To, bool kPerChannel, int kRatio>
+template <typename T, typename To, typename TS, bool kPerChannel, int kRatio>
 __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     Gates gates, const T* __restrict__ z,
-    const float* __restrict__ norm_w, float* __restrict__ state, To* __restrict__ out, int hk,
+    const float* __restrict__ norm_w, TS* __restrict__ state, To* __restrict__ out, int hk,
     int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
   const int b = blockIdx.x / hk;
   const int kh = blockIdx.x % hk;
@@ -81,15 +81,12 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   __shared__ float s_v[kRatio][kD], s_o[kRatio][kD], s_nrm[kRatio][2];
 
   // issue the state loads first; the conv and norms below overlap their latency.
-  // The state is streamed once per step (no reuse), so its loads and stores are
-  // non-temporal.
+  // The state (fp32, or fp16 widened to fp32) is streamed once per step.
   // A window of kWindow rows is in flight: the first rows are issued here and
   // each processed row issues the load of the row kWindow after it, which keeps
   // the registers of two workgroups per CU within the register file.
-  float* S = state + ((int64_t)b * hv + h) * kD * kD;
-  auto load_row = [&](int m) {
-    return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
-  };
+  TS* S = state + ((int64_t)b * hv + h) * kD * kD;
+  auto load_row = [&](int m) { return state_load4(S + (rg + 8 * m) * kD + 4 * cg); };
   f32x4_t sreg[kRowsPerThread];
 #pragma unroll
   for (int m = 0; m < kWindow; ++m) sreg[m] = load_row(m);
@@ -151,7 +148,7 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
     if (cg == 0) s_o[hh][row] = fmaf(u, kq, pq);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
-    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + row * kD + 4 * cg));
+    state_store4(S + row * kD + 4 * cg, sreg[m]);
   }
   __syncthreads();
 
@@ -170,16 +167,17 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   }
 }
 
-template <typename T, typename To, bool kPC>
+template <typename T, typename To, typename TS, bool kPC>
 hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                         const Gates& gt, const void* z, const float* norm_w,
-                        float* state, void* out, int b, hipStream_t s) {
+                        void* state, void* out, int b, hipStream_t s) {
   const int ratio = d.hv / d.hk;
   dim3 grid(b * d.hk);
 #define GDN_DECODE_LAUNCH(R)                                                                      \
-  hipLaunchKernelGGL((decode_step_kernel<T, To, kPC, R>), grid, dim3(kGroup * (R)), 0, s,         \
+  hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC, R>), grid, dim3(kGroup * (R)), 0, s,     \
                      static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,          \
-                     static_cast<const T*>(z), norm_w, state, static_cast<To*>(out), d.hk, d.hv, \
+                     static_cast<const T*>(z), norm_w, static_cast<TS*>(state),                  \
+                     static_cast<To*>(out), d.hk, d.hv,                                          \
                      d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps)
   switch (ratio) {
     case 1: GDN_DECODE_LAUNCH(1); break;
@@ -195,23 +193,54 @@ hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void*
 template <typename T, typename To>
 hipError_t decode_impl(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                        const Gates& gt, const void* z, const float* norm_w,
-                       float* state, void* out, int b, hipStream_t s) {
-  return d.per_channel ? decode_ratio<T, To, true>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
-                       : decode_ratio<T, To, false>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
+                       void* state, bool state_f16, void* out, int b, hipStream_t s) {
+  if (state_f16)
+    return d.per_channel ? decode_ratio<T, To, _Float16, true>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
+                         : decode_ratio<T, To, _Float16, false>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
+  return d.per_channel ? decode_ratio<T, To, float, true>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
+                       : decode_ratio<T, To, float, false>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
+}
+
+// Recurrent state width conversion, fp32 <-> fp16 (narrowing rounds to
+// nearest even).  Four values per thread, grid-stride.
+template <typename Ts, typename Td>
+__global__ __launch_bounds__(kGroup) void state_convert_kernel(const Ts* __restrict__ src, Td* __restrict__ dst,
+                                                               int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * kGroup * 4;
+  for (int64_t i = ((int64_t)blockIdx.x * kGroup + threadIdx.x) * 4; i < n; i += stride) {
+    if (i + 4 <= n) {
+      state_store4(dst + i, state_load4(src + i));
+    } else {
+      for (int64_t j = i; j < n; ++j) dst[j] = (Td)(float)src[j];
+    }
+  }
 }
 
 }  // namespace
 
 hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
                               const float* conv_w, void* conv_state, const Gates& gt,
-                              const void* z, const float* norm_w, float* state, void* out, int b,
-                              hipStream_t s) {
+                              const void* z, const float* norm_w, void* state, bool state_f16,
+                              void* out, int b, hipStream_t s) {
   if (b == 0) return hipSuccess;
   if (bf16)
-    return out_bf16 ? decode_impl<uint16_t, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
-                    : decode_impl<uint16_t, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
-  return out_bf16 ? decode_impl<float, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s)
-                  : decode_impl<float, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, out, b, s);
+    return out_bf16 ? decode_impl<uint16_t, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, state_f16, out, b, s)
+                    : decode_impl<uint16_t, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, state_f16, out, b, s);
+  return out_bf16 ? decode_impl<float, uint16_t>(d, x, conv_w, conv_state, gt, z, norm_w, state, state_f16, out, b, s)
+                  : decode_impl<float, float>(d, x, conv_w, conv_state, gt, z, norm_w, state, state_f16, out, b, s);
+}
+
+hipError_t launch_state_convert(const void* src, bool src_f16, void* dst, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int64_t want = (n + 4 * kGroup - 1) / (4 * kGroup);
+  const unsigned blocks = (unsigned)(want < 8192 ? want : 8192);
+  if (src_f16)
+    hipLaunchKernelGGL((state_convert_kernel<_Float16, float>), dim3(blocks), dim3(kGroup), 0, s,
+                       static_cast<const _Float16*>(src), static_cast<float*>(dst), n);
+  else
+    hipLaunchKernelGGL((state_convert_kernel<float, _Float16>), dim3(blocks), dim3(kGroup), 0, s,
+                       static_cast<const float*>(src), static_cast<_Float16*>(dst), n);
+  return hipGetLastError();
 }
 
 }  // namespace gdn

@@ -110,6 +110,24 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// Four consecutive values of a recurrent state, stored as fp32 or as fp16
+// (the fp16 h-state: widened on load, rounded to nearest even on store, so
+// the arithmetic stays fp32 and the state is rounded once per token).  The
+// state is streamed once per step, hence non-temporal.
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4_t state_load4(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+}
+__device__ __forceinline__ f32x4_t state_load4(const _Float16* p) {
+  return __builtin_convertvector(__builtin_nontemporal_load(reinterpret_cast<const f16x4_t*>(p)), f32x4_t);
+}
+__device__ __forceinline__ void state_store4(float* p, f32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(p));
+}
+__device__ __forceinline__ void state_store4(_Float16* p, f32x4_t v) {
+  __builtin_nontemporal_store(__builtin_convertvector(v, f16x4_t), reinterpret_cast<f16x4_t*>(p));
+}
+
 // Sum over the 32 lanes holding one state row (aligned halves of the wave):
 // quad_perm swaps for lane distance 1 and 2, the half-row and row mirrors for
 // 4 and 8, and a swizzle exchanging lane i with i ^ 16 for the last step.

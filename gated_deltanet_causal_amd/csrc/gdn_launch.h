@@ -39,10 +39,13 @@ hipError_t launch_conv1d_step(const Dims& d, bool bf16, const void* x, int64_t x
 hipError_t launch_gated_rmsnorm(const Dims& d, bool o_bf16, bool z_bf16, bool out_bf16,
                                 const void* o, const void* z, const float* w, void* out,
                                 int64_t rows, hipStream_t s);
+// state: fp32, or fp16 (state_f16) widened on load and rounded on store
 hipError_t launch_decode_step(const Dims& d, bool bf16, bool out_bf16, const void* x,
                               const float* conv_w, void* conv_state, const Gates& gt,
-                              const void* z, const float* norm_w, float* state, void* out, int b,
-                              hipStream_t s);
+                              const void* z, const float* norm_w, void* state, bool state_f16,
+                              void* out, int b, hipStream_t s);
+// n state values fp32 -> fp16 (rounded to nearest even) or fp16 -> fp32
+hipError_t launch_state_convert(const void* src, bool src_f16, void* dst, int64_t n, hipStream_t s);
 
 // Speculative verify transaction (gdn_verify.hip).  The workspace holds the
 // per-row update vectors the commit replays: u [b][k][hv][dv] then the

@@ -54,7 +54,9 @@ typedef enum {
   GDN_ERR_HIP = 5           /* a HIP launch or runtime call failed              */
 } gdn_status_t;
 
-typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype_t;
+/* GDN_F16 (IEEE half) is a storage type of recurrent states only
+ * (gdn_decode_step_h16, gdn_state_convert); activations are fp32 or bf16. */
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1, GDN_F16 = 2 } gdn_dtype_t;
 
 typedef void* gdn_stream_t; /* a hipStream_t */
 
@@ -262,6 +264,29 @@ gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dty
                              const void* x, const float* conv_w, void* conv_state, const float* g,
                              const float* beta, const void* z, const float* norm_w, float* state,
                              void* out, int32_t B, gdn_stream_t stream);
+
+/*
+ * gdn_decode_step with the recurrent state stored in fp16 (the Qwen3SsmLayer
+ * field notes' FP16 h-state: the same expressions and accumulation order as
+ * the fp32 kernel, the state widened to fp32 on load and rounded to the
+ * nearest fp16 once per token on store).  state is fp16 [B][Hv][dv][dk],
+ * 16-byte aligned; every other argument as for gdn_decode_step.  This changes
+ * the numerics: the state carries a relative rounding of at most 2^-11 per
+ * token on top of the fp32 path (the tests state the bound they check).
+ */
+gdn_status_t gdn_decode_step_h16(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
+                                 const void* x, const float* conv_w, void* conv_state, const float* g,
+                                 const float* beta, const void* z, const float* norm_w, void* state,
+                                 void* out, int32_t B, gdn_stream_t stream);
+
+/*
+ * Width converter of recurrent states (the field notes' matched pair around
+ * the fp32 prefill kernels for an fp16-sized state pool): n values from src to
+ * dst, GDN_F16 -> GDN_F32 (exact) or GDN_F32 -> GDN_F16 (round to nearest
+ * even).  src and dst 16-byte aligned, not overlapping.
+ */
+gdn_status_t gdn_state_convert(const void* src, gdn_dtype_t src_dtype, void* dst, gdn_dtype_t dst_dtype,
+                               int64_t n, gdn_stream_t stream);
 
 /* gdn_decode_step with derived gates; a, b [B][Hv] in dtype. */
 gdn_status_t gdn_decode_step_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,

@@ -96,6 +96,12 @@ def round_bf16(x) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0) / 256.0, e)
 
 
+def round_f16(x) -> np.ndarray:
+    """Round fp64 values to the nearest IEEE half (ties to even, subnormals kept),
+    returned as fp64.  Used only where the library stores an fp16 recurrent state."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
 class Oracle:
     """Thin numpy front end over the C routines.  ``lib`` selects a build (the
     default oracle, or a mutant in the mutation tests)."""
@@ -177,9 +183,11 @@ class Oracle:
     # -- fused decode (a10) -------------------------------------------------
     def decode_step(self, x, conv_w, conv_state, g, beta, z, norm_w, state, *, Hk: int, Hv: int,
                     dk: int, dv: int, act: int = 1, l2_eps: float = 1e-6,
-                    q_scale: Optional[float] = None, rms_eps: float = 1e-6):
+                    q_scale: Optional[float] = None, rms_eps: float = 1e-6, state_f16: bool = False):
         """x [B,Cc]; conv_state [B,3,Cc]; g [B,Hv] (or [B,Hv,dk]); beta [B,Hv]; z [B,Hv,dv];
-        state [B,Hv,dv,dk] -> (out [B,Hv,dv], new conv_state, new state)."""
+        state [B,Hv,dv,dk] -> (out [B,Hv,dv], new conv_state, new state).  ``state_f16``: the
+        new state is rounded to fp16, as where the library stores an fp16 state (once per
+        token)."""
         x, conv_w, g, beta, z, norm_w = map(_f64, (x, conv_w, g, beta, z, norm_w))
         cs = _f64(conv_state).copy()
         st = _f64(state).copy()
@@ -191,6 +199,8 @@ class Oracle:
         self.lib.gdn_oracle_decode_step(Hk, Hv, dk, dv, per_channel, act, l2_eps, float(q_scale),
                                         rms_eps, B, _ptr(x), _ptr(conv_w), _ptr(cs), _ptr(g),
                                         _ptr(beta), _ptr(z), _ptr(norm_w), _ptr(st), _ptr(out))
+        if state_f16:
+            st = round_f16(st)
         return out, cs, st
 
     # -- speculative verify transaction --------------------------------------

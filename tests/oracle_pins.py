@@ -522,6 +522,15 @@ def pin_gates_identities_and_tails(orc):
     _close(g[0, 2:], -A[2:] * math.log(2.0), 1e-14, "per-head A at softplus(0)")
 
 
+def pin_round_f16_ieee_half(orc):
+    """The fp16 rounding step at IEEE half facts: 1 + 2^-11 is a tie and goes to 1 (even),
+    1 + 3 * 2^-11 goes up to 1 + 2^-9, 65504 is the largest finite half, 2^-24 the smallest
+    subnormal and 2^-26 rounds to zero."""
+    import oracle as oracle_pkg
+    got = oracle_pkg.round_f16([1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65504.0, 2.0 ** -24, 2.0 ** -26, -1.5])
+    assert np.array_equal(got, [1.0, 1 + 2.0 ** -9, 65504.0, 2.0 ** -24, 0.0, -1.5])
+
+
 def read_golden_geometry():
     cases = {}
     path = os.path.join(GOLDEN, "golden_pr_geometry.txt")

@@ -258,3 +258,19 @@ def test_verify_argument_checks(lib):
     assert got == gdn.GDN_ERR_INVALID_ARG                                         # accepted missing
     assert lib.gdn_verify(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, None, None, None, None, None, None, None,
                           None, None, 0, 4, None, 0, None) == 0                   # nothing to do
+
+
+def test_state_convert_and_h16_decode_argument_checks(lib):
+    conv = lambda sd, dd, src=FAKE, n=64: lib.gdn_state_convert(src, sd, ctypes.c_void_p(0x2000000), dd, n, None)
+    assert conv(gdn.GDN_F32, gdn.GDN_BF16) == gdn.GDN_ERR_UNSUPPORTED
+    assert conv(gdn.GDN_F16, gdn.GDN_F16) == gdn.GDN_ERR_UNSUPPORTED
+    assert conv(gdn.GDN_F32, gdn.GDN_F16, src=ctypes.c_void_p(0x10008)) == gdn.GDN_ERR_INVALID_ARG
+    assert conv(gdn.GDN_F32, gdn.GDN_F16, src=ctypes.c_void_p(0x2000000 - 64)) == gdn.GDN_ERR_INVALID_ARG  # overlap
+    assert conv(gdn.GDN_F32, gdn.GDN_F16, n=0) == 0
+    cfg = _cfg()
+    got = lib.gdn_decode_step_h16(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, None, FAKE, 4, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG                                  # state missing
+    got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_F16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                              FAKE, FAKE, FAKE, FAKE, 4, None)
+    assert got == gdn.GDN_ERR_UNSUPPORTED                                  # fp16 is not an activation dtype

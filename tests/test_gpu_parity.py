@@ -505,6 +505,103 @@ def test_prefill_ab_bf16(orc, lengths):
 
 
 # ---------------------------------------------------------------------------
+# fp16 recurrent state storage (gdn_decode_step_h16, gdn_state_convert)
+# ---------------------------------------------------------------------------
+
+def test_state_convert_matches_ieee_half():
+    """Narrowing rounds to the nearest half with ties to even (numpy's float16, bit for bit),
+    including subnormals, the largest finite half, overflow to infinity and a ragged tail;
+    widening is exact."""
+    rng = np.random.default_rng(77)
+    x = np.concatenate([rng.standard_normal(4093) * 10.0 ** rng.integers(-9, 5, 4093),
+                        [1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 65504.0, 65520.0, 2.0 ** -24, 2.0 ** -26, 0.0]])
+    x = x.astype(np.float32)
+    h = gdn.state_convert(torch.from_numpy(x).cuda(), torch.float16)
+    back = gdn.state_convert(h, torch.float32)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):   # 65520 rounds to infinity, as intended
+        want = x.astype(np.float16)
+    assert np.array_equal(h.cpu().numpy().view(np.uint16), want.view(np.uint16)), "narrowing != IEEE RNE"
+    assert np.array_equal(back.cpu().numpy(), want.astype(np.float32)), "widening must be exact"
+
+
+def test_decode_h16_three_steps(orc):
+    """The 64-sequence decode with an fp16 state, three steps, against the oracle rounding its
+    fp64 state to fp16 after each token.  Where the GPU's fp32 result and the oracle's fp64
+    result fall on either side of a rounding boundary the stored values differ by one half
+    ulp (2^-10 relative), inside the 2e-3 bound."""
+    d = gi.gen_decode(1007, 64)
+    s0 = oracle.round_f16(d["state"])
+    cs, st = dev(d["conv_state"], True), torch.from_numpy(s0.astype(np.float16)).cuda()
+    cs_ref, st_ref = d["conv_state"], s0
+    rng = np.random.default_rng(8)
+    for step in range(3):
+        x = d["x"] if step == 0 else gi.bf16_round(rng.standard_normal(d["x"].shape, dtype=np.float32))
+        out = gdn.decode_step(dev(x, True), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]), dev(d["z"], True),
+                              dev(d["norm_w"]), st, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        o_ref, cs_ref, st_ref = orc.decode_step(x, d["conv_w"], cs_ref, d["g"], d["beta"], d["z"], d["norm_w"],
+                                                st_ref, Hk=HK, Hv=HV, dk=D, dv=D, state_f16=True)
+        check(host(out), o_ref, TOL_BF16, f"h16 decode out step {step}", stored_bf16=True)
+        check(host(st), st_ref, TOL_BF16, f"h16 decode state step {step}")
+        assert np.array_equal(host(cs), cs_ref)
+
+
+def test_decode_h16_drift_policy(orc):
+    """Quality policy of the fp16 state over 32 tokens (8 sequences): every value finite; the
+    state's error against the unrounded fp64 oracle stays within the accumulated rounding bound
+    N * 2^-11 * max|S| (each token's rounding to the nearest half moves a value by at most
+    2^-11 of itself, fp16's unit roundoff, and the token map is non-expansive for
+    0 <= beta <= 1, alpha <= 1); the output's error stays within 2e-3; the state's Frobenius
+    norm drifts by less than 1e-3 relative."""
+    B, N = 8, 32
+    d = gi.gen_decode(1008, B)
+    st16 = torch.from_numpy(d["state"].astype(np.float16)).cuda()
+    cs = dev(d["conv_state"], True)
+    cs_ref, st_ref = d["conv_state"], d["state"].astype(np.float16).astype(np.float64)
+    rng = np.random.default_rng(12)
+    worst_state, worst_out = 0.0, 0.0
+    for step in range(N):
+        x = gi.bf16_round(rng.standard_normal(d["x"].shape, dtype=np.float32))
+        out = gdn.decode_step(dev(x, True), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]), dev(d["z"], True),
+                              dev(d["norm_w"]), st16, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, cs_ref, st_ref = orc.decode_step(x, d["conv_w"], cs_ref, d["g"], d["beta"], d["z"], d["norm_w"],
+                                                st_ref, Hk=HK, Hv=HV, dk=D, dv=D)
+        s_got, o_got = host(st16), host(out)
+        assert np.all(np.isfinite(s_got)) and np.all(np.isfinite(o_got)), f"non-finite at token {step}"
+        scale = np.max(np.abs(st_ref))
+        worst_state = max(worst_state, np.max(np.abs(s_got - st_ref)) / scale)
+        assert np.max(np.abs(s_got - st_ref)) <= (step + 1) * 2.0 ** -11 * scale * 1.05, f"state drift at {step}"
+        worst_out = max(worst_out, np.max(np.abs(o_got - o_ref)) / np.max(np.abs(o_ref)))
+    drift = abs(np.linalg.norm(s_got) / np.linalg.norm(st_ref) - 1.0)
+    print(f"[h16 policy] {N} tokens: state max err {worst_state:.3e} of max|S| (bound {N * 2.0 ** -11:.3e}), "
+          f"output max-rel {worst_out:.3e}, norm drift {drift:.3e}", flush=True)
+    assert worst_out <= TOL_BF16, "output error over the fp16-state policy bound"
+    assert drift < 1e-3, "state norm drift"
+
+
+def test_prefill_with_fp16_state_pool(orc):
+    """An fp16 state pool around the fp32 prefill: widen the sequences' states, run the
+    one-call prefill, narrow the final states back; against the oracle from the same fp16
+    initial states with its final state rounded to fp16."""
+    lengths = [130, 64, 1]
+    d = gi.gen_prefill(1401, lengths, bf16=True)
+    s16 = torch.from_numpy(d["state_in"].astype(np.float16)).cuda()
+    s32 = gdn.state_convert(s16, torch.float32)
+    out, fs = gdn.prefill(dev(d["x"], True), dev(d["conv_w"]), dev_i32(d["cu"]), dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], True), dev(d["norm_w"]), cu_host=d["cu"], initial_state=s32,
+                          out_dtype=torch.bfloat16)
+    fs16 = gdn.state_convert(fs, torch.float16)
+    torch.cuda.synchronize()
+    s_in = d["state_in"].astype(np.float16).astype(np.float64)
+    out_ref, _, s_ref, _, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                          Hk=HK, Hv=HV, dk=D, dv=D, state_in=s_in, round_y_bf16=True)
+    check(host(out), out_ref, TOL_BF16, "prefill from an fp16 pool: out", stored_bf16=True)
+    check(host(fs16), oracle.round_f16(s_ref), TOL_BF16, "prefill into an fp16 pool: final state")
+
+
+# ---------------------------------------------------------------------------
 # speculative verify transaction (gdn_verify / gdn_verify_commit)
 # ---------------------------------------------------------------------------
 
