@@ -99,8 +99,8 @@ def time_calls(fn, n_sets, steps, warmup):
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 207.8e6 + 206.0e6
-PREFILL_S4096_TRAFFIC_BYTES = None     # the one-call prefill: not yet measured
-VARLEN_TRAFFIC_BYTES = None
+PREFILL_S4096_TRAFFIC_BYTES = 455.6e6 + 341.1e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 3122.5e6 + 1940.7e6
 KDA_TRAFFIC_BYTES = 3019.3e6 + 817.9e6
 
 
