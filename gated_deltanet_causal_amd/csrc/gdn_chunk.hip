@@ -319,17 +319,17 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 
 
 // Shared tail of the intra kernels: T = (I + A)^-1 from sA, then Tt = T diag(beta)
-// and Pt (sP) written to the record in MFMA A-operand lane layout, masked to
-// the lower triangle (hi/lo bf16 fragment pairs, or fp32).  kPairK selects the
+// and (kWithP) Pt (sP) written to the record in MFMA A-operand lane layout, masked
+// to the lower triangle (hi/lo bf16 fragment pairs, or fp32).  kPairK selects the
 // paired-tile k order of the register-resident spine (element e of lane l in
 // k step ks holds column pair_k(ks, l/16, e)) instead of the plain order
 // (column 32 ks + 8 (l/16) + e).  All threads.
-template <bool F32, int kAP, bool kPairK = false>
+template <bool F32, int kAP, bool kPairK = false, bool kWithP = true>
 __device__ __forceinline__ void write_operands(const float* sA, const float* sP, float* sT, float* sM,
                                                const float* s_beta, uint8_t* rec) {
   const int tid = threadIdx.x;
   unit_lower_inverse<kAP>(sA, sT, sM);
-  for (int which = 0; which < 2; ++which) {
+  for (int which = 0; which < (kWithP ? 2 : 1); ++which) {
     const float* src = which == 0 ? sT : sP;
     const bool scale_cols = which == 0;
     uint8_t* dst = rec + which * kFragBytes;
@@ -570,15 +570,17 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   constexpr int kPitch = kD + O::kPadK;
   constexpr int kAP = kC + 1;        // fp32 64x64 scratch pitch
   // K / Q tiles are dead once the Gram tiles are in registers, so the 64x64
-  // scratch (A, Pt, T) reuses their LDS.
+  // scratch (A, T and, in the plain k order, Pt) reuses their LDS.  In the
+  // paired-tile k order Pt goes from the Gram registers straight to the record
+  // (below), which keeps three workgroups per CU within the LDS.
   constexpr int kKQBytes = 2 * kC * kPitch * (int)sizeof(E);
-  constexpr int kScratchBytes = 3 * kC * kAP * (int)sizeof(float);
+  constexpr int kScratchBytes = (kPairK ? 2 : 3) * kC * kAP * (int)sizeof(float);
   __shared__ __attribute__((aligned(16))) uint8_t s_pool[kKQBytes > kScratchBytes ? kKQBytes : kScratchBytes];
   E* sK = reinterpret_cast<E*>(s_pool);
   E* sQ = sK + kC * kPitch;
   float* sA = reinterpret_cast<float*>(s_pool);
-  float* sP = sA + kC * kAP;
-  float* sT = sP + kC * kAP;
+  float* sT = sA + kC * kAP;
+  float* sP = sT + kC * kAP;   // plain k order only
   __shared__ float sM[3 * 16 * 17];
   __shared__ __attribute__((aligned(16))) float s_rk[kC], s_rq[kC];
   __shared__ __attribute__((aligned(16))) float s_gam[2][kC], s_beta[2][kC];   // per value head, double-buffered
@@ -666,7 +668,9 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     }
   }
 
-  // G = K K^T and H = Q K^T, lower-triangular tiles of row-tile `wave`
+  // G = K K^T (tiles (wave, nt), nt <= wave) and H = Q K^T: in the paired-tile
+  // k order H is formed transposed, tiles (nt, wave) of H^T = K Q^T, whose
+  // accumulators pairs are Pt's operand fragments as they stand
   f32x4_t accG[4], accH[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
@@ -681,7 +685,8 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
       if (nt <= wave) {
         const auto b = frag<F32>(sK, kPitch, 16 * nt, ks);
         accG[nt] = mma<F32>(ak, b, accG[nt]);
-        accH[nt] = mma<F32>(aq, b, accH[nt]);
+        if constexpr (kPairK) accH[nt] = mma<F32>(b, aq, accH[nt]);
+        else accH[nt] = mma<F32>(aq, b, accH[nt]);
       }
     }
   }
@@ -695,6 +700,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
     const float* gam = s_gam[buf];
     const float* bet = s_beta[buf];
 
+    uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
     // A (strictly lower) and Pt (lower incl. diagonal) from the Gram tiles
     {
       const int r0 = 16 * wave + 4 * (lane >> 4);
@@ -712,18 +718,51 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
             const int r = r0 + e;
             const float dec = __expf(gr[e] - gj);
             const float a = br[e] * dec * rkr[e] * rkj * accG[nt][e];
-            const float pv = rqr[e] * rkj * dec * accH[nt][e];
             sA[r * kAP + j] = j < r ? a : 0.0f;
-            sP[r * kAP + j] = j <= r ? pv : 0.0f;
+            if constexpr (!kPairK) {
+              const float pv = rqr[e] * rkj * dec * accH[nt][e];
+              sP[r * kAP + j] = j <= r ? pv : 0.0f;
+            }
           }
         }
+      }
+    }
+    if constexpr (kPairK) {
+      // Pt fragments (mt = wave, ks) straight from the H^T tiles (2 ks, wave) and
+      // (2 ks + 1, wave): lane l holds Pt[r][j], r = 16 wave + l%16,
+      // j = 16 nt + 4 (l/16) + e (the record's paired-tile k order)
+      const int r = 16 * wave + (lane & 15);
+      const float gr = gam[r], rqr = s_rq[r];
+      f32x4_t pv[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        pv[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        if (nt <= wave) {
+          const int j0 = 16 * nt + 4 * (lane >> 4);
+          const f32x4_t gj = *reinterpret_cast<const f32x4_t*>(gam + j0);
+          const f32x4_t rkj = *reinterpret_cast<const f32x4_t*>(s_rk + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            pv[nt][e] = j0 + e <= r ? rqr * rkj[e] * __expf(gr - gj[e]) * accH[nt][e] : 0.0f;
+        }
+      }
+      uint8_t* dst = rec + kFragBytes;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        uint32_t hp[4], lp[4];
+        split2(pv[2 * ks][0], pv[2 * ks][1], hp[0], lp[0]);
+        split2(pv[2 * ks][2], pv[2 * ks][3], hp[1], lp[1]);
+        split2(pv[2 * ks + 1][0], pv[2 * ks + 1][1], hp[2], lp[2]);
+        split2(pv[2 * ks + 1][2], pv[2 * ks + 1][3], hp[3], lp[3]);
+        const int f = 2 * wave + ks;
+        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 0) * kWave + lane) * 16) = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
+        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 1) * kWave + lane) * 16) = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
       }
     }
     __syncthreads();
 
     // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
-    uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
-    write_operands<F32, kAP, kPairK>(sA, sP, sT, sM, bet, rec);
+    write_operands<F32, kAP, kPairK, !kPairK>(sA, sP, sT, sM, bet, rec);
 
     // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
     if (tid < kC) {
