@@ -337,6 +337,46 @@ def test_varlen_32k_full_size_sampled(orc):
     check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen state")
 
 
+def test_chunk_prefill_4200_short_sequences(orc):
+    """More sequences than the plan's longest-first ordering covers (over 4096: identity
+    order), most of them empty or a few tokens long, some crossing a chunk, zero initial
+    states: every output row and final state of the value heads of key head 3, and zero final
+    states for the empty sequences."""
+    rng = np.random.default_rng(31)
+    lengths = [int(x) for x in rng.choice([0, 1, 2, 3, 65], size=4200, p=[0.3, 0.3, 0.2, 0.15, 0.05])]
+    d = gi.gen_qkv(2500, lengths, init_state=False)
+    o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                              dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vheads, o_ref, s_ref = _sampled_heads(orc, d, [3])
+    check(host(o)[:, vheads], o_ref, TOL_BF16, "4200 short sequences out")
+    check(host(fs)[:, vheads], s_ref, TOL_BF16, "4200 short sequences state")
+    empty = [n for n, L in enumerate(lengths) if L == 0]
+    assert not torch.any(fs[empty]), "an empty sequence hands its (zero) state through"
+
+
+@pytest.mark.parametrize("case", ["beta0", "g0", "g_minus30"])
+def test_chunk_prefill_degenerate_gates(orc, case):
+    """beta = 0 (no writes: the state only decays and is read), g = 0 (no decay) and
+    g = -30 per token (every in-chunk decay factor underflows to zero): batched and single
+    sequence spines against the oracle."""
+    for lengths in ([130], [64, 63, 65, 1, 129, 70]):
+        d = gi.gen_qkv(2600 + len(lengths), lengths)
+        if case == "beta0":
+            d["beta"][:] = 0.0
+        elif case == "g0":
+            d["g"][:] = 0.0
+        else:
+            d["g"][:] = -30.0
+        o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
+                                  dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
+                                  initial_state=dev(d["state_in"]), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+        check(host(o), o_ref, TOL_BF16, f"{case} out {lengths}")
+        check(host(fs), s_ref, TOL_BF16, f"{case} state {lengths}")
+
+
 # ---------------------------------------------------------------------------
 # the whole prefill in one call (gdn_prefill)
 # ---------------------------------------------------------------------------
