@@ -34,7 +34,17 @@ namespace {
 
 constexpr int kGroup = 256;             // threads per value head
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
-constexpr int kRows = 16;               // state rows per thread: rows rg + 8 m
+constexpr int kRows = 16;               // commit: state rows per thread, rows rg + 8 m
+constexpr int kVRows = 4;               // verify: state rows per thread, rows rb + 32 m
+
+// Sum over the 8 lanes holding one state row in the verify (lanes 8r .. 8r+7):
+// quad permutes for lane distance 1 and 2, then the half-row mirror (lane i of
+// the eight with lane 7 - i, in the other quad).
+__device__ __forceinline__ float row8_sum(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  return dpp_add<0x141>(v);  // row_half_mirror
+}
 
 // One conv window of a channel, carried in registers across the rows (the
 // taps are read again for each row: they stay in cache and keep registers free).
@@ -78,18 +88,24 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   const int gt = tid;
   const int gwave = gt / kWave;
   const int lane = tid % kWave;
-  const int cg = gt % 32;                 // column group: columns 4cg .. 4cg+3
-  const int rg = gt / 32;                 // row group: rows rg + 8m
+  // Each thread holds 16 columns of 4 state rows: rows rb + 32 m, columns
+  // 32 i + 4 cb + e (i, e < 4).  A row's dot products then reduce over its 8
+  // lanes (three DPP steps), and each 16-byte access of 8 lanes is one full
+  // 128-byte line of a row.
+  const int cb = gt % 8;
+  const int rb = gt / 8;
 
   __shared__ float s_q[kD], s_k[kD], s_scal[2];
   __shared__ float s_v[kD], s_o[kD], s_nrm[2];
 
   // the head's state, read once and carried through the K rows
   const float* S = state + ((int64_t)b * hv + h) * kD * kD;
-  f32x4_t sreg[kRows];
+  f32x4_t sreg[kVRows][4];
 #pragma unroll
-  for (int m = 0; m < kRows; ++m)
-    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  for (int m = 0; m < kVRows; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sreg[m][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rb + 32 * m) * kD + 32 * i + 4 * cb));
 
   // conv windows: thread i owns q channel i (i < kD) or k channel i - kD of the
   // key head, and threads below kD also v channel i of the value head.  The
@@ -105,7 +121,7 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   // a row's global inputs, fetched one row ahead so their latency overlaps the
   // previous row's work
   float xqk_n = 0.0f, xv_n = 0.0f, z_n = 0.0f, bt_n = 0.0f;
-  f32x4_t g_n = {0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t g_n[4] = {};
   auto fetch = [&](int t) {
     const int64_t row_t = (int64_t)b * K + t;
     const T* x_row = x + row_t * cc;
@@ -114,8 +130,12 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
       xv_n = ld(x_row + c_v);
       z_n = ld(z + (row_t * hv + h) * kD + gt);
     }
-    if constexpr (kPerChannel) g_n = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 4 * cg);
-    else g_n[0] = g[row_t * hv + h];
+    if constexpr (kPerChannel) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) g_n[i] = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 32 * i + 4 * cb);
+    } else {
+      g_n[0][0] = g[row_t * hv + h];
+    }
     bt_n = beta[row_t * hv + h];
   };
   fetch(0);
@@ -123,7 +143,9 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   for (int t = 0; t < K; ++t) {
     const int64_t row_t = (int64_t)b * K + t;   // (sequence, verified row)
     const float xqk = xqk_n, xv = xv_n, zv = z_n, bt = bt_n;
-    const f32x4_t gv = g_n;
+    f32x4_t gv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gv[i] = g_n[i];
     if (t + 1 < K) fetch(t + 1);
     if (tid < 2 * kD) {
       const float y = wqk.step(conv_w, c_qk, xqk, act);
@@ -141,16 +163,23 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
     __syncthreads();
     const float rq = s_scal[0] * q_scale, rk = s_scal[1];
     const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
-    float kcol[4], qcol[4], a[4];
+    f32x4_t kcol[4], qcol[4], a[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e] * rk; qcol[e] = s_q[4 * cg + e] * rq; }
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(s_k + 32 * i + 4 * cb);
+      const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(s_q + 32 * i + 4 * cb);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { kcol[i][e] = kv[e] * rk; qcol[i][e] = qv[e] * rq; }
+    }
     if constexpr (kPerChannel) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
-    } else {
-      const float av = __expf(gv[0]);
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[e] = av;
+        for (int e = 0; e < 4; ++e) a[i][e] = __expf(gv[i][e]);
+    } else {
+      const float av = __expf(gv[0][0]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = f32x4_t{av, av, av, av};
     }
     // the normalised key of this row, for the commit's replay
     if (h % (hv / hk) == 0 && gt < kD) rec_k[(row_t * hk + kh) * kD + gt] = s_k[gt] * rk;
@@ -159,24 +188,28 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
     // o = r + u (khat . qtil), S' = Sd + u khat^T (as the decode step)
     float* u_out = rec_u + (row_t * hv + h) * kD;
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) {
-      const int row = rg + 8 * m;
+    for (int m = 0; m < kVRows; ++m) {
+      const int row = rb + 32 * m;
       float pk = 0.0f, pq = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sreg[m][e] *= a[e];
-        pk = fmaf(sreg[m][e], kcol[e], pk);
-        pq = fmaf(sreg[m][e], qcol[e], pq);
-      }
-      pk = row32_sum(pk);
-      pq = row32_sum(pq);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sreg[m][i][e] *= a[i][e];
+          pk = fmaf(sreg[m][i][e], kcol[i][e], pk);
+          pq = fmaf(sreg[m][i][e], qcol[i][e], pq);
+        }
+      pk = row8_sum(pk);
+      pq = row8_sum(pq);
       const float u = bt * (s_v[row] - pk);
-      if (cg == 0) {
+      if (cb == 0) {
         s_o[row] = fmaf(u, kq, pq);
         u_out[row] = u;
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sreg[m][i][e] = fmaf(u, kcol[i][e], sreg[m][i][e]);
     }
     __syncthreads();
 
