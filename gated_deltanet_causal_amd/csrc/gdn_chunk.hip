@@ -789,8 +789,14 @@ constexpr int kSpineThreads = 512;   // 8 waves, two per SIMD
 // The Tt / Pt fragments do not pass through here: each wave loads its own row
 // tile of them straight into registers.
 template <bool F32, bool kPC> struct Stage {
+  // bf16 with per-key-channel decay: K, Q and g staged in one layout (rows 2p,
+  // 2p+1, columns 8cb .. +7) with the rows' rk, rq, so that the decayed operands
+  // are formed in registers at commit
+  static constexpr bool kPCB = kPC && !F32;
   u32x4_t k[F32 ? 4 : 2], q[F32 ? 4 : 2], v;
-  float vec, gv[kPC ? 16 : 1];
+  float vec, gv[kPC && F32 ? 16 : 1];
+  f32x4_t g4[kPCB ? 4 : 1];
+  float rkq[kPCB ? 4 : 1];
 };
 
 // Loads are issued in parts (kParts: bit 0 K and Q, bit 1 V and the vectors,
@@ -814,15 +820,18 @@ __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, c
       sg.q[i] = row16(q, qk_stride, p / 32, 4 * (p % 32));
     }
   } else if constexpr (kParts & 1) {
-    {
-      const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));   // row pair x 8 columns
-      sg.k[0] = row16(k, qk_stride, t, j0);
-      sg.k[1] = row16(k, qk_stride, t + 1, j0);
-    }
+    const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));   // row pair x 8 columns
+    sg.k[0] = row16(k, qk_stride, t, j0);
+    sg.k[1] = row16(k, qk_stride, t + 1, j0);
+    if constexpr (kPC) {
+      sg.q[0] = row16(q, qk_stride, t, j0);
+      sg.q[1] = row16(q, qk_stride, t + 1, j0);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int p = tid + i * kSpineThreads;            // 64 rows x 16 pieces of 8
-      sg.q[i] = row16(q, qk_stride, p / 16, 8 * (p % 16));
+      for (int i = 0; i < 2; ++i) {
+        const int p = tid + i * kSpineThreads;            // 64 rows x 16 pieces of 8
+        sg.q[i] = row16(q, qk_stride, p / 16, 8 * (p % 16));
+      }
     }
   }
   if constexpr (kParts & 2) {
@@ -830,8 +839,26 @@ __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, c
     else sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
     if constexpr (kPC) sg.vec = tid < 2 * kC ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
     else sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
+    if constexpr (kPC && !F32) {
+      // rk and rq of this thread's row pair (zero past the end)
+      const float* vec = reinterpret_cast<const float*>(rec + 2 * kFragBytes);
+      const int t = 2 * (tid % (kC / 2));
+      sg.rkq[0] = vec[t];
+      sg.rkq[1] = vec[t + 1];
+      sg.rkq[2] = vec[kC + t];
+      sg.rkq[3] = vec[kC + t + 1];
+    }
   }
-  if constexpr ((kParts & 4) && kPC) {
+  if constexpr ((kParts & 4) && kPC && !F32) {
+    // log decays of the row pair, columns 8cb .. +7 (zero past the end)
+    const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
+    const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+        sg.g4[2 * r + h2] = t + r < L ? *reinterpret_cast<const f32x4_t*>(g + (int64_t)(t + r) * hv * kD + j0 + 4 * h2) : zf;
+  } else if constexpr ((kParts & 4) && kPC) {
     // channel tid/4, rows 16 (tid%4) .. +15 of the chunk
     const int ch = tid / 4, r0 = 16 * (tid % 4);
 #pragma unroll
@@ -906,6 +933,105 @@ __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename
   }
 }
 
+// Inclusive prefix sum over each aligned group of 32 lanes: shifts by 1, 2, 4, 8
+// inside each row of 16 lanes, then the last lane of rows 0 and 2 added to
+// rows 1 and 3.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_shift_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask,
+                                                                   0xF, true));
+}
+__device__ __forceinline__ float scan32(float v) {
+  v = dpp_shift_add<0x111, 0xF>(v);   // row_shr:1
+  v = dpp_shift_add<0x112, 0xF>(v);   // row_shr:2
+  v = dpp_shift_add<0x114, 0xF>(v);   // row_shr:4
+  v = dpp_shift_add<0x118, 0xF>(v);   // row_shr:8
+  return dpp_shift_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+}
+
+// Commit of a chunk for bf16 inputs with per-key-channel decay: the decayed
+// operands of the chunk's products, formed once per workgroup.  Thread (row pair
+// p, column block cb) holds K, Q and g of rows t = 2p, t + 1, columns j0 = 8cb
+// .. +7; the within-chunk cumulative log decay gam is a scan over the 32 lanes
+// of the row pairs and gam_L its total.  Written as hi / lo bf16:
+//   Kd[t][j]  = K[t][j] rk[t] e^{gam[t][j]}            (Y = Kd S0^T)
+//   Qd[t][j]  = Q[t][j] rq[t] e^{gam[t][j]}            (Z = Qd S0^T)
+//   Ku^T[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam[t][j]}  (the update K^T W)
+// and eL[j] = e^{gam_L[j]}, the state's column decay.
+__device__ __forceinline__ void stage_commit_pcb(const Stage<false, true>& sg, uint16_t* sKh, uint16_t* sKl,
+                                                 uint16_t* sQh, uint16_t* sQl, uint16_t* sKth, uint16_t* sKtl,
+                                                 int pitch, int tpitch, float* sV, int vpitch, float* eL,
+                                                 float* s_vec) {
+  const int tid = threadIdx.x;
+  const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
+  float g0[8], g1[8], gam0[8], gam1[8], gl[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    g0[c] = sg.g4[c / 4][c % 4];
+    g1[c] = sg.g4[2 + c / 4][c % 4];
+  }
+  const int lane = tid % kWave;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const float incl = scan32(g0[c] + g1[c]);
+    gam0[c] = incl - g1[c];
+    gam1[c] = incl;
+    const float tot31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 31));
+    const float tot63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
+    gl[c] = lane < 32 ? tot31 : tot63;
+  }
+  auto bf = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); };
+  auto pack = [](__bf16 a, __bf16 b) {
+    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+  };
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const float* gam = r ? gam1 : gam0;
+    const float rk = sg.rkq[r], rq = sg.rkq[2 + r];
+    uint32_t kh[4], kl[4], qh[4], ql[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      __bf16 a0, b0, a1, b1, c0, d0, c1, d1;
+      const float e0 = __expf(gam[2 * w]), e1 = __expf(gam[2 * w + 1]);
+      split_bf16(bf(sg.k[r][w], 0) * rk * e0, a0, b0);
+      split_bf16(bf(sg.k[r][w], 1) * rk * e1, a1, b1);
+      split_bf16(bf(sg.q[r][w], 0) * rq * e0, c0, d0);
+      split_bf16(bf(sg.q[r][w], 1) * rq * e1, c1, d1);
+      kh[w] = pack(a0, a1);
+      kl[w] = pack(b0, b1);
+      qh[w] = pack(c0, c1);
+      ql[w] = pack(d0, d1);
+    }
+    const int off = (t + r) * pitch + j0;
+    *reinterpret_cast<u32x4_t*>(sKh + off) = u32x4_t{kh[0], kh[1], kh[2], kh[3]};
+    *reinterpret_cast<u32x4_t*>(sKl + off) = u32x4_t{kl[0], kl[1], kl[2], kl[3]};
+    *reinterpret_cast<u32x4_t*>(sQh + off) = u32x4_t{qh[0], qh[1], qh[2], qh[3]};
+    *reinterpret_cast<u32x4_t*>(sQl + off) = u32x4_t{ql[0], ql[1], ql[2], ql[3]};
+  }
+  // the update's operand, transposed: column j of rows t, t+1 as one 4-byte pair
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    __bf16 h0, l0, h1, l1;
+    split_bf16(bf(sg.k[0][c / 2], c & 1) * sg.rkq[0] * __expf(gl[c] - gam0[c]), h0, l0);
+    split_bf16(bf(sg.k[1][c / 2], c & 1) * sg.rkq[1] * __expf(gl[c] - gam1[c]), h1, l1);
+    *reinterpret_cast<uint32_t*>(sKth + (j0 + c) * tpitch + t) = pack(h0, h1);
+    *reinterpret_cast<uint32_t*>(sKtl + (j0 + c) * tpitch + t) = pack(l0, l1);
+  }
+  if (t == 0) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) eL[j0 + c] = __expf(gl[c]);
+  }
+  if (tid < kC * 4) {
+    const int tv = tid / 4, i0 = 8 * (tid % 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sV[tv * vpitch + i0 + 2 * e] = __uint_as_float(sg.v[e] << 16);
+      sV[tv * vpitch + i0 + 2 * e + 1] = __uint_as_float(sg.v[e] & 0xffff0000u);
+    }
+  }
+  if (tid < 2 * kC) s_vec[tid] = sg.vec;
+}
+
 template <bool F32, bool kPC, typename Tin, typename To>
 __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
@@ -915,13 +1041,21 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
-  constexpr int kPitch = kD + O::kPadK;          // K, Q and state rows
-  constexpr int kTP = kC + O::kPadK;             // transposed [i][t] tiles
+  // bf16 with per-key-channel decay: the decayed operands are formed once per
+  // chunk at commit and held as hi / lo (see stage_commit_pcb); a pad of 8
+  // (rows 272 / 144 bytes apart, conflict-free for the 16-byte row reads) keeps
+  // the LDS within 160 KB
+  constexpr bool kPCB = kPC && !F32;
+  constexpr int kPad = kPCB ? 8 : O::kPadK;
+  constexpr int kPitch = kD + kPad;              // K, Q and state rows
+  constexpr int kTP = kC + kPad;                 // transposed [i][t] tiles
   constexpr int kVP = kTile + 1;                 // fp32 V tile pitch
   constexpr int kGP = kD + 4;                    // per-channel log decay pitch
   __shared__ __attribute__((aligned(16))) E sK[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sQ[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sKt[F32 ? 1 : kD * kTP];
+  __shared__ __attribute__((aligned(16))) E sKl[kPCB ? kC * kPitch : 1], sQl[kPCB ? kC * kPitch : 1];
+  __shared__ __attribute__((aligned(16))) E sKtl[kPCB ? kD * kTP : 1];
   // The fp32 state tile lives in the waves' MFMA accumulators across chunks;
   // LDS holds it as the B operand of product 1, split into bf16 hi / lo
   // (fp32 on the fp32 path), row-major [i][j].
@@ -930,7 +1064,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sRh[kTile * kTP], sRl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
-  __shared__ __attribute__((aligned(16))) float sGam[kPC ? kC * kGP : 1];
+  __shared__ __attribute__((aligned(16))) float sGam[kPCB ? kD : (kPC ? kC * kGP : 1)];   // kPCB: e^{gam_L}
   __shared__ __attribute__((aligned(16))) float s_vec[3 * kC + 4];
 
   // Block -> (sequence, key head) group and member (value head of the group,
@@ -1042,7 +1176,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const int L = min(kC, seq_end - t0);
     const bool more = t0 + kC < seq_end;
     __syncthreads();   // the previous chunk is done with every LDS tile
-    stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec);
+    if constexpr (kPCB)
+      stage_commit_pcb(stage, sK, sKl, sQ, sQl, sKt, sKtl, kPitch, kTP, sV, kVP, sGam, s_vec);
+    else
+      stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec);
     if (more) issue(std::integral_constant<int, 3>{}, t0 + kC, c + 1);   // K, Q, V, vectors
     __syncthreads();
 
@@ -1054,7 +1191,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
       const F bh = frag<F32>(sSh, kPitch, 16 * hf, ks);
       F bl{};
       if constexpr (!F32) bl = frag<F32>(sSl, kPitch, 16 * hf, ks);
-      if constexpr (kPC) {
+      if constexpr (kPCB) {
+        accY = mma3<F32>(frag<F32>(sK, kPitch, 16 * mt, ks), frag<F32>(sKl, kPitch, 16 * mt, ks), bh, bl, accY);
+        accZ = mma3<F32>(frag<F32>(sQ, kPitch, 16 * mt, ks), frag<F32>(sQl, kPitch, 16 * mt, ks), bh, bl, accZ);
+      } else if constexpr (kPC) {
         F kh_, kl_, qh_, ql_;
         decayed_frag<F32>(sK, kPitch, sGam, kGP, nullptr, s_vec, 16 * mt, ks, 1.0f, kh_, kl_);
         decayed_frag<F32>(sQ, kPitch, sGam, kGP, nullptr, s_vec + kC, 16 * mt, ks, 1.0f, qh_, ql_);
@@ -1141,7 +1281,12 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     // (per-key-channel decay: column j decays by e^{gam_L[j]} and the key rows
     //  enter as khat_t e^{gam_L - gam_t})
     {
-      if constexpr (kPC) {
+      if constexpr (kPCB) {
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sacc[q2][e] *= sGam[16 * (nj0 + q2) + 4 * (lane >> 4) + e];
+      } else if constexpr (kPC) {
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
@@ -1162,7 +1307,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
           const int j = 16 * (nj0 + q2) + (lane & 15);
-          if constexpr (kPC) {
+          if constexpr (kPCB) {
+            sacc[q2] = mma3<F32>(frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks), frag<F32>(sKtl, kTP, 16 * (nj0 + q2), ks),
+                                 bh, bl, sacc[q2]);
+          } else if constexpr (kPC) {
             // A[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam_t[j]}, t = ks + E (l/16) + e
             F ah, al;
             const int tb = ks + O::kEpl * (lane >> 4);
