@@ -319,7 +319,7 @@ static gdn_status_t decode_step_checked(const gdn_config_t* cfg, gdn_dtype_t dty
   if (st != GDN_OK) return st;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
   if (B < 0 || B > 65535 * 64) return GDN_ERR_INVALID_ARG;
-  if (d.hv / d.hk > 4) return GDN_ERR_UNSUPPORTED;   // one workgroup holds a key head's value heads
+  if ((int64_t)B * d.hv > INT32_MAX) return GDN_ERR_INVALID_ARG;   // one workgroup per (sequence, value head)
   st = check_gates(d, gt, B > 0);
   if (st != GDN_OK) return st;
   if (B > 0 && (!x || !conv_w || !conv_state || !z || !norm_w || !state || !out))

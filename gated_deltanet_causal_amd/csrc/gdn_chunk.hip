@@ -1533,8 +1533,11 @@ struct ChunkStage {
     } else if (i < Cf::kLoads - 1) {
       const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
       *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * (tid + j * kT)) = tri[j];
-    } else if (tid < kC) {
-      reinterpret_cast<u32x4_t*>(base + Cf::kOffVec)[tid] = vec;
+    } else {
+      // every thread loaded piece tid % kC and writes it (duplicates carry the same
+      // bytes): a write under tid < kC would let the compiler sink the load into
+      // that branch and wait for it there, a full memory round trip per chunk
+      reinterpret_cast<u32x4_t*>(base + Cf::kOffVec)[tid % kC] = vec;
     }
   }
 };
@@ -1636,6 +1639,20 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       sst[jt] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + 16 * jt + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
+  // gate inputs of a chunk's outputs (tokens 16 mt + m, columns iw + 4 g .. +3), bf16
+  // bits; a chunk past the end of the sequence has an empty range
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  u32x2_t zr[4], zn[4];
+  auto load_z = [&](int cl, u32x2_t* dst) {
+    const int t0 = seq_beg + cl * kC;
+    const uint32_t L = cl < n_chunks ? (uint32_t)min(kC, seq_end - t0) : 0u;
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(nrm.z + ((int64_t)min(t0, seq_end) * hv + h) * kD + iw, L * hv * kD * 2);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+      dst[mt] = __builtin_amdgcn_raw_buffer_load_b64(rz, (16 * mt + m) * (uint32_t)(hv * kD * 2) + 8 * g, 0, 0);
+  };
+  if constexpr (kNorm) load_z(0, zr);
+
   if (n_chunks > 0 && (kLoaders == 0 || loader)) {
     stage.load_all(stage.rsrc(0));
     stage.commit_all(s_in[0]);
@@ -1670,17 +1687,6 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     auto tri_frag = [&](int which, int x, int hl) {
       return load_bf16x8(reinterpret_cast<const uint16_t*>(tri + (which * 12 + 2 * x + hl) * 1024 + 16 * lane));
     };
-    // gate inputs of this chunk's outputs (tokens 16 mt + m, columns iw + 4 g .. +3),
-    // issued now so they land during the chunk
-    typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-    u32x2_t zr[4];
-    if constexpr (kNorm) {
-      const __amdgpu_buffer_rsrc_t rz = make_rsrc(nrm.z + ((int64_t)t0 * hv + h) * kD + iw, (uint32_t)L * hv * kD * 2);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-        zr[mt] = __builtin_amdgcn_raw_buffer_load_b64(rz, (16 * mt + m) * (uint32_t)(hv * kD * 2) + 8 * g, 0, 0);
-    }
-
     // LDS operands of the first k step of Y / Z, the V tile, the vectors
     bf16x8_t fk[4], fq[4];
 #pragma unroll
@@ -1740,6 +1746,11 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
         for (int mt = 0; mt < 4; ++mt) { fk[mt] = nk[mt]; fq[mt] = nq[mt]; }
       }
     }
+
+    // gate inputs of the next chunk's outputs, issued after the staging loads of
+    // the next chunk: loads complete in issue order, so z issued before them
+    // would hold up their commits; a chunk ahead, z has a whole chunk to land
+    if constexpr (kNorm) load_z(cl + 1, zn);
 
     // LDS operands of the later products: Tt, Pt (this wave's token tiles) and
     // K^T for the state update (transposing reads: A[j][slot (g, e)] =
@@ -1932,6 +1943,10 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
         for (int e = 0; e < 4; ++e) zt[mt][e] *= r;
         buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
       }
+      // (a copy that waits for z of the next chunk here; unrolling two chunks to
+      // alternate the register sets instead spills at this register budget)
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) zr[mt] = zn[mt];
     }
   }
 

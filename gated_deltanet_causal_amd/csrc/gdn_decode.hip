@@ -19,17 +19,19 @@
 //     o   = S' qtil = r + u (khat . qtil)
 // so S is read once and written once.
 //
-// Work split: one workgroup per (sequence, key head) with one 256-thread group
-// per value head of that key head (768 threads for the pages' ratio of 3), so
-// a 64-sequence batch is 1024 equal workgroups.  The workgroup owns the key
-// head's q/k conv channels and its value heads' v channels, so each conv-state
-// element has exactly one writer and is shifted in place.  Within a group, the
-// 64 KiB state of the head is spread as 16 rows x one float4 per thread; a
-// wavefront loads two full 512-byte rows per instruction.  Rows are
-// independent: each row's two dot products are reduced across the 32 lanes
-// that hold it (DPP and a swizzle, no LDS), and the row is updated and stored
-// as soon as its loads land.  The small LDS footprint lets two workgroups share
-// a CU, so one streams its state while the other computes.
+// Work split: one 256-thread workgroup per (sequence, value head), so a
+// 64-sequence batch at 48 value heads is 3072 equal workgroups, each streaming
+// one contiguous 64 KiB state (measured on gfx950: in-place streams of one
+// 64 KiB block per 256-thread workgroup reach ~5.9 TB/s, against ~5.4 TB/s for
+// 768-thread workgroups over a key head's three blocks).  The 64 KiB state of
+// the head is spread as 16 rows x one float4 per thread; a wavefront loads two
+// full 512-byte rows per instruction.  Rows are independent: each row's two dot
+// products are reduced across the 32 lanes that hold it (DPP and a swizzle, no
+// LDS), and the row is updated and stored as soon as its loads land.
+// Conv state: each workgroup shifts its value head's v channels in place (it
+// is their only reader).  The key head's q and k channels are read by all of
+// its value heads, so when the key head is shared (ratio > 1) every workgroup
+// only reads them, and a second small kernel shifts them after the step.
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -41,64 +43,106 @@ constexpr int kD = 128;                 // head_k_dim == head_v_dim
 constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
 constexpr int kWindow = 8;              // state rows in flight per thread
 
-// Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); the
-// channel's state rows become (s1, s2, x).
+// Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); with `shift`
+// the channel's state rows become (s1, s2, x).  The loads are issued by
+// load() and the arithmetic and stores done by finish(), so that other loads
+// can be issued in between.
 template <typename T>
-__device__ __forceinline__ float conv_channel(const T* x_row, const float* conv_w, T* cs_row,
-                                              int c, int cc, int act) {
-  T* p = cs_row + c;
-  const float s0 = ld(p), s1 = ld(p + cc), s2 = ld(p + 2 * cc);
-  const float xv = ld(x_row + c);
-  const f32x4_t w = *reinterpret_cast<const f32x4_t*>(conv_w + (int64_t)c * 4);
-  float y = w[0] * s0;
-  y = fmaf(w[1], s1, y);
-  y = fmaf(w[2], s2, y);
-  y = fmaf(w[3], xv, y);
-  st(p, s1);
-  st(p + cc, s2);
-  st(p + 2 * cc, xv);
-  return act ? y * sigmoidf_(y) : y;
-}
+struct ConvTap {
+  float s0, s1, s2, xv;
+  f32x4_t w;
+  __device__ __forceinline__ void load(const T* x_row, const float* conv_w, const T* cs_row, int c, int cc) {
+    const T* p = cs_row + c;
+    s0 = ld(p);
+    s1 = ld(p + cc);
+    s2 = ld(p + 2 * cc);
+    xv = ld(x_row + c);
+    w = *reinterpret_cast<const f32x4_t*>(conv_w + (int64_t)c * 4);
+  }
+  __device__ __forceinline__ float finish(T* cs_row, int c, int cc, int act, bool shift) const {
+    float y = w[0] * s0;
+    y = fmaf(w[1], s1, y);
+    y = fmaf(w[2], s2, y);
+    y = fmaf(w[3], xv, y);
+    if (shift) {
+      T* p = cs_row + c;
+      st(p, s1);
+      st(p + cc, s2);
+      st(p + 2 * cc, xv);
+    }
+    return act ? y * sigmoidf_(y) : y;
+  }
+};
 
-template <typename T, typename To, typename TS, bool kPerChannel, int kRatio>
-__global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio) void decode_step_kernel(
+template <typename T, typename To, typename TS, bool kPerChannel>
+__global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     Gates gates, const T* __restrict__ z,
     const float* __restrict__ norm_w, TS* __restrict__ state, To* __restrict__ out, int hk,
     int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
-  const int b = blockIdx.x / hk;
-  const int kh = blockIdx.x % hk;
+  const int b = blockIdx.x / hv;
+  const int h = blockIdx.x % hv;
+  const int ratio = hv / hk;
+  const int kh = h / ratio;
   const int tid = threadIdx.x;
-  const int hh = tid / kGroup;            // value head within the key head
-  const int h = kh * kRatio + hh;
-  const int gt = tid % kGroup;            // thread within the value head's group
-  const int gwave = gt / kWave;
+  const int gwave = tid / kWave;
   const int lane = tid % kWave;
-  const int cg = gt % 32;                 // column group: columns 4cg .. 4cg+3
-  const int rg = gt / 32;                 // row group: rows rg + 8m
+  const int cg = tid % 32;                // column group: columns 4cg .. 4cg+3
+  const int rg = tid / 32;                // row group: rows rg + 8m
 
   __shared__ float s_q[kD], s_k[kD], s_scal[2];
-  __shared__ float s_v[kRatio][kD], s_o[kRatio][kD], s_nrm[kRatio][2];
+  __shared__ float s_v[kD], s_o[kD], s_nrm[2];
 
-  // issue the state loads first; the conv and norms below overlap their latency.
-  // The state (fp32, or fp16 widened to fp32) is streamed once per step.
-  // A window of kWindow rows is in flight: the first rows are issued here and
-  // each processed row issues the load of the row kWindow after it, which keeps
-  // the registers of two workgroups per CU within the register file.
+  // The conv inputs are loaded first and then a window of kWindow state rows:
+  // loads complete in issue order, so the conv (which gates the first barrier)
+  // waits only for its own loads while the state rows are still in flight.
+  // Each processed row issues the load of the row kWindow after it, so the
+  // state (fp32, or fp16 widened to fp32) is streamed once per step.
+  const T* x_row = x + (int64_t)b * cc;
+  T* cs_row = conv_state + (int64_t)b * 3 * cc;
+  const int c_qk = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);   // the key head's q / k channel
+  const int c_v = 2 * hk * kD + h * kD + (tid % kD);                             // this head's v channel (tid < kD)
+  ConvTap<T> tap_qk, tap_v;
+  tap_qk.load(x_row, conv_w, cs_row, c_qk, cc);
+  tap_v.load(x_row, conv_w, cs_row, c_v, cc);   // all threads (no branch before the state loads)
+
+  // raw gates (given, or the a / b projections they are derived from)
+  GateRaw<T> graw{};
+  f32x4_t gv;
+  if constexpr (kPerChannel) {
+    gv = *reinterpret_cast<const f32x4_t*>(gates.g + ((int64_t)b * hv + h) * kD + 4 * cg);
+    graw.beta = gates.beta[(int64_t)b * hv + h];
+  } else {
+    graw = gate_raw<T>(gates, b, hv, h);
+  }
+
   TS* S = state + ((int64_t)b * hv + h) * kD * kD;
   auto load_row = [&](int m) { return state_load4(S + (rg + 8 * m) * kD + 4 * cg); };
   f32x4_t sreg[kRowsPerThread];
 #pragma unroll
   for (int m = 0; m < kWindow; ++m) sreg[m] = load_row(m);
+  // nothing that uses the conv or gate loads may move above the state loads
+  __builtin_amdgcn_sched_barrier(0);
 
-  const T* x_row = x + (int64_t)b * cc;
-  T* cs_row = conv_state + (int64_t)b * 3 * cc;
-  if (tid < 2 * kD) {   // the key head's q and k channels
-    const int c = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
-    const float y = conv_channel(x_row, conv_w, cs_row, c, cc, act);
+  // decay factors a and beta
+  float a[4], bt;
+  if constexpr (kPerChannel) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
+    bt = graw.beta;
+  } else {
+    float gs;
+    gate_resolve(gates, graw, gs, bt);
+    const float av = __expf(gs);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[e] = av;
+  }
+
+  {  // q / k are shifted here only when this head is their sole reader
+    const float y = tap_qk.finish(cs_row, c_qk, cc, act, ratio == 1);
     if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
   }
-  if (gt < kD) s_v[hh][gt] = conv_channel(x_row, conv_w, cs_row, 2 * hk * kD + h * kD + gt, cc, act);
+  if (tid < kD) s_v[tid] = tap_v.finish(cs_row, c_v, cc, act, true);
   __syncthreads();
   if (tid < 2 * kWave) {
     const int w = tid / kWave;
@@ -111,22 +155,10 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   const float rq = s_scal[0] * q_scale, rk = s_scal[1];
   // khat . qtil, computed by every wave (no exchange needed)
   const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
-  // this thread's normalised key / query columns and decay factors
-  float kcol[4], qcol[4], a[4], bt;
+  // this thread's normalised key / query columns
+  float kcol[4], qcol[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) { kcol[e] = s_k[4 * cg + e] * rk; qcol[e] = s_q[4 * cg + e] * rq; }
-  if constexpr (kPerChannel) {
-    const f32x4_t gv = *reinterpret_cast<const f32x4_t*>(gates.g + ((int64_t)b * hv + h) * kD + 4 * cg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = __expf(gv[e]);
-    bt = gates.beta[(int64_t)b * hv + h];
-  } else {
-    float gs;
-    gate_pair<T>(gates, b, hv, h, gs, bt);   // given, or derived from the a / b projections
-    const float av = __expf(gs);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[e] = av;
-  }
 
   // per row: decay, the two dot products reduced over the row's 32 lanes,
   // u = beta (v - p), o = r + u (khat . qtil), then the row is updated and
@@ -144,8 +176,8 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
     }
     pk = row32_sum(pk);
     pq = row32_sum(pq);
-    const float u = bt * (s_v[hh][row] - pk);
-    if (cg == 0) s_o[hh][row] = fmaf(u, kq, pq);
+    const float u = bt * (s_v[row] - pk);
+    if (cg == 0) s_o[row] = fmaf(u, kq, pq);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
     state_store4(S + row * kD + 4 * cg, sreg[m]);
@@ -153,40 +185,49 @@ __global__ __launch_bounds__(kGroup * kRatio, kRatio <= 3 ? 2 * kRatio : kRatio)
   __syncthreads();
 
   // the sigmoid gated RMSNorm of the head's 128 outputs
-  if (gt < kD) {
-    const float o = s_o[hh][gt];
+  if (tid < kD) {
+    const float o = s_o[tid];
     const float ss = wave_sum(o * o);
-    if (lane == 0) s_nrm[hh][gwave] = ss;
+    if (lane == 0) s_nrm[gwave] = ss;
   }
   __syncthreads();
-  if (gt < kD) {
-    const float o = s_o[hh][gt];
-    const float r = rsqrtf((s_nrm[hh][0] + s_nrm[hh][1]) * (1.0f / kD) + rms_eps);
-    const int64_t off = ((int64_t)b * hv + h) * kD + gt;
-    st(out + off, o * r * norm_w[gt] * sigmoidf_(ld(z + off)));
+  if (tid < kD) {
+    const float o = s_o[tid];
+    const float r = rsqrtf((s_nrm[0] + s_nrm[1]) * (1.0f / kD) + rms_eps);
+    const int64_t off = ((int64_t)b * hv + h) * kD + tid;
+    st(out + off, o * r * norm_w[tid] * sigmoidf_(ld(z + off)));
   }
+}
+
+// Shift of the shared q / k conv state channels after a step whose workgroups
+// only read them: rows (s0, s1, s2) become (s1, s2, x).  One channel per
+// thread; values move bit for bit.
+template <typename T>
+__global__ __launch_bounds__(kGroup) void conv_shift_kernel(const T* __restrict__ x, T* __restrict__ conv_state,
+                                                            int cc, int n_ch) {
+  const int c = blockIdx.x * kGroup + threadIdx.x;
+  if (c >= n_ch) return;
+  const int64_t b = blockIdx.y;
+  T* p = conv_state + b * 3 * cc + c;
+  const T s1 = p[cc], s2 = p[2 * cc], xv = x[b * cc + c];
+  p[0] = s1;
+  p[cc] = s2;
+  p[2 * cc] = xv;
 }
 
 template <typename T, typename To, typename TS, bool kPC>
 hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                         const Gates& gt, const void* z, const float* norm_w,
                         void* state, void* out, int b, hipStream_t s) {
-  const int ratio = d.hv / d.hk;
-  dim3 grid(b * d.hk);
-#define GDN_DECODE_LAUNCH(R)                                                                      \
-  hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC, R>), grid, dim3(kGroup * (R)), 0, s,     \
-                     static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,          \
-                     static_cast<const T*>(z), norm_w, static_cast<TS*>(state),                  \
-                     static_cast<To*>(out), d.hk, d.hv,                                          \
-                     d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps)
-  switch (ratio) {
-    case 1: GDN_DECODE_LAUNCH(1); break;
-    case 2: GDN_DECODE_LAUNCH(2); break;
-    case 3: GDN_DECODE_LAUNCH(3); break;
-    case 4: GDN_DECODE_LAUNCH(4); break;
-    default: return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC>), dim3(b * d.hv), dim3(kGroup), 0, s,
+                     static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,
+                     static_cast<const T*>(z), norm_w, static_cast<TS*>(state),
+                     static_cast<To*>(out), d.hk, d.hv, d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
+  if (d.hv != d.hk) {   // shared q / k channels: shifted once, after every head has read them
+    const int n_ch = 2 * d.hk * kD;
+    hipLaunchKernelGGL(conv_shift_kernel<T>, dim3((n_ch + kGroup - 1) / kGroup, b), dim3(kGroup), 0, s,
+                       static_cast<const T*>(x), static_cast<T*>(conv_state), d.cc, n_ch);
   }
-#undef GDN_DECODE_LAUNCH
   return hipGetLastError();
 }
 

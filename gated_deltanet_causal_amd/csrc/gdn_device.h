@@ -155,17 +155,46 @@ __device__ __forceinline__ void derive_gates(float a, float b, float A_log, floa
   beta = sigmoidf_(b);
 }
 
+// The raw gate inputs of row t, value head h (scalar decay): a, b (storage
+// type, unconverted), A_log, dt_bias when the gates are derived, else g and
+// beta.  Loaded apart from gate_resolve() so that a kernel can issue the loads
+// early: nothing in the loading branch uses a loaded value, so no wait for
+// them is placed there.
+template <typename T>
+struct GateRaw {
+  T a, b;
+  float g, beta, A_log, dt_bias;
+};
+template <typename T>
+__device__ __forceinline__ GateRaw<T> gate_raw(const Gates& gt, int64_t t, int hv, int h) {
+  const int64_t i = t * hv + h;
+  GateRaw<T> r{};
+  if (gt.a) {
+    r.a = static_cast<const T*>(gt.a)[i];
+    r.b = static_cast<const T*>(gt.b)[i];
+    r.A_log = gt.A_log[h];
+    r.dt_bias = gt.dt_bias[h];
+  } else {
+    r.g = gt.g[i];
+    r.beta = gt.beta[i];
+  }
+  return r;
+}
+// Branch-free (both forms computed, one selected), so that a compiler cannot
+// merge it into gate_raw's branch and pull the arithmetic up to the loads.
+template <typename T>
+__device__ __forceinline__ void gate_resolve(const Gates& gt, const GateRaw<T>& r, float& g, float& beta) {
+  float gd, bd;
+  derive_gates(ld(&r.a), ld(&r.b), r.A_log, r.dt_bias, gd, bd);
+  const bool derived = gt.a != nullptr;
+  g = derived ? gd : r.g;
+  beta = derived ? bd : r.beta;
+}
+
 // g and beta of row t, value head h (scalar decay)
 template <typename T>
 __device__ __forceinline__ void gate_pair(const Gates& gt, int64_t t, int hv, int h, float& g, float& beta) {
-  const int64_t i = t * hv + h;
-  if (gt.a) {
-    derive_gates(ld(static_cast<const T*>(gt.a) + i), ld(static_cast<const T*>(gt.b) + i), gt.A_log[h],
-                 gt.dt_bias[h], g, beta);
-  } else {
-    g = gt.g[i];
-    beta = gt.beta[i];
-  }
+  gate_resolve(gt, gate_raw<T>(gt, t, hv, h), g, beta);
 }
 
 }  // namespace gdn

@@ -258,7 +258,10 @@ gdn_status_t gdn_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtyp
  *   z            [B][Hv][dv];  norm_w fp32 [dv]
  *   state        fp32 [B][Hv][dv][dk], updated in place
  *   out          [B][Hv][dv]
- * Requires Hv / Hk <= 4 (GDN_ERR_UNSUPPORTED otherwise).
+ * B * Hv must not exceed INT32_MAX (GDN_ERR_INVALID_ARG).  When Hk < Hv the
+ * key head's q / k conv-state channels are read by all its value heads, and
+ * the step is two launches on the stream: the fused step, then a shift of
+ * those channels.
  */
 gdn_status_t gdn_decode_step(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtype_t out_dtype,
                              const void* x, const float* conv_w, void* conv_state, const float* g,

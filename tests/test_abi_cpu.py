@@ -162,11 +162,12 @@ def test_empty_calls_launch_nothing(lib):
                                  None, 0, None) == 0
 
 
-def test_decode_rejects_more_than_four_value_heads_per_key_head(lib):
-    cfg = _cfg(num_k_heads=8, num_v_heads=48)
+def test_decode_rejects_grids_past_int32(lib):
+    """One workgroup per (sequence, value head): B * Hv must fit a 32-bit grid."""
+    cfg = _cfg(num_k_heads=1, num_v_heads=1 << 20)
     got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
-                              FAKE, FAKE, FAKE, FAKE, 4, None)
-    assert got == gdn.GDN_ERR_UNSUPPORTED
+                              FAKE, FAKE, FAKE, FAKE, 4096, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG
 
 
 def _prefill_ws(lib, n, t, dtype=gdn.GDN_BF16, cfg=None):

@@ -208,6 +208,29 @@ def test_decode_step_per_channel_h64_bf16_two_steps(orc):
         assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
 
 
+@pytest.mark.parametrize("hk,hv", [(8, 48), (2, 4)], ids=["ratio6", "ratio2"])
+def test_decode_step_other_ratios_three_steps(orc, hk, hv):
+    """Repeat-interleave ratios other than the pages' 3 (6 and 2), bf16 activations: every
+    value head reads its key head's q / k conv channels, which are shifted once after the
+    step; three steps so that later steps read the shifted conv state."""
+    geo = gi.Geometry(hk=hk, hv=hv)
+    d = gi.gen_decode(1008 + hk, 7, geo)
+    cfg = gdn.config(num_k_heads=hk, num_v_heads=hv)
+    cs, st = dev(d["conv_state"], True), dev(d["state"])
+    cs_ref, st_ref = d["conv_state"], d["state"]
+    rng = np.random.default_rng(8 + hk)
+    for step in range(3):
+        x = d["x"] if step == 0 else gi.bf16_round(rng.standard_normal(d["x"].shape, dtype=np.float32))
+        out = gdn.decode_step(dev(x, True), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]),
+                              dev(d["z"], True), dev(d["norm_w"]), st, out_dtype=torch.bfloat16, cfg=cfg)
+        torch.cuda.synchronize()
+        o_ref, cs_ref, st_ref = orc.decode_step(x, d["conv_w"], cs_ref, d["g"], d["beta"], d["z"], d["norm_w"],
+                                                st_ref, Hk=hk, Hv=hv, dk=D, dv=D)
+        check(host(out), o_ref, TOL_BF16, f"decode ratio {hv // hk} out step {step}", stored_bf16=True)
+        check(host(st), st_ref, TOL_BF16, f"decode ratio {hv // hk} state step {step}")
+        assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
+
+
 # ---------------------------------------------------------------------------
 # chunk prefill
 # ---------------------------------------------------------------------------
