@@ -41,7 +41,29 @@ namespace {
 constexpr int kGroup = 256;             // threads per value head
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
 constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
-constexpr int kWindow = 8;              // state rows in flight per thread
+constexpr int kWindow = 4;              // state rows in flight per thread
+
+// Four state values at a buffer offset, streamed (non-temporal: the state is
+// touched once per step); fp16 is widened on load and rounded to nearest even
+// on store.
+template <typename TS>
+__device__ __forceinline__ f32x4_t state_buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  if constexpr (sizeof(TS) == 4) {
+    return __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2));
+  } else {
+    return __builtin_convertvector(__builtin_bit_cast(f16x4_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 2)),
+                                   f32x4_t);
+  }
+}
+template <typename TS>
+__device__ __forceinline__ void state_buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, f32x4_t v) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  if constexpr (sizeof(TS) == 4) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, soff, 2);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, __builtin_convertvector(v, f16x4_t)), r, voff, soff, 2);
+  }
+}
 
 // Conv of one channel for one token: y = act(w . (s0, s1, s2, x)); with `shift`
 // the channel's state rows become (s1, s2, x).  The loads are issued by
@@ -97,7 +119,9 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
   // loads complete in issue order, so the conv (which gates the first barrier)
   // waits only for its own loads while the state rows are still in flight.
   // Each processed row issues the load of the row kWindow after it, so the
-  // state (fp32, or fp16 widened to fp32) is streamed once per step.
+  // state (fp32, or fp16 widened to fp32) is streamed once per step.  A short
+  // window keeps a thread within 64 registers: eight waves per SIMD (eight
+  // workgroups per CU) keep as many rows in flight as a longer window would.
   const T* x_row = x + (int64_t)b * cc;
   T* cs_row = conv_state + (int64_t)b * 3 * cc;
   const int c_qk = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);   // the key head's q / k channel
@@ -116,8 +140,12 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
     graw = gate_raw<T>(gates, b, hv, h);
   }
 
+  // the head's state through a buffer descriptor: a 32-bit lane offset and the
+  // row step in the scalar offset, so that no 64-bit address is held per row
   TS* S = state + ((int64_t)b * hv + h) * kD * kD;
-  auto load_row = [&](int m) { return state_load4(S + (rg + 8 * m) * kD + 4 * cg); };
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, kD * kD * (int)sizeof(TS), 0x00020000);
+  const uint32_t voff = (uint32_t)(rg * kD + 4 * cg) * sizeof(TS);
+  auto load_row = [&](int m) { return state_buf_load4<TS>(rs, voff, (uint32_t)(8 * m * kD * sizeof(TS))); };
   f32x4_t sreg[kRowsPerThread];
 #pragma unroll
   for (int m = 0; m < kWindow; ++m) sreg[m] = load_row(m);
@@ -180,7 +208,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
     if (cg == 0) s_o[row] = fmaf(u, kq, pq);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
-    state_store4(S + row * kD + 4 * cg, sreg[m]);
+    state_buf_store4<TS>(rs, voff, (uint32_t)(8 * m * kD * sizeof(TS)), sreg[m]);
   }
   __syncthreads();
 
