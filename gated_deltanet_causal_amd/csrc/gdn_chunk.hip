@@ -351,6 +351,8 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
         const int p = tid + it * kThreads;
         const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
         const int mt = f / 2, ks = f % 2;
+        // fragments (0, 1) and (1, 1) lie above the diagonal: all zero, never read
+        if (ks == 1 && mt < 2) continue;   // uniform per wave
         const int r = 16 * mt + (l & 15);
         float v[8];
 #pragma unroll
