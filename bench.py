@@ -98,10 +98,10 @@ def time_calls(fn, n_sets, steps, warmup):
 
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
-DECODE_TRAFFIC_BYTES = 207.8e6 + 206.0e6
-PREFILL_S4096_TRAFFIC_BYTES = 455.6e6 + 341.1e6    # gdn_prefill, all its kernels
-VARLEN_TRAFFIC_BYTES = 3122.5e6 + 1940.7e6
-KDA_TRAFFIC_BYTES = 3019.3e6 + 817.9e6
+DECODE_TRAFFIC_BYTES = 214.0e6 + 206.0e6          # both launches of a step
+PREFILL_S4096_TRAFFIC_BYTES = 455.9e6 + 328.6e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 3116.7e6 + 1838.8e6
+KDA_TRAFFIC_BYTES = 3017.4e6 + 683.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
@@ -356,7 +356,7 @@ def main():
         return
     wl = args.workload
     cpu = not args.no_cpu_baseline
-    small_steps, small_warm = max(5, args.steps // 10), max(2, args.warmup // 4)
+    small_steps, small_warm = max(5, args.steps // 10), max(2, args.warmup)   # the clocks settle over the first calls
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
     workloads = {}
@@ -370,7 +370,7 @@ def main():
                        "activations": "bf16", "state": "f32 [64,48,128,128], 3 sets rotated"},
             "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
             "head_updates_per_s": dec["updates_per_s"] * HV,
-            "roofline": dict(dec["roofline"], kernel="decode_step_kernel (one launch per step)",
+            "roofline": dict(dec["roofline"], kernel="decode_step_kernel + conv_shift_kernel (the two launches of one step, timed together)",
                              bytes_per_update=DECODE_BYTES_PER_UPDATE),
         })
         if cpu:
