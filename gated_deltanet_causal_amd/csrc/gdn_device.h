@@ -135,6 +135,14 @@ template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float v) {
   return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, false));
 }
+// Sum over each row of 16 lanes (quad sums, then rotations by 4 and 8 within the row).
+__device__ __forceinline__ float row16_sum(float v) {
+  v = quad_sum(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
+  return v;
+}
+
 __device__ __forceinline__ float row32_sum(float v) {
   v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
   v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]

@@ -56,13 +56,6 @@ __device__ __forceinline__ void st8(T* p, const float (&v)[8]) {
 }
 
 // Sum over each row of 16 lanes (quad sums, then rotations by 4 and 8 lanes).
-__device__ __forceinline__ float row16_sum(float v) {
-  v = quad_sum(v);
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x124, 0xF, 0xF, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, true));
-  return v;
-}
-
 template <typename Ti, typename Tz, typename To>
 __global__ __launch_bounds__(kNormThreads) void gated_rmsnorm_kernel(
     const Ti* o, const Tz* __restrict__ z, const float* __restrict__ w, To* out,

@@ -682,13 +682,13 @@ def _verify_dev(d, bf16):
                 beta=dev(d["beta"]), z=dev(d["z"], bf16), nw=dev(d["norm_w"]), st=dev(d["state"]))
 
 
-@pytest.mark.parametrize("K", [1, 4], ids=["K1", "K4"])
+@pytest.mark.parametrize("K", [1, 4, 16, 17], ids=["K1", "K4", "K16", "K17"])
 def test_verify_commit_equals_decode_steps(K):
     """Verified row t matches decode step t, the verify leaves both states as they were, and a
     commit of c rows leaves the states c decode steps leave (c = 0 .. K, out-of-range counts
     clamped).  The two kernels sum a state row's dot products in different orders (the verify
     over 8 lanes of 16 columns, the decode over 32 lanes of 4), so the match is to fp32
-    rounding (1e-5); the conv state is exact."""
+    rounding (1e-5), also over windows of 16 and 17 rows; the conv state is exact."""
     B = 8
     d = _verify_inputs(2100, B, K)
     t_ = _verify_dev(d, True)
