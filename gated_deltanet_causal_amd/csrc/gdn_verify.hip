@@ -26,6 +26,8 @@
 //
 // HBM per transaction: the state is read twice and written once (2R + 1W),
 // against 1R + KW for per-row snapshots plus a copy at commit.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -65,13 +67,35 @@ struct ConvWindow {
   }
 };
 
+// A stored value as loaded (bf16: its 16 bits, zero-extended; fp32: the value),
+// widened to fp32 at its use.  pin() marks the register as written at that point,
+// so that neither the widening nor anything else that uses the load can be
+// moved above it: placed after the state loads, the wait for an early load then
+// comes after the state loads are issued.
 template <typename T>
-__device__ __forceinline__ ConvWindow load_window(const T* cs_row, int c, int cc) {
-  ConvWindow cw;
-  cw.s0 = ld(cs_row + c);
-  cw.s1 = ld(cs_row + cc + c);
-  cw.s2 = ld(cs_row + 2 * cc + c);
-  return cw;
+struct Raw {
+  typename std::conditional<sizeof(T) == 2, uint32_t, float>::type r;
+  __device__ __forceinline__ void load(const T* p) { r = *p; }
+  __device__ __forceinline__ float widen() const {
+    if constexpr (sizeof(T) == 2) return __uint_as_float(r << 16); else return r;
+  }
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(r)); }
+};
+
+// The window's three stored values, loaded early and widened after the pin.
+template <typename T>
+struct RawWindow {
+  Raw<T> s0, s1, s2;
+  __device__ __forceinline__ void pin() { s0.pin(); s1.pin(); s2.pin(); }
+  __device__ __forceinline__ ConvWindow widen() const { return ConvWindow{s0.widen(), s1.widen(), s2.widen()}; }
+};
+template <typename T>
+__device__ __forceinline__ RawWindow<T> load_window(const T* cs_row, int c, int cc) {
+  RawWindow<T> w;
+  w.s0.load(cs_row + c);
+  w.s1.load(cs_row + cc + c);
+  w.s2.load(cs_row + 2 * cc + c);
+  return w;
 }
 
 template <typename T, typename To, bool kPerChannel>
@@ -98,38 +122,29 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   __shared__ float s_q[kD], s_k[kD], s_scal[2];
   __shared__ float s_v[kD], s_o[kD], s_nrm[2];
 
-  // the head's state, read once and carried through the K rows
-  const float* S = state + ((int64_t)b * hv + h) * kD * kD;
-  f32x4_t sreg[kVRows][4];
-#pragma unroll
-  for (int m = 0; m < kVRows; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      sreg[m][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rb + 32 * m) * kD + 32 * i + 4 * cb));
-
   // conv windows: thread i owns q channel i (i < kD) or k channel i - kD of the
   // key head, and threads below kD also v channel i of the value head.  The
   // conv state is only read, so the value heads of a key head each redo the
   // key head's q / k conv (a workgroup per value head).
   const T* cs_row = conv_state + (int64_t)b * 3 * cc;
   const int c_qk = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);
-  const int c_v = 2 * hk * kD + h * kD + gt;
-  ConvWindow wqk = {}, wv = {};
-  if (tid < 2 * kD) wqk = load_window(cs_row, c_qk, cc);
-  if (gt < kD) wv = load_window(cs_row, c_v, cc);
+  const int c_v = 2 * hk * kD + h * kD + gt % kD;
+  // loaded by every thread (threads past kD repeat a channel, unused): a load
+  // under a branch is waited for inside it, before the state loads are issued
+  RawWindow<T> raw_qk = load_window(cs_row, c_qk, cc);
+  RawWindow<T> raw_v = load_window(cs_row, c_v, cc);
 
   // a row's global inputs, fetched one row ahead so their latency overlaps the
   // previous row's work
-  float xqk_n = 0.0f, xv_n = 0.0f, z_n = 0.0f, bt_n = 0.0f;
+  Raw<T> xqk_n, xv_n, z_n;   // stored values, widened at their use
+  float bt_n = 0.0f;
   f32x4_t g_n[4] = {};
   auto fetch = [&](int t) {
     const int64_t row_t = (int64_t)b * K + t;
     const T* x_row = x + row_t * cc;
-    if (tid < 2 * kD) xqk_n = ld(x_row + c_qk);
-    if (gt < kD) {
-      xv_n = ld(x_row + c_v);
-      z_n = ld(z + (row_t * hv + h) * kD + gt);
-    }
+    xqk_n.load(x_row + c_qk);
+    xv_n.load(x_row + c_v);
+    z_n.load(z + (row_t * hv + h) * kD + gt % kD);
     if constexpr (kPerChannel) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) g_n[i] = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 32 * i + 4 * cb);
@@ -140,14 +155,42 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   };
   fetch(0);
 
-  for (int t = 0; t < K; ++t) {
+  // the head's state, read once and carried through the K rows.  Its loads are
+  // issued after the conv windows and the first row's inputs: loads complete in
+  // issue order, so the first row's conv and norms wait only for their own
+  // inputs while the 64 KiB of state is still in flight
+  // (buffer loads, streamed: a plain load would be sunk to its first use)
+  const float* S = state + ((int64_t)b * hv + h) * kD * kD;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(S), (short)0,
+                                                                     kD * kD * (int)sizeof(float), 0x00020000);
+  const uint32_t voff = (uint32_t)(rb * kD + 4 * cb) * sizeof(float);
+  f32x4_t sreg[kVRows][4];
+#pragma unroll
+  for (int m = 0; m < kVRows; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      sreg[m][i] = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (uint32_t)((32 * m * kD + 32 * i) * sizeof(float)), 2));
+  // nothing that uses the window or row loads may move above the state loads
+  __builtin_amdgcn_sched_barrier(0);
+  raw_qk.pin();
+  raw_v.pin();
+  xqk_n.pin();
+  xv_n.pin();
+  z_n.pin();
+  ConvWindow wqk = raw_qk.widen(), wv = raw_v.widen();
+
+  // K >= 1 (checked before the launch): a do-while has no entry test, which
+  // would let the compiler sink the state loads behind it
+  int t = 0;
+  do {
     const int64_t row_t = (int64_t)b * K + t;   // (sequence, verified row)
-    const float xqk = xqk_n, xv = xv_n, zv = z_n, bt = bt_n;
+    const float xqk = xqk_n.widen(), xv = xv_n.widen(), zv = z_n.widen(), bt = bt_n;
     f32x4_t gv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) gv[i] = g_n[i];
     if (t + 1 < K) fetch(t + 1);
-    if (tid < 2 * kD) {
+    {
       const float y = wqk.step(conv_w, c_qk, xqk, act);
       if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
     }
@@ -225,7 +268,7 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
       const float r = rsqrtf((s_nrm[0] + s_nrm[1]) * (1.0f / kD) + rms_eps);
       st(out + (row_t * hv + h) * kD + gt, o * r * norm_w[gt] * sigmoidf_(zv));
     }
-  }
+  } while (++t < K);
 }
 
 // Commit of the recurrent state: sequence b keeps its first clamp(accepted[b],
