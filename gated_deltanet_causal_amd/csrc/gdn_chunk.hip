@@ -50,6 +50,7 @@ constexpr int kC = 64;           // chunk
 constexpr int kD = 128;          // head dim (k and v)
 constexpr int kTile = 32;        // dv rows per spine workgroup
 constexpr int kThreads = 256;
+constexpr int kIntraMinWaves = 4;   // intra: waves per SIMD the register budget must allow (bf16: 128 VGPRs)
 constexpr size_t kFragBytes = 16384;           // one 64x64 operand in lane layout
 constexpr size_t kRecBytes = 2 * kFragBytes + 1024;  // Tt, Pt, vectors
 constexpr int kSortMax = 4096;                 // longest-first order up to this many sequences
@@ -563,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
 // ---------------------------------------------------------------------------
 template <bool F32, typename Tin, bool kPairK>
-__global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
+__global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     Gates gates, const int32_t* __restrict__ cu,
     int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
@@ -574,7 +575,10 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   // K / Q tiles are dead once the Gram tiles are in registers, so the 64x64
   // scratch (A, T and, in the plain k order, Pt) reuses their LDS.  In the
   // paired-tile k order Pt goes from the Gram registers straight to the record
-  // (below), which keeps three workgroups per CU within the LDS.
+  // (below).  The diagonal-block scratch of write_operands sits after A and T in
+  // the same pool, so bf16 inputs take 38.4 KB of LDS: with at most 128 VGPRs
+  // (kIntraMinWaves) four workgroups share a CU, and a 4096-token sequence's
+  // 1024 (chunk, key head) workgroups run in one round instead of 1.33.
   constexpr int kKQBytes = 2 * kC * kPitch * (int)sizeof(E);
   constexpr int kScratchBytes = (kPairK ? 2 : 3) * kC * kAP * (int)sizeof(float);
   __shared__ __attribute__((aligned(16))) uint8_t s_pool[kKQBytes > kScratchBytes ? kKQBytes : kScratchBytes];
@@ -583,7 +587,11 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_kernel(
   float* sA = reinterpret_cast<float*>(s_pool);
   float* sT = sA + kC * kAP;
   float* sP = sT + kC * kAP;   // plain k order only
-  __shared__ float sM[3 * 16 * 17];
+  // write_operands' 16x16 blocks, after the scratch in the same pool (used only
+  // once the K / Q tiles are dead)
+  static_assert(kScratchBytes + 3 * 16 * 17 * (int)sizeof(float) <= (kKQBytes > kScratchBytes ? kKQBytes : kScratchBytes),
+                "the pool holds the scratch and the blocks");
+  float* sM = reinterpret_cast<float*>(s_pool + kScratchBytes);
   __shared__ __attribute__((aligned(16))) float s_rk[kC], s_rq[kC];
   __shared__ __attribute__((aligned(16))) float s_gam[2][kC], s_beta[2][kC];   // per value head, double-buffered
 
