@@ -19,13 +19,15 @@
 //     o   = S' qtil = r + u (khat . qtil)
 // so S is read once and written once.
 //
-// Work split: one 256-thread workgroup per (sequence, value head), so a
+// Work split: one 512-thread workgroup per (sequence, value head), so a
 // 64-sequence batch at 48 value heads is 3072 equal workgroups, each streaming
 // one contiguous 64 KiB state (measured on gfx950: in-place streams of one
-// 64 KiB block per 256-thread workgroup reach ~5.9 TB/s, against ~5.4 TB/s for
-// 768-thread workgroups over a key head's three blocks).  The 64 KiB state of
-// the head is spread as 16 rows x one float4 per thread; a wavefront loads two
-// full 512-byte rows per instruction.  Rows are independent: each row's two dot
+// 64 KiB block per workgroup reach ~5.9 TB/s, against ~5.4 TB/s for 768-thread
+// workgroups over a key head's three blocks).  At eight waves per SIMD four
+// such workgroups share a CU, so the 3072 run as three full rounds of 1024
+// (256-thread workgroups, eight per CU, left the last of 1.5 rounds half
+// empty).  The 64 KiB state of the head is spread as 8 rows x one float4 per
+// thread; a wavefront loads two full 512-byte rows per instruction.  Rows are independent: each row's two dot
 // products are reduced across the 32 lanes that hold it (DPP and a swizzle, no
 // LDS), and the row is updated and stored as soon as its loads land.
 // Conv state: each workgroup shifts its value head's v channels in place (it
@@ -38,9 +40,11 @@
 namespace gdn {
 namespace {
 
-constexpr int kGroup = 256;             // threads per value head
+constexpr int kGroup = 256;             // threads per workgroup of the small kernels
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
-constexpr int kRowsPerThread = 16;      // 128 rows over 8 row groups
+constexpr int kStepThreads = 512;       // threads per value head (the step kernel)
+constexpr int kRowGroups = kStepThreads / 32;
+constexpr int kRowsPerThread = kD / kRowGroups;
 constexpr int kWindow = 4;              // state rows in flight per thread
 
 // Four state values at a buffer offset, streamed (non-temporal: the state is
@@ -97,7 +101,7 @@ struct ConvTap {
 };
 
 template <typename T, typename To, typename TS, bool kPerChannel>
-__global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
+__global__ __launch_bounds__(kStepThreads, kStepThreads / 64) void decode_step_kernel(
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     Gates gates, const T* __restrict__ z,
     const float* __restrict__ norm_w, TS* __restrict__ state, To* __restrict__ out, int hk,
@@ -110,7 +114,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
   const int gwave = tid / kWave;
   const int lane = tid % kWave;
   const int cg = tid % 32;                // column group: columns 4cg .. 4cg+3
-  const int rg = tid / 32;                // row group: rows rg + 8m
+  const int rg = tid / 32;                // row group: rows rg + kRowGroups m
 
   __shared__ float s_q[kD], s_k[kD], s_scal[2];
   __shared__ float s_v[kD], s_o[kD], s_nrm[2];
@@ -120,15 +124,18 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
   // waits only for its own loads while the state rows are still in flight.
   // Each processed row issues the load of the row kWindow after it, so the
   // state (fp32, or fp16 widened to fp32) is streamed once per step.  A short
-  // window keeps a thread within 64 registers: eight waves per SIMD (eight
+  // window keeps a thread within 64 registers: eight waves per SIMD (four
   // workgroups per CU) keep as many rows in flight as a longer window would.
+  // Every thread loads a q / k and a v conv input (threads past the channels
+  // repeat one, unused): no branch before the state loads.
   const T* x_row = x + (int64_t)b * cc;
   T* cs_row = conv_state + (int64_t)b * 3 * cc;
-  const int c_qk = tid < kD ? kh * kD + tid : hk * kD + kh * kD + (tid - kD);   // the key head's q / k channel
+  const int tq = tid % (2 * kD);
+  const int c_qk = tq < kD ? kh * kD + tq : hk * kD + kh * kD + (tq - kD);   // the key head's q / k channel
   const int c_v = 2 * hk * kD + h * kD + (tid % kD);                             // this head's v channel (tid < kD)
   ConvTap<T> tap_qk, tap_v;
   tap_qk.load(x_row, conv_w, cs_row, c_qk, cc);
-  tap_v.load(x_row, conv_w, cs_row, c_v, cc);   // all threads (no branch before the state loads)
+  tap_v.load(x_row, conv_w, cs_row, c_v, cc);
 
   // raw gates (given, or the a / b projections they are derived from)
   GateRaw<T> graw{};
@@ -145,7 +152,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
   TS* S = state + ((int64_t)b * hv + h) * kD * kD;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(S, (short)0, kD * kD * (int)sizeof(TS), 0x00020000);
   const uint32_t voff = (uint32_t)(rg * kD + 4 * cg) * sizeof(TS);
-  auto load_row = [&](int m) { return state_buf_load4<TS>(rs, voff, (uint32_t)(8 * m * kD * sizeof(TS))); };
+  auto load_row = [&](int m) { return state_buf_load4<TS>(rs, voff, (uint32_t)(kRowGroups * m * kD * sizeof(TS))); };
   f32x4_t sreg[kRowsPerThread];
 #pragma unroll
   for (int m = 0; m < kWindow; ++m) sreg[m] = load_row(m);
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
     for (int e = 0; e < 4; ++e) a[e] = av;
   }
 
-  {  // q / k are shifted here only when this head is their sole reader
+  if (tid < 2 * kD) {  // q / k are shifted here only when this head is their sole reader
     const float y = tap_qk.finish(cs_row, c_qk, cc, act, ratio == 1);
     if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
   }
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
 #pragma unroll
   for (int m = 0; m < kRowsPerThread; ++m) {
     if (m + kWindow < kRowsPerThread) sreg[m + kWindow] = load_row(m + kWindow);
-    const int row = rg + 8 * m;
+    const int row = rg + kRowGroups * m;
     float pk = 0.0f, pq = 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -208,7 +215,7 @@ __global__ __launch_bounds__(kGroup, 8) void decode_step_kernel(
     if (cg == 0) s_o[row] = fmaf(u, kq, pq);
 #pragma unroll
     for (int e = 0; e < 4; ++e) sreg[m][e] = fmaf(u, kcol[e], sreg[m][e]);
-    state_buf_store4<TS>(rs, voff, (uint32_t)(8 * m * kD * sizeof(TS)), sreg[m]);
+    state_buf_store4<TS>(rs, voff, (uint32_t)(kRowGroups * m * kD * sizeof(TS)), sreg[m]);
   }
   __syncthreads();
 
@@ -247,7 +254,7 @@ template <typename T, typename To, typename TS, bool kPC>
 hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void* conv_state,
                         const Gates& gt, const void* z, const float* norm_w,
                         void* state, void* out, int b, hipStream_t s) {
-  hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC>), dim3(b * d.hv), dim3(kGroup), 0, s,
+  hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC>), dim3(b * d.hv), dim3(kStepThreads), 0, s,
                      static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,
                      static_cast<const T*>(z), norm_w, static_cast<TS*>(state),
                      static_cast<To*>(out), d.hk, d.hv, d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
