@@ -99,9 +99,9 @@ def time_calls(fn, n_sets, steps, warmup):
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 214.0e6 + 206.0e6          # both launches of a step
-PREFILL_S4096_TRAFFIC_BYTES = 455.9e6 + 328.6e6    # gdn_prefill, all its kernels
-VARLEN_TRAFFIC_BYTES = 3116.7e6 + 1838.8e6
-KDA_TRAFFIC_BYTES = 3017.4e6 + 683.7e6
+PREFILL_S4096_TRAFFIC_BYTES = 457.9e6 + 333.8e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 3215.6e6 + 1881.3e6
+KDA_TRAFFIC_BYTES = 3018.0e6 + 683.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
