@@ -36,7 +36,9 @@ namespace {
 
 constexpr int kGroup = 256;             // threads per value head
 constexpr int kD = 128;                 // head_k_dim == head_v_dim
-constexpr int kRows = 16;               // commit: state rows per thread, rows rg + 8 m
+constexpr int kCThreads = 512;          // commit: threads per value head
+constexpr int kCRowGroups = kCThreads / 32;
+constexpr int kCRows = kD / kCRowGroups;  // commit: state rows per thread, rows rg + kCRowGroups m
 constexpr int kVRows = 4;               // verify: state rows per thread, rows rb + 32 m
 
 // Sum over the 8 lanes holding one state row in the verify (lanes 8r .. 8r+7):
@@ -272,9 +274,12 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
 }
 
 // Commit of the recurrent state: sequence b keeps its first clamp(accepted[b],
-// 0, K) verified rows.  One workgroup per (sequence, value head).
+// 0, K) verified rows.  One 512-thread workgroup per (sequence, value head),
+// eight state rows per thread: four share a CU at eight waves per SIMD, so the
+// 3072 heads of a 64-sequence batch run as three full rounds (256-thread
+// workgroups, 96 VGPRs, ran 2.4 rounds).
 template <bool kPerChannel>
-__global__ __launch_bounds__(kGroup) void verify_commit_state_kernel(
+__global__ __launch_bounds__(kCThreads, kCThreads / 64) void verify_commit_state_kernel(
     const int32_t* __restrict__ accepted, const float* __restrict__ g, const float* __restrict__ rec_u,
     const float* __restrict__ rec_k, float* __restrict__ state, int K, int hk, int hv) {
   const int b = blockIdx.x / hv;
@@ -285,10 +290,10 @@ __global__ __launch_bounds__(kGroup) void verify_commit_state_kernel(
   const int gt = threadIdx.x;
   const int cg = gt % 32, rg = gt / 32;
   float* S = state + ((int64_t)b * hv + h) * kD * kD;
-  f32x4_t sreg[kRows];
+  f32x4_t sreg[kCRows];
 #pragma unroll
-  for (int m = 0; m < kRows; ++m)
-    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  for (int m = 0; m < kCRows; ++m)
+    sreg[m] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(S + (rg + kCRowGroups * m) * kD + 4 * cg));
   for (int t = 0; t < c; ++t) {
     const int64_t row_t = (int64_t)b * K + t;
     float a[4];
@@ -304,8 +309,8 @@ __global__ __launch_bounds__(kGroup) void verify_commit_state_kernel(
     const f32x4_t kcol = *reinterpret_cast<const f32x4_t*>(rec_k + (row_t * hk + kh) * kD + 4 * cg);
     const float* u_in = rec_u + (row_t * hv + h) * kD;
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) {
-      const float u = u_in[rg + 8 * m];
+    for (int m = 0; m < kCRows; ++m) {
+      const float u = u_in[rg + kCRowGroups * m];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sreg[m][e] *= a[e];
@@ -314,8 +319,8 @@ __global__ __launch_bounds__(kGroup) void verify_commit_state_kernel(
     }
   }
 #pragma unroll
-  for (int m = 0; m < kRows; ++m)
-    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + 8 * m) * kD + 4 * cg));
+  for (int m = 0; m < kCRows; ++m)
+    __builtin_nontemporal_store(sreg[m], reinterpret_cast<f32x4_t*>(S + (rg + kCRowGroups * m) * kD + 4 * cg));
 }
 
 // Commit of the conv state: the last three inputs of (the state's rows, x rows
@@ -389,10 +394,10 @@ hipError_t launch_verify_commit(const Dims& d, bool bf16, const int32_t* accepte
   const float* rec_u = static_cast<const float*>(ws);
   const float* rec_k = rec_u + (size_t)b * k * d.hv * d.dv;
   if (d.per_channel)
-    hipLaunchKernelGGL(verify_commit_state_kernel<true>, dim3(b * d.hv), dim3(kGroup), 0, s, accepted, g, rec_u,
+    hipLaunchKernelGGL(verify_commit_state_kernel<true>, dim3(b * d.hv), dim3(kCThreads), 0, s, accepted, g, rec_u,
                        rec_k, state, k, d.hk, d.hv);
   else
-    hipLaunchKernelGGL(verify_commit_state_kernel<false>, dim3(b * d.hv), dim3(kGroup), 0, s, accepted, g, rec_u,
+    hipLaunchKernelGGL(verify_commit_state_kernel<false>, dim3(b * d.hv), dim3(kCThreads), 0, s, accepted, g, rec_u,
                        rec_k, state, k, d.hk, d.hv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
