@@ -161,6 +161,54 @@ def _cu_host(cu: torch.Tensor, cu_host) -> ctypes.Array:
     return (ctypes.c_int32 * len(vals))(*vals)
 
 
+_F32 = (torch.float32,)
+_ACT = (torch.bfloat16, torch.float32)
+
+
+def _need(t: Optional[torch.Tensor], name: str, dtypes, shape=None, contiguous: bool = True) -> None:
+    """Raise ValueError unless t (when given) has one of dtypes, the given shape and is
+    contiguous: the C ABI takes bare pointers and cannot check any of this itself."""
+    if t is None:
+        return
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_rows(t: torch.Tensor, name: str, dtypes, rows: int, width: int) -> None:
+    """A [rows, ...] tensor (row stride free) whose rows hold `width` elements."""
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if t.dim() < 2 or t.shape[0] != rows or math.prod(t.shape[1:]) != width:
+        raise ValueError(f"{name} must be [{rows}, {width}] (rows of {width} elements), got {tuple(t.shape)}")
+
+
+def _need_gates(g, beta, lead, cfg: "GDNConfig", name: str = "") -> None:
+    """g [*lead, Hv] (or [*lead, Hv, dk] with per-key-channel decay) and beta [*lead, Hv], fp32."""
+    hv = cfg.num_v_heads
+    gshape = (*lead, hv, cfg.head_k_dim) if cfg.decay_per_key_channel else (*lead, hv)
+    _need(g, name + "g", _F32, gshape)
+    _need(beta, name + "beta", _F32, (*lead, hv))
+
+
+def _need_ab(ab, lead, act_dtype, cfg: "GDNConfig") -> None:
+    if ab is None:
+        return
+    a, b, A_log, dt_bias = ab
+    hv = cfg.num_v_heads
+    _need(a, "a", (act_dtype,), (*lead, hv))
+    _need(b, "b", (act_dtype,), (*lead, hv))
+    _need(A_log, "A_log", _F32, (hv,))
+    _need(dt_bias, "dt_bias", _F32, (hv,))
+
+
+def _state_shape(n: int, cfg: "GDNConfig"):
+    return (n, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim)
+
+
 def conv1d_prefill(x: torch.Tensor, w: torch.Tensor, cu: torch.Tensor, *, cu_host=None,
                    conv_state_in: Optional[torch.Tensor] = None,
                    conv_state_out: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
@@ -169,8 +217,15 @@ def conv1d_prefill(x: torch.Tensor, w: torch.Tensor, cu: torch.Tensor, *, cu_hos
     cfg = cfg or config()
     T = x.shape[0]
     N = cu.numel() - 1
+    Cc = cfg.conv_channels
     if y is None:
-        y = torch.empty((T, cfg.conv_channels), dtype=x.dtype, device=x.device)
+        y = torch.empty((T, Cc), dtype=x.dtype, device=x.device)
+    _need_rows(x, "x", _ACT, T, Cc)
+    _need_rows(y, "y", (x.dtype,), T, Cc)
+    _need(w, "conv weight", _F32, (Cc, cfg.conv_width))
+    _need(cu, "cu_seqlens", (torch.int32,), (N + 1,))
+    _need(conv_state_in, "conv_state_in", (x.dtype,), (N, cfg.conv_width - 1, Cc))
+    _need(conv_state_out, "conv_state_out", (x.dtype,), (N, cfg.conv_width - 1, Cc))
     hc = _cu_host(cu, cu_host)
     _check("gdn_conv1d_prefill", load_library().gdn_conv1d_prefill(
         ctypes.byref(cfg), _dtype(x), _ptr(x), _row_stride(x), _ptr(w), _ptr(conv_state_in),
@@ -183,8 +238,13 @@ def conv1d_step(x: torch.Tensor, w: torch.Tensor, conv_state: torch.Tensor, *,
     """x [B, Cc], conv_state [B, 3, Cc] (updated in place) -> y [B, Cc]."""
     cfg = cfg or config()
     B = x.shape[0]
+    Cc = cfg.conv_channels
     if y is None:
-        y = torch.empty((B, cfg.conv_channels), dtype=x.dtype, device=x.device)
+        y = torch.empty((B, Cc), dtype=x.dtype, device=x.device)
+    _need_rows(x, "x", _ACT, B, Cc)
+    _need_rows(y, "y", (x.dtype,), B, Cc)
+    _need(w, "conv weight", _F32, (Cc, cfg.conv_width))
+    _need(conv_state, "conv_state", (x.dtype,), (B, cfg.conv_width - 1, Cc))
     _check("gdn_conv1d_step", load_library().gdn_conv1d_step(
         ctypes.byref(cfg), _dtype(x), _ptr(x), _row_stride(x), _ptr(w), _ptr(conv_state), _ptr(y),
         _row_stride(y), B, _stream()))
@@ -224,6 +284,10 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     cfg = cfg or config()
     T = q.shape[0]
     N = cu.numel() - 1
+    hk, hv = cfg.num_k_heads, cfg.num_v_heads
+    _need_rows(q, "q", _ACT, T, hk * cfg.head_k_dim)
+    _need_rows(k, "k", (q.dtype,), T, hk * cfg.head_k_dim)
+    _need_rows(v, "v", (q.dtype,), T, hv * cfg.head_v_dim)
     qs, ks = _row_stride(q), _row_stride(k)
     if qs != ks:
         raise ValueError("q and k must share a row stride")
@@ -233,9 +297,16 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
     if final_state is None:
         final_state = torch.empty((N, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim),
                                   dtype=torch.float32, device=q.device)
+    _need(cu, "cu_seqlens", (torch.int32,), (N + 1,))
+    _need_gates(g, beta, (T,), cfg)
+    _need_ab(ab, (T,), q.dtype, cfg)
+    _need(initial_state, "initial_state", _F32, _state_shape(N, cfg))
+    _need(final_state, "final_state", _F32, _state_shape(N, cfg))
+    _need(out, "out", _ACT, (T, hv, cfg.head_v_dim))
     need = chunk_prefill_workspace_size(N, T, cfg)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace", (torch.uint8,))
     hc = _cu_host(cu, cu_host)
     gates, derived = _gate_args(g, beta, ab)
     name = "gdn_chunk_prefill_ab" if derived else "gdn_chunk_prefill"
@@ -254,9 +325,11 @@ def gated_rmsnorm(o: torch.Tensor, z: torch.Tensor, w: torch.Tensor, *,
     rows = o.shape[0]
     if out is None:
         out = torch.empty(o.shape, dtype=out_dtype or o.dtype, device=o.device)
-    for t in (o, z, out):
-        if not t.is_contiguous():
-            raise ValueError("gated_rmsnorm tensors must be contiguous")
+    vshape = (rows, cfg.num_v_heads, cfg.head_v_dim)
+    _need(o, "o", _ACT, vshape)
+    _need(z, "z", _ACT, vshape)
+    _need(out, "out", _ACT, vshape)
+    _need(w, "norm weight", _F32, (cfg.head_v_dim,))
     _check("gdn_gated_rmsnorm", load_library().gdn_gated_rmsnorm(
         ctypes.byref(cfg), _dtype(o), _dtype(z), _dtype(out), _ptr(o), _ptr(z), _ptr(w), _ptr(out),
         rows, _stream()))
@@ -292,9 +365,20 @@ def prefill(x: torch.Tensor, conv_w: torch.Tensor, cu: torch.Tensor, g: Optional
     if final_state is None:
         final_state = torch.empty((N, cfg.num_v_heads, cfg.head_v_dim, cfg.head_k_dim),
                                   dtype=torch.float32, device=x.device)
-    for t in (g, beta, z, out):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("prefill g, beta, z and out must be contiguous")
+    Cc, hv = cfg.conv_channels, cfg.num_v_heads
+    _need_rows(x, "x", _ACT, T, Cc)
+    _need(conv_w, "conv weight", _F32, (Cc, cfg.conv_width))
+    _need(cu, "cu_seqlens", (torch.int32,), (N + 1,))
+    _need(conv_state_in, "conv_state_in", (x.dtype,), (N, cfg.conv_width - 1, Cc))
+    _need(conv_state_out, "conv_state_out", (x.dtype,), (N, cfg.conv_width - 1, Cc))
+    _need_gates(g, beta, (T,), cfg)
+    _need_ab(ab, (T,), x.dtype, cfg)
+    _need(z, "z", (x.dtype,), (T, hv, cfg.head_v_dim))
+    _need(norm_w, "norm weight", _F32, (cfg.head_v_dim,))
+    _need(initial_state, "initial_state", _F32, _state_shape(N, cfg))
+    _need(final_state, "final_state", _F32, _state_shape(N, cfg))
+    _need(out, "out", _ACT, (T, hv, cfg.head_v_dim))
+    _need(workspace, "workspace", (torch.uint8,))
     if workspace is None:
         workspace = torch.empty(prefill_workspace_size(N, T, x.dtype, cfg), dtype=torch.uint8,
                                 device=x.device)
@@ -320,9 +404,16 @@ def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
     B = x.shape[0]
     if out is None:
         out = torch.empty((B, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype, device=x.device)
-    for t in (x, conv_state, g, beta, z, state, out):
-        if t is not None and not t.is_contiguous():
-            raise ValueError("decode_step tensors must be contiguous")
+    Cc, hv = cfg.conv_channels, cfg.num_v_heads
+    _need(x, "x", _ACT, (B, Cc))
+    _need(conv_w, "conv weight", _F32, (Cc, cfg.conv_width))
+    _need(conv_state, "conv_state", (x.dtype,), (B, cfg.conv_width - 1, Cc))
+    _need_gates(g, beta, (B,), cfg)
+    _need_ab(ab, (B,), x.dtype, cfg)
+    _need(z, "z", (x.dtype,), (B, hv, cfg.head_v_dim))
+    _need(norm_w, "norm weight", _F32, (cfg.head_v_dim,))
+    _need(state, "state", (torch.float32, torch.float16), _state_shape(B, cfg))
+    _need(out, "out", _ACT, (B, hv, cfg.head_v_dim))
     gates, derived = _gate_args(g, beta, ab)
     if state.dtype == torch.float16:
         if derived:
@@ -338,8 +429,9 @@ def decode_step(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor,
 
 def state_convert(src: torch.Tensor, dtype: torch.dtype) -> torch.Tensor:
     """A recurrent state widened (fp16 -> fp32) or narrowed (fp32 -> fp16, round to nearest even)."""
-    if not src.is_contiguous():
-        raise ValueError("state_convert needs a contiguous state")
+    _need(src, "state", (torch.float32, torch.float16))
+    if dtype not in (torch.float32, torch.float16) or dtype == src.dtype:
+        raise ValueError("state_convert converts between float32 and float16")
     dst = torch.empty(src.shape, dtype=dtype, device=src.device)
     _check("gdn_state_convert", load_library().gdn_state_convert(
         _ptr(src), _dtype(src), _ptr(dst), _dtype(dst), src.numel(), _stream()))
@@ -365,9 +457,16 @@ def verify(x: torch.Tensor, conv_w: torch.Tensor, conv_state: torch.Tensor, g: t
     B, K = x.shape[0], x.shape[1]
     if out is None:
         out = torch.empty((B, K, cfg.num_v_heads, cfg.head_v_dim), dtype=out_dtype or x.dtype, device=x.device)
-    for t in (x, conv_state, g, beta, z, state, out):
-        if not t.is_contiguous():
-            raise ValueError("verify tensors must be contiguous")
+    Cc, hv = cfg.conv_channels, cfg.num_v_heads
+    _need(x, "x", _ACT, (B, K, Cc))
+    _need(conv_w, "conv weight", _F32, (Cc, cfg.conv_width))
+    _need(conv_state, "conv_state", (x.dtype,), (B, cfg.conv_width - 1, Cc))
+    _need_gates(g, beta, (B, K), cfg)
+    _need(z, "z", (x.dtype,), (B, K, hv, cfg.head_v_dim))
+    _need(norm_w, "norm weight", _F32, (cfg.head_v_dim,))
+    _need(state, "state", _F32, _state_shape(B, cfg))
+    _need(out, "out", _ACT, (B, K, hv, cfg.head_v_dim))
+    _need(workspace, "workspace", (torch.uint8,))
     if workspace is None:
         workspace = torch.empty(verify_workspace_size(B, K, cfg), dtype=torch.uint8, device=x.device)
     _check("gdn_verify", load_library().gdn_verify(
@@ -385,6 +484,13 @@ def verify_commit(accepted: torch.Tensor, x: torch.Tensor, g: torch.Tensor, conv
     B, K = x.shape[0], x.shape[1]
     if accepted.dtype != torch.int32 or accepted.numel() != B:
         raise ValueError("accepted must be an int32 tensor of one entry per sequence")
+    Cc = cfg.conv_channels
+    _need(accepted, "accepted", (torch.int32,))
+    _need(x, "x", _ACT, (B, K, Cc))
+    _need_gates(g, None, (B, K), cfg)
+    _need(conv_state, "conv_state", (x.dtype,), (B, cfg.conv_width - 1, Cc))
+    _need(state, "state", _F32, _state_shape(B, cfg))
+    _need(workspace, "workspace", (torch.uint8,))
     _check("gdn_verify_commit", load_library().gdn_verify_commit(
         ctypes.byref(cfg), _dtype(x), _ptr(accepted), _ptr(x), _ptr(g), _ptr(conv_state), _ptr(state), B, K,
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))

@@ -318,7 +318,10 @@ static gdn_status_t decode_step_checked(const gdn_config_t* cfg, gdn_dtype_t dty
   gdn_status_t st = resolve(cfg, &d);
   if (st != GDN_OK) return st;
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return GDN_ERR_UNSUPPORTED;
-  if (B < 0 || B > 65535 * 64) return GDN_ERR_INVALID_ARG;
+  // the q / k conv-state shift that follows the step (Hk < Hv) puts the
+  // sequences on grid.y: checked here so that a refused launch can never leave
+  // a half-applied step behind
+  if (B < 0 || B > 65535) return GDN_ERR_INVALID_ARG;
   if ((int64_t)B * d.hv > INT32_MAX) return GDN_ERR_INVALID_ARG;   // one workgroup per (sequence, value head)
   st = check_gates(d, gt, B > 0);
   if (st != GDN_OK) return st;

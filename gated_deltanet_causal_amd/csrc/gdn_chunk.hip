@@ -377,20 +377,22 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
 
 // Operand fragment of X[row][c] = raw[row][c] * rs[row] * exp(sgn * (gam[row][c] - ref[c]))
 // (ref = 0 when null), rows row0.., columns k0.. in the operand lane layout, split into
-// hi/lo bf16 (fp32: hi only).  raw k-contiguous (pitch), gam fp32 (gpitch).
-template <bool F32>
-__device__ __forceinline__ void decayed_frag(const typename Ops<F32>::E* raw, int pitch, const float* gam,
-                                             int gpitch, const float* ref, const float* rs, int row0, int k0,
+// hi/lo bf16 (fp32: hi only).  raw k-contiguous (pitch), gam (gpitch) fp32, or fp64 on
+// the fp32 path, where the difference is then formed without cancellation.
+template <bool F32, typename GT = float>
+__device__ __forceinline__ void decayed_frag(const typename Ops<F32>::E* raw, int pitch, const GT* gam,
+                                             int gpitch, const GT* ref, const float* rs, int row0, int k0,
                                              float sgn, typename Ops<F32>::F& hi, typename Ops<F32>::F& lo) {
   const int l = threadIdx.x % kWave;
   const int r = row0 + (l & 15);
   const int c0 = k0 + Ops<F32>::kEpl * (l >> 4);
   const float s = rs[r];
   if constexpr (F32) {
-    const float e = gam[r * gpitch + c0] - (ref ? ref[c0] : 0.0f);
+    const float e = (float)(gam[r * gpitch + c0] - (ref ? ref[c0] : GT(0)));
     hi = raw[r * pitch + c0] * s * __expf(sgn * e);
     lo = 0.0f;
   } else {
+    static_assert(sizeof(GT) == sizeof(float), "bf16 operands take fp32 log decays");
     const u32x4_t u = *reinterpret_cast<const u32x4_t*>(raw + r * pitch + c0);
     const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0);
     const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0 + 4);
@@ -425,13 +427,21 @@ __device__ __forceinline__ f32x4_t mma3(typename Ops<F32>::F ah, typename Ops<F3
 
 // ---------------------------------------------------------------------------
 // intra, per-key-channel decay: per (chunk, value head).  With gam[r][c] the
-// within-chunk cumulative log decay of channel c and a reference token b in
-// the middle of the chunk,
+// within-chunk cumulative log decay of channel c (non-increasing in r, since
+// g <= 0), each 16x16 tile (row tile i, column tile n <= i) of
 //   A[r][j]  = beta_r sum_c (khat_r[c] e^{gam_r[c]-gam_b[c]}) (khat_j[c] e^{gam_b[c]-gam_j[c]})   j < r
 //   Pt[r][j] =        sum_c (qtil_r[c] e^{gam_r[c]-gam_b[c]}) (khat_j[c] e^{gam_b[c]-gam_j[c]})   j <= r
-// so every factor is e^{(sum of at most half a chunk of log decays)}; the
-// operands are formed in registers from raw K / Q and gam, split hi/lo.
+// is one MFMA product over channels with its own reference token b:
+//   n < i  b = 16 i, the first row of the later tile: r >= b > j, so both
+//          factors are e^{<= 0} for any decay (underflow only where the exact
+//          product is below the smallest normal);
+//   n = i  b = 16 i + 8: a factor is e^{+-(at most 8 tokens of log decay)}.
+//          Where some channel of the tile decays by more than kDiagLim over
+//          those 8 tokens (|g| > ~10 per token sustained), the tile is
+//          instead summed element by element with e^{gam_r - gam_j} <= 1.
+// The operands are formed in registers from raw K / Q and gam, split hi/lo.
 // ---------------------------------------------------------------------------
+constexpr float kDiagLim = 80.0f;   // largest exponent of a diagonal-tile factor (e^80 ~ 5.5e34)
 template <bool F32, typename Tin>
 __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
@@ -441,21 +451,23 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   using E = typename O::E;
   using F = typename O::F;
   constexpr int kPitch = kD + O::kPadK;
-  constexpr int kGP = kD + 4;        // gam pitch (fp32)
+  // cumulative log decays: fp32, or fp64 on the fp32 path (a difference of two
+  // sums taken after a strong decay would otherwise lose ~|gam| 2^-24 absolute)
+  using GT = std::conditional_t<F32, double, float>;
+  constexpr int kGP = kD + 4;        // gam pitch (elements)
   constexpr int kAP = kC + 1;
-  constexpr int kPhase1 = 2 * kC * kPitch * (int)sizeof(E) + kC * kGP * (int)sizeof(float);
+  constexpr int kPhase1 = 2 * kC * kPitch * (int)sizeof(E) + kC * kGP * (int)sizeof(GT);
   constexpr int kScratchBytes = 3 * kC * kAP * (int)sizeof(float);
   __shared__ __attribute__((aligned(16))) uint8_t s_pool[kPhase1 > kScratchBytes ? kPhase1 : kScratchBytes];
   E* sK = reinterpret_cast<E*>(s_pool);
   E* sQ = sK + kC * kPitch;
-  float* sGam = reinterpret_cast<float*>(s_pool + 2 * kC * kPitch * sizeof(E));
+  GT* sGam = reinterpret_cast<GT*>(s_pool + 2 * kC * kPitch * sizeof(E));
   float* sA = reinterpret_cast<float*>(s_pool);
   float* sP = sA + kC * kAP;
   float* sT = sP + kC * kAP;
   __shared__ float sM[3 * 16 * 17];
   __shared__ float s_rk[kC], s_rq[kC], s_beta[kC];
-  __shared__ __attribute__((aligned(16))) float s_ref[kD];
-  __shared__ float s_tot[kD];
+  __shared__ GT s_tot[kD];
 
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int c = blockIdx.x;
@@ -472,7 +484,12 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     const int r = p / (kD / 4), c4 = 4 * (p % (kD / 4));
     f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
     if (r < L) gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)(t0 + r) * hv + h) * kD + c4);
-    *reinterpret_cast<f32x4_t*>(sGam + r * kGP + c4) = gv;
+    if constexpr (F32) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sGam[r * kGP + c4 + e] = gv[e];
+    } else {
+      *reinterpret_cast<f32x4_t*>(sGam + r * kGP + c4) = gv;
+    }
   }
   if (tid < kC) s_beta[tid] = tid < L ? beta[(int64_t)(t0 + tid) * hv + h] : 0.0f;
   __syncthreads();
@@ -496,21 +513,38 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   }
   {  // per-channel cumulative sum over the chunk: thread (channel, half of the rows)
     const int ch = tid % kD, half = tid / kD;
-    float v[kC / 2];
+    GT v[kC / 2];
 #pragma unroll
     for (int r = 0; r < kC / 2; ++r) v[r] = sGam[(half * (kC / 2) + r) * kGP + ch];
 #pragma unroll
     for (int r = 1; r < kC / 2; ++r) v[r] += v[r - 1];
     if (half == 0) s_tot[ch] = v[kC / 2 - 1];
     __syncthreads();
-    const float off = half ? s_tot[ch] : 0.0f;
+    const GT off = half ? s_tot[ch] : GT(0);
 #pragma unroll
     for (int r = 0; r < kC / 2; ++r) sGam[(half * (kC / 2) + r) * kGP + ch] = v[r] + off;
   }
   __syncthreads();
-  const int b_ref = (L - 1) / 2;
-  if (tid < kD) s_ref[tid] = sGam[b_ref * kGP + tid];
-  __syncthreads();
+  // references of this wave's row tile (rows past L carry gam_{L-1}: g is zero there)
+  const GT* ref_off = sGam + 16 * wave * kGP;
+  const GT* ref_dia = sGam + (16 * wave + 8) * kGP;
+  // the diagonal tile's factors stay finite when no channel decays by more than
+  // kDiagLim between the tile's first row and b or between b and its last row.
+  // On the fp32 path the tile is always summed element by element: a factor
+  // e^{+x} times one e^{-y} carries ~(x + y) 2^-24 of relative error from the
+  // exponent's rounding, above that path's bound for strong decays.
+  bool dia_mfma = !F32;
+  if constexpr (!F32) {
+    const int lane = tid % kWave;
+    float worst = 0.0f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int ch = lane + kWave * h2;
+      const float gb = ref_dia[ch];
+      worst = fmaxf(worst, fmaxf(fabsf(ref_off[ch] - gb), fabsf(gb - sGam[(16 * wave + 15) * kGP + ch])));
+    }
+    dia_mfma = !__any(worst > kDiagLim);
+  }
 
   // decayed Gram tiles of row tile `wave`: G~ = Ka Kb^T, H~ = Qa Kb^T
   f32x4_t accG[4], accH[4];
@@ -521,17 +555,65 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   }
   for (int ks = 0; ks < kD; ks += O::kKs) {
     F kah, kal, qah, qal;
-    decayed_frag<F32>(sK, kPitch, sGam, kGP, s_ref, s_rk, 16 * wave, ks, 1.0f, kah, kal);
-    decayed_frag<F32>(sQ, kPitch, sGam, kGP, s_ref, s_rq, 16 * wave, ks, 1.0f, qah, qal);
+    if (wave > 0) {   // row side of the tiles left of the diagonal (reference 16 wave)
+      decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * wave, ks, 1.0f, kah, kal);
+      decayed_frag<F32, GT>(sQ, kPitch, sGam, kGP, ref_off, s_rq, 16 * wave, ks, 1.0f, qah, qal);
+    }
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (nt <= wave) {
+    for (int nt = 0; nt < 3; ++nt) {
+      if (nt < wave) {
         F bh, bl;
-        decayed_frag<F32>(sK, kPitch, sGam, kGP, s_ref, s_rk, 16 * nt, ks, -1.0f, bh, bl);
+        decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * nt, ks, -1.0f, bh, bl);
         accG[nt] = mma3<F32>(kah, kal, bh, bl, accG[nt]);
         accH[nt] = mma3<F32>(qah, qal, bh, bl, accH[nt]);
       }
     }
+    if (dia_mfma) {   // the diagonal tile (reference 16 wave + 8)
+      F bh, bl;
+      decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_dia, s_rk, 16 * wave, ks, 1.0f, kah, kal);
+      decayed_frag<F32, GT>(sQ, kPitch, sGam, kGP, ref_dia, s_rq, 16 * wave, ks, 1.0f, qah, qal);
+      decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_dia, s_rk, 16 * wave, ks, -1.0f, bh, bl);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        if (nt == wave) {
+          accG[nt] = mma3<F32>(kah, kal, bh, bl, accG[nt]);
+          accH[nt] = mma3<F32>(qah, qal, bh, bl, accH[nt]);
+        }
+      }
+    }
+  }
+  if (!dia_mfma) {
+    // the diagonal tile element by element, e^{gam_r - gam_j} <= 1 per channel:
+    // lane (g, m) holds rows 16 wave + 4 g + e, column 16 wave + m (j <= r only)
+    const int lane = tid % kWave;
+    const int j = 16 * wave + (lane & 15);
+    f32x4_t gd = {0.f, 0.f, 0.f, 0.f}, hd = {0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < kD; ++ch) {
+      float kj;
+      if constexpr (F32) kj = sK[j * kPitch + ch];
+      else kj = bf16_bits_to_f32(sK[j * kPitch + ch]);
+      const GT gj = sGam[j * kGP + ch];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * wave + 4 * (lane >> 4) + e;
+        float kr, qr;
+        if constexpr (F32) { kr = sK[r * kPitch + ch]; qr = sQ[r * kPitch + ch]; }
+        else { kr = bf16_bits_to_f32(sK[r * kPitch + ch]); qr = bf16_bits_to_f32(sQ[r * kPitch + ch]); }
+        const float w = j <= r ? kj * __expf((float)(sGam[r * kGP + ch] - gj)) : 0.0f;
+        gd[e] = fmaf(kr, w, gd[e]);
+        hd[e] = fmaf(qr, w, hd[e]);
+      }
+    }
+    const float rkj = s_rk[j];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * wave + 4 * (lane >> 4) + e;
+      gd[e] *= s_rk[r] * rkj;
+      hd[e] *= s_rq[r] * rkj;
+    }
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+      if (nt == wave) { accG[nt] = gd; accH[nt] = hd; }
   }
   __syncthreads();   // the pool's K / Q / gam are dead from here on
   {
@@ -564,7 +646,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
 // intra: per (chunk, key head) -> Tt, Pt, vectors for each of its value heads
 // ---------------------------------------------------------------------------
 template <bool F32, typename Tin, bool kPairK>
-__global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
+__global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     Gates gates, const int32_t* __restrict__ cu,
     int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
@@ -593,7 +675,11 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
                 "the pool holds the scratch and the blocks");
   float* sM = reinterpret_cast<float*>(s_pool + kScratchBytes);
   __shared__ __attribute__((aligned(16))) float s_rk[kC], s_rq[kC];
-  __shared__ __attribute__((aligned(16))) float s_gam[2][kC], s_beta[2][kC];   // per value head, double-buffered
+  // cumulative log decay per value head (double-buffered): fp64 on the fp32 path,
+  // whose factors e^{gam_r - gam_j} would otherwise lose ~|gam| 2^-24 to cancellation
+  using GT = std::conditional_t<F32, double, float>;
+  __shared__ __attribute__((aligned(16))) GT s_gam[2][kC];
+  __shared__ __attribute__((aligned(16))) float s_beta[2][kC];
 
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int c = blockIdx.x;
@@ -612,10 +698,11 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
     gv = bv = 0.0f;
     if (lane < L) gate_pair<Tin>(gates, t0 + lane, hv, h, gv, bv);
   };
-  auto gb_store = [&](int buf, float gv, float bv) {
+  auto gb_store = [&](int buf, float gv_in, float bv) {
+    GT gv = gv_in;
 #pragma unroll
     for (int o = 1; o < kWave; o <<= 1) {
-      const float up = __shfl_up(gv, o, kWave);
+      const GT up = __shfl_up(gv, o, kWave);
       if (lane >= o) gv += up;
     }
     s_gam[buf][lane] = gv;
@@ -707,14 +794,16 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
     const int h = kh * ratio + hh;
     const int buf = hh & 1;
     if (wave == 0 && hh + 1 < ratio) gb_load(hh + 1, gv_next, bv_next);   // lands during this head
-    const float* gam = s_gam[buf];
+    const GT* gam = s_gam[buf];
     const float* bet = s_beta[buf];
 
     uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
     // A (strictly lower) and Pt (lower incl. diagonal) from the Gram tiles
     {
       const int r0 = 16 * wave + 4 * (lane >> 4);
-      const f32x4_t gr = *reinterpret_cast<const f32x4_t*>(gam + r0);
+      GT gr[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gr[e] = gam[r0 + e];
       const f32x4_t br = *reinterpret_cast<const f32x4_t*>(bet + r0);
       const f32x4_t rkr = *reinterpret_cast<const f32x4_t*>(s_rk + r0);
       const f32x4_t rqr = *reinterpret_cast<const f32x4_t*>(s_rq + r0);
@@ -722,11 +811,12 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
       for (int nt = 0; nt < 4; ++nt) {
         if (nt <= wave) {
           const int j = 16 * nt + (lane & 15);
-          const float gj = gam[j], rkj = s_rk[j];
+          const GT gj = gam[j];
+          const float rkj = s_rk[j];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = r0 + e;
-            const float dec = __expf(gr[e] - gj);
+            const float dec = __expf((float)(gr[e] - gj));
             const float a = br[e] * dec * rkr[e] * rkj * accG[nt][e];
             sA[r * kAP + j] = j < r ? a : 0.0f;
             if constexpr (!kPairK) {
@@ -741,6 +831,7 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
       // Pt fragments (mt = wave, ks) straight from the H^T tiles (2 ks, wave) and
       // (2 ks + 1, wave): lane l holds Pt[r][j], r = 16 wave + l%16,
       // j = 16 nt + 4 (l/16) + e (the record's paired-tile k order)
+      static_assert(!kPairK || !F32, "the paired-tile order is the bf16 records'");
       const int r = 16 * wave + (lane & 15);
       const float gr = gam[r], rqr = s_rq[r];
       f32x4_t pv[4];
@@ -777,11 +868,11 @@ __global__ __launch_bounds__(kThreads, kIntraMinWaves) void chunk_intra_kernel(
     // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
     if (tid < kC) {
       float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
-      const float gl = gam[kC - 1];
-      vec[tid] = __expf(gam[tid]) * s_rk[tid];
-      vec[kC + tid] = s_rq[tid] * __expf(gam[tid]);
-      vec[2 * kC + tid] = s_rk[tid] * __expf(gl - gam[tid]);
-      if (tid == 0) vec[3 * kC] = __expf(gl);
+      const GT gl = gam[kC - 1];
+      vec[tid] = __expf((float)gam[tid]) * s_rk[tid];
+      vec[kC + tid] = s_rq[tid] * __expf((float)gam[tid]);
+      vec[2 * kC + tid] = s_rk[tid] * __expf((float)(gl - gam[tid]));
+      if (tid == 0) vec[3 * kC] = __expf((float)gl);
     }
     if (wave == 0 && hh + 1 < ratio) gb_store(buf ^ 1, gv_next, bv_next);
     __syncthreads();   // sA, sP and this head's decay buffer are rewritten next
@@ -880,7 +971,7 @@ template <bool F32, bool kPC>
 __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename Ops<F32>::E* sK,
                                              typename Ops<F32>::E* sKt, typename Ops<F32>::E* sQ, int pitch,
                                              int tpitch, float* sV, int vpitch, float* sGam,
-                                             int gpitch, float* s_vec) {
+                                             int gpitch, float* s_vec, float2* sGLP = nullptr) {
   const int tid = threadIdx.x;
   if constexpr (F32) {
 #pragma unroll
@@ -921,22 +1012,53 @@ __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename
     }
   }
   if constexpr (kPC) {
-    // cumulative log decay per channel: prefix over this thread's 16 rows, then
-    // over the four row blocks of the channel (adjacent lanes)
+    // cumulative log decay per channel.  The products need both gam_t (Y, Z)
+    // and gam_L - gam_t (the update), and one of the two is a difference of
+    // large sums after a strong decay.  Both are therefore summed directly,
+    // each over terms of one sign (the part totals come by shuffle, so nothing
+    // is subtracted), and with p_c the number of rows where |gam_t| <= |gam_L| / 2,
+    // rows t < p_c keep gam_t and the others gam_L - gam_t: the value not kept
+    // is then gam_L minus one of at most half its size, accurate to fp32
+    // rounding.
+    static_assert(F32, "the bf16 per-channel spine commits through stage_commit_pcb");
     const int ch = tid / 4, part = tid % 4;
-    float run[16];
-    run[0] = sg.gv[0];
+    float own = 0.0f;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) run[r] = run[r - 1] + sg.gv[r];
-    float incl = run[15];
+    for (int r = 0; r < 16; ++r) own += sg.gv[r];
+    float excl = 0.0f, later = 0.0f;
 #pragma unroll
-    for (int o = 1; o < 4; o <<= 1) {
-      const float up = __shfl_up(incl, o, 4);
-      if (part >= o) incl += up;
+    for (int o = 0; o < 4; ++o) {
+      const float t_o = __shfl(own, o, 4);
+      if (o < part) excl += t_o;
+      if (o > part) later += t_o;
     }
-    const float excl = incl - run[15];
+    const float tot = (excl + own) + later;
+    int cnt = 0;
+    {
+      float run = excl;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sGam[(16 * part + r) * gpitch + ch] = run[r] + excl;
+      for (int r = 0; r < 16; ++r) {
+        run += sg.gv[r];
+        cnt += fabsf(run) <= 0.5f * fabsf(tot);
+      }
+    }
+    cnt += __shfl_xor(cnt, 1, 4);
+    cnt += __shfl_xor(cnt, 2, 4);
+    {
+      float run = excl;   // gam_t of row 16 part + r
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        run += sg.gv[r];
+        if (16 * part + r < cnt) sGam[(16 * part + r) * gpitch + ch] = run;
+      }
+      float suf = later;  // gam_L - gam_t: the log decays after row 16 part + r
+#pragma unroll
+      for (int r = 15; r >= 0; --r) {
+        if (16 * part + r >= cnt) sGam[(16 * part + r) * gpitch + ch] = suf;
+        suf += sg.gv[r];
+      }
+    }
+    if (part == 0) sGLP[ch] = make_float2(tot, (float)cnt);
     if (tid < 2 * kC) s_vec[tid] = sg.vec;
   } else {
     if (tid < 3 * kC + 1) s_vec[tid] = sg.vec;
@@ -1075,6 +1197,9 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) float sGam[kPCB ? kD : (kPC ? kC * kGP : 1)];   // kPCB: e^{gam_L}
+  // fp32 per-key-channel path: (gam_L, p_c) per channel, p_c the prefix / suffix
+  // switch row (sGam holds gam_t for rows t < p_c, gam_L - gam_t from p_c on)
+  __shared__ float2 sGLP[kPC && F32 ? kD : 1];
   __shared__ __attribute__((aligned(16))) float s_vec[3 * kC + 4];
 
   // Block -> (sequence, key head) group and member (value head of the group,
@@ -1189,7 +1314,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     if constexpr (kPCB)
       stage_commit_pcb(stage, sK, sKl, sQ, sQl, sKt, sKtl, kPitch, kTP, sV, kVP, sGam, s_vec);
     else
-      stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec);
+      stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec, sGLP);
     if (more) issue(std::integral_constant<int, 3>{}, t0 + kC, c + 1);   // K, Q, V, vectors
     __syncthreads();
 
@@ -1205,11 +1330,13 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
         accY = mma3<F32>(frag<F32>(sK, kPitch, 16 * mt, ks), frag<F32>(sKl, kPitch, 16 * mt, ks), bh, bl, accY);
         accZ = mma3<F32>(frag<F32>(sQ, kPitch, 16 * mt, ks), frag<F32>(sQl, kPitch, 16 * mt, ks), bh, bl, accZ);
       } else if constexpr (kPC) {
-        F kh_, kl_, qh_, ql_;
-        decayed_frag<F32>(sK, kPitch, sGam, kGP, nullptr, s_vec, 16 * mt, ks, 1.0f, kh_, kl_);
-        decayed_frag<F32>(sQ, kPitch, sGam, kGP, nullptr, s_vec + kC, 16 * mt, ks, 1.0f, qh_, ql_);
-        accY = mma3<F32>(kh_, kl_, bh, bl, accY);
-        accZ = mma3<F32>(qh_, ql_, bh, bl, accZ);
+        // fp32: A = K rk e^{gam_t}, Q rq e^{gam_t}, gam_t recovered from the split store
+        const int r = 16 * mt + (lane & 15), c0 = ks + (lane >> 4);
+        const float gv = sGam[r * kGP + c0];
+        const float2 lp = sGLP[c0];
+        const float ex = __expf((float)r < lp.y ? gv : lp.x - gv);
+        accY = mma<F32>(sK[r * kPitch + c0] * s_vec[r] * ex, bh, accY);
+        accZ = mma<F32>(sQ[r * kPitch + c0] * s_vec[kC + r] * ex, bh, accZ);
       } else {
         const F ak = frag<F32>(sK, kPitch, 16 * mt, ks);
         const F aq = frag<F32>(sQ, kPitch, 16 * mt, ks);
@@ -1300,8 +1427,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sacc[q2][e] *= __expf(sGam[(L - 1) * kGP + 16 * (nj0 + q2) + 4 * (lane >> 4) + e]);
+          for (int e = 0; e < 4; ++e) sacc[q2][e] *= __expf(sGLP[16 * (nj0 + q2) + 4 * (lane >> 4) + e].x);
       } else {
         const float d = s_vec[3 * kC];
 #pragma unroll
@@ -1321,24 +1447,15 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
             sacc[q2] = mma3<F32>(frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks), frag<F32>(sKtl, kTP, 16 * (nj0 + q2), ks),
                                  bh, bl, sacc[q2]);
           } else if constexpr (kPC) {
-            // A[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam_t[j]}, t = ks + E (l/16) + e
+            // A[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam_t[j]}, t = ks + l/16 (fp32: the
+            // suffix gam_L - gam_t from the split store)
+            static_assert(F32, "the bf16 per-channel update reads the committed K^T operand");
             F ah, al;
-            const int tb = ks + O::kEpl * (lane >> 4);
-            const float gl = sGam[(L - 1) * kGP + j];
-            if constexpr (F32) {
-              ah = sK[tb * kPitch + j] * s_vec[tb] * __expf(gl - sGam[tb * kGP + j]);
-              al = 0.0f;
-            } else {
-              const u32x4_t u = *reinterpret_cast<const u32x4_t*>(sKt + j * kTP + tb);
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float kv = (e & 1) ? __uint_as_float(u[e / 2] & 0xffff0000u) : __uint_as_float(u[e / 2] << 16);
-                __bf16 a_, b_;
-                split_bf16(kv * s_vec[tb + e] * __expf(gl - sGam[(tb + e) * kGP + j]), a_, b_);
-                ah[e] = a_;
-                al[e] = b_;
-              }
-            }
+            const int tb = ks + (lane >> 4);
+            const float gv = sGam[tb * kGP + j];
+            const float2 lp = sGLP[j];
+            ah = sK[tb * kPitch + j] * s_vec[tb] * __expf((float)tb < lp.y ? lp.x - gv : gv);
+            al = 0.0f;
             sacc[q2] = mma3<F32>(ah, al, bh, bl, sacc[q2]);
           } else {
             F a;

@@ -135,6 +135,38 @@ def gen_qkv(seed: int, lengths: List[int], geo: Geometry = Geometry(), *, bf16: 
     return dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in, cu=seqlens_to_cu(lengths))
 
 
+STRONG_DECAY_PATTERNS = ("quarter_m10", "all_m3", "all_m30", "bursts_m30")
+
+
+def strong_channel_decay(g: np.ndarray, pattern: str, seed: int) -> np.ndarray:
+    """A per-key-channel log decay g [T, Hv, dk] with strong decays written in:
+      quarter_m10  g = -10 in a random quarter of each head's channels (the rest as drawn)
+      all_m3       g = -3 everywhere
+      all_m30      g = -30 everywhere (every in-chunk factor between tokens underflows)
+      bursts_m30   g = -30 on 8-token runs (aligned to 8) of random channels, about one run in 8
+    All values stay <= 0, the method's range for g.  A scalar decay g [T, Hv] takes the
+    same patterns with the heads in the place of the channels."""
+    if np.ndim(g) == 2:
+        return strong_channel_decay(np.asarray(g)[:, None, :], pattern, seed)[:, 0, :]
+    rng = np.random.default_rng(seed)
+    g = np.array(g, dtype=np.float32, copy=True)
+    T, hv, dk = g.shape
+    if pattern == "quarter_m10":
+        for h in range(hv):
+            g[:, h, rng.permutation(dk)[: dk // 4]] = -10.0
+    elif pattern == "all_m3":
+        g[:] = -3.0
+    elif pattern == "all_m30":
+        g[:] = -30.0
+    elif pattern == "bursts_m30":
+        runs = (T + 7) // 8
+        hit = rng.random((runs, hv, dk)) < 0.125
+        g[np.repeat(hit, 8, axis=0)[:T]] = -30.0
+    else:
+        raise ValueError(f"unknown pattern {pattern!r}")
+    return g
+
+
 def gen_decode(seed: int, batch: int, geo: Geometry = Geometry(), *, bf16: bool = True,
                per_channel: bool = False, state_sd: float = 0.1) -> Dict[str, np.ndarray]:
     """Inputs for one fused decode step of ``batch`` sequences:

@@ -258,7 +258,7 @@ gdn_status_t gdn_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t dtype, gdn_dtyp
  *   z            [B][Hv][dv];  norm_w fp32 [dv]
  *   state        fp32 [B][Hv][dv][dk], updated in place
  *   out          [B][Hv][dv]
- * B * Hv must not exceed INT32_MAX (GDN_ERR_INVALID_ARG).  When Hk < Hv the
+ * 0 <= B <= 65535, else GDN_ERR_INVALID_ARG before anything is enqueued.  When Hk < Hv the
  * key head's q / k conv-state channels are read by all its value heads, and
  * the step is two launches on the stream: the fused step, then a shift of
  * those channels.

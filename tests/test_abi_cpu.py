@@ -162,6 +162,19 @@ def test_empty_calls_launch_nothing(lib):
                                  None, 0, None) == 0
 
 
+def test_decode_rejects_batches_past_the_shift_grid(lib):
+    """The q / k conv-state shift after the step takes the sequences on grid.y (at most
+    65535): a larger batch is refused before anything is launched, for every decode call."""
+    cfg = _cfg()
+    for fn in (lib.gdn_decode_step, lib.gdn_decode_step_h16):
+        got = fn(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                 FAKE, FAKE, FAKE, FAKE, 65536, None)
+        assert got == gdn.GDN_ERR_INVALID_ARG
+    got = lib.gdn_decode_step_ab(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 65536, None)
+    assert got == gdn.GDN_ERR_INVALID_ARG
+
+
 def test_decode_rejects_grids_past_int32(lib):
     """One workgroup per (sequence, value head): B * Hv must fit a 32-bit grid."""
     cfg = _cfg(num_k_heads=1, num_v_heads=1 << 20)

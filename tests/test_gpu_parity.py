@@ -901,6 +901,38 @@ def test_chunk_prefill_per_channel_varlen(orc):
     check(host(fs), s_ref, TOL_BF16, "per-channel varlen state")
 
 
+@pytest.mark.parametrize("pattern", gi.STRONG_DECAY_PATTERNS)
+@pytest.mark.parametrize("lengths", [[64], [65], [129], [70, 0, 1, 64, 200]],
+                         ids=["T64", "T65", "T129", "varlen"])
+def test_chunk_prefill_per_channel_strong_decay_bf16(orc, pattern, lengths):
+    """Per-key-channel decays far stronger than the workload's (g = -10 in a quarter of the
+    channels, -3 or -30 everywhere, -30 in 8-token bursts): the in-chunk decay factors span
+    e^0 .. e^-1900, single sequence and batched, against the oracle."""
+    geo = gi.Geometry(hk=4, hv=12)
+    d = gi.gen_qkv(470 + 7 * len(lengths) + lengths[0], lengths, geo, per_channel=True)
+    d["g"] = gi.strong_channel_decay(d["g"], pattern, seed=480 + lengths[0])
+    cfg = gdn.config(num_k_heads=4, num_v_heads=12, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"per-channel {pattern} out {lengths}")
+    check(host(fs), s_ref, TOL_BF16, f"per-channel {pattern} state {lengths}")
+
+
+@pytest.mark.parametrize("pattern", gi.STRONG_DECAY_PATTERNS)
+@pytest.mark.parametrize("lengths", [[65], [129, 0, 64, 1]], ids=["T65", "varlen"])
+def test_chunk_prefill_per_channel_strong_decay_fp32(orc, pattern, lengths):
+    geo = gi.Geometry(hk=2, hv=6)
+    d = gi.gen_qkv(490 + lengths[0], lengths, geo, bf16=False, per_channel=True)
+    d["g"] = gi.strong_channel_decay(d["g"], pattern, seed=495 + lengths[0])
+    cfg = gdn.config(num_k_heads=2, num_v_heads=6, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg, bf16=False)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_F32, f"per-channel fp32 {pattern} out {lengths}")
+    check(host(fs), s_ref, TOL_F32, f"per-channel fp32 {pattern} state {lengths}")
+
+
 def test_per_channel_with_equal_channels_matches_scalar_decay():
     """A per-key-channel decay equal across channels runs the same recurrence as the
     scalar-decay path: the two GPU paths agree to the tolerance."""
@@ -928,3 +960,40 @@ def test_kda_h64_s16384_full_size_sampled(orc):
     check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 out (3 heads)")
     check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 state (3 heads)")
     assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
+
+
+def test_kda_h64_s16384_strong_channels(orc):
+    """The long-context per-key-channel workload with g = -10 in a quarter of every head's
+    channels: every output and state element finite, heads 5 and 40 against the oracle."""
+    geo = gi.Geometry(hk=64, hv=64)
+    d = gi.gen_qkv(1015, [16384], geo, per_channel=True)
+    d["g"] = gi.strong_channel_decay(d["g"], "quarter_m10", seed=1016)
+    cfg = gdn.config(num_k_heads=64, num_v_heads=64, decay_per_key_channel=1)
+    o, fs = _run_chunk(d, cfg)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()), "non-finite output"
+    assert bool(torch.isfinite(fs).all()), "non-finite final state"
+    heads = [5, 40]
+    o_ref, s_ref = orc.delta_rule(d["q"][:, heads], d["k"][:, heads], d["v"][:, heads], d["g"][:, heads],
+                                  d["beta"][:, heads], d["cu"], d["state_in"][:, heads])
+    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 strong channels out (2 heads)")
+    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 strong channels state (2 heads)")
+
+
+@pytest.mark.parametrize("pattern", gi.STRONG_DECAY_PATTERNS)
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+def test_chunk_prefill_scalar_strong_decay(orc, pattern, bf16):
+    """Scalar decays g = -10 in a quarter of the heads, -3 or -30 everywhere, -30 in 8-token
+    bursts: single sequence and batched, on the bf16 spines and on the fp32 path (whose
+    within-chunk log decay sums are taken in fp64)."""
+    geo = gi.Geometry(hk=2, hv=6) if not bf16 else gi.Geometry()
+    for lengths in ([130], [129, 0, 64, 1, 70]):
+        d = gi.gen_qkv(2700 + len(lengths), lengths, geo, bf16=bf16)
+        d["g"] = gi.strong_channel_decay(d["g"], pattern, seed=2710 + len(lengths))
+        cfg = gdn.config(num_k_heads=geo.hk, num_v_heads=geo.hv)
+        o, fs = _run_chunk(d, cfg, bf16=bf16)
+        torch.cuda.synchronize()
+        o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+        tol = TOL_BF16 if bf16 else TOL_F32
+        check(host(o), o_ref, tol, f"scalar {pattern} out {lengths}")
+        check(host(fs), s_ref, tol, f"scalar {pattern} state {lengths}")
