@@ -29,7 +29,8 @@ EXPORTS = ("gdn_abi_version", "gdn_status_string", "gdn_config_default", "gdn_co
            "gdn_conv1d_step", "gdn_chunk_prefill_workspace_size", "gdn_chunk_prefill",
            "gdn_chunk_prefill_ab", "gdn_gated_rmsnorm", "gdn_prefill_workspace_size", "gdn_prefill",
            "gdn_prefill_ab", "gdn_decode_step", "gdn_decode_step_ab", "gdn_verify_workspace_size",
-           "gdn_verify", "gdn_verify_commit", "gdn_decode_step_h16", "gdn_state_convert")
+           "gdn_verify", "gdn_verify_commit", "gdn_decode_step_h16", "gdn_state_convert",
+           "gdn_chunk_prefill_noalloc")
 
 
 class GDNError(RuntimeError):
@@ -75,6 +76,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
         "gdn_chunk_prefill_workspace_size": ([cfgp, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
         "gdn_chunk_prefill": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp, vp, vp, vp,
                                i32, i32, vp, vp, vp, sz, vp], ctypes.c_int),
+        "gdn_chunk_prefill_noalloc": ([cfgp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64, vp, vp, vp, vp,
+                                       vp, i32, i32, vp, vp, vp], ctypes.c_int),
         "gdn_gated_rmsnorm": ([cfgp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp, vp, i64, vp], ctypes.c_int),
         "gdn_prefill_workspace_size": ([cfgp, ctypes.c_int, i32, i32, ctypes.POINTER(sz)], ctypes.c_int),
         "gdn_prefill": ([cfgp, ctypes.c_int, ctypes.c_int, vp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -314,6 +317,36 @@ def chunk_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional
         ctypes.byref(cfg), _dtype(q), _dtype(out), _ptr(q), _ptr(k), qs, _ptr(v), _row_stride(v),
         *gates, _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return out, final_state
+
+
+def chunk_prefill_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, cu: torch.Tensor, *, cu_host=None,
+                          initial_state: Optional[torch.Tensor] = None, out: torch.Tensor,
+                          final_state: Optional[torch.Tensor] = None, cfg: Optional[GDNConfig] = None):
+    """chunk_prefill with the library's fixed device scratch as the workspace
+    (gdn_chunk_prefill_noalloc): the caller passes every output, nothing is allocated.
+    Calls that overlap on one GPU race on the scratch."""
+    cfg = cfg or config()
+    T = q.shape[0]
+    N = cu.numel() - 1
+    hk, hv = cfg.num_k_heads, cfg.num_v_heads
+    _need_rows(q, "q", _ACT, T, hk * cfg.head_k_dim)
+    _need_rows(k, "k", (q.dtype,), T, hk * cfg.head_k_dim)
+    _need_rows(v, "v", (q.dtype,), T, hv * cfg.head_v_dim)
+    _need(cu, "cu_seqlens", (torch.int32,), (N + 1,))
+    _need_gates(g, beta, (T,), cfg)
+    _need(initial_state, "initial_state", _F32, _state_shape(N, cfg))
+    _need(final_state, "final_state", _F32, _state_shape(N, cfg))
+    _need(out, "out", _ACT, (T, hv, cfg.head_v_dim))
+    qs, ks = _row_stride(q), _row_stride(k)
+    if qs != ks:
+        raise ValueError("q and k must share a row stride")
+    hc = _cu_host(cu, cu_host)
+    _check("gdn_chunk_prefill_noalloc", load_library().gdn_chunk_prefill_noalloc(
+        ctypes.byref(cfg), _dtype(q), _dtype(out), _ptr(q), _ptr(k), qs, _ptr(v), _row_stride(v),
+        _ptr(g), _ptr(beta), _ptr(initial_state), _ptr(cu), hc, N, T, _ptr(out), _ptr(final_state),
+        _stream()))
     return out, final_state
 
 

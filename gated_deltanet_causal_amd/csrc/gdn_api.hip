@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "gdn.h"
 #include "gdn_launch.h"
 
@@ -343,6 +345,53 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
                                size_t ws_bytes, gdn_stream_t stream) {
   return chunk_prefill_checked(cfg, in_dtype, out_dtype, q, k, qk_stride, v, v_stride, given_gates(g, beta),
                                initial_state, cu_dev, cu_host, N, T, out, final_state, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// gdn_chunk_prefill_noalloc: the chunk workspace in a fixed device array.
+// Each GPU the library runs on holds its own copy of `scratch` from module load
+// until the process ends.  In host code the array's name is not a device
+// address, so its address is looked up once per device (with that device
+// current) and only that pointer is ever handed to the kernels.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[GDN_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+gdn_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+}  // namespace
+
+gdn_status_t gdn_chunk_prefill_noalloc(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                                       gdn_dtype_t out_dtype, const void* q, const void* k,
+                                       int64_t qk_stride, const void* v, int64_t v_stride,
+                                       const float* g, const float* beta, const float* initial_state,
+                                       const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                       int32_t T, void* out, float* final_state, gdn_stream_t stream) {
+  Dims d;
+  gdn_status_t st = resolve(cfg, &d);
+  if (st != GDN_OK) return st;
+  if (N < 0 || T < 0) return GDN_ERR_INVALID_ARG;
+  if (gdn::chunk_workspace_bytes(d, N, T) > (size_t)GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+  if (N == 0) return GDN_OK;
+  void* ws = nullptr;
+  st = scratch_on_current_device(&ws);
+  if (st != GDN_OK) return st;
+  return chunk_prefill_checked(cfg, in_dtype, out_dtype, q, k, qk_stride, v, v_stride, given_gates(g, beta),
+                               initial_state, cu_dev, cu_host, N, T, out, final_state, ws,
+                               (size_t)GDN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 gdn_status_t gdn_chunk_prefill_ab(const gdn_config_t* cfg, gdn_dtype_t in_dtype,

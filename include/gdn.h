@@ -158,6 +158,32 @@ gdn_status_t gdn_chunk_prefill(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
                                size_t ws_bytes, gdn_stream_t stream);
 
 /*
+ * gdn_chunk_prefill for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments without ws / ws_bytes.  The workspace is a fixed device
+ * array of GDN_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held
+ * from the library's load on that GPU until the process ends; its address is
+ * looked up once per device (on the first call with that device current).
+ * The call allocates nothing.
+ *   - Sizes whose gdn_chunk_prefill_workspace_size exceeds the array return
+ *     GDN_ERR_WORKSPACE before anything is enqueued (128 MiB covers, e.g., one
+ *     4096-token sequence at 48 value heads: 105 MB).
+ *   - Every call on one GPU shares that GPU's array and overwrites it (nothing
+ *     in it needs clearing: each call writes before it reads).  Calls that
+ *     overlap on one GPU (other streams, other host threads) race on it and
+ *     must be serialised by the caller.
+ *   - The current device must be the one `stream` belongs to.
+ * Results are bit-identical to gdn_chunk_prefill (the same kernels).
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (128u << 20)
+gdn_status_t gdn_chunk_prefill_noalloc(const gdn_config_t* cfg, gdn_dtype_t in_dtype,
+                                       gdn_dtype_t out_dtype, const void* q, const void* k,
+                                       int64_t qk_stride, const void* v, int64_t v_stride,
+                                       const float* g, const float* beta, const float* initial_state,
+                                       const int32_t* cu_dev, const int32_t* cu_host, int32_t N,
+                                       int32_t T, void* out, float* final_state, gdn_stream_t stream);
+
+/*
  * The gates of a call from the a / b projections.  The golden PR's prepare
  * stage derives the raw g/beta from the in_proj_a / in_proj_b outputs with the
  * layer's A_log and dt_bias vectors, and the TDD ledger lists the GDN

@@ -288,3 +288,20 @@ def test_state_convert_and_h16_decode_argument_checks(lib):
     got = lib.gdn_decode_step(ctypes.byref(cfg), gdn.GDN_F16, gdn.GDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
                               FAKE, FAKE, FAKE, FAKE, 4, None)
     assert got == gdn.GDN_ERR_UNSUPPORTED                                  # fp16 is not an activation dtype
+
+
+def test_noalloc_chunk_prefill_rejects_sizes_past_its_scratch(lib):
+    """gdn_chunk_prefill_noalloc refuses any size whose workspace exceeds the fixed array
+    (before any HIP call, so this runs without a GPU); an empty batch is a no-op."""
+    cfg = _cfg()
+    limit = 128 << 20
+    s = ctypes.c_size_t()
+    assert lib.gdn_chunk_prefill_workspace_size(ctypes.byref(cfg), 1, 8192, ctypes.byref(s)) == 0
+    assert s.value > limit
+    hc = (ctypes.c_int32 * 2)(0, 8192)
+    got = lib.gdn_chunk_prefill_noalloc(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_F32, FAKE, FAKE, 10240, FAKE,
+                                        10240, FAKE, FAKE, None, FAKE, hc, 1, 8192, FAKE, None, None)
+    assert got == gdn.GDN_ERR_WORKSPACE
+    h0 = (ctypes.c_int32 * 1)(0)
+    assert lib.gdn_chunk_prefill_noalloc(ctypes.byref(cfg), gdn.GDN_BF16, gdn.GDN_F32, None, None, 10240, None,
+                                         10240, None, None, None, FAKE, h0, 0, 0, None, None, None) == 0
