@@ -58,12 +58,10 @@ constexpr int kXcds = 8;                       // XCDs; workgroups are dealt to 
 // Spine kernels (the sequential walk over a sequence's chunks)
 constexpr int kSpineLds = 0;    // 8 waves per 32 value rows, intermediates through LDS (fp32, per key channel)
 constexpr int kSpineWave = 1;   // register-resident, a value head per workgroup
-constexpr int kSpinePair = 2;   // register-resident, two waves per 16 value rows (key halves)
+constexpr int kSpineRows = 2;   // register-resident, 32 value rows per workgroup
+constexpr int kRowsNW = 2;        // kSpineRows: compute waves (16 value rows each)
+constexpr int kRowsLoaders = 2;   // kSpineRows: loader waves staging the next chunk
 constexpr int kWaveSpineMinBlocks = 256;   // value heads x sequences from which kSpineWave is used
-#ifndef GDN_PAIR_LOADERS
-#define GDN_PAIR_LOADERS 2
-#endif
-constexpr int kPairLoaders = GDN_PAIR_LOADERS;   // loader waves of the key-split spine
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -1669,17 +1667,9 @@ struct ChunkStage {
   }
 };
 
-// Register-resident spine.  kNW waves per workgroup; kSplit waves share each
-// block of 16 value rows, wave `half` of a block owning key columns
-// [128 half / kSplit, 128 (half + 1) / kSplit) of its state:
-//   kSplit = 1: a wave holds all 128 key columns of its 16 rows (every product
-//               of the chunk step is wave-local);
-//   kSplit = 2: Y = K S0^T and Z^T = S0 Q^T are summed over the two halves
-//               through LDS once per chunk; both waves then form R, Vnew and W
-//               (shared work), each updates its own half of the state and
-//               writes two of the four 16-token tiles of the output.  The
-//               chain that carries the state from chunk to chunk is half as
-//               long per wave, which is what a single sequence waits on.
+// Register-resident spine.  kNW waves per workgroup, each holding all 128 key
+// columns of its 16 value rows, so every product of the chunk step is
+// wave-local.
 // kLoaders > 0 adds that many loader waves: they stage chunk cl+1 into the other
 // LDS slot while the kNW compute waves work on chunk cl, so the compute waves
 // never wait at the texture path; without them the compute waves stage in
@@ -1694,20 +1684,19 @@ struct FusedNorm {
   float eps;
 };
 
-template <int kNW, int kSplit, int kLoaders, typename To, bool kNorm = false>
+template <int kNW, int kLoaders, typename To, bool kNorm = false>
 __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
     const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
     To* __restrict__ out, float* final_state, FusedNorm nrm) {
-  using Cf = SpineCfg<kNW * kWave, 16 * kNW / kSplit>;
+  using Cf = SpineCfg<kNW * kWave, 16 * kNW>;
   using StageCf = SpineCfg<(kLoaders > 0 ? kLoaders : kNW) * kWave, Cf::kRows>;   // same LDS layout
-  static_assert(!kNorm || (kSplit == 1 && kNW * 16 == kD), "the fused norm needs a whole value head per workgroup");
-  constexpr int kKS = 4 / kSplit;                 // 32-key steps of a wave's state
-  constexpr int kJT = 8 / kSplit;                 // 16-key tiles of a wave's state
-  // kSplit = 2: per wave Y and two Z^T partial tiles; kNorm: per chunk parity,
-  // token and wave a partial sum of squares
-  constexpr int kExch = kSplit == 2 ? kNW * 6 * 1024 : (kNorm ? 2 * kC * kNW * 4 : 16);
+  static_assert(!kNorm || kNW * 16 == kD, "the fused norm needs a whole value head per workgroup");
+  constexpr int kKS = 4;                          // 32-key steps of a wave's state
+  constexpr int kJT = 8;                          // 16-key tiles of a wave's state
+  // kNorm: per chunk parity, token and wave a partial sum of squares
+  constexpr int kExch = kNorm ? 2 * kC * kNW * 4 : 16;
   __shared__ __attribute__((aligned(1024))) uint8_t s_in[2][Cf::kSlotBytes];
   __shared__ __attribute__((aligned(16))) uint8_t s_ex[kExch];
 
@@ -1729,9 +1718,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   const int i0 = (member % blocks_per_head) * Cf::kRows;     // first value row of the workgroup
   const int tid = threadIdx.x, lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int half = wave % kSplit;                            // key half (kSplit = 2)
-  const int iw = 16 * (wave / kSplit);                       // the wave's rows within the block
-  const int jh = half * (kD / kSplit);                       // the wave's first key column
+  const int iw = 16 * wave;                                  // the wave's rows within the block
   const int g = lane >> 4, m = lane & 15;
   const int seq_beg = cu[n], seq_end = cu[n + 1];
   const int n_chunks = (seq_end - seq_beg + kC - 1) / kC;
@@ -1752,15 +1739,13 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   stage.init();
   constexpr int kLoads = StageCf::kLoads;
 
-  // output tiles of this wave: all four, or (kSplit = 2) mt = half and half + 2
-  auto owns_mt = [&](int mt) { return kSplit == 1 || (mt & 1) == half; };
 
-  // ---- the state: S^T tiles, lane holds S[i0 + iw + m][jh + 16 jt + 4 g + e], jt < kJT ----
+  // ---- the state: S^T tiles, lane holds S[i0 + iw + m][16 jt + 4 g + e], jt < kJT ----
   f32x4_t sst[kJT];
   f32x4_t nw = {0.f, 0.f, 0.f, 0.f};   // norm weights of the lane's output columns iw + 4 g .. +3
   if constexpr (kNorm) nw = *reinterpret_cast<const f32x4_t*>(nrm.w + iw + 4 * g);
   if (!loader) {
-    const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh : nullptr;
+    const float* s0 = init_state ? init_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD : nullptr;
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt)
       sst[jt] = s0 ? *reinterpret_cast<const f32x4_t*>(s0 + 16 * jt + 4 * g) : f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1798,7 +1783,6 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       // stage chunk cl+1 into the other slot (free since the last barrier),
       // meeting the compute waves at each of their barriers
       stage.load_all(stage.rsrc(cl + 1));
-      if constexpr (kSplit == 2) __syncthreads();
       stage.commit_all(s_in[slot ^ 1]);
       __syncthreads();
       continue;
@@ -1818,7 +1802,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     bf16x8_t fk[4], fq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const int off = (16 * mt + m) * kWP + jh + 8 * g;
+      const int off = (16 * mt + m) * kWP + 8 * g;
       fk[mt] = load_bf16x8(sk + off);
       fq[mt] = load_bf16x8(sq + off);
     }
@@ -1848,7 +1832,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       if (ks + 1 < kKS) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const int off = (16 * mt + m) * kWP + jh + 32 * (ks + 1) + 8 * g;
+          const int off = (16 * mt + m) * kWP + 32 * (ks + 1) + 8 * g;
           nk[mt] = load_bf16x8(sk + off);
           nq[mt] = load_bf16x8(sq + off);
         }
@@ -1881,41 +1865,21 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 
     // LDS operands of the later products: Tt, Pt (this wave's token tiles) and
     // K^T for the state update (transposing reads: A[j][slot (g, e)] =
-    // K[k0 + pair_k(0, g, e)][jh + 16 jt + j]).  With the key split (half the
-    // key tiles per wave) there are registers to issue each a phase early, Tt
-    // and the first K^T step before the exchange so they land during it.
-    constexpr bool kEarly = kSplit == 2;
-    bf16x8_t th[kNF], tl[kNF], ph[kNF], pl[kNF], kt[kJT], kt2[kEarly ? kJT : 1];
+    // K[k0 + pair_k(0, g, e)][16 jt + j])
+    bf16x8_t th[kNF], tl[kNF], ph[kNF], pl[kNF], kt[kJT];
     auto read_tt = [&]() {
 #pragma unroll
       for (int x = 0; x < kNF; ++x) { th[x] = tri_frag(0, x, 0); tl[x] = tri_frag(0, x, 1); }
     };
     auto read_pt = [&]() {
 #pragma unroll
-      for (int x = 0; x < kNF; ++x)
-        if (owns_mt(frag_mt(x))) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+      for (int x = 0; x < kNF; ++x) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
     };
     auto read_kt = [&](int k0, bf16x8_t* dst) {
 #pragma unroll
       for (int jt = 0; jt < kJT; ++jt)
-        dst[jt] = lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(jh + 16 * jt + 4 * (m & 3)), 16 * kWP);
+        dst[jt] = lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
     };
-    if constexpr (kEarly) { read_tt(); read_kt(0, kt); }
-
-    if constexpr (kSplit == 2) {
-      // sum the two key halves: Y for all four token tiles, Z^T for the partner's tiles
-      f32x4_t* mine = reinterpret_cast<f32x4_t*>(s_ex + wave * 6 * 1024) + lane;
-      const f32x4_t* other = reinterpret_cast<const f32x4_t*>(s_ex + (wave ^ 1) * 6 * 1024) + lane;
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) mine[mt * kWave] = y[mt];
-      mine[4 * kWave] = zt[1 - half];
-      mine[5 * kWave] = zt[3 - half];
-      __syncthreads();
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) y[mt] += other[mt * kWave];
-      zt[half] += other[4 * kWave];
-      zt[half + 2] += other[5 * kWave];
-    }
 
     // ---- R = V - a Y (accumulator layout: rows 16 mt + 4 g + e, column iw + m) ----
     bf16x8_t rbh[2], rbl[2];
@@ -1929,7 +1893,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       split_pair(r[2], r[3], rbh[1], rbl[1]);
     }
 
-    if constexpr (!kEarly) { read_kt(0, kt); read_tt(); }
+    read_kt(0, kt);
+    read_tt();
 
     // ---- Vnew = Tt R ----
     f32x4_t vn[4];
@@ -1944,7 +1909,6 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(tl[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
     }
 
-    if constexpr (kEarly) { read_pt(); read_kt(32, kt2); }
 
     bf16x8_t nbh[2], nbl[2], wbh[2], wbl[2];
     split_pair(vn[0], vn[1], nbh[0], nbl[0]);
@@ -1984,27 +1948,24 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (!kEarly) { read_kt(32, kt); read_pt(); }   // the second k step reuses kt
+    read_kt(32, kt);   // the second k step reuses kt
+    read_pt();
 
     // ---- O^T = Z^T diag(b) + Vnew^T Pt^T on this wave's token tiles ----
     // (rows i, columns t: A = Vnew pairs, B = Pt fragments)
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      if (owns_mt(mt)) {
-        const float b = vec[kC + 16 * mt + m];
+      const float b = vec[kC + 16 * mt + m];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
-      }
+      for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
     }
     {
 #pragma unroll
       for (int x = 0; x < kNF; ++x) {
         commit_group(kJT + x);
-        if (owns_mt(frag_mt(x))) {
-          zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-          zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-          zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
-        }
+        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+        zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
+        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
         if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
     }
@@ -2012,9 +1973,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) {
       commit_group(kJT + kNF + jt);
-      const bf16x8_t a2 = kEarly ? kt2[kEarly ? jt : 0] : kt[jt];
-      u[jt] = mfma_bf16(a2, wbh[1], u[jt]);
-      u[jt] = mfma_bf16(a2, wbl[1], u[jt]);
+      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
+      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -2055,7 +2015,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     } else {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        if (owns_mt(mt)) buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
+        buf_store4(ro, (16 * mt + m) * orow + 4 * g * (uint32_t)sizeof(To), zt[mt], (To*)nullptr);
     }
     __syncthreads();
     if constexpr (kNorm) {
@@ -2078,7 +2038,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   }
 
   if (final_state && !loader) {
-    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD + jh;
+    float* s_out = final_state + (((int64_t)n * hv + h) * kD + i0 + iw + m) * kD;
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) *reinterpret_cast<f32x4_t*>(s_out + 16 * jt + 4 * g) = sst[jt];
   }
@@ -2086,7 +2046,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 
 int chunk_spine_kind(const Dims& d, bool in_bf16, int n) {
   if (!in_bf16 || d.per_channel) return kSpineLds;
-  return n * d.hv >= kWaveSpineMinBlocks ? kSpineWave : kSpinePair;
+  return n * d.hv >= kWaveSpineMinBlocks ? kSpineWave : kSpineRows;
 }
 
 template <bool F32, bool kPC, typename Tin, typename To>
@@ -2097,10 +2057,10 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   uint8_t* w = static_cast<uint8_t*>(ws);
   // bf16 inputs with scalar decay run a register-resident spine: a whole
   // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
-  // work overlaps the other's MFMAs) once there is a workgroup for every CU;
-  // for fewer sequences the key-split form (two waves per 16 value rows, four
-  // waves and 32 rows per workgroup) spreads them over eight times as many
-  // workgroups and halves each wave's serial work per chunk.
+  // work overlaps the other's MFMAs, and the gated norm can be fused) once
+  // there is a workgroup for every CU; for fewer sequences 32 value rows per
+  // workgroup (two compute waves, one per SIMD, and two loader waves) spread
+  // them over four times as many workgroups.
   const int spine = chunk_spine_kind(d, !F32, n);
   hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
                      reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
@@ -2123,20 +2083,20 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     if (nrm.z)
-      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
+      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
     else
-      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 1, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
+      hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
-  } else if (!F32 && spine == kSpinePair) {
-    const int members = (d.hv / d.hk) * (kD / 32);
+  } else if (!F32 && spine == kSpineRows) {
+    const int members = (d.hv / d.hk) * (kD / (16 * kRowsNW));
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<4, 2, kPairLoaders, To>), dim3(blocks),
-                       dim3((4 + kPairLoaders) * kWave), 0, s,
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<kRowsNW, kRowsLoaders, To>), dim3(blocks),
+                       dim3((kRowsNW + kRowsLoaders) * kWave), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state, nrm);

@@ -90,10 +90,17 @@ def _iptr(a: np.ndarray):
 
 def round_bf16(x) -> np.ndarray:
     """Round fp64 values to the nearest bfloat16 value (8 significant bits, ties to
-    even), returned as fp64.  Used only where the library stores bf16."""
-    x = np.asarray(x, dtype=np.float64)
-    m, e = np.frexp(x)                 # x = m * 2**e, 0.5 <= |m| < 1
-    return np.ldexp(np.rint(m * 256.0) / 256.0, e)
+    even), returned as fp64.  Used only where the library stores bf16.
+
+    On the fp64 bit pattern: 8 significant bits keep the top 7 of the 52 stored
+    fraction bits, so the low 45 bits are rounded away to nearest, ties to the
+    even kept bit (a carry into the exponent is the correct rounding up to the
+    next binade).  Finite, normal fp64 inputs; equal to rint(m * 256) / 256 * 2^e
+    with x = m 2^e, 1/2 <= |m| < 1."""
+    u = np.ascontiguousarray(x, dtype=np.float64).view(np.uint64)
+    half = np.uint64((1 << 44) - 1)
+    r = (u + half + ((u >> np.uint64(45)) & np.uint64(1))) & ~np.uint64((1 << 45) - 1)
+    return r.view(np.float64)
 
 
 def round_f16(x) -> np.ndarray:

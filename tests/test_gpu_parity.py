@@ -332,30 +332,29 @@ def _sampled_heads(orc, d, kheads):
     return vheads, o, s
 
 
-def test_chunk_prefill_s4096_full_size_sampled(orc):
-    """The 4096-token prefill workload (bf16, random initial state) run whole; heads of
-    key heads 0, 7 and 15 compared with the oracle over all tokens."""
+def test_chunk_prefill_s4096_full_size_all_heads(orc):
+    """The 4096-token prefill workload (bf16, random initial state) run whole, every value
+    head compared with the oracle over all tokens."""
     d = gi.gen_qkv(1003, [4096])
     o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
                               dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
                               initial_state=dev(d["state_in"]), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    vheads, o_ref, s_ref = _sampled_heads(orc, d, [0, 7, 15])
-    check(host(o)[:, vheads], o_ref, TOL_BF16, "S=4096 out (9 heads)")
-    check(host(fs)[:, vheads], s_ref, TOL_BF16, "S=4096 state (9 heads)")
-    assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "S=4096 out (48 heads)")
+    check(host(fs), s_ref, TOL_BF16, "S=4096 state (48 heads)")
 
 
 def test_varlen_32k_full_size_sampled(orc):
     """The varlen workload: 63, 64, 65 plus five lengths in [1, 8192] (~32k tokens), per-sequence
-    initial states; value heads of key head 5 compared over every token."""
+    initial states; the value heads of key heads 5 and 12 compared over every token."""
     lengths, seed = gi.varlen_lengths()
     d = gi.gen_qkv(1004, lengths)
     o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
                               dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
                               initial_state=dev(d["state_in"]), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    vheads, o_ref, s_ref = _sampled_heads(orc, d, [5])
+    vheads, o_ref, s_ref = _sampled_heads(orc, d, [5, 12])
     check(host(o)[:, vheads], o_ref, TOL_BF16, f"varlen {lengths} out")
     check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen state")
 
@@ -466,6 +465,18 @@ def test_prefill_entry_fused_norm_equals_separate_calls():
     torch.cuda.synchronize()
     check(host(out), host(out2), TOL_F32, "fused norm vs separate norm")
     assert torch.equal(fs, fs2), "the final state does not depend on the norm"
+
+
+def test_prefill_entry_s4096_all_heads(orc):
+    """The benchmarked call: the 4096-token one-call prefill (bf16 in and out, conv state and
+    recurrent state carried in) against the oracle's conv -> delta rule -> gated norm, every
+    value head over every token."""
+    d = gi.gen_prefill(1003, [4096], bf16=True, conv_state=True)
+    out, fs, cso = _prefill_gpu(d, True, torch.bfloat16)
+    out_ref, s_ref, cso_ref = _prefill_ref(orc, d, True)
+    check(host(out), out_ref, TOL_BF16, "S=4096 prefill out (48 heads)", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, "S=4096 prefill state (48 heads)")
+    assert np.array_equal(host(cso), cso_ref)
 
 
 def test_prefill_entry_varlen_full_size_sampled(orc):
@@ -954,11 +965,11 @@ def test_kda_h64_s16384_full_size_sampled(orc):
     cfg = gdn.config(num_k_heads=64, num_v_heads=64, decay_per_key_channel=1)
     o, fs = _run_chunk(d, cfg)
     torch.cuda.synchronize()
-    heads = [0, 31, 63]
+    heads = [0, 13, 26, 39, 52, 63]
     o_ref, s_ref = orc.delta_rule(d["q"][:, heads], d["k"][:, heads], d["v"][:, heads], d["g"][:, heads],
                                   d["beta"][:, heads], d["cu"], d["state_in"][:, heads])
-    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 out (3 heads)")
-    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 state (3 heads)")
+    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 out (6 heads)")
+    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 state (6 heads)")
     assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
 
 
