@@ -45,7 +45,7 @@ class GDNConfig(ctypes.Structure):
         ("num_k_heads", ctypes.c_int32), ("num_v_heads", ctypes.c_int32),
         ("head_k_dim", ctypes.c_int32), ("head_v_dim", ctypes.c_int32),
         ("conv_width", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
-        ("conv_act", ctypes.c_int32), ("decay_per_key_channel", ctypes.c_int32),
+        ("conv_act", ctypes.c_int32), ("decay_per_key_channel", ctypes.c_int32), ("qk_l2norm", ctypes.c_int32),
         ("l2_eps", ctypes.c_float), ("rms_eps", ctypes.c_float), ("q_scale", ctypes.c_float),
     ]
 

@@ -21,6 +21,7 @@ gdn_status_t resolve(const gdn_config_t* cfg, Dims* d) {
   if (cfg->conv_width != 4 || cfg->chunk_size != 64) return GDN_ERR_UNSUPPORTED;
   if (cfg->conv_act != 0 && cfg->conv_act != 1) return GDN_ERR_INVALID_ARG;
   if (cfg->decay_per_key_channel != 0 && cfg->decay_per_key_channel != 1) return GDN_ERR_INVALID_ARG;
+  if (cfg->qk_l2norm != 0 && cfg->qk_l2norm != 1) return GDN_ERR_INVALID_ARG;
   if (!(cfg->l2_eps >= 0.0f) || !(cfg->rms_eps >= 0.0f)) return GDN_ERR_INVALID_ARG;
   d->hk = cfg->num_k_heads;
   d->hv = cfg->num_v_heads;
@@ -29,6 +30,7 @@ gdn_status_t resolve(const gdn_config_t* cfg, Dims* d) {
   d->cc = 2 * d->hk * d->dk + d->hv * d->dv;
   d->act = cfg->conv_act;
   d->per_channel = cfg->decay_per_key_channel;
+  d->l2norm = cfg->qk_l2norm;
   d->l2_eps = cfg->l2_eps;
   d->rms_eps = cfg->rms_eps;
   d->q_scale = cfg->q_scale > 0.0f ? cfg->q_scale : 1.0f / sqrtf((float)cfg->head_k_dim);
@@ -118,6 +120,7 @@ gdn_status_t gdn_config_default(gdn_config_t* cfg) {
   cfg->chunk_size = 64;
   cfg->conv_act = 1;
   cfg->decay_per_key_channel = 0;
+  cfg->qk_l2norm = 1;
   cfg->l2_eps = 1e-6f;
   cfg->rms_eps = 1e-6f;
   cfg->q_scale = 1.0f / sqrtf(128.0f);

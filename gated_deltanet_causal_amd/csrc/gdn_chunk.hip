@@ -444,7 +444,7 @@ template <bool F32, typename Tin>
 __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
+    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
@@ -505,8 +505,8 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     sk = group_sum<4>(sk);
     sq = group_sum<4>(sq);
     if (part == 0) {
-      s_rk[r] = r < L ? 1.0f / sqrtf(sk + l2_eps) : 0.0f;
-      s_rq[r] = r < L ? q_scale / sqrtf(sq + l2_eps) : 0.0f;
+      s_rk[r] = r < L ? (l2norm ? 1.0f / sqrtf(sk + l2_eps) : 1.0f) : 0.0f;
+      s_rq[r] = r < L ? (l2norm ? q_scale / sqrtf(sq + l2_eps) : q_scale) : 0.0f;
     }
   }
   {  // per-channel cumulative sum over the chunk: thread (channel, half of the rows)
@@ -647,7 +647,7 @@ template <bool F32, typename Tin, bool kPairK>
 __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     Gates gates, const int32_t* __restrict__ cu,
-    int n_seq, int hk, int hv, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
+    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
   using O = Ops<F32>;
   using E = typename O::E;
   constexpr int kPitch = kD + O::kPadK;
@@ -758,8 +758,8 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
     sk = quad_sum(sk);
     sq = quad_sum(sq);
     if (part == 0) {
-      s_rk[r] = r < L ? 1.0f / sqrtf(sk + l2_eps) : 0.0f;
-      s_rq[r] = r < L ? q_scale / sqrtf(sq + l2_eps) : 0.0f;
+      s_rk[r] = r < L ? (l2norm ? 1.0f / sqrtf(sk + l2_eps) : 1.0f) : 0.0f;
+      s_rq[r] = r < L ? (l2norm ? q_scale / sqrtf(sq + l2_eps) : q_scale) : 0.0f;
     }
   }
 
@@ -2070,11 +2070,11 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     if constexpr (kPC)
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt.g, gt.beta,
-                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
+                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w);
     else   // bf16: records in the paired-tile k order of the register-resident spines
       hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, !F32>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt,
-                         cu_dev, n, d.hk, d.hv, d.l2_eps, d.q_scale, w);
+                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kStepThreads, kStepThreads / 64) void decode_step_k
     const T* __restrict__ x, const float* __restrict__ conv_w, T* __restrict__ conv_state,
     Gates gates, const T* __restrict__ z,
     const float* __restrict__ norm_w, TS* __restrict__ state, To* __restrict__ out, int hk,
-    int hv, int cc, int act, float l2_eps, float q_scale, float rms_eps) {
+    int hv, int cc, int act, int l2norm, float l2_eps, float q_scale, float rms_eps) {
   const int b = blockIdx.x / hv;
   const int h = blockIdx.x % hv;
   const int ratio = hv / hk;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kStepThreads, kStepThreads / 64) void decode_step_k
     const float* src = w == 0 ? s_q : s_k;
     const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
     const float ss = wave_sum(a0 * a0 + a1 * a1);
-    if (lane == 0) s_scal[w] = 1.0f / sqrtf(ss + l2_eps);
+    if (lane == 0) s_scal[w] = l2norm ? 1.0f / sqrtf(ss + l2_eps) : 1.0f;
   }
   __syncthreads();
   const float rq = s_scal[0] * q_scale, rk = s_scal[1];
@@ -257,7 +257,7 @@ hipError_t decode_ratio(const Dims& d, const void* x, const float* conv_w, void*
   hipLaunchKernelGGL((decode_step_kernel<T, To, TS, kPC>), dim3(b * d.hv), dim3(kStepThreads), 0, s,
                      static_cast<const T*>(x), conv_w, static_cast<T*>(conv_state), gt,
                      static_cast<const T*>(z), norm_w, static_cast<TS*>(state),
-                     static_cast<To*>(out), d.hk, d.hv, d.cc, d.act, d.l2_eps, d.q_scale, d.rms_eps);
+                     static_cast<To*>(out), d.hk, d.hv, d.cc, d.act, d.l2norm, d.l2_eps, d.q_scale, d.rms_eps);
   if (d.hv != d.hk) {   // shared q / k channels: shifted once, after every head has read them
     const int n_ch = 2 * d.hk * kD;
     hipLaunchKernelGGL(conv_shift_kernel<T>, dim3((n_ch + kGroup - 1) / kGroup, b), dim3(kGroup), 0, s,

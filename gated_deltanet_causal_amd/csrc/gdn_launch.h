@@ -26,6 +26,7 @@ struct Dims {
   int cc;           // conv channels 2*hk*dk + hv*dv
   int act;          // conv activation: 0 none, 1 SiLU
   int per_channel;  // decay per key channel
+  int l2norm;       // 1: q, k L2-normalised in the kernels; 0: used as given
   float l2_eps, rms_eps, q_scale;
 };
 

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
     const float* __restrict__ g, const float* __restrict__ beta, const T* __restrict__ z,
     const float* __restrict__ norm_w, const float* __restrict__ state, To* __restrict__ out,
     float* __restrict__ rec_u, float* __restrict__ rec_k, int K, int hk, int hv, int cc, int act,
-    float l2_eps, float q_scale, float rms_eps) {
+    int l2norm, float l2_eps, float q_scale, float rms_eps) {
   const int b = blockIdx.x / hv;
   const int h = blockIdx.x % hv;
   const int kh = h / (hv / hk);           // the key head it reads (repeat-interleave)
@@ -203,7 +203,7 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
       const float* src = w == 0 ? s_q : s_k;
       const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
       const float ss = wave_sum(a0 * a0 + a1 * a1);
-      if (lane == 0) s_scal[w] = 1.0f / sqrtf(ss + l2_eps);
+      if (lane == 0) s_scal[w] = l2norm ? 1.0f / sqrtf(ss + l2_eps) : 1.0f;
     }
     __syncthreads();
     const float rq = s_scal[0] * q_scale, rk = s_scal[1];
@@ -354,7 +354,7 @@ hipError_t verify_launch(const Dims& d, const void* x, const float* conv_w, cons
                          hipStream_t s) {
   hipLaunchKernelGGL((verify_kernel<T, To, kPC>), dim3(b * d.hv), dim3(kGroup), 0, s, static_cast<const T*>(x),
                      conv_w, static_cast<const T*>(conv_state), g, beta, static_cast<const T*>(z), norm_w, state,
-                     static_cast<To*>(out), rec_u, rec_k, k, d.hk, d.hv, d.cc, d.act, d.l2_eps, d.q_scale,
+                     static_cast<To*>(out), rec_u, rec_k, k, d.hk, d.hv, d.cc, d.act, d.l2norm, d.l2_eps, d.q_scale,
                      d.rms_eps);
   return hipGetLastError();
 }

@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
   GDN_OK = 0,
@@ -71,6 +71,9 @@ typedef struct {
   int32_t chunk_size;            /* 64 (only value built)                            */
   int32_t conv_act;              /* 0: none, 1: SiLU after the conv (default 1)      */
   int32_t decay_per_key_channel; /* 0: g is [T][Hv]; 1: g is [T][Hv][dk]             */
+  int32_t qk_l2norm;             /* 1 (default): q, k L2-normalised inside the calls; */
+                                 /* 0: q, k used as given (the caller's separate unit- */
+                                 /* L2 stage, GLM ledger row I2a); q_scale applies     */
   float l2_eps;                  /* q,k: x / sqrt(sum x^2 + l2_eps); default 1e-6    */
   float rms_eps;                 /* gated norm: rsqrt(mean o^2 + rms_eps); 1e-6      */
   float q_scale;                 /* <= 0 selects 1/sqrt(head_k_dim)                  */

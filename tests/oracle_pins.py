@@ -308,6 +308,33 @@ def pin_l2_eps_and_scale(orc):
         _close(o[0, 0], want, 1e-13, f"l2 norm={norm} eps={eps}")
 
 
+def pin_l2norm_off_takes_keys_as_given(orc):
+    """qk_l2norm = 0 (the L2 stage bound outside the call) uses q and k as given: fed the
+    unit-normalised rows it reproduces the qk_l2norm = 1 result (eps 0); fed the raw rows of
+    norm c it differs (beta k k^T grows as c^2), and on a single token from a zero state with
+    g = 0, beta = 1 and q = k it gives v * scale * |k|^2 (the closed form without the division)."""
+    rng = np.random.default_rng(41)
+    T, hk, hv, d = 9, 2, 4, 8
+    q = rng.standard_normal((T, hk, d))
+    k = rng.standard_normal((T, hk, d))
+    v = rng.standard_normal((T, hv, d))
+    g = -np.abs(rng.standard_normal((T, hv))) * 0.3
+    beta = rng.random((T, hv))
+    s0 = rng.standard_normal((1, hv, d, d)) * 0.1
+    o1, s1 = orc.delta_rule(q, k, v, g, beta, [0, T], s0, l2_eps=0.0)
+    qu = q / np.linalg.norm(q, axis=-1, keepdims=True)
+    ku = k / np.linalg.norm(k, axis=-1, keepdims=True)
+    o0, s0_ = orc.delta_rule(qu, ku, v, g, beta, [0, T], s0, l2norm=0, l2_eps=0.0)
+    _close(o0, o1, 1e-12, "l2norm=0 on unit rows == l2norm=1")
+    _close(s0_, s1, 1e-12, "l2norm=0 on unit rows == l2norm=1 (state)")
+    o2, _ = orc.delta_rule(q, k, v, g, beta, [0, T], s0, l2norm=0, l2_eps=0.0)
+    assert np.max(np.abs(o2 - o1)) > 1e-3, "l2norm=0 must not normalise"
+    kk = rng.standard_normal((1, 1, d)) * 2.0
+    vv = rng.standard_normal((1, 1, d))
+    o3, _ = orc.delta_rule(kk.copy(), kk, vv, np.zeros((1, 1)), np.ones((1, 1)), [0, 1], None, l2norm=0)
+    _close(o3[0, 0], vv[0, 0] / math.sqrt(d) * float(np.sum(kk * kk)), 1e-12, "l2norm=0 closed form")
+
+
 def pin_head_repeat_interleave(orc):
     """Value head h reads key head h // (Hv/Hk): running each value head alone
     with its key head reproduces the packed multi-head result."""

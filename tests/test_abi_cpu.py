@@ -52,10 +52,14 @@ def test_abi_version_matches_header(lib):
 
 
 def test_config_struct_layout_and_defaults(lib):
-    assert ctypes.sizeof(gdn.GDNConfig) == 11 * 4
+    assert ctypes.sizeof(gdn.GDNConfig) == 12 * 4
+    assert [f for f, _ in gdn.GDNConfig._fields_] == [
+        "num_k_heads", "num_v_heads", "head_k_dim", "head_v_dim", "conv_width", "chunk_size", "conv_act",
+        "decay_per_key_channel", "qk_l2norm", "l2_eps", "rms_eps", "q_scale"]
     cfg = gdn.config()
     assert (cfg.num_k_heads, cfg.num_v_heads, cfg.head_k_dim, cfg.head_v_dim) == (16, 48, 128, 128)
     assert (cfg.conv_width, cfg.chunk_size, cfg.conv_act, cfg.decay_per_key_channel) == (4, 64, 1, 0)
+    assert cfg.qk_l2norm == 1
     assert cfg.l2_eps == pytest.approx(1e-6) and cfg.rms_eps == pytest.approx(1e-6)
     assert cfg.q_scale == pytest.approx(1 / 128 ** 0.5)
     assert cfg.conv_channels == 10240
@@ -78,7 +82,7 @@ def test_config_validation(lib):
     for kw, want in [(dict(head_k_dim=64), gdn.GDN_ERR_UNSUPPORTED), (dict(conv_width=3), gdn.GDN_ERR_UNSUPPORTED),
                      (dict(chunk_size=32), gdn.GDN_ERR_UNSUPPORTED), (dict(num_v_heads=47), gdn.GDN_ERR_INVALID_ARG),
                      (dict(num_k_heads=0), gdn.GDN_ERR_INVALID_ARG), (dict(conv_act=2), gdn.GDN_ERR_INVALID_ARG),
-                     (dict(l2_eps=-1.0), gdn.GDN_ERR_INVALID_ARG)]:
+                     (dict(l2_eps=-1.0), gdn.GDN_ERR_INVALID_ARG), (dict(qk_l2norm=2), gdn.GDN_ERR_INVALID_ARG)]:
         got = lib.gdn_chunk_prefill_workspace_size(ctypes.byref(_cfg(**kw)), 1, 64, ctypes.byref(size))
         assert got == want, kw
     assert lib.gdn_chunk_prefill_workspace_size(None, 1, 64, ctypes.byref(size)) == gdn.GDN_ERR_INVALID_ARG

@@ -774,6 +774,25 @@ def test_verify_transaction_full_size_poisoned_tail(orc):
     assert np.array_equal(host(t_["cs"]), cs_ref), "committed conv state must be exact"
 
 
+def test_verify_largest_window_k64(orc):
+    """The largest window the library takes (GDN_MAX_VERIFY_ROWS = 64 rows), 3 sequences,
+    committing 64, 33 and 0 rows, against the oracle's transaction."""
+    B, K = 3, 64
+    d = _verify_inputs(2250, B, K)
+    t_ = _verify_dev(d, True)
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.float32)
+    accepted = np.array([64, 33, 0])
+    gdn.verify_commit(torch.from_numpy(accepted.astype(np.int32)).cuda(), t_["x"], t_["g"], t_["cs"], t_["st"], ws)
+    torch.cuda.synchronize()
+    out_ref, snaps = orc.verify(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    cs_ref, st_ref = orc.commit(snaps, accepted)
+    check(host(out_v), out_ref, TOL_BF16, "verify rows, K = 64")
+    check(host(t_["st"]), st_ref, TOL_BF16, "committed state, K = 64")
+    assert np.array_equal(host(t_["cs"]), cs_ref), "committed conv state must be exact"
+
+
 def test_verify_per_channel_fp32(orc):
     """Per-key-channel decay on the fp32 path, 3 sequences x 3 rows, at the fp32 bound."""
     B, K = 3, 3
@@ -1008,3 +1027,94 @@ def test_chunk_prefill_scalar_strong_decay(orc, pattern, bf16):
         tol = TOL_BF16 if bf16 else TOL_F32
         check(host(o), o_ref, tol, f"scalar {pattern} out {lengths}")
         check(host(fs), s_ref, tol, f"scalar {pattern} state {lengths}")
+
+
+# ---------------------------------------------------------------------------
+# qk_l2norm = 0: q and k used as given (the caller binds the unit-L2 stage)
+# ---------------------------------------------------------------------------
+
+def _unit_rows(a, bf16):
+    """Inputs for qk_l2norm = 0: rows drawn on the unit sphere (the caller's L2 stage already
+    applied), rounded to bf16 where the workload is bf16 (so only close to unit norm)."""
+    u = np.asarray(a, dtype=np.float64)
+    u = (u / np.linalg.norm(u, axis=-1, keepdims=True)).astype(np.float32)
+    return gi.bf16_round(u) if bf16 else u
+
+
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "f32"])
+@pytest.mark.parametrize("per_channel", [False, True], ids=["scalar", "per_channel"])
+def test_chunk_prefill_l2norm_off(orc, bf16, per_channel):
+    geo = gi.Geometry(hk=4, hv=12)
+    for lengths in ([130], [64, 1, 0, 70]):
+        d = gi.gen_qkv(3300 + len(lengths), lengths, geo, bf16=bf16, per_channel=per_channel)
+        d["q"], d["k"] = _unit_rows(d["q"], bf16), _unit_rows(d["k"], bf16)
+        cfg = gdn.config(num_k_heads=4, num_v_heads=12, decay_per_key_channel=int(per_channel), qk_l2norm=0)
+        o, fs = _run_chunk(d, cfg, bf16=bf16)
+        torch.cuda.synchronize()
+        o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"], l2norm=0)
+        tol = TOL_BF16 if bf16 else TOL_F32
+        check(host(o), o_ref, tol, f"qk_l2norm=0 out {lengths}")
+        check(host(fs), s_ref, tol, f"qk_l2norm=0 state {lengths}")
+
+
+def _decode_inputs_l2norm_off(seed, B, geo=gi.Geometry()):
+    """Decode inputs whose q / k conv output is a unit row: identity taps (0, 0, 0, 1) on the
+    q / k channels, no activation, and unit q / k rows of x."""
+    d = gi.gen_decode(seed, B, geo)
+    nqk = 2 * geo.hk * geo.dk
+    d["conv_w"][:nqk] = np.array([0.0, 0.0, 0.0, 1.0], dtype=np.float32)
+    d["x"][:, :nqk] = _unit_rows(d["x"][:, :nqk].reshape(B, 2 * geo.hk, geo.dk), True).reshape(B, nqk)
+    return d
+
+
+def _oracle_decode_l2norm_off(orc, x, conv_w, conv_state, g, beta, z, norm_w, state, geo=gi.Geometry()):
+    """The oracle's decode step with q and k taken as given: its conv step (no activation),
+    its rule over one token per sequence with l2norm = 0, its gated norm."""
+    B = x.shape[0]
+    y, cs = orc.conv1d_step(x, conv_w, conv_state, act=0)
+    q = y[:, : geo.hk * geo.dk].reshape(B, geo.hk, geo.dk)
+    k = y[:, geo.hk * geo.dk: 2 * geo.hk * geo.dk].reshape(B, geo.hk, geo.dk)
+    v = y[:, 2 * geo.hk * geo.dk:].reshape(B, geo.hv, geo.dv)
+    o, s = orc.delta_rule(q, k, v, g, beta, np.arange(B + 1, dtype=np.int32), state, l2norm=0)
+    return orc.gated_rmsnorm(o, z, norm_w), cs, s
+
+
+def test_decode_step_l2norm_off(orc):
+    B = 16
+    d = _decode_inputs_l2norm_off(3400, B)
+    cfg = gdn.config(conv_act=0, qk_l2norm=0)
+    cs, st = dev(d["conv_state"], True), dev(d["state"])
+    out = gdn.decode_step(dev(d["x"], True), dev(d["conv_w"]), cs, dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], True), dev(d["norm_w"]), st, out_dtype=torch.float32, cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, cs_ref, s_ref = _oracle_decode_l2norm_off(orc, d["x"], d["conv_w"], d["conv_state"], d["g"],
+                                                       d["beta"], d["z"], d["norm_w"], d["state"])
+    check(host(out), out_ref, TOL_BF16, "qk_l2norm=0 decode out")
+    check(host(st), s_ref, TOL_BF16, "qk_l2norm=0 decode state")
+    assert np.array_equal(host(cs), cs_ref)
+
+
+def test_verify_l2norm_off(orc):
+    """The verify transaction with q and k as given: each row against the composed oracle
+    step from the state the previous rows leave; commit of all rows."""
+    B, K = 4, 3
+    steps = [_decode_inputs_l2norm_off(3500 + t, B) for t in range(K)]
+    for st_ in steps[1:]:
+        st_["conv_w"] = steps[0]["conv_w"]
+    d = dict(steps[0])
+    for key in ("x", "g", "beta", "z"):
+        d[key] = np.stack([st_[key] for st_ in steps], axis=1)
+    cfg = gdn.config(conv_act=0, qk_l2norm=0)
+    t_ = _verify_dev(d, True)
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.float32, cfg=cfg)
+    gdn.verify_commit(torch.full((B,), K, dtype=torch.int32, device="cuda"), t_["x"], t_["g"], t_["cs"], t_["st"],
+                      ws, cfg=cfg)
+    torch.cuda.synchronize()
+    cs, s = d["conv_state"], d["state"]
+    for t in range(K):
+        o_ref, cs, s = _oracle_decode_l2norm_off(orc, d["x"][:, t], d["conv_w"], cs, d["g"][:, t], d["beta"][:, t],
+                                                 d["z"][:, t], d["norm_w"], s)
+        check(host(out_v[:, t]), o_ref, TOL_BF16, f"qk_l2norm=0 verify row {t}")
+    check(host(t_["st"]), s, TOL_BF16, "qk_l2norm=0 committed state")
+    assert np.array_equal(host(t_["cs"]), cs)
