@@ -72,10 +72,11 @@ def t_dev(a, bf16=False):
 
 
 def time_calls(fn, n_sets, steps, warmup):
-    """Run fn(i) warmup + steps times; time the steps with events on the current stream.
-    Returns (mean ms, per-step ms list).  The mean comes from one event pair around all
-    steps (nothing recorded between launches); the per-step times from a second pass
-    with an event after every step."""
+    """Run fn(i) warmup + steps times, rotating over n_sets input sets; time the steps with
+    events on the current stream (the stream every library call enqueues on).  Returns
+    (mean ms, per-step ms list): the mean from one event pair around all steps (nothing
+    recorded between launches), the per-step times from a second pass with an event after
+    every step."""
     for i in range(warmup):
         fn(i % n_sets)
     torch.cuda.synchronize()
@@ -96,12 +97,26 @@ def time_calls(fn, n_sets, steps, warmup):
     return mean, per
 
 
+def spread(per):
+    """Median, p10 and p90 of per-step times (ms)."""
+    a = np.asarray(per)
+    return {"median_ms": float(np.median(a)), "p10_ms": float(np.percentile(a, 10)),
+            "p90_ms": float(np.percentile(a, 90)), "timed_calls": int(a.size)}
+
+
+def rotated(tensors, n_sets):
+    """n_sets device copies of each tensor (None stays None): the timed calls rotate over
+    them, so no call finds its inputs or state left in the 256 MB Infinity Cache by the
+    call before."""
+    return [[None if t is None else t.clone() for t in tensors] for _ in range(n_sets)]
+
+
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 214.0e6 + 206.0e6          # both launches of a step
 PREFILL_S4096_TRAFFIC_BYTES = 457.9e6 + 333.8e6    # gdn_prefill, all its kernels
 VARLEN_TRAFFIC_BYTES = 3215.6e6 + 1881.3e6
-KDA_TRAFFIC_BYTES = 3018.0e6 + 683.7e6
+KDA_TRAFFIC_BYTES = 3020.0e6 + 683.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
@@ -110,8 +125,28 @@ def roofline(bytes_alg, ms, traffic=None):
             "frac": achieved / PEAK_HBM_GBS, "traffic": traffic}
 
 
-def oracle_threads():
-    return int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+# Algorithmic flops of the chunk-wise rule per token and value head (64-token chunks, d = 128;
+# triangles counted as triangles): K K^T, W and U strictly lower (C(C-1)/2 d MACs each),
+# Q K^T and P V lower with the diagonal (C(C+1)/2 d), three full C d^2 products (the state
+# read for the rows, the state read for the output, the state update), and the unit-lower
+# solve (C^3 / 3 flops); divided by C.
+CHUNK_C = 64
+RULE_FLOPS_PER_TOKEN_HEAD = (3 * CHUNK_C * (CHUNK_C - 1) * D + 2 * CHUNK_C * (CHUNK_C + 1) * D
+                             + 3 * 2 * CHUNK_C * D * D + CHUNK_C ** 3 / 3) / CHUNK_C
+# the pipeline adds per token: the width-4 conv (2 flops per tap and channel), the q / k L2
+# norms (2 per element) and the gated norm (5 per output element: square-add, three scalings)
+PIPE_EXTRA_FLOPS_PER_TOKEN = 2 * 4 * CC + 2 * 2 * HK * D + 5 * HV * D
+PREFILL_FLOPS_PER_TOKEN = HV * RULE_FLOPS_PER_TOKEN_HEAD + PIPE_EXTRA_FLOPS_PER_TOKEN
+KDA_FLOPS_PER_TOKEN = KDA_H * RULE_FLOPS_PER_TOKEN_HEAD
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+
+
+def mfma_block(flops, ms):
+    """Achieved matrix throughput from algorithmic flops (the chunk form's contractions are
+    issued on bf16 MFMA, fp32 operands as hi / lo pairs) against the dense bf16 peak."""
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+            "flops_per_call": flops}
 
 
 # ---------------------------------------------------------------------------
@@ -152,7 +187,7 @@ def bench_decode(steps, warmup, batch=64, per_channel=False, derived_gates=False
 
     ms, per = time_calls(step, n_sets, steps, warmup)
     return dict(ms=ms, per=per, updates_per_s=batch / (ms * 1e-3),
-                roofline=roofline(bytes_per * batch, ms, traffic))
+                roofline=roofline(bytes_per * batch, ms, traffic), **spread(per))
 
 
 def bench_verify(steps, warmup, batch=64, K=4):
@@ -178,6 +213,7 @@ def bench_verify(steps, warmup, batch=64, K=4):
         gdn.verify_commit(accepted, x, g, convs[i], states[i], ws, cfg=cfg)
 
     ms, per = time_calls(step, n_sets, steps, warmup)
+    stats = spread(per)
     rec = K * (HV * D + HK * D) * 4
     # per sequence: state read by the verify, read + written by the commit; conv state read
     # by each and written by the commit; x, z, g, beta and out of the K rows; the records
@@ -185,74 +221,99 @@ def bench_verify(steps, warmup, batch=64, K=4):
     per_seq = (3 * STATE_BYTES + 3 * 3 * CC * 2 + K * (2 * CC * 2 + HV * D * 2 + 3 * HV * 4 + HV * D * 2)
                + 2 * rec)
     return dict(ms=ms, rows_per_s=batch * K / (ms * 1e-3), roofline=roofline(per_seq * batch, ms, None),
-                bytes_per_transaction=per_seq * batch)
+                bytes_per_transaction=per_seq * batch, **stats)
 
 
-def cpu_baseline_decode(target_s=10.0):
+def _oracle():
     import oracle
-    orc = oracle.Oracle()
+    return oracle.Oracle()
+
+
+def cpu_baseline_decode(target_s=10.0, single_s=5.0):
+    """The oracle's fused decode step of the 64-sequence batch, repeated for about target_s on
+    every host core, then about single_s on one thread."""
+    orc = _oracle()
     d = gi.gen_decode(1002, 64)
-    reps, t0 = 0, time.perf_counter()
-    state, cs = d["state"], d["conv_state"]
-    while True:
-        _, cs, state = orc.decode_step(d["x"], d["conv_w"], cs, d["g"], d["beta"], d["z"], d["norm_w"], state,
-                                       Hk=HK, Hv=HV, dk=D, dv=D)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= target_s or reps >= 400:
-            break
-    return dict(value=64 * reps / el, unit="state-updates/s", cores=oracle_threads(), kind="oracle",
-                sample=f"{reps} fused decode steps of the 64-sequence batch, fp64, {el:.1f} s")
+
+    def run(limit_s):
+        reps, t0 = 0, time.perf_counter()
+        state, cs = d["state"], d["conv_state"]
+        while True:
+            _, cs, state = orc.decode_step(d["x"], d["conv_w"], cs, d["g"], d["beta"], d["z"], d["norm_w"],
+                                           state, Hk=HK, Hv=HV, dk=D, dv=D)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= limit_s or reps >= 400:
+                return reps, el
+
+    cores = orc.max_threads()
+    reps, el = run(target_s)
+    orc.set_threads(1)
+    reps1, el1 = run(single_s)
+    orc.set_threads(cores)
+    return dict(value=64 * reps / el, unit="state-updates/s", cores=cores, kind="oracle",
+                sample=f"{reps} fused decode steps of the 64-sequence batch, fp64, {el:.1f} s",
+                single_thread=dict(value=64 * reps1 / el1, cores=1,
+                                   sample=f"{reps1} steps of the same batch on one thread, {el1:.1f} s"))
 
 
 # ---------------------------------------------------------------------------
 # prefill pipelines (conv -> chunk -> gated norm)
 # ---------------------------------------------------------------------------
 
-def bench_pipeline(lengths, seed, steps, warmup):
-    """A step is one gdn_prefill call (conv -> chunk -> gated norm).  The same work as three
-    separate calls (conv, chunk with an fp32 output, norm) is timed per call for the split."""
+def bench_pipeline(lengths, seed, steps, warmup, n_sets=3):
+    """A step is one gdn_prefill call (conv -> chunk -> gated norm) on one of n_sets rotated
+    copies of the inputs, states and outputs.  The same work as three separate calls (conv,
+    chunk with an fp32 output, norm) is timed per call for the split."""
     d = gi.gen_prefill(seed, lengths, bf16=True, init_state=True)
     cfg = gdn.config()
     T, N = int(sum(lengths)), len(lengths)
     cu_np = d["cu"]
     cu = torch.from_numpy(cu_np).cuda()
-    x, w, g, beta, z, nw = (t_dev(d["x"], True), t_dev(d["conv_w"]), t_dev(d["g"]), t_dev(d["beta"]),
-                            t_dev(d["z"], True), t_dev(d["norm_w"]))
-    s_in = t_dev(d["state_in"])
-    s_out = torch.empty_like(s_in)
+    base = (t_dev(d["x"], True), t_dev(d["g"]), t_dev(d["beta"]), t_dev(d["z"], True), t_dev(d["state_in"]),
+            torch.empty((N, HV, D, D), dtype=torch.float32, device="cuda"),
+            torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda"))
+    w, nw = t_dev(d["conv_w"]), t_dev(d["norm_w"])
+    del d
+    sets = rotated(base, n_sets)
+    del base
     y = torch.empty((T, CC), dtype=torch.bfloat16, device="cuda")
     o = torch.empty((T, HV, D), dtype=torch.float32, device="cuda")
-    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gdn.chunk_prefill_workspace_size(N, T, cfg), dtype=torch.uint8, device="cuda")
     ws_one = torch.empty(gdn.prefill_workspace_size(N, T, torch.bfloat16, cfg), dtype=torch.uint8, device="cuda")
 
-    def one_call(_):
+    def one_call(i):
+        x, g, beta, z, s_in, s_out, out = sets[i]
         gdn.prefill(x, w, cu, g, beta, z, nw, cu_host=cu_np, initial_state=s_in, out=out, final_state=s_out,
                     workspace=ws_one, cfg=cfg)
 
-    def conv():
-        gdn.conv1d_prefill(x, w, cu, cu_host=cu_np, y=y, cfg=cfg)
+    def conv(i):
+        gdn.conv1d_prefill(sets[i][0], w, cu, cu_host=cu_np, y=y, cfg=cfg)
 
-    def chunk():
+    def chunk(i):
+        x, g, beta, z, s_in, s_out, out = sets[i]
         gdn.chunk_prefill(y[:, : HK * D], y[:, HK * D: 2 * HK * D], y[:, 2 * HK * D:], g, beta, cu,
                           cu_host=cu_np, initial_state=s_in, out=o, final_state=s_out, workspace=ws, cfg=cfg)
 
-    def norm():
-        gdn.gated_rmsnorm(o, z, nw, out=out, cfg=cfg)
+    def norm(i):
+        gdn.gated_rmsnorm(o, sets[i][3], nw, out=sets[i][6], cfg=cfg)
 
-    ms, per = time_calls(one_call, 1, steps, warmup)
+    ms, per = time_calls(one_call, n_sets, steps, warmup)
     # the separate calls, each timed, over a few passes
     split = {"conv_ms": 0.0, "chunk_ms": 0.0, "norm_ms": 0.0}
     reps = 3
-    for _ in range(reps):
+    conv(0)   # first launches of these kernel variants load their code, untimed
+    chunk(0)
+    norm(0)
+    torch.cuda.synchronize()
+    for r in range(reps):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         evs[0].record()
-        conv()
+        conv(r % n_sets)
         evs[1].record()
-        chunk()
+        chunk(r % n_sets)
         evs[2].record()
-        norm()
+        norm(r % n_sets)
         evs[3].record()
         torch.cuda.synchronize()
         for i, key in enumerate(split):
@@ -261,13 +322,11 @@ def bench_pipeline(lengths, seed, steps, warmup):
     traffic = {(4096,): PREFILL_S4096_TRAFFIC_BYTES,
                tuple(gi.varlen_lengths()[0]): VARLEN_TRAFFIC_BYTES}.get(tuple(lengths))
     return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, traffic),
-                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, separate_calls=split)
+                mfma=mfma_block(PREFILL_FLOPS_PER_TOKEN * T, ms),
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, separate_calls=split, **spread(per))
 
 
-def cpu_baseline_pipeline(lengths, seed, max_tokens):
-    """The oracle over the first sequences of the workload, up to max_tokens tokens."""
-    import oracle
-    orc = oracle.Oracle()
+def _head_of(lengths, max_tokens):
     take, total = [], 0
     for n in lengths:
         if total + n > max_tokens:
@@ -275,55 +334,107 @@ def cpu_baseline_pipeline(lengths, seed, max_tokens):
             break
         take.append(n)
         total += n
-    take = [n for n in take if n > 0]
-    d = gi.gen_prefill(seed, take, bf16=True, init_state=True)
-    t0 = time.perf_counter()
-    orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"], Hk=HK, Hv=HV, dk=D, dv=D,
-                state_in=d["state_in"], round_y_bf16=True)
-    el = time.perf_counter() - t0
-    T = int(sum(take))
-    return dict(value=T / el, unit="tokens/s", cores=oracle_threads(), kind="oracle",
-                sample=f"{T} tokens (sequence lengths {take}) of the workload, all 48 heads, fp64, {el:.1f} s")
+    return [n for n in take if n > 0]
+
+
+def _repeat(run, limit_s):
+    """Call run() (which returns its own seconds) until limit_s have passed; returns (calls, s)."""
+    n, el = 0, 0.0
+    while el < limit_s:
+        el += run()
+        n += 1
+    return n, el
+
+
+def cpu_baseline_pipeline(lengths, seed, max_tokens, single_tokens=1024, target_s=10.0, single_s=5.0):
+    """The oracle's conv -> rule -> norm over the first sequences of the workload (up to
+    max_tokens tokens), repeated for about target_s on every host core, then over up to
+    single_tokens repeated for about single_s on one thread."""
+    orc = _oracle()
+
+    def sample(limit):
+        take = _head_of(lengths, limit)
+        d = gi.gen_prefill(seed, take, bf16=True, init_state=True)
+
+        def run():
+            t0 = time.perf_counter()
+            orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"], d["norm_w"], Hk=HK, Hv=HV, dk=D,
+                        dv=D, state_in=d["state_in"], round_y_bf16=True)
+            return time.perf_counter() - t0
+        return take, run
+
+    cores = orc.max_threads()
+    take, run = sample(max_tokens)
+    n, el = _repeat(run, target_s)
+    orc.set_threads(1)
+    take1, run1 = sample(single_tokens)
+    n1, el1 = _repeat(run1, single_s)
+    orc.set_threads(cores)
+    T, T1 = int(sum(take)), int(sum(take1))
+    return dict(value=n * T / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n} passes over {T} tokens (sequence lengths {take}) of the workload, all 48 heads, fp64, "
+                       f"{el:.1f} s",
+                single_thread=dict(value=n1 * T1 / el1, cores=1,
+                                   sample=f"{n1} passes over {T1} tokens (lengths {take1}) on one thread, {el1:.1f} s"))
 
 
 # ---------------------------------------------------------------------------
 # per-key-channel decay, chunk call alone
 # ---------------------------------------------------------------------------
 
-def bench_kda(steps, warmup, T=16384):
+def bench_kda(steps, warmup, T=16384, n_sets=3):
+    """The per-key-channel chunk call on n_sets rotated copies of its inputs (1.4 GB each)."""
     geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
     d = gi.gen_qkv(1005, [T], geo, per_channel=True)
     cfg = gdn.config(num_k_heads=KDA_H, num_v_heads=KDA_H, decay_per_key_channel=1)
     cu_np = d["cu"]
     cu = torch.from_numpy(cu_np).cuda()
-    q, k, v = t_dev(d["q"], True), t_dev(d["k"], True), t_dev(d["v"], True)
-    g, beta, s_in = t_dev(d["g"]), t_dev(d["beta"]), t_dev(d["state_in"])
+    base = (t_dev(d["q"], True), t_dev(d["k"], True), t_dev(d["v"], True), t_dev(d["g"]), t_dev(d["beta"]),
+            t_dev(d["state_in"]), torch.empty((1, KDA_H, D, D), dtype=torch.float32, device="cuda"),
+            torch.empty((T, KDA_H, D), dtype=torch.bfloat16, device="cuda"))
     del d
-    s_out = torch.empty_like(s_in)
-    out = torch.empty((T, KDA_H, D), dtype=torch.bfloat16, device="cuda")
+    sets = rotated(base, n_sets)
+    del base
     ws = torch.empty(gdn.chunk_prefill_workspace_size(1, T, cfg), dtype=torch.uint8, device="cuda")
 
-    def step(_):
+    def step(i):
+        q, k, v, g, beta, s_in, s_out, out = sets[i]
         gdn.chunk_prefill(q, k, v, g, beta, cu, cu_host=cu_np, initial_state=s_in, out=out, final_state=s_out,
                           workspace=ws, cfg=cfg)
 
-    ms, per = time_calls(step, 1, steps, warmup)
+    ms, per = time_calls(step, n_sets, steps, warmup)
     bytes_alg = KDA_BYTES_PER_TOKEN * T + 2 * KDA_STATE_BYTES
     return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, KDA_TRAFFIC_BYTES),
-                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3)
+                mfma=mfma_block(KDA_FLOPS_PER_TOKEN * T, ms),
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, **spread(per))
 
 
-def cpu_baseline_kda(tokens=2048):
-    import oracle
-    orc = oracle.Oracle()
+def cpu_baseline_kda(tokens=2048, single_tokens=256, target_s=10.0, single_s=5.0):
+    """The oracle's per-key-channel rule over the first tokens of the workload, repeated for
+    about target_s on every host core and single_s on one thread."""
+    orc = _oracle()
     geo = gi.Geometry(hk=KDA_H, hv=KDA_H)
-    d = gi.gen_qkv(1005, [tokens], geo, per_channel=True)
-    t0 = time.perf_counter()
-    orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
-    el = time.perf_counter() - t0
-    return dict(value=tokens / el, unit="tokens/s", cores=oracle_threads(), kind="oracle",
-                sample=f"first {tokens} tokens of the 16384-token per-key-channel workload, 64 heads, fp64, "
-                       f"{el:.1f} s")
+
+    def sample(n):
+        d = gi.gen_qkv(1005, [n], geo, per_channel=True)
+
+        def run():
+            t0 = time.perf_counter()
+            orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+            return time.perf_counter() - t0
+        return run
+
+    cores = orc.max_threads()
+    n, el = _repeat(sample(tokens), target_s)
+    orc.set_threads(1)
+    n1, el1 = _repeat(sample(single_tokens), single_s)
+    orc.set_threads(cores)
+    return dict(value=n * tokens / el, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{n} passes over the first {tokens} tokens of the 16384-token per-key-channel workload, "
+                       f"64 heads, fp64, {el:.1f} s",
+                single_thread=dict(value=n1 * single_tokens / el1, cores=1,
+                                   sample=f"{n1} passes over the first {single_tokens} tokens on one thread, "
+                                          f"{el1:.1f} s"))
 
 
 def calibration_copy(steps):
@@ -356,20 +467,20 @@ def main():
         return
     wl = args.workload
     cpu = not args.no_cpu_baseline
-    small_steps, small_warm = max(5, args.steps // 10), max(2, args.warmup)   # the clocks settle over the first calls
+    # at least 20 timed calls of each workload; the clocks settle over the first calls
+    small_steps, small_warm = max(20, args.steps // 10), max(5, args.warmup)
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
     workloads = {}
     if wl in ("all", "decode"):
         dec = bench_decode(args.steps, args.warmup)
-        per = np.array(dec["per"])
         line.update({
             "value": dec["updates_per_s"], "unit": "state-updates/s", "ms_per_step": dec["ms"],
             "dtype": "f32",
             "config": {"workload": "decode_b64_bf16", "batch": 64, "k_heads": HK, "v_heads": HV, "head_dim": D,
                        "activations": "bf16", "state": "f32 [64,48,128,128], 3 sets rotated"},
-            "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
-            "head_updates_per_s": dec["updates_per_s"] * HV,
+            "median_ms": dec["median_ms"], "p10_ms": dec["p10_ms"], "p90_ms": dec["p90_ms"],
+            "input_sets": 3, "head_updates_per_s": dec["updates_per_s"] * HV,
             "roofline": dict(dec["roofline"], kernel="decode_step_kernel + conv_shift_kernel (the two launches of one step, timed together)",
                              bytes_per_update=DECODE_BYTES_PER_UPDATE),
         })
@@ -379,8 +490,9 @@ def main():
         pre = bench_pipeline([4096], 1003, small_steps, small_warm)
         workloads["prefill_s4096_bf16"] = dict(
             metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], call="gdn_prefill",
-            separate_calls=pre["separate_calls"], roofline=pre["roofline"],
-            roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate")
+            separate_calls=pre["separate_calls"], roofline=pre["roofline"], mfma=pre["mfma"],
+            roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate",
+            input_sets=3, **{k: pre[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")})
         if cpu:
             workloads["prefill_s4096_bf16"]["cpu_baseline"] = cpu_baseline_pipeline([4096], 1003, 4096)
     if wl in ("all", "varlen"):
@@ -388,37 +500,43 @@ def main():
         var = bench_pipeline(lengths, 1004, small_steps, small_warm)
         workloads["varlen8_33k_bf16"] = dict(
             metric="tokens/s", value=var["tokens_per_s"], ms=var["ms"], tokens=var["tokens"], lengths=lengths,
-            call="gdn_prefill", separate_calls=var["separate_calls"], roofline=var["roofline"],
-            roofline_ms=var["roofline_ms"])
+            call="gdn_prefill", separate_calls=var["separate_calls"], roofline=var["roofline"], mfma=var["mfma"],
+            roofline_ms=var["roofline_ms"], input_sets=3,
+            **{k: var[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")})
         if cpu:
             workloads["varlen8_33k_bf16"]["cpu_baseline"] = cpu_baseline_pipeline(lengths, 1004, 4096)
     if wl in ("all", "kda"):
-        kda = bench_kda(max(3, args.steps // 40), 1)
+        kda = bench_kda(small_steps, 3)
         workloads["kda_h64_s16384_bf16"] = dict(
-            metric="tokens/s", value=kda["tokens_per_s"], ms=kda["ms"], roofline=kda["roofline"],
-            roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel")
+            metric="tokens/s", value=kda["tokens_per_s"], ms=kda["ms"], roofline=kda["roofline"], mfma=kda["mfma"],
+            roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel", input_sets=3,
+            **{k: kda[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")})
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
     if wl in ("all", "decode_h16"):
         dh = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), state_f16=True)
         workloads["decode_b64_h16_bf16"] = dict(
             metric="state-updates/s", value=dh["updates_per_s"], ms=dh["ms"], roofline=dh["roofline"],
+            median_ms=dh["median_ms"], p10_ms=dh["p10_ms"], p90_ms=dh["p90_ms"],
             call="gdn_decode_step_h16: the recurrent state stored in fp16 (rounded once per token)")
     if wl in ("all", "verify"):
         ver = bench_verify(max(20, args.steps // 4), max(5, args.warmup // 4))
         workloads["verify_k4_b64_bf16"] = dict(
             metric="state-updates/s", value=ver["rows_per_s"], ms=ver["ms"], roofline=ver["roofline"],
+            median_ms=ver["median_ms"], p10_ms=ver["p10_ms"], p90_ms=ver["p90_ms"],
             bytes_per_transaction=ver["bytes_per_transaction"],
             call="gdn_verify (64 sequences x 4 rows) + gdn_verify_commit accepting all 4; one update = one row")
     if wl in ("all", "decode_ab"):
         dab = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), derived_gates=True)
         workloads["decode_b64_ab_bf16"] = dict(
             metric="state-updates/s", value=dab["updates_per_s"], ms=dab["ms"], roofline=dab["roofline"],
+            median_ms=dab["median_ms"], p10_ms=dab["p10_ms"], p90_ms=dab["p90_ms"],
             call="gdn_decode_step_ab: g, beta derived in the kernel from the a / b projections")
     if wl in ("all", "kda_decode"):
         kdd = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), per_channel=True)
         workloads["kda_decode_b64_h64_bf16"] = dict(
             metric="state-updates/s", value=kdd["updates_per_s"], ms=kdd["ms"], roofline=kdd["roofline"],
+            median_ms=kdd["median_ms"], p10_ms=kdd["p10_ms"], p90_ms=kdd["p90_ms"],
             bytes_per_update=KDA_DECODE_BYTES_PER_UPDATE,
             call="gdn_decode_step, decay per key channel, 64 heads, state f32 [64,64,128,128], 3 sets rotated")
     if wl != "decode" and "value" not in line:
@@ -426,6 +544,9 @@ def main():
         name, obj = next(iter(workloads.items()))
         line.update({"value": obj["value"], "unit": obj["metric"], "ms_per_step": obj["ms"], "dtype": "bf16",
                      "config": {"workload": name}, "roofline": obj["roofline"]})
+        for key in ("mfma", "median_ms", "p10_ms", "p90_ms"):
+            if key in obj:
+                line[key] = obj[key]
         if "cpu_baseline" in obj:
             line["cpu_baseline"] = obj["cpu_baseline"]
     if workloads:

@@ -116,6 +116,17 @@ class Oracle:
     def __init__(self, lib: Optional[ctypes.CDLL] = None):
         self.lib = lib if lib is not None else load()
 
+    def set_threads(self, n: int) -> None:
+        """OpenMP threads for the routines' parallel loops (the runtime the oracle is
+        built against; its independent (sequence, head) or channel loops only)."""
+        self.lib.omp_set_num_threads.argtypes = [ctypes.c_int]
+        self.lib.omp_set_num_threads.restype = None
+        self.lib.omp_set_num_threads(int(n))
+
+    def max_threads(self) -> int:
+        self.lib.omp_get_max_threads.restype = ctypes.c_int
+        return int(self.lib.omp_get_max_threads())
+
     # -- conv (a1) ---------------------------------------------------------
     def conv1d(self, x, w, cu, state_in=None, act: int = 1) -> Tuple[np.ndarray, np.ndarray]:
         """x [T,C], w [C,4], cu [N+1] -> (y [T,C], state_out [N,3,C])."""
