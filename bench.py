@@ -21,11 +21,16 @@ Also measured in the same run (``workloads``):
 each in tokens/s (state-updates/s for the decode) with its roofline fraction (algorithmic HBM
 bytes / time / 8 TB/s).
 
-Every launch is a library call on torch's current stream (the stream the
-library enqueues on), timed with events on that stream.  ``cpu_baseline``
-runs the fp64 oracle (test infrastructure) on the host cores over a bounded
-sample of the same workload.  ``--calibration-copy`` only runs 256 MiB device
-copies (the known-size reference for the HBM traffic counters).
+Every workload rotates three copies of its inputs, states and outputs and times
+at least 20 calls.  Every launch is a library call on torch's current stream
+(the stream the library enqueues on), timed with events on that stream: the
+mean from one event pair around all timed calls, median / p10 / p90 from a
+second pass with an event after each call.  The prefill-side workloads also
+report an ``mfma`` block (the method's algorithmic flops against the dense bf16
+peak).  ``cpu_baseline`` runs the fp64 oracle (test infrastructure) over a
+bounded sample of the same workload, on every host core and on one thread.
+``--calibration-copy`` only runs 256 MiB device copies (the known-size
+reference for the HBM traffic counters).
 """
 from __future__ import annotations
 
