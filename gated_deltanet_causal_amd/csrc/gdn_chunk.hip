@@ -60,7 +60,7 @@ constexpr int kSpineLds = 0;    // 8 waves per 32 value rows, intermediates thro
 constexpr int kSpineWave = 1;   // register-resident, a value head per workgroup
 constexpr int kSpineRows = 2;   // register-resident, 32 value rows per workgroup
 constexpr int kRowsNW = 2;        // kSpineRows: compute waves (16 value rows each)
-constexpr int kRowsLoaders = 2;   // kSpineRows: loader waves staging the next chunk
+constexpr int kRowsLoaders = 4;   // kSpineRows: loader waves staging the next chunk
 constexpr int kWaveSpineMinBlocks = 256;   // value heads x sequences from which kSpineWave is used
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -124,6 +124,16 @@ __device__ __forceinline__ void store_acc_transposed(typename Ops<F32>::E* hi, t
     *reinterpret_cast<uint2*>(hi + off) = make_uint2(h2[0], h2[1]);
     *reinterpret_cast<uint2*>(lo + off) = make_uint2(l2[0], l2[1]);
   }
+}
+
+// The plan's outputs.  A single sequence needs no plan: its chunks start at 0
+// and it is the whole order, so the plan kernel is not launched for it and
+// its workspace entries are never read.
+__device__ __forceinline__ int plan_first(const int32_t* first, int n_seq, int n) {
+  return n_seq == 1 ? 0 : first[n];
+}
+__device__ __forceinline__ int plan_order(const int32_t* order, int n_seq, int i) {
+  return n_seq == 1 ? 0 : order[i];
 }
 
 // Chunk index -> sequence: largest n with first[n] <= c (first is a prefix sum).
@@ -473,7 +483,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   const int kh = h / (hv / hk);
   const int tid = threadIdx.x, wave = tid / kWave;
   const int n = chunk_sequence(first, n_seq, c);
-  const int t0 = cu[n] + (c - first[n]) * kC;
+  const int t0 = cu[n] + (c - plan_first(first, n_seq, n)) * kC;
   const int L = min(kC, cu[n + 1] - t0);
 
   load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
   const int kh = blockIdx.y;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int n = chunk_sequence(first, n_seq, c);
-  const int t0 = cu[n] + (c - first[n]) * kC;
+  const int t0 = cu[n] + (c - plan_first(first, n_seq, n)) * kC;
   const int L = min(kC, cu[n + 1] - t0);
   const int ratio = hv / hk;
 
@@ -1212,7 +1222,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   const int member = rest % members;
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int32_t* order = first + n_seq + 1;
-  const int n = order[grp / hk];
+  const int n = plan_order(order, n_seq, grp / hk);
   const int kh = grp % hk;
   const int h = kh * ratio + member / (kD / kTile);
   const int tile = member % (kD / kTile);
@@ -1220,7 +1230,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const uint8_t* recs = ws + records_offset(n_seq);
   const int seq_beg = cu[n], seq_end = cu[n + 1];
-  const int chunk0 = first[n];
+  const int chunk0 = plan_first(first, n_seq, n);
   auto rec_of = [&](int cidx) { return recs + ((size_t)cidx * hv + h) * kRecBytes; };
 
   // Roles.  Wave w owns token row tile mt = w % 4 and dv half hf = w / 4 of
@@ -1712,7 +1722,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   const int member = rest % members;
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int32_t* order = first + n_seq + 1;
-  const int n = order[grp / hk];
+  const int n = plan_order(order, n_seq, grp / hk);
   const int kh = grp % hk;
   const int h = kh * ratio + member / blocks_per_head;
   const int i0 = (member % blocks_per_head) * Cf::kRows;     // first value row of the workgroup
@@ -1730,7 +1740,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   stage.vp = v + h * kD + i0;
   stage.qk_stride = qk_stride;
   stage.v_stride = v_stride;
-  stage.rec0 = ws + records_offset(n_seq) + ((size_t)first[n] * hv + h) * kRecBytes;
+  stage.rec0 = ws + records_offset(n_seq) + ((size_t)plan_first(first, n_seq, n) * hv + h) * kRecBytes;
   stage.rec_step = (size_t)hv * kRecBytes;
   stage.seq_beg = seq_beg;
   stage.seq_end = seq_end;
@@ -2062,10 +2072,13 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   // workgroup (two compute waves, one per SIMD, and two loader waves) spread
   // them over four times as many workgroups.
   const int spine = chunk_spine_kind(d, !F32, n);
-  hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
-                     reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  if (n > 1) {   // one sequence: the kernels know its plan (plan_first, plan_order)
+    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(kThreads), 0, s, cu_dev, n,
+                       reinterpret_cast<int32_t*>(w), reinterpret_cast<int32_t*>(w) + n + 1);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (total_chunks > 0) {
     if constexpr (kPC)
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
