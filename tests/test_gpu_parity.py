@@ -429,7 +429,7 @@ def _prefill_ref(orc, d, bf16):
 @pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float32], ids=["out_bf16", "out_f32"])
 def test_prefill_entry_bf16(orc, lengths, out_dtype):
     """conv -> chunk -> gated norm in one call, bf16 activations, carried conv and recurrent
-    state.  One sequence runs the key-split spine and a separate norm; six or more sequences
+    state.  One sequence runs the 32-row spine and a separate norm; six or more sequences
     of 48 value heads run the whole-head spine with the norm applied in its epilogue."""
     d = gi.gen_prefill(500 + sum(lengths), lengths, bf16=True, conv_state=True)
     out, fs, cso = _prefill_gpu(d, True, out_dtype)
@@ -437,6 +437,30 @@ def test_prefill_entry_bf16(orc, lengths, out_dtype):
     check(host(out), out_ref, TOL_BF16, f"prefill out {lengths}", stored_bf16=out_dtype == torch.bfloat16)
     check(host(fs), s_ref, TOL_BF16, f"prefill state {lengths}")
     assert np.array_equal(host(cso), cso_ref), "conv state out: the last three inputs, copied"
+
+
+@pytest.mark.parametrize("act", [1, 0], ids=["silu", "noact"])
+def test_prefill_entry_few_sequences_conv_state_in_place(orc, act):
+    """Five sequences (one empty, one of two tokens) on the 32-row spine, the conv state
+    updated in place: the taps before each sequence start come from the carried state, which
+    the call overwrites with each sequence's last three inputs."""
+    lengths = [70, 0, 2, 130, 64]
+    d = gi.gen_prefill(560 + act, lengths, bf16=True, conv_state=True)
+    cfg = gdn.config(conv_act=act)
+    x = dev(d["x"], True)
+    cs = dev(d["conv_state_in"], True)
+    out, fs = gdn.prefill(x, dev(d["conv_w"]), dev_i32(d["cu"]), dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], True), dev(d["norm_w"]), cu_host=d["cu"], conv_state_in=cs,
+                          conv_state_out=cs, initial_state=dev(d["state_in"]), out_dtype=torch.float32,
+                          cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, _, s_ref, cso_ref, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"],
+                                                d["norm_w"], Hk=HK, Hv=HV, dk=D, dv=D,
+                                                conv_state_in=d["conv_state_in"], state_in=d["state_in"],
+                                                act=act, round_y_bf16=True)
+    check(host(out), out_ref, TOL_BF16, f"prefill out {lengths} act={act}")
+    check(host(fs), s_ref, TOL_BF16, f"prefill state {lengths} act={act}")
+    assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
 
 
 def test_prefill_entry_fp32_s80(orc):
