@@ -1936,7 +1936,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     }
 
     // The next chunk's inputs go to the other LDS slot in pieces between the
-    // remaining MFMAs (groups: U first half, O^T, U second half).
+    // remaining MFMAs (groups: U first half, U second half, O^T).
     constexpr int kCGroups = 2 * kJT + kNF;
     constexpr int kCPer = (kLoads + kCGroups - 1) / kCGroups;
     auto commit_group = [&](int grp_idx) {
@@ -1961,6 +1961,25 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     read_kt(32, kt);   // the second k step reuses kt
     read_pt();
 
+    // the second half of U and the state update before O^T: the update is the
+    // chain into the next chunk, O^T only feeds this chunk's output
+#pragma unroll
+    for (int jt = 0; jt < kJT; ++jt) {
+      commit_group(kJT + kNF + jt);
+      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
+      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
+      if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- S <- d S + U ----
+    {
+      const float d = vec[3 * kC];
+#pragma unroll
+      for (int jt = 0; jt < kJT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sst[jt][e] = fmaf(d, sst[jt][e], u[jt][e]);
+    }
+
     // ---- O^T = Z^T diag(b) + Vnew^T Pt^T on this wave's token tiles ----
     // (rows i, columns t: A = Vnew pairs, B = Pt fragments)
 #pragma unroll
@@ -1978,23 +1997,6 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
         zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
         if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
-    }
-
-#pragma unroll
-    for (int jt = 0; jt < kJT; ++jt) {
-      commit_group(kJT + kNF + jt);
-      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
-      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
-      if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
-    }
-
-    // ---- S <- d S + U ----
-    {
-      const float d = vec[3 * kC];
-#pragma unroll
-      for (int jt = 0; jt < kJT; ++jt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sst[jt][e] = fmaf(d, sst[jt][e], u[jt][e]);
     }
 
     // ---- the output: lane (g, m) of tile mt holds O[16 mt + m][iw + 4 g .. +3] ----
