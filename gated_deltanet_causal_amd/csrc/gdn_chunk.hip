@@ -114,13 +114,7 @@ __device__ __forceinline__ void store_acc_transposed(typename Ops<F32>::E* hi, t
   } else {
     uint32_t h2[2], l2[2];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      __bf16 ha, la, hb, lb;
-      split_bf16(v[2 * e], ha, la);
-      split_bf16(v[2 * e + 1], hb, lb);
-      h2[e] = __builtin_bit_cast(uint16_t, ha) | (uint32_t(__builtin_bit_cast(uint16_t, hb)) << 16);
-      l2[e] = __builtin_bit_cast(uint16_t, la) | (uint32_t(__builtin_bit_cast(uint16_t, lb)) << 16);
-    }
+    for (int e = 0; e < 2; ++e) split2(v[2 * e], v[2 * e + 1], h2[e], l2[e]);
     *reinterpret_cast<uint2*>(hi + off) = make_uint2(h2[0], h2[1]);
     *reinterpret_cast<uint2*>(lo + off) = make_uint2(l2[0], l2[1]);
   }
@@ -409,15 +403,18 @@ __device__ __forceinline__ void decayed_frag(const typename Ops<F32>::E* raw, in
       f0 = *reinterpret_cast<const f32x4_t*>(ref + c0);
       f1 = *reinterpret_cast<const f32x4_t*>(ref + c0 + 4);
     }
+    float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float kv = (e & 1) ? __uint_as_float(u[e / 2] & 0xffff0000u) : __uint_as_float(u[e / 2] << 16);
       const float ge = e < 4 ? g0[e] - f0[e] : g1[e - 4] - f1[e - 4];
-      __bf16 a, b;
-      split_bf16(kv * s * __expf(sgn * ge), a, b);
-      hi[e] = a;
-      lo[e] = b;
+      x[e] = kv * s * __expf(sgn * ge);
     }
+    uint32_t hp[4], lp[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split2(x[2 * e], x[2 * e + 1], hp[e], lp[e]);
+    hi = __builtin_bit_cast(bf16x8_t, u32x4_t{hp[0], hp[1], hp[2], hp[3]});
+    lo = __builtin_bit_cast(bf16x8_t, u32x4_t{lp[0], lp[1], lp[2], lp[3]});
   }
 }
 
@@ -1121,9 +1118,6 @@ __device__ __forceinline__ void stage_commit_pcb(const Stage<false, true>& sg, u
     gl[c] = lane < 32 ? tot31 : tot63;
   }
   auto bf = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); };
-  auto pack = [](__bf16 a, __bf16 b) {
-    return uint32_t(__builtin_bit_cast(uint16_t, a)) | (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
-  };
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     const float* gam = r ? gam1 : gam0;
@@ -1131,16 +1125,9 @@ __device__ __forceinline__ void stage_commit_pcb(const Stage<false, true>& sg, u
     uint32_t kh[4], kl[4], qh[4], ql[4];
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      __bf16 a0, b0, a1, b1, c0, d0, c1, d1;
       const float e0 = __expf(gam[2 * w]), e1 = __expf(gam[2 * w + 1]);
-      split_bf16(bf(sg.k[r][w], 0) * rk * e0, a0, b0);
-      split_bf16(bf(sg.k[r][w], 1) * rk * e1, a1, b1);
-      split_bf16(bf(sg.q[r][w], 0) * rq * e0, c0, d0);
-      split_bf16(bf(sg.q[r][w], 1) * rq * e1, c1, d1);
-      kh[w] = pack(a0, a1);
-      kl[w] = pack(b0, b1);
-      qh[w] = pack(c0, c1);
-      ql[w] = pack(d0, d1);
+      split2(bf(sg.k[r][w], 0) * rk * e0, bf(sg.k[r][w], 1) * rk * e1, kh[w], kl[w]);
+      split2(bf(sg.q[r][w], 0) * rq * e0, bf(sg.q[r][w], 1) * rq * e1, qh[w], ql[w]);
     }
     const int off = (t + r) * pitch + j0;
     *reinterpret_cast<u32x4_t*>(sKh + off) = u32x4_t{kh[0], kh[1], kh[2], kh[3]};
@@ -1151,11 +1138,11 @@ __device__ __forceinline__ void stage_commit_pcb(const Stage<false, true>& sg, u
   // the update's operand, transposed: column j of rows t, t+1 as one 4-byte pair
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    __bf16 h0, l0, h1, l1;
-    split_bf16(bf(sg.k[0][c / 2], c & 1) * sg.rkq[0] * __expf(gl[c] - gam0[c]), h0, l0);
-    split_bf16(bf(sg.k[1][c / 2], c & 1) * sg.rkq[1] * __expf(gl[c] - gam1[c]), h1, l1);
-    *reinterpret_cast<uint32_t*>(sKth + (j0 + c) * tpitch + t) = pack(h0, h1);
-    *reinterpret_cast<uint32_t*>(sKtl + (j0 + c) * tpitch + t) = pack(l0, l1);
+    uint32_t hp, lp;
+    split2(bf(sg.k[0][c / 2], c & 1) * sg.rkq[0] * __expf(gl[c] - gam0[c]),
+           bf(sg.k[1][c / 2], c & 1) * sg.rkq[1] * __expf(gl[c] - gam1[c]), hp, lp);
+    *reinterpret_cast<uint32_t*>(sKth + (j0 + c) * tpitch + t) = hp;
+    *reinterpret_cast<uint32_t*>(sKtl + (j0 + c) * tpitch + t) = lp;
   }
   if (t == 0) {
 #pragma unroll
