@@ -463,6 +463,33 @@ def test_prefill_entry_few_sequences_conv_state_in_place(orc, act):
     assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
 
 
+@pytest.mark.parametrize("bf16", [True, False], ids=["bf16", "fp32"])
+def test_prefill_entry_per_channel(orc, bf16):
+    """The one-call prefill with per-key-channel decay (conv -> per-channel chunk -> gated
+    norm): 2 key / 6 value heads, packed sequences with an empty and a sub-chunk one, carried
+    conv and recurrent state, the conv state updated in place, and g = -10 in a quarter of
+    each head's channels."""
+    geo = gi.Geometry(hk=2, hv=6)
+    lengths = [70, 0, 3, 129]
+    d = gi.gen_prefill(580 + int(bf16), lengths, geo, bf16=bf16, conv_state=True, per_channel=True)
+    d["g"] = gi.strong_channel_decay(d["g"], "quarter_m10", 581)
+    cfg = gdn.config(num_k_heads=2, num_v_heads=6, decay_per_key_channel=1)
+    cs = dev(d["conv_state_in"], bf16)
+    out, fs = gdn.prefill(dev(d["x"], bf16), dev(d["conv_w"]), dev_i32(d["cu"]), dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], bf16), dev(d["norm_w"]), cu_host=d["cu"], conv_state_in=cs,
+                          conv_state_out=cs, initial_state=dev(d["state_in"]), out_dtype=torch.float32,
+                          cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, _, s_ref, cso_ref, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"],
+                                                d["norm_w"], Hk=2, Hv=6, dk=D, dv=D,
+                                                conv_state_in=d["conv_state_in"], state_in=d["state_in"],
+                                                round_y_bf16=bf16)
+    tol = TOL_BF16 if bf16 else TOL_F32
+    check(host(out), out_ref, tol, f"per-channel prefill out {lengths}")
+    check(host(fs), s_ref, tol, f"per-channel prefill state {lengths}")
+    assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
+
+
 def test_prefill_entry_fp32_s80(orc):
     """The 80-token fp32 case through the one-call prefill, at the fp32 bound."""
     d = gi.gen_prefill(1001, [80], bf16=False, conv_state=True)
