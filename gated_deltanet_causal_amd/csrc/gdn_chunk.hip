@@ -1489,10 +1489,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
 // registers: nothing but the chunk's shared inputs passes through LDS.  K and Q
 // are stored in LDS with each 32-column block in paired-tile order, so an A
 // fragment is one 16-byte read.  A workgroup is kNW waves (16 kNW value rows of
-// one head) sharing the chunk's K, Q, V and vectors, double-buffered in LDS
-// and staged through registers one chunk ahead; Tt and Pt go straight from the
-// record into each wave's registers, also one chunk ahead.  One barrier per
-// chunk.
+// one head) sharing the chunk's K, Q, V, vectors and the record's Tt / Pt
+// fragments, double-buffered in LDS and staged through registers one chunk
+// ahead; each wave reads the Tt / Pt fragments from LDS as A operands.  One
+// barrier per chunk.
 // ---------------------------------------------------------------------------
 constexpr int kWP = kD + 16;   // K / Q row pitch in LDS (bf16 elements): 288 bytes
 
@@ -2058,7 +2058,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
   // work overlaps the other's MFMAs, and the gated norm can be fused) once
   // there is a workgroup for every CU; for fewer sequences 32 value rows per
-  // workgroup (two compute waves, one per SIMD, and two loader waves) spread
+  // workgroup (two compute waves, one per SIMD, and four loader waves) spread
   // them over four times as many workgroups.
   const int spine = chunk_spine_kind(d, !F32, n);
   hipError_t e = hipSuccess;
