@@ -3,8 +3,9 @@
 Inputs are seeded and synthetic (gdn_inputs), with the pages' geometry (16 key
 and 48 value heads of 128, conv 4, chunk 64) and the workloads' distributions.
 Small cases compare every element; the full-size workloads (4096-token
-prefill, 64-sequence decode, the ~32k-token varlen batch) run whole on the GPU
-and are compared on sampled heads that the oracle computes over every token.
+prefill, 64-sequence decode, the ~32k-token varlen batch, the 64-head
+16384-token per-key-channel call) run whole on the GPU and are compared with the
+oracle over every head and token.
 """
 import numpy as np
 import pytest
@@ -320,18 +321,6 @@ def test_chunk_prefill_varlen_empty_and_inplace_state(orc):
     check(host(fs2), s_ref2, TOL_BF16, "varlen state, zero state")
 
 
-def _sampled_heads(orc, d, kheads):
-    """Oracle over every token for the value heads of the given key heads."""
-    ratio = HV // HK
-    vheads = [kh * ratio + r for kh in kheads for r in range(ratio)]
-    q = d["q"][:, kheads]
-    k = d["k"][:, kheads]
-    v = d["v"][:, vheads]
-    s_in = None if d["state_in"] is None else d["state_in"][:, vheads]
-    o, s = orc.delta_rule(q, k, v, d["g"][:, vheads], d["beta"][:, vheads], d["cu"], s_in)
-    return vheads, o, s
-
-
 def test_chunk_prefill_s4096_full_size_all_heads(orc):
     """The 4096-token prefill workload (bf16, random initial state) run whole, every value
     head compared with the oracle over all tokens."""
@@ -345,34 +334,34 @@ def test_chunk_prefill_s4096_full_size_all_heads(orc):
     check(host(fs), s_ref, TOL_BF16, "S=4096 state (48 heads)")
 
 
-def test_varlen_32k_full_size_sampled(orc):
+def test_varlen_32k_full_size_all_heads(orc):
     """The varlen workload: 63, 64, 65 plus five lengths in [1, 8192] (~32k tokens), per-sequence
-    initial states; the value heads of key heads 5 and 12 compared over every token."""
+    initial states; every value head compared with the oracle over every token."""
     lengths, seed = gi.varlen_lengths()
     d = gi.gen_qkv(1004, lengths)
     o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
                               dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"],
                               initial_state=dev(d["state_in"]), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    vheads, o_ref, s_ref = _sampled_heads(orc, d, [5, 12])
-    check(host(o)[:, vheads], o_ref, TOL_BF16, f"varlen {lengths} out")
-    check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen state")
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"varlen {lengths} out (48 heads)")
+    check(host(fs), s_ref, TOL_BF16, "varlen state (48 heads)")
 
 
 def test_chunk_prefill_4200_short_sequences(orc):
     """More sequences than the plan's longest-first ordering covers (over 4096: identity
     order), most of them empty or a few tokens long, some crossing a chunk, zero initial
-    states: every output row and final state of the value heads of key head 3, and zero final
-    states for the empty sequences."""
+    states: every output row and final state of every value head, and zero final states for
+    the empty sequences."""
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.choice([0, 1, 2, 3, 65], size=4200, p=[0.3, 0.3, 0.2, 0.15, 0.05])]
     d = gi.gen_qkv(2500, lengths, init_state=False)
     o, fs = gdn.chunk_prefill(dev(d["q"], True), dev(d["k"], True), dev(d["v"], True), dev(d["g"]),
                               dev(d["beta"]), dev_i32(d["cu"]), cu_host=d["cu"], out_dtype=torch.float32)
     torch.cuda.synchronize()
-    vheads, o_ref, s_ref = _sampled_heads(orc, d, [3])
-    check(host(o)[:, vheads], o_ref, TOL_BF16, "4200 short sequences out")
-    check(host(fs)[:, vheads], s_ref, TOL_BF16, "4200 short sequences state")
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], None)
+    check(host(o), o_ref, TOL_BF16, "4200 short sequences out")
+    check(host(fs), s_ref, TOL_BF16, "4200 short sequences state")
     empty = [n for n, L in enumerate(lengths) if L == 0]
     assert not torch.any(fs[empty]), "an empty sequence hands its (zero) state through"
 
@@ -530,28 +519,17 @@ def test_prefill_entry_s4096_all_heads(orc):
     assert np.array_equal(host(cso), cso_ref)
 
 
-def test_prefill_entry_varlen_full_size_sampled(orc):
+def test_prefill_entry_varlen_full_size_all_heads(orc):
     """The ~32k-token varlen workload through the one-call prefill (eight sequences: the
-    norm runs in the spine's epilogue); the value heads of key head 5 compared with the
-    oracle's conv -> delta rule -> norm over every token."""
+    norm runs in the spine's epilogue) against the oracle's conv -> delta rule -> norm, every
+    value head over every token, and the carried conv state."""
     lengths, _ = gi.varlen_lengths()
     d = gi.gen_prefill(1005, lengths, bf16=True, conv_state=True)
     out, fs, cso = _prefill_gpu(d, True, torch.bfloat16)
-    kh, ratio = 5, HV // HK
-    vheads = [kh * ratio + r for r in range(ratio)]
-    cols = np.concatenate([np.arange(kh * D, (kh + 1) * D), np.arange((HK + kh) * D, (HK + kh + 1) * D)] +
-                          [np.arange(2 * HK * D + h * D, 2 * HK * D + (h + 1) * D) for h in vheads])
-    y, cso_ref = orc.conv1d(d["x"][:, cols], d["conv_w"][cols], d["cu"], d["conv_state_in"][:, :, cols])
-    y = oracle.round_bf16(y)
-    T = y.shape[0]
-    o_ref, s_ref = orc.delta_rule(y[:, :D].reshape(T, 1, D), y[:, D: 2 * D].reshape(T, 1, D),
-                                  y[:, 2 * D:].reshape(T, ratio, D), d["g"][:, vheads], d["beta"][:, vheads],
-                                  d["cu"], d["state_in"][:, vheads])
-    out_ref = orc.gated_rmsnorm(o_ref, d["z"][:, vheads], d["norm_w"])
-    check(host(out)[:, vheads], out_ref, TOL_BF16, f"varlen prefill out {lengths}", stored_bf16=True)
-    check(host(fs)[:, vheads], s_ref, TOL_BF16, "varlen prefill state")
-    assert np.array_equal(host(cso)[:, :, cols], cso_ref)
-    assert np.all(np.isfinite(host(out))), "non-finite output in unsampled heads"
+    out_ref, s_ref, cso_ref = _prefill_ref(orc, d, True)
+    check(host(out), out_ref, TOL_BF16, f"varlen prefill out {lengths} (48 heads)", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, "varlen prefill state (48 heads)")
+    assert np.array_equal(host(cso), cso_ref)
 
 
 # ---------------------------------------------------------------------------
@@ -1027,25 +1005,22 @@ def test_per_channel_with_equal_channels_matches_scalar_decay():
     check(host(s2), host(s1), TOL_BF16, "per-channel == scalar state")
 
 
-def test_kda_h64_s16384_full_size_sampled(orc):
+def test_kda_h64_s16384_full_size_all_heads(orc):
     """The long-context per-key-channel workload: 64 heads (no repeat), 16384 tokens, bf16,
-    random initial state; heads 0, 31 and 63 compared with the token-by-token oracle."""
+    random initial state; every head compared with the token-by-token oracle."""
     geo = gi.Geometry(hk=64, hv=64)
     d = gi.gen_qkv(1005, [16384], geo, per_channel=True)
     cfg = gdn.config(num_k_heads=64, num_v_heads=64, decay_per_key_channel=1)
     o, fs = _run_chunk(d, cfg)
     torch.cuda.synchronize()
-    heads = [0, 13, 26, 39, 52, 63]
-    o_ref, s_ref = orc.delta_rule(d["q"][:, heads], d["k"][:, heads], d["v"][:, heads], d["g"][:, heads],
-                                  d["beta"][:, heads], d["cu"], d["state_in"][:, heads])
-    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 out (6 heads)")
-    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 state (6 heads)")
-    assert np.all(np.isfinite(host(o))), "non-finite output in unsampled heads"
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "KDA S=16384 out (64 heads)")
+    check(host(fs), s_ref, TOL_BF16, "KDA S=16384 state (64 heads)")
 
 
 def test_kda_h64_s16384_strong_channels(orc):
     """The long-context per-key-channel workload with g = -10 in a quarter of every head's
-    channels: every output and state element finite, heads 5 and 40 against the oracle."""
+    channels: every output and state element finite, and every head against the oracle."""
     geo = gi.Geometry(hk=64, hv=64)
     d = gi.gen_qkv(1015, [16384], geo, per_channel=True)
     d["g"] = gi.strong_channel_decay(d["g"], "quarter_m10", seed=1016)
@@ -1054,11 +1029,9 @@ def test_kda_h64_s16384_strong_channels(orc):
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()), "non-finite output"
     assert bool(torch.isfinite(fs).all()), "non-finite final state"
-    heads = [5, 40]
-    o_ref, s_ref = orc.delta_rule(d["q"][:, heads], d["k"][:, heads], d["v"][:, heads], d["g"][:, heads],
-                                  d["beta"][:, heads], d["cu"], d["state_in"][:, heads])
-    check(host(o)[:, heads], o_ref, TOL_BF16, "KDA S=16384 strong channels out (2 heads)")
-    check(host(fs)[:, heads], s_ref, TOL_BF16, "KDA S=16384 strong channels state (2 heads)")
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "KDA S=16384 strong channels out (64 heads)")
+    check(host(fs), s_ref, TOL_BF16, "KDA S=16384 strong channels state (64 heads)")
 
 
 @pytest.mark.parametrize("pattern", gi.STRONG_DECAY_PATTERNS)
