@@ -277,14 +277,19 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
     float tc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m) tc[m] = (4 * m + part == c) ? 1.0f : 0.0f;
-    // A's row r, columns 4m + part, read up front (independent of the recurrence)
+    // A's row r, columns 4m + part (independent of the recurrence): the first
+    // eight rows up front, each later one eight rows ahead of its use, which
+    // keeps the bf16 intra kernel within its 128 registers without spilling
     float ar[16][4];
-#pragma unroll
-    for (int r = 1; r < 16; ++r)
+    auto read_row = [&](int r) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) ar[r][m] = (4 * m < r && 4 * m + part < r) ? Ab[r * kAP + 4 * m + part] : 0.0f;
+    };
+#pragma unroll
+    for (int r = 1; r < 9; ++r) read_row(r);
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
+      if (r + 8 < 16) read_row(r + 8);
       float acc = 0.0f;
 #pragma unroll
       for (int m = 0; m < 4; ++m)
@@ -348,8 +353,10 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
       // fragment (mt, ks, term): lane l holds src[16mt + l%16][kk(e)], kk(e) = pair_k(ks, l/16, e)
       // (paired-tile order) or 32ks + 8(l/16) + e; entries above the diagonal are zero.
       // All loads are issued unconditionally (the upper part of sT is never
-      // written; the select drops those values).
-#pragma unroll
+      // written; the select drops those values).  Not unrolled: the bf16 intra
+      // kernel holds its Gram tiles across this and has no registers for two
+      // fragments' loads at once.
+#pragma unroll 1
       for (int it = 0; it < 8 * kWave / kThreads; ++it) {
         const int p = tid + it * kThreads;
         const int l = p % kWave, f = p / kWave;   // f = mt * 2 + ks
