@@ -13,7 +13,10 @@
 //   verify  per (sequence, value head) workgroup, the head's state is read
 //           once into registers and carried through the K rows; row
 //           t is exactly the fused decode step (conv from register windows,
-//           L2 / q scale, decay, predict, write, output, gated norm).  Besides
+//           L2 / q scale, decay, predict, write, output, gated norm), with the
+//           state-free parts (conv, gates, norms) of four rows at a time done
+//           before those rows' state work, so a group of rows costs four
+//           barriers rather than four per row.  Besides
 //           the outputs it records, per row, the update's two vectors: u
 //           ([Hv][dv]) and the normalised key ([Hk][dk]).  The state and the
 //           conv state in memory are not written.
@@ -40,6 +43,7 @@ constexpr int kCThreads = 512;          // commit: threads per value head
 constexpr int kCRowGroups = kCThreads / 32;
 constexpr int kCRows = kD / kCRowGroups;  // commit: state rows per thread, rows rg + kCRowGroups m
 constexpr int kVRows = 4;               // verify: state rows per thread, rows rb + 32 m
+constexpr int kVGroup = 4;              // verify: rows of the window prepared together
 
 // Sum over the 8 lanes holding one state row in the verify (lanes 8r .. 8r+7):
 // quad permutes for lane distance 1 and 2, then the half-row mirror (lane i of
@@ -121,8 +125,11 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   const int cb = gt % 8;
   const int rb = gt / 8;
 
-  __shared__ float s_q[kD], s_k[kD], s_scal[2];
-  __shared__ float s_v[kD], s_o[kD], s_nrm[2];
+  // per row of the current group: conv outputs, decay factors (per channel, or
+  // one), beta, the q / k norm factors, the outputs and their sums of squares
+  __shared__ float s_q[kVGroup][kD], s_k[kVGroup][kD], s_v[kVGroup][kD], s_o[kVGroup][kD];
+  __shared__ float s_a[kVGroup][kPerChannel ? kD : 1], s_bt[kVGroup];
+  __shared__ float s_scal[kVGroup][2], s_nrm[kVGroup][2];
 
   // conv windows: thread i owns q channel i (i < kD) or k channel i - kD of the
   // key head, and threads below kD also v channel i of the value head.  The
@@ -136,30 +143,30 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   RawWindow<T> raw_qk = load_window(cs_row, c_qk, cc);
   RawWindow<T> raw_v = load_window(cs_row, c_v, cc);
 
-  // a row's global inputs, fetched one row ahead so their latency overlaps the
-  // previous row's work
-  Raw<T> xqk_n, xv_n, z_n;   // stored values, widened at their use
-  float bt_n = 0.0f;
-  f32x4_t g_n[4] = {};
-  auto fetch = [&](int t) {
-    const int64_t row_t = (int64_t)b * K + t;
-    const T* x_row = x + row_t * cc;
-    xqk_n.load(x_row + c_qk);
-    xv_n.load(x_row + c_v);
-    z_n.load(z + (row_t * hv + h) * kD + gt % kD);
-    if constexpr (kPerChannel) {
+  // A group's row inputs, fetched for all its rows at once (the first group's
+  // before the state loads, each later one at the end of the group before it).
+  // Thread i < kD also loads the per-channel log decay of channel i; the
+  // scalar gates are loaded by every thread.
+  Raw<T> xqk_n[kVGroup], xv_n[kVGroup], z_n[kVGroup];
+  float g_n[kVGroup], bt_n[kVGroup];
+  auto fetch = [&](int t0, int nb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) g_n[i] = *reinterpret_cast<const f32x4_t*>(g + (row_t * hv + h) * kD + 32 * i + 4 * cb);
-    } else {
-      g_n[0][0] = g[row_t * hv + h];
+    for (int j = 0; j < kVGroup; ++j) {
+      const int t = t0 + min(j, nb - 1);   // rows past the group repeat its last (unused)
+      const int64_t row_t = (int64_t)b * K + t;
+      const T* x_row = x + row_t * cc;
+      xqk_n[j].load(x_row + c_qk);
+      xv_n[j].load(x_row + c_v);
+      z_n[j].load(z + (row_t * hv + h) * kD + gt % kD);
+      g_n[j] = kPerChannel ? g[(row_t * hv + h) * kD + gt % kD] : g[row_t * hv + h];
+      bt_n[j] = beta[row_t * hv + h];
     }
-    bt_n = beta[row_t * hv + h];
   };
-  fetch(0);
+  fetch(0, min(K, kVGroup));
 
   // the head's state, read once and carried through the K rows.  Its loads are
-  // issued after the conv windows and the first row's inputs: loads complete in
-  // issue order, so the first row's conv and norms wait only for their own
+  // issued after the conv windows and the first group's inputs: loads complete
+  // in issue order, so the first group's conv and norms wait only for their own
   // inputs while the 64 KiB of state is still in flight
   // (buffer loads, streamed: a plain load would be sunk to its first use)
   const float* S = state + ((int64_t)b * hv + h) * kD * kD;
@@ -177,100 +184,130 @@ __global__ __launch_bounds__(kGroup) void verify_kernel(
   __builtin_amdgcn_sched_barrier(0);
   raw_qk.pin();
   raw_v.pin();
-  xqk_n.pin();
-  xv_n.pin();
-  z_n.pin();
+#pragma unroll
+  for (int j = 0; j < kVGroup; ++j) {
+    xqk_n[j].pin();
+    xv_n[j].pin();
+    z_n[j].pin();
+  }
   ConvWindow wqk = raw_qk.widen(), wv = raw_v.widen();
 
+  // Rows in groups of kVGroup.  Per group: the conv, gates and q / k norms of
+  // all its rows first (they do not depend on the state), then the state rows
+  // through all of them without a barrier, then the rows' gated norms.  Each
+  // row's arithmetic is the decode step's, in the same order.
   // K >= 1 (checked before the launch): a do-while has no entry test, which
   // would let the compiler sink the state loads behind it
-  int t = 0;
+  int t0 = 0;
   do {
-    const int64_t row_t = (int64_t)b * K + t;   // (sequence, verified row)
-    const float xqk = xqk_n.widen(), xv = xv_n.widen(), zv = z_n.widen(), bt = bt_n;
-    f32x4_t gv[4];
+    const int nb = min(K - t0, kVGroup);
+    float zv[kVGroup];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) gv[i] = g_n[i];
-    if (t + 1 < K) fetch(t + 1);
-    {
-      const float y = wqk.step(conv_w, c_qk, xqk, act);
-      if (tid < kD) s_q[tid] = y; else s_k[tid - kD] = y;
+    for (int j = 0; j < kVGroup; ++j) {
+      if (j < nb) {
+        const float y = wqk.step(conv_w, c_qk, xqk_n[j].widen(), act);
+        if (tid < kD) s_q[j][tid] = y; else s_k[j][tid - kD] = y;
+        if (gt < kD) {
+          s_v[j][gt] = wv.step(conv_w, c_v, xv_n[j].widen(), act);
+          if constexpr (kPerChannel) s_a[j][gt] = __expf(g_n[j]);
+        }
+        if (tid == 0) {
+          if constexpr (!kPerChannel) s_a[j][0] = __expf(g_n[j]);
+          s_bt[j] = bt_n[j];
+        }
+      }
+      zv[j] = z_n[j].widen();
     }
-    if (gt < kD) s_v[gt] = wv.step(conv_w, c_v, xv, act);
     __syncthreads();
-    if (tid < 2 * kWave) {
-      const int w = tid / kWave;
-      const float* src = w == 0 ? s_q : s_k;
+    // q / k norm factors: (row, q or k) tasks over the waves
+    for (int task = gwave; task < 2 * nb; task += kGroup / kWave) {
+      const int j = task >> 1, w = task & 1;
+      const float* src = w == 0 ? s_q[j] : s_k[j];
       const float a0 = src[2 * lane], a1 = src[2 * lane + 1];
       const float ss = wave_sum(a0 * a0 + a1 * a1);
-      if (lane == 0) s_scal[w] = l2norm ? 1.0f / sqrtf(ss + l2_eps) : 1.0f;
+      if (lane == 0) s_scal[j][w] = l2norm ? 1.0f / sqrtf(ss + l2_eps) : 1.0f;
     }
     __syncthreads();
-    const float rq = s_scal[0] * q_scale, rk = s_scal[1];
-    const float kq = wave_sum(s_k[2 * lane] * s_q[2 * lane] + s_k[2 * lane + 1] * s_q[2 * lane + 1]) * rq * rk;
-    f32x4_t kcol[4], qcol[4], a[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(s_k + 32 * i + 4 * cb);
-      const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(s_q + 32 * i + 4 * cb);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { kcol[i][e] = kv[e] * rk; qcol[i][e] = qv[e] * rq; }
-    }
-    if constexpr (kPerChannel) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) a[i][e] = __expf(gv[i][e]);
-    } else {
-      const float av = __expf(gv[0][0]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = f32x4_t{av, av, av, av};
-    }
-    // the normalised key of this row, for the commit's replay
-    if (h % (hv / hk) == 0 && gt < kD) rec_k[(row_t * hk + kh) * kD + gt] = s_k[gt] * rk;
+    // the next group's inputs, in flight during this group's state work
+    if (t0 + kVGroup < K) fetch(t0 + kVGroup, min(K - t0 - kVGroup, kVGroup));
 
-    // per state row: decay, the two dot products, u = beta (v - p),
-    // o = r + u (khat . qtil), S' = Sd + u khat^T (as the decode step)
-    float* u_out = rec_u + (row_t * hv + h) * kD;
 #pragma unroll
-    for (int m = 0; m < kVRows; ++m) {
-      const int row = rb + 32 * m;
-      float pk = 0.0f, pq = 0.0f;
+    for (int j = 0; j < kVGroup; ++j) {
+      if (j < nb) {
+        const int64_t row_t = (int64_t)b * K + t0 + j;   // (sequence, verified row)
+        const float rq = s_scal[j][0] * q_scale, rk = s_scal[j][1];
+        const float kq = wave_sum(s_k[j][2 * lane] * s_q[j][2 * lane] + s_k[j][2 * lane + 1] * s_q[j][2 * lane + 1]) * rq * rk;
+        f32x4_t kcol[4], qcol[4], a[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t kv = *reinterpret_cast<const f32x4_t*>(&s_k[j][32 * i + 4 * cb]);
+          const f32x4_t qv = *reinterpret_cast<const f32x4_t*>(&s_q[j][32 * i + 4 * cb]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          sreg[m][i][e] *= a[i][e];
-          pk = fmaf(sreg[m][i][e], kcol[i][e], pk);
-          pq = fmaf(sreg[m][i][e], qcol[i][e], pq);
+          for (int e = 0; e < 4; ++e) { kcol[i][e] = kv[e] * rk; qcol[i][e] = qv[e] * rq; }
+          if constexpr (kPerChannel) {
+            a[i] = *reinterpret_cast<const f32x4_t*>(&s_a[j][32 * i + 4 * cb]);
+          } else {
+            const float av = s_a[j][0];
+            a[i] = f32x4_t{av, av, av, av};
+          }
         }
-      pk = row8_sum(pk);
-      pq = row8_sum(pq);
-      const float u = bt * (s_v[row] - pk);
-      if (cb == 0) {
-        s_o[row] = fmaf(u, kq, pq);
-        u_out[row] = u;
+        const float bt = s_bt[j];
+        // the normalised key of this row, for the commit's replay
+        if (h % (hv / hk) == 0 && gt < kD) rec_k[(row_t * hk + kh) * kD + gt] = s_k[j][gt] * rk;
+
+        // per state row: decay, the two dot products, u = beta (v - p),
+        // o = r + u (khat . qtil), S' = Sd + u khat^T (as the decode step)
+        float* u_out = rec_u + (row_t * hv + h) * kD;
+#pragma unroll
+        for (int m = 0; m < kVRows; ++m) {
+          const int row = rb + 32 * m;
+          float pk = 0.0f, pq = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sreg[m][i][e] *= a[i][e];
+              pk = fmaf(sreg[m][i][e], kcol[i][e], pk);
+              pq = fmaf(sreg[m][i][e], qcol[i][e], pq);
+            }
+          pk = row8_sum(pk);
+          pq = row8_sum(pq);
+          const float u = bt * (s_v[j][row] - pk);
+          if (cb == 0) {
+            s_o[j][row] = fmaf(u, kq, pq);
+            u_out[row] = u;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sreg[m][i][e] = fmaf(u, kcol[i][e], sreg[m][i][e]);
+        }
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sreg[m][i][e] = fmaf(u, kcol[i][e], sreg[m][i][e]);
     }
     __syncthreads();
 
-    // the sigmoid gated RMSNorm of the row's 128 outputs per value head
-    if (gt < kD) {
-      const float o = s_o[gt];
+    // the sigmoid gated RMSNorm of each row's 128 outputs: the sums of squares
+    // of the two 64-output halves, (row, half) tasks over the waves
+    for (int task = gwave; task < 2 * nb; task += kGroup / kWave) {
+      const int j = task >> 1, half = task & 1;
+      const float o = s_o[j][64 * half + lane];
       const float ss = wave_sum(o * o);
-      if (lane == 0) s_nrm[gwave] = ss;
+      if (lane == 0) s_nrm[j][half] = ss;
     }
     __syncthreads();
     if (gt < kD) {
-      const float o = s_o[gt];
-      const float r = rsqrtf((s_nrm[0] + s_nrm[1]) * (1.0f / kD) + rms_eps);
-      st(out + (row_t * hv + h) * kD + gt, o * r * norm_w[gt] * sigmoidf_(zv));
+#pragma unroll
+      for (int j = 0; j < kVGroup; ++j) {
+        if (j < nb) {
+          const int64_t row_t = (int64_t)b * K + t0 + j;
+          const float o = s_o[j][gt];
+          const float r = rsqrtf((s_nrm[j][0] + s_nrm[j][1]) * (1.0f / kD) + rms_eps);
+          st(out + (row_t * hv + h) * kD + gt, o * r * norm_w[gt] * sigmoidf_(zv[j]));
+        }
+      }
     }
-  } while (++t < K);
+    t0 += kVGroup;
+  } while (t0 < K);
 }
 
 // Commit of the recurrent state: sequence b keeps its first clamp(accepted[b],
