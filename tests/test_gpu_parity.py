@@ -479,6 +479,57 @@ def test_prefill_entry_per_channel(orc, bf16):
     assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
 
 
+def _ratio_lengths(hv, one_seq):
+    """One 129-token sequence (the 32-row spine), or enough short and empty sequences that
+    sequences x value heads reach 256 (the whole-head spine, the norm in its epilogue)."""
+    if one_seq:
+        return [129]
+    n = -(-256 // hv) + 1
+    cycle = [65, 1, 0, 64, 3, 130, 7]
+    return [cycle[i % len(cycle)] for i in range(n)]
+
+
+@pytest.mark.parametrize("one_seq", [True, False], ids=["rows32", "whole_head"])
+@pytest.mark.parametrize("hk,hv", [(8, 48), (4, 4), (2, 4)], ids=["ratio6", "ratio1", "ratio2"])
+def test_chunk_prefill_bf16_other_ratios(orc, hk, hv, one_seq):
+    """The bf16 scalar-decay chunk call at key / value head ratios other than 3 (the
+    register-resident spines map (sequence, key head) groups and their value heads' row
+    blocks onto workgroups by the ratio), on both spine shapes, against the oracle."""
+    geo = gi.Geometry(hk=hk, hv=hv)
+    lengths = _ratio_lengths(hv, one_seq)
+    d = gi.gen_qkv(3100 + hk * 10 + hv + int(one_seq), lengths, geo)
+    o, fs = _run_chunk(d, gdn.config(num_k_heads=hk, num_v_heads=hv))
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, f"chunk out {hk}/{hv} {len(lengths)} sequences")
+    check(host(fs), s_ref, TOL_BF16, f"chunk state {hk}/{hv} {len(lengths)} sequences")
+
+
+@pytest.mark.parametrize("one_seq", [True, False], ids=["rows32_norm_kernel", "whole_head_fused_norm"])
+@pytest.mark.parametrize("hk,hv", [(8, 48), (2, 4)], ids=["ratio6", "ratio2"])
+def test_prefill_entry_bf16_other_ratios(orc, hk, hv, one_seq):
+    """The bf16 one-call prefill (conv -> chunk -> gated norm, conv state updated in place) at
+    ratios 6 and 2, with the separate norm kernel (one sequence) and with the norm fused into
+    the whole-head spine (many sequences)."""
+    geo = gi.Geometry(hk=hk, hv=hv)
+    lengths = _ratio_lengths(hv, one_seq)
+    d = gi.gen_prefill(3200 + hk * 10 + hv + int(one_seq), lengths, geo, bf16=True, conv_state=True)
+    cfg = gdn.config(num_k_heads=hk, num_v_heads=hv)
+    cs = dev(d["conv_state_in"], True)
+    out, fs = gdn.prefill(dev(d["x"], True), dev(d["conv_w"]), dev_i32(d["cu"]), dev(d["g"]), dev(d["beta"]),
+                          dev(d["z"], True), dev(d["norm_w"]), cu_host=d["cu"], conv_state_in=cs,
+                          conv_state_out=cs, initial_state=dev(d["state_in"]), out_dtype=torch.bfloat16,
+                          cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, _, s_ref, cso_ref, _ = orc.prefill(d["x"], d["conv_w"], d["cu"], d["g"], d["beta"], d["z"],
+                                                d["norm_w"], Hk=hk, Hv=hv, dk=D, dv=D,
+                                                conv_state_in=d["conv_state_in"], state_in=d["state_in"],
+                                                round_y_bf16=True)
+    check(host(out), out_ref, TOL_BF16, f"prefill out {hk}/{hv} {len(lengths)} sequences", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, f"prefill state {hk}/{hv} {len(lengths)} sequences")
+    assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
+
+
 def test_prefill_entry_fp32_s80(orc):
     """The 80-token fp32 case through the one-call prefill, at the fp32 bound."""
     d = gi.gen_prefill(1001, [80], bf16=False, conv_state=True)
