@@ -169,6 +169,19 @@ def test_decode_step_batch64_bf16(orc):
     assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
 
 
+@pytest.mark.parametrize("B", [1, 300], ids=["B1", "B300"])
+def test_decode_step_batch_sizes_bf16(orc, B):
+    """One sequence, and 300 (14,400 workgroups, several rounds, not a multiple of any tile):
+    bf16 activations, fp32 state, against the oracle; conv state exact."""
+    d = gi.gen_decode(1010 + B, B)
+    out, cs, st = run_decode(d, True, True)
+    o_ref, cs_ref, st_ref = orc.decode_step(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"],
+                                            d["z"], d["norm_w"], d["state"], Hk=HK, Hv=HV, dk=D, dv=D)
+    check(host(out), o_ref, TOL_BF16, f"decode out B={B}", stored_bf16=True)
+    check(host(st), st_ref, TOL_BF16, f"decode state B={B}")
+    assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
+
+
 @pytest.mark.parametrize("per_channel", [False, True], ids=["scalar", "per_channel"])
 def test_decode_step_f32_two_steps(orc, per_channel):
     d = gi.gen_decode(21, 5, bf16=False, per_channel=per_channel)
