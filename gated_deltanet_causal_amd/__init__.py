@@ -150,7 +150,10 @@ def _stream():
 
 
 def _row_stride(t: torch.Tensor) -> int:
-    """Elements between rows of a [rows, ...] tensor whose inner dims are contiguous."""
+    """Elements between rows of a [rows, ...] tensor whose inner dims are contiguous (an
+    empty tensor, whose strides carry no layout, counts as packed rows)."""
+    if t.numel() == 0:
+        return math.prod(t.shape[1:]) if t.dim() > 1 else 0
     inner = 1
     for s, n in zip(reversed(t.stride()[1:]), reversed(t.shape[1:])):
         if s != inner:

@@ -136,3 +136,17 @@ def test_state_convert_rejects_other_dtypes():
         gdn.state_convert(_bf16(1, HV, D, D), torch.float32)
     with pytest.raises(ValueError, match="converts between"):
         gdn.state_convert(_f32(1, HV, D, D), torch.float32)
+
+
+def test_row_stride_of_empty_and_strided_rows():
+    """Row strides the binding passes on: an empty tensor counts as packed rows whatever
+    strides it reports (numpy-made empties report zeros), a row-strided view its own stride,
+    and a view whose inner dimensions are not contiguous is refused."""
+    import numpy as np
+    empty = torch.from_numpy(np.zeros((0, CC), dtype=np.float32)).to(torch.bfloat16)
+    assert gdn._row_stride(empty) == CC
+    assert gdn._row_stride(torch.zeros(0, HV, D)) == HV * D
+    wide = torch.zeros(4, CC + 64)
+    assert gdn._row_stride(wide[:, :CC]) == CC + 64
+    with pytest.raises(ValueError, match="inner dimensions must be contiguous"):
+        gdn._row_stride(torch.zeros(4, 2 * CC)[:, ::2])

@@ -14,7 +14,7 @@ import torch
 import gated_deltanet_causal_amd as gdn
 import gdn_inputs as gi
 import oracle
-from gpu_common import TOL_BF16, TOL_F32, check, dev, dev_i32, host, worst_ratio
+from gpu_common import DEV, TOL_BF16, TOL_F32, check, dev, dev_i32, host, worst_ratio
 
 pytestmark = pytest.mark.gpu
 
@@ -490,6 +490,32 @@ def test_prefill_entry_per_channel(orc, bf16):
     check(host(out), out_ref, tol, f"per-channel prefill out {lengths}")
     check(host(fs), s_ref, tol, f"per-channel prefill state {lengths}")
     assert np.array_equal(host(cs), cso_ref), "conv state updated in place"
+
+
+@pytest.mark.parametrize("N", [1, 6], ids=["one_empty", "six_empty"])
+def test_prefill_all_sequences_empty(orc, N):
+    """A batch whose sequences are all empty (T = 0): the chunk call and the one-call prefill
+    hand every initial state through bit for bit (zero without one), the conv state too, and
+    touch no output row; one sequence takes the 32-row spine, six the whole-head one."""
+    lengths = [0] * N
+    d = gi.gen_qkv(3300 + N, lengths)
+    cu = dev_i32(d["cu"])
+    empty = lambda cols: torch.empty((0, cols), dtype=torch.bfloat16, device=DEV)
+    s_in = dev(d["state_in"])
+    o, fs = gdn.chunk_prefill(empty(HK * D), empty(HK * D), empty(HV * D), torch.empty((0, HV), device=DEV),
+                              torch.empty((0, HV), device=DEV), cu, cu_host=d["cu"], initial_state=s_in,
+                              out_dtype=torch.float32)
+    _, fs0 = gdn.chunk_prefill(empty(HK * D), empty(HK * D), empty(HV * D), torch.empty((0, HV), device=DEV),
+                               torch.empty((0, HV), device=DEV), cu, cu_host=d["cu"], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0
+    assert torch.equal(fs, s_in), "the initial state passes through an empty sequence unchanged"
+    assert not torch.any(fs0), "no initial state: the final state is zero"
+    p = gi.gen_prefill(3310 + N, lengths, bf16=True, conv_state=True)
+    out, fs, cso = _prefill_gpu(p, True, torch.bfloat16)
+    assert out.shape[0] == 0
+    assert torch.equal(fs, dev(p["state_in"])), "one-call prefill: initial state handed through"
+    assert np.array_equal(host(cso), p["conv_state_in"]), "one-call prefill: conv state handed through"
 
 
 def _ratio_lengths(hv, one_seq):
