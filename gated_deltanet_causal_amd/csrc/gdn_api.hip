@@ -308,6 +308,7 @@ gdn_status_t gdn_gated_rmsnorm(const gdn_config_t* cfg, gdn_dtype_t o_dtype, gdn
     const size_t n = (size_t)rows * d.hv * d.dv;
     if (overlaps(out, n * dsize(out_dtype), o, n * dsize(o_dtype))) return GDN_ERR_INVALID_ARG;
   }
+  if (rows == 0) return GDN_OK;   // (empty buffers may share a null address)
   if (out == o && o_dtype != out_dtype) return GDN_ERR_INVALID_ARG;
   return hip_status(gdn::launch_gated_rmsnorm(d, o_dtype == GDN_BF16, z_dtype == GDN_BF16,
                                               out_dtype == GDN_BF16, o, z, w, out, rows,

@@ -164,6 +164,9 @@ def test_empty_calls_launch_nothing(lib):
                                None, None, None, None, 0, None) == 0
     assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_F32, gdn.GDN_F32, None, None, None,
                                  None, 0, None) == 0
+    # no rows, output dtype other than o's: empty buffers may both sit at address 0
+    assert lib.gdn_gated_rmsnorm(ctypes.byref(cfg), gdn.GDN_F32, gdn.GDN_BF16, gdn.GDN_BF16, None, None, None,
+                                 None, 0, None) == 0
 
 
 def test_decode_rejects_batches_past_the_shift_grid(lib):

@@ -518,6 +518,39 @@ def test_prefill_all_sequences_empty(orc, N):
     assert np.array_equal(host(cso), p["conv_state_in"]), "one-call prefill: conv state handed through"
 
 
+def test_zero_size_calls():
+    """Calls with nothing to do return without error and leave every buffer as it was: a
+    decode step and a verify transaction of no sequences, a norm of no rows, a conv over no
+    tokens of two empty sequences (the conv state handed through), a chunk call of no
+    sequences."""
+    bf = torch.bfloat16
+    z0 = lambda *shape, dt=torch.float32: torch.zeros(shape, dtype=dt, device=DEV)
+    CC = 2 * HK * D + HV * D
+    w = z0(CC, 4)
+    out = gdn.decode_step(z0(0, CC, dt=bf), w, z0(0, 3, CC, dt=bf), z0(0, HV), z0(0, HV), z0(0, HV, D, dt=bf),
+                          z0(D), z0(0, HV, D, D), out_dtype=bf)
+    assert out.shape == (0, HV, D)
+    o_v, ws = gdn.verify(z0(0, 4, CC, dt=bf), w, z0(0, 3, CC, dt=bf), z0(0, 4, HV), z0(0, 4, HV),
+                         z0(0, 4, HV, D, dt=bf), z0(D), z0(0, HV, D, D), out_dtype=bf)
+    gdn.verify_commit(torch.zeros(0, dtype=torch.int32, device=DEV), z0(0, 4, CC, dt=bf), z0(0, 4, HV),
+                      z0(0, 3, CC, dt=bf), z0(0, HV, D, D), ws)
+    assert o_v.shape[0] == 0
+    n = gdn.gated_rmsnorm(z0(0, HV, D), z0(0, HV, D, dt=bf), z0(D), out_dtype=bf)
+    assert n.shape == (0, HV, D)
+    cs = torch.randn(2, 3, CC, device=DEV).to(bf)
+    cs0 = cs.clone()
+    cso = torch.empty_like(cs)
+    y = gdn.conv1d_prefill(z0(0, CC, dt=bf), w, dev_i32([0, 0, 0]), cu_host=[0, 0, 0], conv_state_in=cs,
+                           conv_state_out=cso)
+    torch.cuda.synchronize()
+    assert y.shape == (0, CC)
+    assert torch.equal(cso, cs0) and torch.equal(cs, cs0), "empty sequences hand their conv rows through"
+    o, fs = gdn.chunk_prefill(z0(0, HK * D, dt=bf), z0(0, HK * D, dt=bf), z0(0, HV * D, dt=bf), z0(0, HV),
+                              z0(0, HV), dev_i32([0]), cu_host=[0], out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert o.shape[0] == 0 and fs.shape[0] == 0
+
+
 def _ratio_lengths(hv, one_seq):
     """One 129-token sequence (the 32-row spine), or enough short and empty sequences that
     sequences x value heads reach 256 (the whole-head spine, the norm in its epilogue)."""
