@@ -169,10 +169,11 @@ def test_decode_step_batch64_bf16(orc):
     assert np.array_equal(host(cs), cs_ref), "conv state must be exact"
 
 
-@pytest.mark.parametrize("B", [1, 300], ids=["B1", "B300"])
+@pytest.mark.parametrize("B", [1, 300, 2048], ids=["B1", "B300", "B2048"])
 def test_decode_step_batch_sizes_bf16(orc, B):
-    """One sequence, and 300 (14,400 workgroups, several rounds, not a multiple of any tile):
-    bf16 activations, fp32 state, against the oracle; conv state exact."""
+    """One sequence, 300 (14,400 workgroups, several rounds, not a multiple of any tile) and
+    2048 (98,304 workgroups, 6.4 GB of state): bf16 activations, fp32 state, against the
+    oracle; conv state exact."""
     d = gi.gen_decode(1010 + B, B)
     out, cs, st = run_decode(d, True, True)
     o_ref, cs_ref, st_ref = orc.decode_step(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"],
@@ -345,6 +346,20 @@ def test_chunk_prefill_s4096_full_size_all_heads(orc):
     o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
     check(host(o), o_ref, TOL_BF16, "S=4096 out (48 heads)")
     check(host(fs), s_ref, TOL_BF16, "S=4096 state (48 heads)")
+
+
+def test_chunk_prefill_65536_tokens_one_sequence(orc):
+    """One 65,536-token sequence, 1,024 chunks chained through the 32-row spine (2 key / 6
+    value heads keep the inputs small), bf16, random initial state: every value head against
+    the oracle over every token, and the final states."""
+    T = 65536
+    geo = gi.Geometry(hk=2, hv=6)
+    d = gi.gen_qkv(3400, [T], geo)
+    o, fs = _run_chunk(d, gdn.config(num_k_heads=2, num_v_heads=6), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    o_ref, s_ref = orc.delta_rule(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu"], d["state_in"])
+    check(host(o), o_ref, TOL_BF16, "65536-token out", stored_bf16=True)
+    check(host(fs), s_ref, TOL_BF16, "65536-token state")
 
 
 def test_varlen_32k_full_size_all_heads(orc):
