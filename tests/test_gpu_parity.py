@@ -941,6 +941,29 @@ def test_verify_transaction_full_size_poisoned_tail(orc):
     assert np.array_equal(host(t_["cs"]), cs_ref), "committed conv state must be exact"
 
 
+@pytest.mark.parametrize("hk,hv,B,K", [(8, 48, 3, 5), (2, 4, 1, 9), (4, 4, 2, 4)],
+                         ids=["ratio6_B3_K5", "ratio2_B1_K9", "ratio1_B2_K4"])
+def test_verify_transaction_other_ratios(orc, hk, hv, B, K):
+    """The verify transaction at head ratios 6, 2 and 1, for windows that end inside a group
+    of four rows (5, 9) and on one (4), and a single sequence, against the oracle's
+    transaction, every accepted count from 0 to K among the sequences' commits."""
+    geo = gi.Geometry(hk=hk, hv=hv)
+    cfg = gdn.config(num_k_heads=hk, num_v_heads=hv)
+    d = _verify_inputs(2260 + hk + K, B, K, geo)
+    t_ = _verify_dev(d, True)
+    out_v, ws = gdn.verify(t_["x"], t_["conv_w"], t_["cs"], t_["g"], t_["beta"], t_["z"], t_["nw"], t_["st"],
+                           out_dtype=torch.float32, cfg=cfg)
+    accepted = np.array([(K - b) % (K + 1) for b in range(B)], dtype=np.int32)
+    gdn.verify_commit(torch.from_numpy(accepted).cuda(), t_["x"], t_["g"], t_["cs"], t_["st"], ws, cfg=cfg)
+    torch.cuda.synchronize()
+    out_ref, snaps = orc.verify(d["x"], d["conv_w"], d["conv_state"], d["g"], d["beta"], d["z"], d["norm_w"],
+                                d["state"], Hk=hk, Hv=hv, dk=D, dv=D)
+    cs_ref, st_ref = orc.commit(snaps, accepted)
+    check(host(out_v), out_ref, TOL_BF16, f"verify rows {hk}/{hv} K={K}")
+    check(host(t_["st"]), st_ref, TOL_BF16, f"committed state {hk}/{hv} K={K}")
+    assert np.array_equal(host(t_["cs"]), cs_ref), "committed conv state must be exact"
+
+
 def test_verify_largest_window_k64(orc):
     """The largest window the library takes (GDN_MAX_VERIFY_ROWS = 64 rows), 3 sequences,
     committing 64, 33 and 0 rows, against the oracle's transaction."""
