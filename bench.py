@@ -326,9 +326,13 @@ def bench_pipeline(lengths, seed, steps, warmup, n_sets=3):
     bytes_alg = PREFILL_BYTES_PER_TOKEN * T + 2 * STATE_BYTES * N
     traffic = {(4096,): PREFILL_S4096_TRAFFIC_BYTES,
                tuple(gi.varlen_lengths()[0]): VARLEN_TRAFFIC_BYTES}.get(tuple(lengths))
+    # the latency floor: the longest sequence's chunks are a serial chain
+    serial = max((n + CHUNK_C - 1) // CHUNK_C for n in lengths)
     return dict(ms=ms, tokens=T, tokens_per_s=T / (ms * 1e-3), roofline=roofline(bytes_alg, ms, traffic),
                 mfma=mfma_block(PREFILL_FLOPS_PER_TOKEN * T, ms),
-                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, separate_calls=split, **spread(per))
+                roofline_ms=bytes_alg / (PEAK_HBM_GBS * 1e9) * 1e3, separate_calls=split,
+                serial_chunk_steps=serial, chunk_call_us_per_serial_step=split["chunk_ms"] * 1e3 / serial,
+                **spread(per))
 
 
 def _head_of(lengths, max_tokens):
@@ -497,7 +501,8 @@ def main():
             metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], call="gdn_prefill",
             separate_calls=pre["separate_calls"], roofline=pre["roofline"], mfma=pre["mfma"],
             roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate",
-            input_sets=3, **{k: pre[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")})
+            input_sets=3, **{k: pre[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls",
+                                                  "serial_chunk_steps", "chunk_call_us_per_serial_step")})
         if cpu:
             workloads["prefill_s4096_bf16"]["cpu_baseline"] = cpu_baseline_pipeline([4096], 1003, 4096)
     if wl in ("all", "varlen"):
@@ -507,7 +512,8 @@ def main():
             metric="tokens/s", value=var["tokens_per_s"], ms=var["ms"], tokens=var["tokens"], lengths=lengths,
             call="gdn_prefill", separate_calls=var["separate_calls"], roofline=var["roofline"], mfma=var["mfma"],
             roofline_ms=var["roofline_ms"], input_sets=3,
-            **{k: var[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls")})
+            **{k: var[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls",
+                                   "serial_chunk_steps", "chunk_call_us_per_serial_step")})
         if cpu:
             workloads["varlen8_33k_bf16"]["cpu_baseline"] = cpu_baseline_pipeline(lengths, 1004, 4096)
     if wl in ("all", "kda"):
