@@ -476,8 +476,9 @@ def main():
         return
     wl = args.workload
     cpu = not args.no_cpu_baseline
-    # at least 20 timed calls of each workload; the clocks settle over the first calls
-    small_steps, small_warm = max(20, args.steps // 10), max(5, args.warmup)
+    # the other workloads: at least 100 timed calls after at least 10 untimed (15 ms to 0.2 s
+    # of GPU time each); the clocks settle over the first calls
+    small_steps, small_warm = max(100, args.steps // 2), max(10, args.warmup)
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
     workloads = {}
@@ -517,7 +518,7 @@ def main():
         if cpu:
             workloads["varlen8_33k_bf16"]["cpu_baseline"] = cpu_baseline_pipeline(lengths, 1004, 4096)
     if wl in ("all", "kda"):
-        kda = bench_kda(small_steps, 3)
+        kda = bench_kda(small_steps, 10)
         workloads["kda_h64_s16384_bf16"] = dict(
             metric="tokens/s", value=kda["tokens_per_s"], ms=kda["ms"], roofline=kda["roofline"], mfma=kda["mfma"],
             roofline_ms=kda["roofline_ms"], call="gdn_chunk_prefill, decay per key channel", input_sets=3,
@@ -525,26 +526,26 @@ def main():
         if cpu:
             workloads["kda_h64_s16384_bf16"]["cpu_baseline"] = cpu_baseline_kda()
     if wl in ("all", "decode_h16"):
-        dh = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), state_f16=True)
+        dh = bench_decode(small_steps, small_warm, state_f16=True)
         workloads["decode_b64_h16_bf16"] = dict(
             metric="state-updates/s", value=dh["updates_per_s"], ms=dh["ms"], roofline=dh["roofline"],
             median_ms=dh["median_ms"], p10_ms=dh["p10_ms"], p90_ms=dh["p90_ms"],
             call="gdn_decode_step_h16: the recurrent state stored in fp16 (rounded once per token)")
     if wl in ("all", "verify"):
-        ver = bench_verify(max(20, args.steps // 4), max(5, args.warmup // 4))
+        ver = bench_verify(small_steps, small_warm)
         workloads["verify_k4_b64_bf16"] = dict(
             metric="state-updates/s", value=ver["rows_per_s"], ms=ver["ms"], roofline=ver["roofline"],
             median_ms=ver["median_ms"], p10_ms=ver["p10_ms"], p90_ms=ver["p90_ms"],
             bytes_per_transaction=ver["bytes_per_transaction"],
             call="gdn_verify (64 sequences x 4 rows) + gdn_verify_commit accepting all 4; one update = one row")
     if wl in ("all", "decode_ab"):
-        dab = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), derived_gates=True)
+        dab = bench_decode(small_steps, small_warm, derived_gates=True)
         workloads["decode_b64_ab_bf16"] = dict(
             metric="state-updates/s", value=dab["updates_per_s"], ms=dab["ms"], roofline=dab["roofline"],
             median_ms=dab["median_ms"], p10_ms=dab["p10_ms"], p90_ms=dab["p90_ms"],
             call="gdn_decode_step_ab: g, beta derived in the kernel from the a / b projections")
     if wl in ("all", "kda_decode"):
-        kdd = bench_decode(max(20, args.steps // 4), max(5, args.warmup // 4), per_channel=True)
+        kdd = bench_decode(small_steps, small_warm, per_channel=True)
         workloads["kda_decode_b64_h64_bf16"] = dict(
             metric="state-updates/s", value=kdd["updates_per_s"], ms=kdd["ms"], roofline=kdd["roofline"],
             median_ms=kdd["median_ms"], p10_ms=kdd["p10_ms"], p90_ms=kdd["p90_ms"],
