@@ -1,6 +1,6 @@
 """Helpers shared by the GPU parity tests: device transfer and the tolerance.
 
-Tolerance (the bar the benchmark spec sets, read as max-relative):
+Tolerance (the max-relative bound of the bf16 sublayer with an fp32 state):
     err = max_i |got_i - ref_i| / max_i |ref_i|
 must be <= 2e-3 for bf16 inputs with fp32 state, <= 1e-5 for the fp32 path.
 Where the library stores bf16, one bf16 ulp of |ref_i| (2^-7 |ref_i| bounds
