@@ -467,7 +467,7 @@ def main():
     ap.add_argument("--calibration-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the library has no "
               f"multi-GPU path)", file=sys.stderr)
         sys.exit(2)
     if args.calibration_copy:
