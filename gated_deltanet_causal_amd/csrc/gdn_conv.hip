@@ -43,11 +43,10 @@ __device__ __forceinline__ void load8(const T* p, float (&v)[kConvVec]) {
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&v)[kConvVec]) {
   if constexpr (sizeof(T) == 2) {
-    u32x4_t u;
+    u32x4_t u;   // pairs through one conversion each (round to nearest even)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      u[i] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i])) |
-             (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * i + 1])) << 16);
+      u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * i], v[2 * i + 1]}, bf16x2_t));
     *reinterpret_cast<u32x4_t*>(p) = u;
   } else {
     f32x4_t a, b;
@@ -59,7 +58,7 @@ __device__ __forceinline__ void store8(T* p, const float (&v)[kConvVec]) {
 }
 
 __device__ __forceinline__ float conv_activation(float y, int act) {
-  return act ? y * sigmoidf_(y) : y;
+  return act ? silu_conv(y) : y;
 }
 
 // Sequence holding token t: the n with cu[n] <= t < cu[n+1] (empty sequences skipped).

@@ -96,7 +96,7 @@ struct ConvTap {
       st(p + cc, s2);
       st(p + 2 * cc, xv);
     }
-    return act ? y * sigmoidf_(y) : y;
+    return act ? silu_conv(y) : y;
   }
 };
 

@@ -110,6 +110,14 @@ __device__ __forceinline__ float quad_sum(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
+// The conv's SiLU activation, y sigmoid(y), with the sigmoid as 1 / (1 + 2^(-y log2 e)) on the
+// hardware exp2 and reciprocal (each within 1 ulp) instead of an IEEE division: the conv is
+// VALU-bound on long batches and the division was half its instructions.  Every conv (the
+// prefill kernel, the decode step, the verify window) uses this one.
+__device__ __forceinline__ float silu_conv(float y) {
+  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * y));
+}
+
 // Four consecutive values of a recurrent state, stored as fp32 or as fp16
 // (the fp16 h-state: widened on load, rounded to nearest even on store, so
 // the arithmetic stays fp32 and the state is rounded once per token).  The

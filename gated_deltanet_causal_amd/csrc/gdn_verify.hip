@@ -69,7 +69,7 @@ struct ConvWindow {
     s0 = s1;
     s1 = s2;
     s2 = xv;
-    return act ? y * sigmoidf_(y) : y;
+    return act ? silu_conv(y) : y;
   }
 };
 
