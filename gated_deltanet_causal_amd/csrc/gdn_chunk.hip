@@ -2008,15 +2008,14 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
         ss[mt] += __shfl_xor(ss[mt], 32, kWave);
       }
       s_ss[(16 * g + m) * kNW + wave] = g == 0 ? ss[0] : g == 1 ? ss[1] : g == 2 ? ss[2] : ss[3];
-      // w * sigmoid(z), folded into the output tiles; sigmoid as 1 / (1 + 2^(-z log2 e))
-      // with the hardware exp2 and reciprocal (each within 1 ulp)
+      // w * sigmoid(z), folded into the output tiles
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const float zf[4] = {__uint_as_float(zr[mt][0] << 16), __uint_as_float(zr[mt][0] & 0xffff0000u),
                              __uint_as_float(zr[mt][1] << 16), __uint_as_float(zr[mt][1] & 0xffff0000u)};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          zt[mt][e] *= nw[e] * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * zf[e]));
+          zt[mt][e] *= nw[e] * sigmoidf_(zf[e]);
       }
     } else {
 #pragma unroll

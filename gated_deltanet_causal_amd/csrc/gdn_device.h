@@ -108,15 +108,16 @@ __device__ __forceinline__ float quad_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
-
-// The conv's SiLU activation, y sigmoid(y), with the sigmoid as 1 / (1 + 2^(-y log2 e)) on the
-// hardware exp2 and reciprocal (each within 1 ulp) instead of an IEEE division: the conv is
-// VALU-bound on long batches and the division was half its instructions.  Every conv (the
-// prefill kernel, the decode step, the verify window) uses this one.
-__device__ __forceinline__ float silu_conv(float y) {
-  return y * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * y));
+// sigmoid(x) = 1 / (1 + 2^(-x log2 e)) on the hardware exp2 and reciprocal (each within 1 ulp),
+// not an IEEE division, which was half the conv's instructions where the conv is VALU-bound.
+// Every sigmoid of the library (the conv's SiLU, the norm's output gate, beta from b) is this
+// one, so that the paths that compute the same value agree.
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504f * x));
 }
+
+// The conv's SiLU activation, y sigmoid(y).
+__device__ __forceinline__ float silu_conv(float y) { return y * sigmoidf_(y); }
 
 // Four consecutive values of a recurrent state, stored as fp32 or as fp16
 // (the fp16 h-state: widened on load, rounded to nearest even on store, so
