@@ -118,10 +118,10 @@ def rotated(tensors, n_sets):
 
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
-DECODE_TRAFFIC_BYTES = 214.0e6 + 206.0e6          # both launches of a step
-PREFILL_S4096_TRAFFIC_BYTES = 456.0e6 + 328.6e6    # gdn_prefill, all its kernels
-VARLEN_TRAFFIC_BYTES = 3193.0e6 + 1838.8e6
-KDA_TRAFFIC_BYTES = 3019.7e6 + 683.7e6
+DECODE_TRAFFIC_BYTES = 213.9e6 + 206.1e6          # both launches of a step
+PREFILL_S4096_TRAFFIC_BYTES = 454.8e6 + 328.6e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 3190.3e6 + 1838.8e6
+KDA_TRAFFIC_BYTES = 3019.9e6 + 683.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
