@@ -27,15 +27,24 @@
 //   intra  one workgroup per (chunk, key head): K K^T and Q K^T on MFMA once
 //          for the key head, then per value head A, the unit-lower triangular
 //          inverse, Tt and Pt.  Tt and Pt are written to the workspace already
-//          in the MFMA A-operand lane layout (hi/lo bf16 pairs, or fp32).
-//   spine  one workgroup per (sequence, value head, 32-row dv tile): walks the
-//          sequence's chunks in order with the fp32 state tile in LDS, running
-//          the four products above on MFMA.
-// Numerics: the raw bf16 K, Q and V enter MFMA exactly; every fp32 operand
-// (state, R, Vnew, Tt, Pt) is split into hi + lo bf16 and multiplied as
-// hi*hi + hi*lo + lo*hi (exact-input products need two terms), so products are
-// accurate to ~2^-16 relative with fp32 accumulation.  The fp32 input path
-// uses fp32 MFMA instead.
+//          in the MFMA A-operand lane layout (fp16 for the register-resident
+//          spines, hi/lo bf16 pairs for the LDS spine, or fp32).
+//   spine  walks a sequence's chunks in order with the fp32 state in MFMA
+//          accumulators (register-resident: 16 value rows per wave) or in LDS,
+//          running the products above on MFMA.
+// Numerics.  The Gram products K K^T and Q K^T take the raw bf16 rows exactly.
+// bf16 inputs with scalar decay (the register-resident spines): every operand
+// of the state and output products -- khat = rk K and qtil = rq Q (formed once
+// per chunk and key head by the intra kernel), the chunk-start state, R,
+// Vnew, Tt, Pt -- is rounded once to fp16 (2^-11 relative) and multiplied on
+// fp16 MFMA with fp32 accumulation; the state itself stays fp32 in the
+// accumulators.  A numpy model of these rounding points put the error at
+// 6-9e-4 max-relative over 1-4k tokens (with and without decay), inside the
+// 2e-3 bound; operands must stay within fp16 range (|x| < 65504), which holds
+// for normalised rows, decay factors <= 1 and values and states of the
+// activations' scale.  The LDS spine (per-key-channel decay) splits every fp32
+// operand into hi + lo bf16 (hi*hi + hi*lo + lo*hi, two terms when one side is
+// an exact bf16 input), ~2^-16 relative.  The fp32 input path uses fp32 MFMA.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -53,6 +62,18 @@ constexpr int kThreads = 256;
 constexpr int kIntraMinWaves = 4;   // intra: waves per SIMD the register budget must allow (bf16: 128 VGPRs)
 constexpr size_t kFragBytes = 16384;           // one 64x64 operand in lane layout
 constexpr size_t kRecBytes = 2 * kFragBytes + 1024;  // Tt, Pt, vectors
+// Records of the register-resident spines (bf16 inputs, scalar decay): the six
+// Tt fragments that are not all zero, then the six of Pt, each one fp16 operand
+// of 16 x 32 in lane layout (1 KB), then the chunk vectors.  The normalised key
+// and query rows these spines multiply follow the records in the workspace.
+constexpr size_t kHFrag = 1024;
+constexpr size_t kHRecP = 6 * kHFrag;
+constexpr size_t kHRecVec = 12 * kHFrag;
+constexpr size_t kHRecBytes = kHRecVec + 1024;
+// Tt / Pt fragments (mt, ks) with ks <= mt / 2 (the rest of the 64 x 64 is zero)
+constexpr int kNF = 6;
+__host__ __device__ constexpr int frag_mt(int x) { return x < 4 ? x : x - 2; }     // 0 1 2 3 2 3
+__host__ __device__ constexpr int frag_ks(int x) { return x < 4 ? 0 : 1; }         // 0 0 0 0 1 1
 constexpr int kSortMax = 4096;                 // longest-first order up to this many sequences
 constexpr int kXcds = 8;                       // XCDs; workgroups are dealt to them round-robin
 // Spine kernels (the sequential walk over a sequence's chunks)
@@ -65,9 +86,15 @@ constexpr int kWaveSpineMinBlocks = 256;   // value heads x sequences from which
 
 __host__ __device__ constexpr size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Workspace: first[N+1] | order[N] | per-(chunk, value head) records.
+// Workspace: first[N+1] | order[N] | per-(chunk, value head) records; for the
+// register-resident spines the normalised rows khat [T][Hk][dk] and qtil
+// [T][Hk][dk] (fp16) follow their records.  Records are laid out for the upper
+// bound T / 64 + N of a batch's chunks.
 __host__ __device__ inline size_t records_offset(int n_seq) {
   return align_up(sizeof(int32_t) * (2 * (size_t)n_seq + 1), 256);
+}
+inline size_t hat_offset(int n_seq, int t, int hv) {
+  return align_up(records_offset(n_seq) + ((size_t)t / kC + (size_t)n_seq) * hv * kHRecBytes, 256);
 }
 
 template <bool F32> struct Ops;
@@ -328,10 +355,10 @@ __device__ __forceinline__ void unit_lower_inverse(const float* sA, float* sT, f
 
 // Shared tail of the intra kernels: T = (I + A)^-1 from sA, then Tt = T diag(beta)
 // and (kWithP) Pt (sP) written to the record in MFMA A-operand lane layout, masked
-// to the lower triangle (hi/lo bf16 fragment pairs, or fp32).  kPairK selects the
-// paired-tile k order of the register-resident spine (element e of lane l in
-// k step ks holds column pair_k(ks, l/16, e)) instead of the plain order
-// (column 32 ks + 8 (l/16) + e).  All threads.
+// to the lower triangle: hi/lo bf16 fragment pairs (bf16 inputs) or fp32, in the
+// plain k order (element e of lane l in k step ks holds column 32 ks + 8 (l/16) + e);
+// kPairK writes the register-resident spines' records instead: single fp16
+// fragments in the paired-tile k order (column pair_k(ks, l/16, e)).  All threads.
 template <bool F32, int kAP, bool kPairK = false, bool kWithP = true>
 __device__ __forceinline__ void write_operands(const float* sA, const float* sP, float* sT, float* sM,
                                                const float* s_beta, uint8_t* rec) {
@@ -349,13 +376,30 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
         const int r = 16 * mt + (l & 15), kk = 4 * ks + (l >> 4);
         reinterpret_cast<float*>(dst)[p] = kk <= r ? src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f) : 0.0f;
       }
+    } else if constexpr (kPairK) {
+      // the register-resident spines' records: the six fragments (mt, ks) that are
+      // not all zero, compact index x = mt + 2 ks, each a single fp16 operand in the
+      // paired-tile k order: lane l holds src[16mt + l%16][pair_k(ks, l/16, e)]
+#pragma unroll 1
+      for (int p = tid; p < kNF * kWave; p += kThreads) {
+        const int l = p % kWave, x = p / kWave;
+        const int mt = frag_mt(x), ks = frag_ks(x);
+        const int r = 16 * mt + (l & 15);
+        uint32_t hp[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int k0 = pair_k(ks, l >> 4, e), k1 = pair_k(ks, l >> 4, e + 1);
+          const float v0 = src[r * kAP + k0] * (scale_cols ? s_beta[k0] : 1.0f);
+          const float v1 = src[r * kAP + k1] * (scale_cols ? s_beta[k1] : 1.0f);
+          hp[e / 2] = pack_f16x2(k0 <= r ? v0 : 0.0f, k1 <= r ? v1 : 0.0f);
+        }
+        *reinterpret_cast<u32x4_t*>(rec + which * kHRecP + (size_t)p * 16) = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
+      }
     } else {
-      // fragment (mt, ks, term): lane l holds src[16mt + l%16][kk(e)], kk(e) = pair_k(ks, l/16, e)
-      // (paired-tile order) or 32ks + 8(l/16) + e; entries above the diagonal are zero.
+      // fragment (mt, ks, term): lane l holds src[16mt + l%16][32ks + 8(l/16) + e], as
+      // hi/lo bf16; entries above the diagonal are zero.
       // All loads are issued unconditionally (the upper part of sT is never
-      // written; the select drops those values).  Not unrolled: the bf16 intra
-      // kernel holds its Gram tiles across this and has no registers for two
-      // fragments' loads at once.
+      // written; the select drops those values).
 #pragma unroll 1
       for (int it = 0; it < 8 * kWave / kThreads; ++it) {
         const int p = tid + it * kThreads;
@@ -367,15 +411,14 @@ __device__ __forceinline__ void write_operands(const float* sA, const float* sP,
         float v[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int kk = kPairK ? pair_k(ks, l >> 4, e) : 32 * ks + 8 * (l >> 4) + e;
+          const int kk = 32 * ks + 8 * (l >> 4) + e;
           v[e] = src[r * kAP + kk] * (scale_cols ? s_beta[kk] : 1.0f);
         }
         uint32_t hp[4], lp[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const int k0 = kPairK ? pair_k(ks, l >> 4, e) : 32 * ks + 8 * (l >> 4) + e;
-          const int k1 = kPairK ? pair_k(ks, l >> 4, e + 1) : k0 + 1;
-          split2(k0 <= r ? v[e] : 0.0f, k1 <= r ? v[e + 1] : 0.0f, hp[e / 2], lp[e / 2]);
+          const int k0 = 32 * ks + 8 * (l >> 4) + e;
+          split2(k0 <= r ? v[e] : 0.0f, k0 + 1 <= r ? v[e + 1] : 0.0f, hp[e / 2], lp[e / 2]);
         }
         *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 0) * kWave + l) * 16) = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
         *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 1) * kWave + l) * 16) = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
@@ -661,7 +704,8 @@ template <bool F32, typename Tin, bool kPairK>
 __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intra_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     Gates gates, const int32_t* __restrict__ cu,
-    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
+    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws,
+    uint16_t* __restrict__ khat) {
   using O = Ops<F32>;
   using E = typename O::E;
   constexpr int kPitch = kD + O::kPadK;
@@ -771,9 +815,35 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
     }
     sk = quad_sum(sk);
     sq = quad_sum(sq);
+    const float rkv = l2norm ? 1.0f / sqrtf(sk + l2_eps) : 1.0f;
+    const float rqv = l2norm ? q_scale / sqrtf(sq + l2_eps) : q_scale;
     if (part == 0) {
-      s_rk[r] = r < L ? (l2norm ? 1.0f / sqrtf(sk + l2_eps) : 1.0f) : 0.0f;
-      s_rq[r] = r < L ? (l2norm ? q_scale / sqrtf(sq + l2_eps) : q_scale) : 0.0f;
+      s_rk[r] = r < L ? rkv : 0.0f;
+      s_rq[r] = r < L ? rqv : 0.0f;
+    }
+    if constexpr (kPairK) {
+      // the rows the register-resident spines multiply, normalised and rounded
+      // once to fp16: khat = rk k and qtil = rq q (q_scale included), the
+      // lane's 32 columns of its row (rows past the chunk's end belong to the
+      // next sequence and are not written)
+      if (r < L) {
+        // qtil [T][Hk][dk] follows khat (cu[n_seq] = T)
+        uint16_t* qhat = khat + (int64_t)cu[n_seq] * hk * kD;
+        const int64_t off = ((int64_t)(t0 + r) * hk + kh) * kD + part * 32;
+#pragma unroll
+        for (int e8 = 0; e8 < 32; e8 += 8) {
+          const u32x4_t ku = *reinterpret_cast<const u32x4_t*>(sK + r * kPitch + part * 32 + e8);
+          const u32x4_t qu = *reinterpret_cast<const u32x4_t*>(sQ + r * kPitch + part * 32 + e8);
+          u32x4_t kh16, qh16;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            kh16[w] = pack_f16x2(__uint_as_float(ku[w] << 16) * rkv, __uint_as_float(ku[w] & 0xffff0000u) * rkv);
+            qh16[w] = pack_f16x2(__uint_as_float(qu[w] << 16) * rqv, __uint_as_float(qu[w] & 0xffff0000u) * rqv);
+          }
+          *reinterpret_cast<u32x4_t*>(khat + off + e8) = kh16;
+          *reinterpret_cast<u32x4_t*>(qhat + off + e8) = qh16;
+        }
+      }
     }
   }
 
@@ -809,7 +879,7 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
     const GT* gam = s_gam[buf];
     const float* bet = s_beta[buf];
 
-    uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
+    uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * (kPairK ? kHRecBytes : kRecBytes);
     // A (strictly lower) and Pt (lower incl. diagonal) from the Gram tiles
     {
       const int r0 = 16 * wave + 4 * (lane >> 4);
@@ -859,17 +929,15 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
             pv[nt][e] = j0 + e <= r ? rqr * rkj[e] * __expf(gr - gj[e]) * accH[nt][e] : 0.0f;
         }
       }
-      uint8_t* dst = rec + kFragBytes;
+      // single fp16 fragments, compact index x = wave + 2 ks; (mt, ks) = (0, 1) and
+      // (1, 1) lie above the diagonal and are not written
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        uint32_t hp[4], lp[4];
-        split2(pv[2 * ks][0], pv[2 * ks][1], hp[0], lp[0]);
-        split2(pv[2 * ks][2], pv[2 * ks][3], hp[1], lp[1]);
-        split2(pv[2 * ks + 1][0], pv[2 * ks + 1][1], hp[2], lp[2]);
-        split2(pv[2 * ks + 1][2], pv[2 * ks + 1][3], hp[3], lp[3]);
-        const int f = 2 * wave + ks;
-        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 0) * kWave + lane) * 16) = u32x4_t{hp[0], hp[1], hp[2], hp[3]};
-        *reinterpret_cast<u32x4_t*>(dst + ((size_t)(f * 2 + 1) * kWave + lane) * 16) = u32x4_t{lp[0], lp[1], lp[2], lp[3]};
+        if (ks == 1 && wave < 2) continue;   // uniform per wave
+        const u32x4_t hp = {pack_f16x2(pv[2 * ks][0], pv[2 * ks][1]), pack_f16x2(pv[2 * ks][2], pv[2 * ks][3]),
+                            pack_f16x2(pv[2 * ks + 1][0], pv[2 * ks + 1][1]),
+                            pack_f16x2(pv[2 * ks + 1][2], pv[2 * ks + 1][3])};
+        *reinterpret_cast<u32x4_t*>(rec + kHRecP + (size_t)(wave + 2 * ks) * kHFrag + 16 * lane) = hp;
       }
     }
     __syncthreads();
@@ -877,13 +945,15 @@ __global__ __launch_bounds__(kThreads, F32 ? 2 : kIntraMinWaves) void chunk_intr
     // T = (I + A)^-1; Tt = T diag(beta) is formed while writing the fragments
     write_operands<F32, kAP, kPairK, !kPairK>(sA, sP, sT, sM, bet, rec);
 
-    // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L}
+    // vectors: a = e^gam rk, b = rq e^gam, c = rk e^{gam_L - gam}, d = e^{gam_L};
+    // the register-resident spines multiply khat and qtil, which carry rk and rq
     if (tid < kC) {
-      float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
+      float* vec = reinterpret_cast<float*>(rec + (kPairK ? kHRecVec : 2 * kFragBytes));
       const GT gl = gam[kC - 1];
-      vec[tid] = __expf((float)gam[tid]) * s_rk[tid];
-      vec[kC + tid] = s_rq[tid] * __expf((float)gam[tid]);
-      vec[2 * kC + tid] = s_rk[tid] * __expf((float)(gl - gam[tid]));
+      const float rk = kPairK ? 1.0f : s_rk[tid], rq = kPairK ? 1.0f : s_rq[tid];
+      vec[tid] = __expf((float)gam[tid]) * rk;
+      vec[kC + tid] = rq * __expf((float)gam[tid]);
+      vec[2 * kC + tid] = rk * __expf((float)(gl - gam[tid]));
       if (tid == 0) vec[3 * kC] = __expf((float)gl);
     }
     if (wave == 0 && hh + 1 < ratio) gb_store(buf ^ 1, gv_next, bv_next);
@@ -1484,39 +1554,36 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
 // spine, register-resident form (bf16 inputs, scalar decay).
 //
 // One wave owns 16 value rows i of a head's state, for all 128 key columns and
-// all 64 tokens of a chunk, so every product of the chunk step is wave-local:
-//   Y, Z   = K S0^T, Q S0^T          (A: K / Q rows from LDS, B: the state)
+// all 64 tokens of a chunk, so every product of the chunk step is wave-local
+// (khat = rk K, qtil = rq Q, the normalised fp16 rows the intra kernel wrote):
+//   Y, Z   = khat S0^T, qtil S0^T    (A: khat / qtil rows from LDS, B: the state)
 //   R      = V - a Y
 //   Vnew   = Tt R                     (A: Tt from the record, B: R)
 //   O      = b Z + Pt Vnew            (A: Pt, B: Vnew)
-//   S^T   <- d S^T + K^T (c Vnew)     (A: K^T by transposing LDS reads, B: c Vnew)
-// The state is held as eight 16x16 accumulator tiles of S^T (key rows j, value
-// columns i).  In the paired-tile k order every B operand above is a pair of
-// accumulator tiles of the previous product, split into bf16 hi + lo in
-// registers: nothing but the chunk's shared inputs passes through LDS.  K and Q
-// are stored in LDS with each 32-column block in paired-tile order, so an A
-// fragment is one 16-byte read.  A workgroup is kNW waves (16 kNW value rows of
-// one head) sharing the chunk's K, Q, V, vectors and the record's Tt / Pt
+//   S^T   <- d S^T + khat^T (c Vnew)  (A: khat^T by transposing LDS reads, B: c Vnew)
+// with a = b = e^gam, c = e^{gam_L - gam}, d = e^{gam_L}.  The state is held as
+// eight 16x16 fp32 accumulator tiles of S^T (key rows j, value columns i).  In
+// the paired-tile k order every B operand above is a pair of accumulator tiles
+// of the previous product, rounded to fp16 in registers: nothing but the
+// chunk's shared inputs passes through LDS.  khat and qtil are stored in LDS
+// with each 32-column block in paired-tile order, so an A fragment is one
+// 16-byte read.  A workgroup is kNW waves (16 kNW value rows of one head)
+// sharing the chunk's khat, qtil, V, vectors and the record's Tt / Pt
 // fragments, double-buffered in LDS and staged through registers one chunk
 // ahead; each wave reads the Tt / Pt fragments from LDS as A operands.  One
 // barrier per chunk.
 // ---------------------------------------------------------------------------
-constexpr int kWP = kD + 16;   // K / Q row pitch in LDS (bf16 elements): 288 bytes
+constexpr int kWP = kD + 16;   // khat / qtil row pitch in LDS (fp16 elements): 288 bytes
 
 // LDS column of logical column j of a K / Q row (paired-tile order per 32 columns)
 __device__ __forceinline__ int wave_col(int j) {
   return (j & ~31) + 8 * ((j >> 2) & 3) + 4 * ((j >> 4) & 1) + (j & 3);
 }
 
-// two accumulator tiles -> one B operand in paired-tile k order, as hi and lo
-__device__ __forceinline__ void split_pair(const f32x4_t& a, const f32x4_t& b, bf16x8_t& hi, bf16x8_t& lo) {
-  uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
-  split2(a[0], a[1], h0, l0);
-  split2(a[2], a[3], h1, l1);
-  split2(b[0], b[1], h2, l2);
-  split2(b[2], b[3], h3, l3);
-  hi = __builtin_bit_cast(bf16x8_t, u32x4_t{h0, h1, h2, h3});
-  lo = __builtin_bit_cast(bf16x8_t, u32x4_t{l0, l1, l2, l3});
+// two accumulator tiles -> one fp16 operand in paired-tile k order
+__device__ __forceinline__ f16x8_t f16_pair(const f32x4_t& a, const f32x4_t& b) {
+  return as_f16x8(u32x4_t{pack_f16x2(a[0], a[1]), pack_f16x2(a[2], a[3]), pack_f16x2(b[0], b[1]),
+                          pack_f16x2(b[2], b[3])});
 }
 
 // 4 bf16 of a transposing LDS read: within each 16-lane group, lane 4r + q
@@ -1561,27 +1628,23 @@ struct SpineCfg {
   static constexpr int kThreadsW = kThreadsT;
   static constexpr int kRows = kRowsT;                    // value rows per workgroup
   static constexpr int kVP = kRows + 8;                   // V row pitch (bf16)
-  // one LDS slot (bytes): K | Q | V (bf16) | Tt, Pt fragments | chunk vectors
+  // one LDS slot (bytes): khat | qtil | V (fp16, fp16, bf16) | Tt, Pt fragments | chunk vectors
   static constexpr int kOffQ = kC * kWP * 2;
   static constexpr int kOffV = 2 * kOffQ;
   static constexpr int kOffTri = kOffV + kC * kVP * 2;
-  static constexpr int kTriFrags = 24;                    // (Tt, Pt) x 6 fragments x (hi, lo), 1 KB each
-  static constexpr int kOffVec = kOffTri + kTriFrags * 1024;
+  static constexpr int kTriFrags = 2 * kNF;               // (Tt, Pt) x 6 fp16 fragments, 1 KB each
+  static constexpr int kOffVec = kOffTri + kTriFrags * (int)kHFrag;
   static constexpr int kSlotBytes = kOffVec + 1024;
-  static constexpr int kPiecesKQ = kC * kD / 8 / kThreadsW;    // 16-byte pieces of K (and Q) per thread
+  static constexpr int kPiecesKQ = kC * kD / 8 / kThreadsW;    // 16-byte pieces of khat (and qtil) per thread
   static constexpr int kPiecesV = kC * kRows / 8 / kThreadsW;  // ... of V
-  static constexpr int kPiecesTri = kTriFrags * kWave / kThreadsW;
+  // ... of the fragments: the last round may cover only some of the waves
+  static constexpr int kPiecesTri = (kTriFrags * kWave + kThreadsW - 1) / kThreadsW;
   static constexpr int kLoads = 2 * kPiecesKQ + kPiecesV + kPiecesTri + 1;   // + the vectors
   static_assert(kPiecesKQ * kThreadsW == kC * kD / 8 && kPiecesV * kThreadsW == kC * kRows / 8 &&
-                kPiecesTri * kThreadsW == kTriFrags * kWave, "pieces must divide evenly over the threads");
+                kThreadsW % kWave == 0, "pieces must divide evenly over the threads");
 };
 
-// Tt / Pt fragments (mt, ks) with ks <= mt / 2 (the rest of the 64 x 64 is zero)
-constexpr int kNF = 6;
-__host__ __device__ constexpr int frag_mt(int x) { return x < 4 ? x : x - 2; }     // 0 1 2 3 2 3
-__host__ __device__ constexpr int frag_ks(int x) { return x < 4 ? 0 : 1; }         // 0 0 0 0 1 1
-
-// One chunk's inputs (K and Q rows, the workgroup's V columns, the Tt / Pt
+// One chunk's inputs (khat and qtil rows, the workgroup's V columns, the Tt / Pt
 // fragments and the chunk vectors of its record) staged through registers into
 // an LDS slot, one 16-byte piece per call so the loads and the LDS writes can
 // be spread between MFMAs.  Per chunk a buffer descriptor covers its rows:
@@ -1612,7 +1675,7 @@ struct ChunkStage {
     r.k = make_rsrc(kp + (int64_t)t0 * qk_stride, L * qk_row);
     r.q = make_rsrc(qp + (int64_t)t0 * qk_stride, L * qk_row);
     r.v = make_rsrc(vp + (int64_t)t0 * v_stride, L * v_row);
-    r.r = make_rsrc(rec0 + (in ? cl : 0) * rec_step, in ? (uint32_t)kRecBytes : 0u);
+    r.r = make_rsrc(rec0 + (in ? cl : 0) * rec_step, in ? (uint32_t)kHRecBytes : 0u);
     return r;
   }
   __device__ void load(const Rsrc& r, int i) {   // i < kLoads, a compile-time constant after unrolling
@@ -1626,14 +1689,12 @@ struct ChunkStage {
       const int j = i - 2 * Cf::kPiecesKQ;
       v[j] = buf_load16(r.v, off_v + (uint32_t)j * (kT / (Cf::kRows / 8)) * v_row, 0);
     } else if (i < Cf::kLoads - 1) {
-      // slot fragment f = record fragment (Tt then Pt, x, hi / lo)
+      // the record's twelve fragments are the slot's, in the same order
       const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
-      const int f = (tid + j * kT) / kWave;                 // uniform per wave
-      const int which = f / 12, x = (f % 12) / 2, hl = f % 2;
-      const int rf = 2 * (2 * frag_mt(x) + frag_ks(x)) + hl;
-      tri[j] = buf_load16(r.r, 16 * (tid % kWave) + (uint32_t)(which * kFragBytes + rf * 1024), 0);
+      const int p = tid + j * kT;
+      if (p < Cf::kTriFrags * kWave) tri[j] = buf_load16(r.r, 16 * (uint32_t)p, 0);   // uniform per wave
     } else {
-      vec = buf_load16(r.r, 16 * (tid % kC) + (uint32_t)(2 * kFragBytes), 0);
+      vec = buf_load16(r.r, 16 * (tid % kC) + (uint32_t)kHRecVec, 0);
     }
   }
   // every piece, with each index a compile-time constant (so the staging
@@ -1661,7 +1722,8 @@ struct ChunkStage {
       *reinterpret_cast<u32x4_t*>(base + Cf::kOffV + 2 * (r * Cf::kVP + c8)) = v[j];
     } else if (i < Cf::kLoads - 1) {
       const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
-      *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * (tid + j * kT)) = tri[j];
+      const int p = tid + j * kT;
+      if (p < Cf::kTriFrags * kWave) *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * p) = tri[j];
     } else {
       // every thread loaded piece tid % kC and writes it (duplicates carry the same
       // bytes): a write under tid < kC would let the compiler sink the load into
@@ -1734,8 +1796,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   stage.vp = v + h * kD + i0;
   stage.qk_stride = qk_stride;
   stage.v_stride = v_stride;
-  stage.rec0 = ws + records_offset(n_seq) + ((size_t)plan_first(first, n_seq, n) * hv + h) * kRecBytes;
-  stage.rec_step = (size_t)hv * kRecBytes;
+  stage.rec0 = ws + records_offset(n_seq) + ((size_t)plan_first(first, n_seq, n) * hv + h) * kHRecBytes;
+  stage.rec_step = (size_t)hv * kHRecBytes;
   stage.seq_beg = seq_beg;
   stage.seq_end = seq_end;
   stage.n_chunks = n_chunks;
@@ -1799,16 +1861,16 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     const uint16_t* sv = reinterpret_cast<const uint16_t*>(base + Cf::kOffV);
     const uint8_t* tri = base + Cf::kOffTri;
     const float* vec = reinterpret_cast<const float*>(base + Cf::kOffVec);
-    auto tri_frag = [&](int which, int x, int hl) {
-      return load_bf16x8(reinterpret_cast<const uint16_t*>(tri + (which * 12 + 2 * x + hl) * 1024 + 16 * lane));
+    auto tri_frag = [&](int which, int x) {
+      return load_f16x8(reinterpret_cast<const uint16_t*>(tri + (which * kNF + x) * kHFrag + 16 * lane));
     };
     // LDS operands of the first k step of Y / Z, the V tile, the vectors
-    bf16x8_t fk[4], fq[4];
+    f16x8_t fk[4], fq[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const int off = (16 * mt + m) * kWP + 8 * g;
-      fk[mt] = load_bf16x8(sk + off);
-      fq[mt] = load_bf16x8(sq + off);
+      fk[mt] = load_f16x8(sk + off);
+      fq[mt] = load_f16x8(sq + off);
     }
     v4s_t vv[4];
     f32x4_t va[4];
@@ -1819,11 +1881,11 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     }
 
     // state as B operands (and, for Z^T = S Q^T, as A operands): k step ks = key tiles 2ks, 2ks+1
-    bf16x8_t sbh[kKS], sbl[kKS];
+    f16x8_t sb[kKS];
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks) split_pair(sst[2 * ks], sst[2 * ks + 1], sbh[ks], sbl[ks]);
+    for (int ks = 0; ks < kKS; ++ks) sb[ks] = f16_pair(sst[2 * ks], sst[2 * ks + 1]);
 
-    // ---- Y = K S0^T (rows t, columns i) and Z^T = S0 Q^T (rows i, columns t), over this wave's keys ----
+    // ---- Y = khat S0^T (rows t, columns i) and Z^T = S0 qtil^T (rows i, columns t), over this wave's keys ----
     f32x4_t y[4], zt[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) y[mt] = zt[mt] = zero4;
@@ -1832,13 +1894,13 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     constexpr int kLPer = (kLoads + 4 * kKS - 1) / (4 * kKS);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
-      bf16x8_t nk[4], nq[4];
+      f16x8_t nk[4], nq[4];
       if (ks + 1 < kKS) {
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const int off = (16 * mt + m) * kWP + 32 * (ks + 1) + 8 * g;
-          nk[mt] = load_bf16x8(sk + off);
-          nq[mt] = load_bf16x8(sq + off);
+          nk[mt] = load_f16x8(sk + off);
+          nq[mt] = load_f16x8(sq + off);
         }
       }
 #pragma unroll
@@ -1850,10 +1912,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
             if (i < kLoads) stage.load(rn, i);
           }
         }
-        y[mt] = mfma_bf16(fk[mt], sbh[ks], y[mt]);
-        zt[mt] = mfma_bf16(sbh[ks], fq[mt], zt[mt]);
-        y[mt] = mfma_bf16(fk[mt], sbl[ks], y[mt]);
-        zt[mt] = mfma_bf16(sbl[ks], fq[mt], zt[mt]);
+        y[mt] = mfma_f16(fk[mt], sb[ks], y[mt]);
+        zt[mt] = mfma_f16(sb[ks], fq[mt], zt[mt]);
         if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
       if (ks + 1 < kKS) {
@@ -1868,33 +1928,33 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     if constexpr (kNorm) load_z(cl + 1, zn);
 
     // LDS operands of the later products: Tt, Pt (this wave's token tiles) and
-    // K^T for the state update (transposing reads: A[j][slot (g, e)] =
-    // K[k0 + pair_k(0, g, e)][16 jt + j])
-    bf16x8_t th[kNF], tl[kNF], ph[kNF], pl[kNF], kt[kJT];
+    // khat^T for the state update (transposing reads: A[j][slot (g, e)] =
+    // khat[k0 + pair_k(0, g, e)][16 jt + j])
+    f16x8_t th[kNF], ph[kNF], kt[kJT];
     auto read_tt = [&]() {
 #pragma unroll
-      for (int x = 0; x < kNF; ++x) { th[x] = tri_frag(0, x, 0); tl[x] = tri_frag(0, x, 1); }
+      for (int x = 0; x < kNF; ++x) th[x] = tri_frag(0, x);
     };
     auto read_pt = [&]() {
 #pragma unroll
-      for (int x = 0; x < kNF; ++x) { ph[x] = tri_frag(1, x, 0); pl[x] = tri_frag(1, x, 1); }
+      for (int x = 0; x < kNF; ++x) ph[x] = tri_frag(1, x);
     };
-    auto read_kt = [&](int k0, bf16x8_t* dst) {
+    auto read_kt = [&](int k0, f16x8_t* dst) {
 #pragma unroll
       for (int jt = 0; jt < kJT; ++jt)
-        dst[jt] = lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP);
+        dst[jt] = __builtin_bit_cast(f16x8_t, lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP));
     };
 
     // ---- R = V - a Y (accumulator layout: rows 16 mt + 4 g + e, column iw + m) ----
-    bf16x8_t rbh[2], rbl[2];
+    f16x8_t rb[2];
     {
       f32x4_t r[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int e = 0; e < 4; ++e) r[mt][e] = bf16_bits_to_f32((uint16_t)vv[mt][e]) - va[mt][e] * y[mt][e];
-      split_pair(r[0], r[1], rbh[0], rbl[0]);
-      split_pair(r[2], r[3], rbh[1], rbl[1]);
+      rb[0] = f16_pair(r[0], r[1]);
+      rb[1] = f16_pair(r[2], r[3]);
     }
 
     read_kt(0, kt);
@@ -1906,17 +1966,12 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) vn[mt] = zero4;
 #pragma unroll
-      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(th[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
-#pragma unroll
-      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(th[x], rbl[frag_ks(x)], vn[frag_mt(x)]);
-#pragma unroll
-      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_bf16(tl[x], rbh[frag_ks(x)], vn[frag_mt(x)]);
+      for (int x = 0; x < kNF; ++x) vn[frag_mt(x)] = mfma_f16(th[x], rb[frag_ks(x)], vn[frag_mt(x)]);
     }
 
-
-    bf16x8_t nbh[2], nbl[2], wbh[2], wbl[2];
-    split_pair(vn[0], vn[1], nbh[0], nbl[0]);
-    split_pair(vn[2], vn[3], nbh[1], nbl[1]);
+    f16x8_t nb[2], wb[2];
+    nb[0] = f16_pair(vn[0], vn[1]);
+    nb[1] = f16_pair(vn[2], vn[3]);
     {
       f32x4_t w[4];
 #pragma unroll
@@ -1925,8 +1980,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[mt][e] = c[e] * vn[mt][e];
       }
-      split_pair(w[0], w[1], wbh[0], wbl[0]);
-      split_pair(w[2], w[3], wbh[1], wbl[1]);
+      wb[0] = f16_pair(w[0], w[1]);
+      wb[1] = f16_pair(w[2], w[3]);
     }
 
     // The next chunk's inputs go to the other LDS slot in pieces between the
@@ -1948,8 +2003,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) {
       commit_group(jt);
-      u[jt] = mfma_bf16(kt[jt], wbh[0], zero4);
-      u[jt] = mfma_bf16(kt[jt], wbl[0], u[jt]);
+      u[jt] = mfma_f16(kt[jt], wb[0], zero4);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
     read_kt(32, kt);   // the second k step reuses kt
@@ -1960,8 +2014,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) {
       commit_group(kJT + kNF + jt);
-      u[jt] = mfma_bf16(kt[jt], wbh[1], u[jt]);
-      u[jt] = mfma_bf16(kt[jt], wbl[1], u[jt]);
+      u[jt] = mfma_f16(kt[jt], wb[1], u[jt]);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -1986,9 +2039,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
       for (int x = 0; x < kNF; ++x) {
         commit_group(kJT + x);
-        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-        zt[frag_mt(x)] = mfma_bf16(nbl[frag_ks(x)], ph[x], zt[frag_mt(x)]);
-        zt[frag_mt(x)] = mfma_bf16(nbh[frag_ks(x)], pl[x], zt[frag_mt(x)]);
+        zt[frag_mt(x)] = mfma_f16(nb[frag_ks(x)], ph[x], zt[frag_mt(x)]);
         if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);   // keep the staging interleaved
       }
     }
@@ -2057,9 +2108,14 @@ int chunk_spine_kind(const Dims& d, bool in_bf16, int n) {
 template <bool F32, bool kPC, typename Tin, typename To>
 hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_stride, const void* v,
                       int64_t v_stride, const Gates& gt, const float* init_state,
-                      const int32_t* cu_dev, int n, int total_chunks, void* out,
+                      const int32_t* cu_dev, int n, int t, int total_chunks, void* out,
                       float* final_state, void* ws, const FusedNorm& nrm, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
+  // register-resident spines: normalised fp16 rows written by the intra kernel
+  // (khat [T][Hk][dk], then qtil)
+  uint16_t* khat = F32 || kPC ? nullptr : reinterpret_cast<uint16_t*>(w + hat_offset(n, t, d.hv));
+  uint16_t* qhat = khat ? khat + (size_t)t * d.hk * kD : nullptr;
+  const int64_t hat_stride = (int64_t)d.hk * kD;
   // bf16 inputs with scalar decay run a register-resident spine: a whole
   // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
   // work overlaps the other's MFMAs, and the gated norm can be fused) once
@@ -2082,7 +2138,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     else   // bf16: records in the paired-tile k order of the register-resident spines
       hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, !F32>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt,
-                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w);
+                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w, khat);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2092,12 +2148,12 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     if (nrm.z)
       hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                         qhat, khat, hat_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
     else
       hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
-                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                         qhat, khat, hat_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
   } else if (!F32 && spine == kSpineRows) {
@@ -2105,7 +2161,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     hipLaunchKernelGGL((chunk_spine_wave_kernel<kRowsNW, kRowsLoaders, To>), dim3(blocks),
                        dim3((kRowsNW + kRowsLoaders) * kWave), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), qk_stride,
+                       qhat, khat, hat_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state, nrm);
   } else if constexpr (F32 || kPC) {
@@ -2122,14 +2178,14 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
 template <bool kPC>
 hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void* q, const void* k,
                           int64_t qk_stride, const void* v, int64_t v_stride, const Gates& gt,
-                          const float* init_state, const int32_t* cu_dev, int n,
+                          const float* init_state, const int32_t* cu_dev, int n, int t,
                           int total, void* out, float* final_state, void* ws, const FusedNorm& nrm,
                           hipStream_t s) {
   if (in_bf16)
-    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
-  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+    return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
+                    : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
+  return out_bf16 ? chunk_impl<true, kPC, float, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
+                  : chunk_impl<true, kPC, float, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace
@@ -2140,7 +2196,11 @@ bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n) {
 
 size_t chunk_workspace_bytes(const Dims& d, int n, int t) {
   const size_t max_chunks = (size_t)t / kC + (size_t)n;
-  return records_offset(n) + max_chunks * d.hv * kRecBytes;
+  // the larger of the two layouts: hi/lo or fp32 records (fp32 inputs, per-key-channel
+  // decay), or fp16 records and the normalised rows (the register-resident spines)
+  const size_t split = records_offset(n) + max_chunks * d.hv * kRecBytes;
+  const size_t half = hat_offset(n, t, d.hv) + 2 * (size_t)t * d.hk * kD * sizeof(uint16_t);
+  return std::max(split, half);
 }
 
 hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
@@ -2150,7 +2210,6 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
                                 const int32_t* cu_host, int n, int t, void* out,
                                 float* final_state, void* ws, size_t ws_bytes,
                                 const uint16_t* norm_z, const float* norm_w, hipStream_t s) {
-  (void)t;
   (void)ws_bytes;
   if (n == 0) return hipSuccess;
   if (norm_z && !chunk_fuses_norm(d, in_bf16, n)) return hipErrorInvalidValue;
@@ -2158,8 +2217,8 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
   for (int i = 0; i < n; ++i) total += (cu_host[i + 1] - cu_host[i] + kC - 1) / kC;
   const FusedNorm nrm{norm_z, norm_w, d.rms_eps};
   return d.per_channel
-             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s)
-             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, total, out, final_state, ws, nrm, s);
+             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
+             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace gdn

@@ -76,6 +76,22 @@ __device__ __forceinline__ f32x4_t mfma_f32(float a, float b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// fp16 operands (the register-resident chunk spines): 11 significant bits, so a
+// single rounding of an fp32 operand costs at most 2^-11 relative.
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x4_t mfma_f16(f16x8_t a, f16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// Two fp32 values rounded to fp16 (nearest even), packed low-first in one dword.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, f16x2_t));
+}
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4_t u) { return __builtin_bit_cast(f16x8_t, u); }
+__device__ __forceinline__ f16x8_t load_f16x8(const uint16_t* p) {  // 16-byte aligned
+  return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const u32x4_t*>(p));
+}
+
 __device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {  // 16-byte aligned
   return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(p));
 }
