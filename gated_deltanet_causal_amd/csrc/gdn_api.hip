@@ -284,11 +284,16 @@ static gdn_status_t prefill_checked(const gdn_config_t* cfg, gdn_dtype_t dtype, 
                                                 final_state, w8 + wl.chunk, wl.o - wl.chunk,
                                                 static_cast<const uint16_t*>(z), norm_w, s));
   }
-  float* o = reinterpret_cast<float*>(w8 + wl.o);
+  // the pre-norm output: fp16 where the spine rounds its operands to fp16 anyway
+  // (half the bytes of the round trip through memory), else fp32
+  void* o = w8 + wl.o;
+  const bool o_f16 = gdn::chunk_out_f16(d, bf16, N);
   e = gdn::launch_chunk_prefill(d, bf16, false, q, k, d.cc, v, d.cc, gt, initial_state, cu_dev,
                                 cu_host, N, T, o, final_state, w8 + wl.chunk, wl.o - wl.chunk,
-                                nullptr, nullptr, s);
+                                nullptr, nullptr, s, o_f16);
   if (e != hipSuccess) return GDN_ERR_HIP;
+  if (o_f16)
+    return hip_status(gdn::launch_gated_rmsnorm_f16o(d, bf16, out_dtype == GDN_BF16, o, z, norm_w, out, T, s));
   return hip_status(gdn::launch_gated_rmsnorm(d, false, bf16, out_dtype == GDN_BF16, o, z, norm_w,
                                               out, T, s));
 }

@@ -1614,6 +1614,10 @@ __device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t
 __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4_t v, float*) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, voff, 0, 0);
 }
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4_t v, _Float16*) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{pack_f16x2(v[0], v[1]), pack_f16x2(v[2], v[3])}, r, voff, 0, 0);
+}
 __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t voff, f32x4_t v, uint16_t*) {
   const uint32_t lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t));
   const uint32_t hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t));
@@ -2146,7 +2150,8 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   if (!F32 && spine == kSpineWave) {
     const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    if (nrm.z)
+    if constexpr (std::is_same_v<To, _Float16>) return hipErrorInvalidValue;   // never asked for
+    else if (nrm.z)
       hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
                          qhat, khat, hat_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
@@ -2176,11 +2181,15 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
 }
 
 template <bool kPC>
-hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void* q, const void* k,
+hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, bool out_f16, const void* q, const void* k,
                           int64_t qk_stride, const void* v, int64_t v_stride, const Gates& gt,
                           const float* init_state, const int32_t* cu_dev, int n, int t,
                           int total, void* out, float* final_state, void* ws, const FusedNorm& nrm,
                           hipStream_t s) {
+  if constexpr (!kPC) {
+    if (in_bf16 && out_f16)
+      return chunk_impl<false, kPC, uint16_t, _Float16>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
+  }
   if (in_bf16)
     return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
                     : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
@@ -2192,6 +2201,10 @@ hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, const void
 
 bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n) {
   return chunk_spine_kind(d, in_bf16, n) == kSpineWave;
+}
+
+bool chunk_out_f16(const Dims& d, bool in_bf16, int n) {
+  return chunk_spine_kind(d, in_bf16, n) == kSpineRows;
 }
 
 size_t chunk_workspace_bytes(const Dims& d, int n, int t) {
@@ -2209,16 +2222,17 @@ hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, cons
                                 const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
                                 float* final_state, void* ws, size_t ws_bytes,
-                                const uint16_t* norm_z, const float* norm_w, hipStream_t s) {
+                                const uint16_t* norm_z, const float* norm_w, hipStream_t s, bool out_f16) {
   (void)ws_bytes;
   if (n == 0) return hipSuccess;
   if (norm_z && !chunk_fuses_norm(d, in_bf16, n)) return hipErrorInvalidValue;
+  if (out_f16 && !chunk_out_f16(d, in_bf16, n)) return hipErrorInvalidValue;
   int total = 0;
   for (int i = 0; i < n; ++i) total += (cu_host[i + 1] - cu_host[i] + kC - 1) / kC;
   const FusedNorm nrm{norm_z, norm_w, d.rms_eps};
   return d.per_channel
-             ? chunk_dispatch<true>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
-             : chunk_dispatch<false>(d, in_bf16, out_bf16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
+             ? chunk_dispatch<true>(d, in_bf16, out_bf16, out_f16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
+             : chunk_dispatch<false>(d, in_bf16, out_bf16, out_f16, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
 }
 
 }  // namespace gdn

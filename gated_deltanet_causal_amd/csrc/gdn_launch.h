@@ -66,13 +66,24 @@ size_t chunk_workspace_bytes(const Dims& d, int n, int t);
 // output itself (norm_z / norm_w of launch_chunk_prefill); the answer depends
 // only on the geometry, the input dtype and n.
 bool chunk_fuses_norm(const Dims& d, bool in_bf16, int n);
+// Whether the chunk prefill for n sequences can write its output as fp16
+// (out_f16): the register-resident spine with 32 value rows per workgroup,
+// whose products already round their operands to fp16; the one-call prefill
+// keeps its pre-norm output in that form when it does not fuse the norm.
+bool chunk_out_f16(const Dims& d, bool in_bf16, int n);
 // norm_z (bf16 [T][Hv][dv]) and norm_w non-null: out receives the gated norm
-// of the chunk output (requires chunk_fuses_norm).
+// of the chunk output (requires chunk_fuses_norm).  out_f16: out is fp16
+// (requires chunk_out_f16; out_bf16 is then ignored).
 hipError_t launch_chunk_prefill(const Dims& d, bool in_bf16, bool out_bf16, const void* q,
                                 const void* k, int64_t qk_stride, const void* v,
                                 int64_t v_stride, const Gates& gt, const float* init_state, const int32_t* cu_dev,
                                 const int32_t* cu_host, int n, int t, void* out,
                                 float* final_state, void* ws, size_t ws_bytes,
-                                const uint16_t* norm_z, const float* norm_w, hipStream_t s);
+                                const uint16_t* norm_z, const float* norm_w, hipStream_t s,
+                                bool out_f16 = false);
+// The gated norm of an fp16 o (the one-call prefill's pre-norm output), z bf16 or fp32.
+hipError_t launch_gated_rmsnorm_f16o(const Dims& d, bool z_bf16, bool out_bf16, const void* o,
+                                     const void* z, const float* w, void* out, int64_t rows,
+                                     hipStream_t s);
 
 }  // namespace gdn

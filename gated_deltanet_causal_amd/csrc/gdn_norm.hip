@@ -13,6 +13,8 @@
 // vectors per step and takes two steps at once so each lane keeps two sets of
 // loads in flight.  The sum of squares is reduced inside each 16-lane row with
 // DPP.  Pure streaming: HBM-bound.
+#include <type_traits>
+
 #include "gdn_device.h"
 #include "gdn_launch.h"
 
@@ -26,7 +28,11 @@ constexpr int kVecPerBlock = kNormThreads / kWave * kVecPerWaveStep * kSteps;   
 
 template <typename T>
 __device__ __forceinline__ void ld8(const T* p, float (&v)[8]) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (std::is_same_v<T, _Float16>) {
+    const f16x8_t h = load_f16x8(reinterpret_cast<const uint16_t*>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)h[i];
+  } else if constexpr (sizeof(T) == 2) {
     const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -117,6 +123,13 @@ hipError_t norm_out(const Dims& d, bool out_bf16, const void* o, const void* z, 
                     void* out, int64_t rows, hipStream_t s) {
   return out_bf16 ? norm_impl<Ti, Tz, uint16_t>(d, o, z, w, out, rows, s)
                   : norm_impl<Ti, Tz, float>(d, o, z, w, out, rows, s);
+}
+
+hipError_t launch_gated_rmsnorm_f16o(const Dims& d, bool z_bf16, bool out_bf16, const void* o,
+                                     const void* z, const float* w, void* out, int64_t rows,
+                                     hipStream_t s) {
+  return z_bf16 ? norm_out<_Float16, uint16_t>(d, out_bf16, o, z, w, out, rows, s)
+                : norm_out<_Float16, float>(d, out_bf16, o, z, w, out, rows, s);
 }
 
 hipError_t launch_gated_rmsnorm(const Dims& d, bool o_bf16, bool z_bf16, bool out_bf16,
