@@ -26,12 +26,14 @@
 //   plan   prefix sum of chunks per sequence (device side, from cu_seqlens).
 //   intra  one workgroup per (chunk, key head): K K^T and Q K^T on MFMA once
 //          for the key head, then per value head A, the unit-lower triangular
-//          inverse, Tt and Pt.  Tt and Pt are written to the workspace already
-//          in the MFMA A-operand lane layout (fp16 for the register-resident
-//          spines, hi/lo bf16 pairs for the LDS spine, or fp32).
+//          inverse, Tt and Pt (per-key-channel decay: one workgroup per (chunk,
+//          value head), decayed Gram tiles).  Tt and Pt are written to the
+//          workspace already in the MFMA A-operand lane layout: fp16 for the
+//          register-resident spines (bf16 inputs), fp32 for the LDS spine.
 //   spine  walks a sequence's chunks in order with the fp32 state in MFMA
-//          accumulators (register-resident: 16 value rows per wave) or in LDS,
-//          running the products above on MFMA.
+//          accumulators, running the products above on MFMA: register-
+//          resident (bf16 inputs, 16 value rows per wave, every product
+//          chained through registers) or through LDS (fp32 inputs).
 // Numerics.  The Gram products K K^T and Q K^T take the raw bf16 rows exactly.
 // bf16 inputs with scalar decay (the register-resident spines): every operand
 // of the state and output products -- khat = rk K and qtil = rq Q (formed once
@@ -42,9 +44,11 @@
 // 6-9e-4 max-relative over 1-4k tokens (with and without decay), inside the
 // 2e-3 bound; operands must stay within fp16 range (|x| < 65504), which holds
 // for normalised rows, decay factors <= 1 and values and states of the
-// activations' scale.  The LDS spine (per-key-channel decay) splits every fp32
-// operand into hi + lo bf16 (hi*hi + hi*lo + lo*hi, two terms when one side is
-// an exact bf16 input), ~2^-16 relative.  The fp32 input path uses fp32 MFMA.
+// activations' scale.  Per-key-channel decay multiplies Kt = khat e^{gam_t},
+// Qt = qtil e^{gam_t} and Kb = khat e^{gam_L - gam_t} instead (fp16, factors
+// <= 1), formed by its intra kernel, whose decayed Gram tiles split every
+// fp32 operand into hi + lo bf16 (hi*hi + hi*lo + lo*hi, ~2^-16 relative).
+// The fp32 input path uses fp32 MFMA throughout.
 #include <algorithm>
 #include <type_traits>
 #include <utility>
@@ -495,13 +499,19 @@ __device__ __forceinline__ f32x4_t mma3(typename Ops<F32>::F ah, typename Ops<F3
 //          those 8 tokens (|g| > ~10 per token sustained), the tile is
 //          instead summed element by element with e^{gam_r - gam_j} <= 1.
 // The operands are formed in registers from raw K / Q and gam, split hi/lo.
+// bf16 inputs: the kernel also writes what the register-resident spine
+// multiplies, each rounded once to fp16 (every factor e^{<= 0}):
+//   Kt[t] = khat_t e^{gam_t},  Qt[t] = qtil_t e^{gam_t},  Kb[t] = khat_t e^{gam_L - gam_t}
+// ([T][Hv][dk] each, Qt and Kb after Kt), its records (Tt, Pt as fp16
+// fragments) and d = e^{gam_L} per channel; the fp32 path keeps the LDS spine.
 // ---------------------------------------------------------------------------
 constexpr float kDiagLim = 80.0f;   // largest exponent of a diagonal-tile factor (e^80 ~ 5.5e34)
 template <bool F32, typename Tin>
 __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
     const float* __restrict__ g, const float* __restrict__ beta, const int32_t* __restrict__ cu,
-    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws) {
+    int n_seq, int hk, int hv, int l2norm, float l2_eps, float q_scale, uint8_t* __restrict__ ws,
+    uint16_t* __restrict__ kpc) {
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
@@ -523,6 +533,7 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   __shared__ float sM[3 * 16 * 17];
   __shared__ float s_rk[kC], s_rq[kC], s_beta[kC];
   __shared__ GT s_tot[kD];
+  __shared__ float s_dl[F32 ? 1 : kD];   // e^{gam_L} per channel (bf16 inputs)
 
   const int32_t* first = reinterpret_cast<const int32_t*>(ws);
   const int c = blockIdx.x;
@@ -580,6 +591,37 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     for (int r = 0; r < kC / 2; ++r) sGam[(half * (kC / 2) + r) * kGP + ch] = v[r] + off;
   }
   __syncthreads();
+  if constexpr (!F32) {
+    // the register-resident spine's operands Kt, Qt, Kb of rows r < L (rows past
+    // the chunk's end belong to the next sequence); gam_L = gam of row 63
+    const int64_t plane = (int64_t)cu[n_seq] * hv * kD;   // [T][Hv][dk]
+    if (tid < kD) s_dl[tid] = __expf(sGam[(kC - 1) * kGP + tid]);
+#pragma unroll 1
+    for (int p = tid; p < kC * kD / 8; p += kThreads) {
+      const int r = p / (kD / 8), c8 = 8 * (p % (kD / 8));
+      if (r >= L) continue;
+      const u32x4_t ku = *reinterpret_cast<const u32x4_t*>(sK + r * kPitch + c8);
+      const u32x4_t qu = *reinterpret_cast<const u32x4_t*>(sQ + r * kPitch + c8);
+      const float rk = s_rk[r], rq = s_rq[r];
+      u32x4_t kt, qt, kb;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int c0 = c8 + 2 * w;
+        const float g0 = sGam[r * kGP + c0], g1 = sGam[r * kGP + c0 + 1];
+        const float e0 = __expf(g0), e1 = __expf(g1);
+        const float f0 = __expf(sGam[(kC - 1) * kGP + c0] - g0), f1 = __expf(sGam[(kC - 1) * kGP + c0 + 1] - g1);
+        const float k0 = __uint_as_float(ku[w] << 16) * rk, k1 = __uint_as_float(ku[w] & 0xffff0000u) * rk;
+        const float q0 = __uint_as_float(qu[w] << 16) * rq, q1 = __uint_as_float(qu[w] & 0xffff0000u) * rq;
+        kt[w] = pack_f16x2(k0 * e0, k1 * e1);
+        qt[w] = pack_f16x2(q0 * e0, q1 * e1);
+        kb[w] = pack_f16x2(k0 * f0, k1 * f1);
+      }
+      uint16_t* dst = kpc + ((int64_t)(t0 + r) * hv + h) * kD + c8;
+      *reinterpret_cast<u32x4_t*>(dst) = kt;
+      *reinterpret_cast<u32x4_t*>(dst + plane) = qt;
+      *reinterpret_cast<u32x4_t*>(dst + 2 * plane) = kb;
+    }
+  }
   // references of this wave's row tile (rows past L carry gam_{L-1}: g is zero there)
   const GT* ref_off = sGam + 16 * wave * kGP;
   const GT* ref_dia = sGam + (16 * wave + 8) * kGP;
@@ -687,13 +729,18 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     }
   }
   __syncthreads();
-  uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * kRecBytes;
-  write_operands<F32, kAP>(sA, sP, sT, sM, s_beta, rec);
-  // vectors for the spine: rk, rq
-  if (tid < kC) {
-    float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
-    vec[tid] = s_rk[tid];
-    vec[kC + tid] = s_rq[tid];
+  uint8_t* rec = ws + records_offset(n_seq) + ((size_t)c * hv + h) * (F32 ? kRecBytes : kHRecBytes);
+  write_operands<F32, kAP, !F32>(sA, sP, sT, sM, s_beta, rec);
+  if constexpr (F32) {
+    // vectors for the LDS spine: rk, rq
+    if (tid < kC) {
+      float* vec = reinterpret_cast<float*>(rec + 2 * kFragBytes);
+      vec[tid] = s_rk[tid];
+      vec[kC + tid] = s_rq[tid];
+    }
+  } else {
+    // the register-resident spine's decay of the state over the chunk, per channel
+    if (tid < kD) reinterpret_cast<float*>(rec + kHRecVec)[tid] = s_dl[tid];
   }
 }
 
@@ -972,14 +1019,8 @@ constexpr int kSpineThreads = 512;   // 8 waves, two per SIMD
 // The Tt / Pt fragments do not pass through here: each wave loads its own row
 // tile of them straight into registers.
 template <bool F32, bool kPC> struct Stage {
-  // bf16 with per-key-channel decay: K, Q and g staged in one layout (rows 2p,
-  // 2p+1, columns 8cb .. +7) with the rows' rk, rq, so that the decayed operands
-  // are formed in registers at commit
-  static constexpr bool kPCB = kPC && !F32;
   u32x4_t k[F32 ? 4 : 2], q[F32 ? 4 : 2], v;
   float vec, gv[kPC && F32 ? 16 : 1];
-  f32x4_t g4[kPCB ? 4 : 1];
-  float rkq[kPCB ? 4 : 1];
 };
 
 // Loads are issued in parts (kParts: bit 0 K and Q, bit 1 V and the vectors,
@@ -1022,26 +1063,8 @@ __device__ __forceinline__ void stage_issue(Stage<F32, kPC>& sg, const Tin* k, c
     else sg.v = tid < kC * 4 ? row16(v, v_stride, tid / 4, 8 * (tid % 4)) : z;
     if constexpr (kPC) sg.vec = tid < 2 * kC ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
     else sg.vec = tid < 3 * kC + 1 ? reinterpret_cast<const float*>(rec + 2 * kFragBytes)[tid] : 0.0f;
-    if constexpr (kPC && !F32) {
-      // rk and rq of this thread's row pair (zero past the end)
-      const float* vec = reinterpret_cast<const float*>(rec + 2 * kFragBytes);
-      const int t = 2 * (tid % (kC / 2));
-      sg.rkq[0] = vec[t];
-      sg.rkq[1] = vec[t + 1];
-      sg.rkq[2] = vec[kC + t];
-      sg.rkq[3] = vec[kC + t + 1];
-    }
   }
-  if constexpr ((kParts & 4) && kPC && !F32) {
-    // log decays of the row pair, columns 8cb .. +7 (zero past the end)
-    const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
-    const f32x4_t zf = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-        sg.g4[2 * r + h2] = t + r < L ? *reinterpret_cast<const f32x4_t*>(g + (int64_t)(t + r) * hv * kD + j0 + 4 * h2) : zf;
-  } else if constexpr ((kParts & 4) && kPC) {
+  if constexpr ((kParts & 4) && kPC) {
     // channel tid/4, rows 16 (tid%4) .. +15 of the chunk
     const int ch = tid / 4, r0 = 16 * (tid % 4);
 #pragma unroll
@@ -1102,7 +1125,7 @@ __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename
     // rows t < p_c keep gam_t and the others gam_L - gam_t: the value not kept
     // is then gam_L minus one of at most half its size, accurate to fp32
     // rounding.
-    static_assert(F32, "the bf16 per-channel spine commits through stage_commit_pcb");
+    static_assert(F32, "per-key-channel decay on the LDS spine is the fp32 path");
     const int ch = tid / 4, part = tid % 4;
     float own = 0.0f;
 #pragma unroll
@@ -1147,95 +1170,6 @@ __device__ __forceinline__ void stage_commit(const Stage<F32, kPC>& sg, typename
   }
 }
 
-// Inclusive prefix sum over each aligned group of 32 lanes: shifts by 1, 2, 4, 8
-// inside each row of 16 lanes, then the last lane of rows 0 and 2 added to
-// rows 1 and 3.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ float dpp_shift_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, kRowMask,
-                                                                   0xF, true));
-}
-__device__ __forceinline__ float scan32(float v) {
-  v = dpp_shift_add<0x111, 0xF>(v);   // row_shr:1
-  v = dpp_shift_add<0x112, 0xF>(v);   // row_shr:2
-  v = dpp_shift_add<0x114, 0xF>(v);   // row_shr:4
-  v = dpp_shift_add<0x118, 0xF>(v);   // row_shr:8
-  return dpp_shift_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-}
-
-// Commit of a chunk for bf16 inputs with per-key-channel decay: the decayed
-// operands of the chunk's products, formed once per workgroup.  Thread (row pair
-// p, column block cb) holds K, Q and g of rows t = 2p, t + 1, columns j0 = 8cb
-// .. +7; the within-chunk cumulative log decay gam is a scan over the 32 lanes
-// of the row pairs and gam_L its total.  Written as hi / lo bf16:
-//   Kd[t][j]  = K[t][j] rk[t] e^{gam[t][j]}            (Y = Kd S0^T)
-//   Qd[t][j]  = Q[t][j] rq[t] e^{gam[t][j]}            (Z = Qd S0^T)
-//   Ku^T[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam[t][j]}  (the update K^T W)
-// and eL[j] = e^{gam_L[j]}, the state's column decay.
-__device__ __forceinline__ void stage_commit_pcb(const Stage<false, true>& sg, uint16_t* sKh, uint16_t* sKl,
-                                                 uint16_t* sQh, uint16_t* sQl, uint16_t* sKth, uint16_t* sKtl,
-                                                 int pitch, int tpitch, float* sV, int vpitch, float* eL,
-                                                 float* s_vec) {
-  const int tid = threadIdx.x;
-  const int t = 2 * (tid % (kC / 2)), j0 = 8 * (tid / (kC / 2));
-  float g0[8], g1[8], gam0[8], gam1[8], gl[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    g0[c] = sg.g4[c / 4][c % 4];
-    g1[c] = sg.g4[2 + c / 4][c % 4];
-  }
-  const int lane = tid % kWave;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const float incl = scan32(g0[c] + g1[c]);
-    gam0[c] = incl - g1[c];
-    gam1[c] = incl;
-    const float tot31 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 31));
-    const float tot63 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, incl), 63));
-    gl[c] = lane < 32 ? tot31 : tot63;
-  }
-  auto bf = [](uint32_t w, int hi) { return __uint_as_float(hi ? (w & 0xffff0000u) : (w << 16)); };
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const float* gam = r ? gam1 : gam0;
-    const float rk = sg.rkq[r], rq = sg.rkq[2 + r];
-    uint32_t kh[4], kl[4], qh[4], ql[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const float e0 = __expf(gam[2 * w]), e1 = __expf(gam[2 * w + 1]);
-      split2(bf(sg.k[r][w], 0) * rk * e0, bf(sg.k[r][w], 1) * rk * e1, kh[w], kl[w]);
-      split2(bf(sg.q[r][w], 0) * rq * e0, bf(sg.q[r][w], 1) * rq * e1, qh[w], ql[w]);
-    }
-    const int off = (t + r) * pitch + j0;
-    *reinterpret_cast<u32x4_t*>(sKh + off) = u32x4_t{kh[0], kh[1], kh[2], kh[3]};
-    *reinterpret_cast<u32x4_t*>(sKl + off) = u32x4_t{kl[0], kl[1], kl[2], kl[3]};
-    *reinterpret_cast<u32x4_t*>(sQh + off) = u32x4_t{qh[0], qh[1], qh[2], qh[3]};
-    *reinterpret_cast<u32x4_t*>(sQl + off) = u32x4_t{ql[0], ql[1], ql[2], ql[3]};
-  }
-  // the update's operand, transposed: column j of rows t, t+1 as one 4-byte pair
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    uint32_t hp, lp;
-    split2(bf(sg.k[0][c / 2], c & 1) * sg.rkq[0] * __expf(gl[c] - gam0[c]),
-           bf(sg.k[1][c / 2], c & 1) * sg.rkq[1] * __expf(gl[c] - gam1[c]), hp, lp);
-    *reinterpret_cast<uint32_t*>(sKth + (j0 + c) * tpitch + t) = hp;
-    *reinterpret_cast<uint32_t*>(sKtl + (j0 + c) * tpitch + t) = lp;
-  }
-  if (t == 0) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) eL[j0 + c] = __expf(gl[c]);
-  }
-  if (tid < kC * 4) {
-    const int tv = tid / 4, i0 = 8 * (tid % 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sV[tv * vpitch + i0 + 2 * e] = __uint_as_float(sg.v[e] << 16);
-      sV[tv * vpitch + i0 + 2 * e + 1] = __uint_as_float(sg.v[e] & 0xffff0000u);
-    }
-  }
-  if (tid < 2 * kC) s_vec[tid] = sg.vec;
-}
-
 template <bool F32, bool kPC, typename Tin, typename To>
 __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const Tin* __restrict__ q, const Tin* __restrict__ k, int64_t qk_stride,
@@ -1245,12 +1179,10 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   using O = Ops<F32>;
   using E = typename O::E;
   using F = typename O::F;
-  // bf16 with per-key-channel decay: the decayed operands are formed once per
-  // chunk at commit and held as hi / lo (see stage_commit_pcb); a pad of 8
-  // (rows 272 / 144 bytes apart, conflict-free for the 16-byte row reads) keeps
-  // the LDS within 160 KB
-  constexpr bool kPCB = kPC && !F32;
-  constexpr int kPad = kPCB ? 8 : O::kPadK;
+  // bf16 inputs (scalar or per-key-channel decay) take the register-resident
+  // spines; this one serves the fp32 path
+  static_assert(F32 || !kPC, "bf16 per-key-channel decay runs on the register-resident spine");
+  constexpr int kPad = O::kPadK;
   constexpr int kPitch = kD + kPad;              // K, Q and state rows
   constexpr int kTP = kC + kPad;                 // transposed [i][t] tiles
   constexpr int kVP = kTile + 1;                 // fp32 V tile pitch
@@ -1258,8 +1190,6 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sK[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sQ[kC * kPitch];
   __shared__ __attribute__((aligned(16))) E sKt[F32 ? 1 : kD * kTP];
-  __shared__ __attribute__((aligned(16))) E sKl[kPCB ? kC * kPitch : 1], sQl[kPCB ? kC * kPitch : 1];
-  __shared__ __attribute__((aligned(16))) E sKtl[kPCB ? kD * kTP : 1];
   // The fp32 state tile lives in the waves' MFMA accumulators across chunks;
   // LDS holds it as the B operand of product 1, split into bf16 hi / lo
   // (fp32 on the fp32 path), row-major [i][j].
@@ -1268,7 +1198,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
   __shared__ __attribute__((aligned(16))) E sRh[kTile * kTP], sRl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sNh[kTile * kTP], sNl[F32 ? 1 : kTile * kTP];
   __shared__ __attribute__((aligned(16))) E sWh[kTile * kTP], sWl[F32 ? 1 : kTile * kTP];
-  __shared__ __attribute__((aligned(16))) float sGam[kPCB ? kD : (kPC ? kC * kGP : 1)];   // kPCB: e^{gam_L}
+  __shared__ __attribute__((aligned(16))) float sGam[kPC ? kC * kGP : 1];
   // fp32 per-key-channel path: (gam_L, p_c) per channel, p_c the prefix / suffix
   // switch row (sGam holds gam_t for rows t < p_c, gam_L - gam_t from p_c on)
   __shared__ float2 sGLP[kPC && F32 ? kD : 1];
@@ -1383,10 +1313,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     const int L = min(kC, seq_end - t0);
     const bool more = t0 + kC < seq_end;
     __syncthreads();   // the previous chunk is done with every LDS tile
-    if constexpr (kPCB)
-      stage_commit_pcb(stage, sK, sKl, sQ, sQl, sKt, sKtl, kPitch, kTP, sV, kVP, sGam, s_vec);
-    else
-      stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec, sGLP);
+    stage_commit<F32, kPC>(stage, sK, sKt, sQ, kPitch, kTP, sV, kVP, sGam, kGP, s_vec, sGLP);
     if (more) issue(std::integral_constant<int, 3>{}, t0 + kC, c + 1);   // K, Q, V, vectors
     __syncthreads();
 
@@ -1398,10 +1325,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
       const F bh = frag<F32>(sSh, kPitch, 16 * hf, ks);
       F bl{};
       if constexpr (!F32) bl = frag<F32>(sSl, kPitch, 16 * hf, ks);
-      if constexpr (kPCB) {
-        accY = mma3<F32>(frag<F32>(sK, kPitch, 16 * mt, ks), frag<F32>(sKl, kPitch, 16 * mt, ks), bh, bl, accY);
-        accZ = mma3<F32>(frag<F32>(sQ, kPitch, 16 * mt, ks), frag<F32>(sQl, kPitch, 16 * mt, ks), bh, bl, accZ);
-      } else if constexpr (kPC) {
+      if constexpr (kPC) {
         // fp32: A = K rk e^{gam_t}, Q rq e^{gam_t}, gam_t recovered from the split store
         const int r = 16 * mt + (lane & 15), c0 = ks + (lane >> 4);
         const float gv = sGam[r * kGP + c0];
@@ -1490,12 +1414,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
     // (per-key-channel decay: column j decays by e^{gam_L[j]} and the key rows
     //  enter as khat_t e^{gam_L - gam_t})
     {
-      if constexpr (kPCB) {
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sacc[q2][e] *= sGam[16 * (nj0 + q2) + 4 * (lane >> 4) + e];
-      } else if constexpr (kPC) {
+      if constexpr (kPC) {
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
@@ -1515,10 +1434,7 @@ __global__ __launch_bounds__(kSpineThreads) void chunk_spine_kernel(
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
           const int j = 16 * (nj0 + q2) + (lane & 15);
-          if constexpr (kPCB) {
-            sacc[q2] = mma3<F32>(frag<F32>(sKt, kTP, 16 * (nj0 + q2), ks), frag<F32>(sKtl, kTP, 16 * (nj0 + q2), ks),
-                                 bh, bl, sacc[q2]);
-          } else if constexpr (kPC) {
+          if constexpr (kPC) {
             // A[j][t] = K[t][j] rk[t] e^{gam_L[j] - gam_t[j]}, t = ks + l/16 (fp32: the
             // suffix gam_L - gam_t from the split store)
             static_assert(F32, "the bf16 per-channel update reads the committed K^T operand");
@@ -1626,15 +1542,19 @@ __device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t vo
 }
 
 // Workgroup shape of the register-resident spines: kThreadsT threads sharing
-// one chunk's inputs for kRowsT value rows of one head.
-template <int kThreadsT, int kRowsT>
+// one chunk's inputs for kRowsT value rows of one head; kPCT: per-key-channel
+// decay, whose state update multiplies a third row tile (Kb) instead of khat.
+template <int kThreadsT, int kRowsT, bool kPCT = false>
 struct SpineCfg {
   static constexpr int kThreadsW = kThreadsT;
   static constexpr int kRows = kRowsT;                    // value rows per workgroup
   static constexpr int kVP = kRows + 8;                   // V row pitch (bf16)
-  // one LDS slot (bytes): khat | qtil | V (fp16, fp16, bf16) | Tt, Pt fragments | chunk vectors
+  static constexpr int kTiles = kPCT ? 3 : 2;             // fp16 row tiles of 64 x 128
+  // one LDS slot (bytes): khat | qtil [| Kb] | V (fp16 tiles, bf16 V) | Tt, Pt fragments | chunk vectors
+  // (per-key-channel decay: Kt | Qt | Kb)
   static constexpr int kOffQ = kC * kWP * 2;
-  static constexpr int kOffV = 2 * kOffQ;
+  static constexpr int kOffKb = 2 * kOffQ;
+  static constexpr int kOffV = kTiles * kOffQ;
   static constexpr int kOffTri = kOffV + kC * kVP * 2;
   static constexpr int kTriFrags = 2 * kNF;               // (Tt, Pt) x 6 fp16 fragments, 1 KB each
   static constexpr int kOffVec = kOffTri + kTriFrags * (int)kHFrag;
@@ -1643,7 +1563,7 @@ struct SpineCfg {
   static constexpr int kPiecesV = kC * kRows / 8 / kThreadsW;  // ... of V
   // ... of the fragments: the last round may cover only some of the waves
   static constexpr int kPiecesTri = (kTriFrags * kWave + kThreadsW - 1) / kThreadsW;
-  static constexpr int kLoads = 2 * kPiecesKQ + kPiecesV + kPiecesTri + 1;   // + the vectors
+  static constexpr int kLoads = kTiles * kPiecesKQ + kPiecesV + kPiecesTri + 1;   // + the vectors
   static_assert(kPiecesKQ * kThreadsW == kC * kD / 8 && kPiecesV * kThreadsW == kC * kRows / 8 &&
                 kThreadsW % kWave == 0, "pieces must divide evenly over the threads");
 };
@@ -1656,9 +1576,10 @@ struct SpineCfg {
 // the sequence has an empty range (no access at all).
 template <typename Cf>
 struct ChunkStage {
-  u32x4_t k[Cf::kPiecesKQ], q[Cf::kPiecesKQ], v[Cf::kPiecesV], tri[Cf::kPiecesTri], vec;
-  struct Rsrc { __amdgpu_buffer_rsrc_t k, q, v, r; };
-  const uint16_t *kp, *qp, *vp;      // key head / value head / value row base of row 0
+  static constexpr int kKQ = Cf::kPiecesKQ, kT3 = Cf::kTiles * kKQ;   // pieces of the row tiles
+  u32x4_t k[kKQ], q[kKQ], kb[Cf::kTiles == 3 ? kKQ : 1], v[Cf::kPiecesV], tri[Cf::kPiecesTri], vec;
+  struct Rsrc { __amdgpu_buffer_rsrc_t k, q, kb, v, r; };
+  const uint16_t *kp, *qp, *kbp, *vp;   // row tiles' head / value head / value row base of row 0
   int64_t qk_stride, v_stride;
   const uint8_t* rec0;               // the sequence's first record of this value head
   size_t rec_step;                   // bytes between the records of consecutive chunks
@@ -1678,23 +1599,27 @@ struct ChunkStage {
     Rsrc r;
     r.k = make_rsrc(kp + (int64_t)t0 * qk_stride, L * qk_row);
     r.q = make_rsrc(qp + (int64_t)t0 * qk_stride, L * qk_row);
+    r.kb = make_rsrc(kbp + (int64_t)t0 * qk_stride, L * qk_row);
     r.v = make_rsrc(vp + (int64_t)t0 * v_stride, L * v_row);
     r.r = make_rsrc(rec0 + (in ? cl : 0) * rec_step, in ? (uint32_t)kHRecBytes : 0u);
     return r;
   }
   __device__ void load(const Rsrc& r, int i) {   // i < kLoads, a compile-time constant after unrolling
     constexpr int kT = Cf::kThreadsW;
-    if (i < Cf::kPiecesKQ) {
+    if (i < kKQ) {
       k[i] = buf_load16(r.k, off_kq + (uint32_t)i * (kT / 16) * qk_row, 0);
-    } else if (i < 2 * Cf::kPiecesKQ) {
-      const int j = i - Cf::kPiecesKQ;
+    } else if (i < 2 * kKQ) {
+      const int j = i - kKQ;
       q[j] = buf_load16(r.q, off_kq + (uint32_t)j * (kT / 16) * qk_row, 0);
-    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
-      const int j = i - 2 * Cf::kPiecesKQ;
+    } else if (i < kT3) {
+      const int j = i - 2 * kKQ;
+      kb[j] = buf_load16(r.kb, off_kq + (uint32_t)j * (kT / 16) * qk_row, 0);
+    } else if (i < kT3 + Cf::kPiecesV) {
+      const int j = i - kT3;
       v[j] = buf_load16(r.v, off_v + (uint32_t)j * (kT / (Cf::kRows / 8)) * v_row, 0);
     } else if (i < Cf::kLoads - 1) {
       // the record's twelve fragments are the slot's, in the same order
-      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      const int j = i - kT3 - Cf::kPiecesV;
       const int p = tid + j * kT;
       if (p < Cf::kTriFrags * kWave) tri[j] = buf_load16(r.r, 16 * (uint32_t)p, 0);   // uniform per wave
     } else {
@@ -1712,20 +1637,20 @@ struct ChunkStage {
 
   __device__ void commit(uint8_t* base, int i) const {
     constexpr int kT = Cf::kThreadsW;
-    if (i < 2 * Cf::kPiecesKQ) {
-      const int j = i % Cf::kPiecesKQ;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(base + (i < Cf::kPiecesKQ ? 0 : Cf::kOffQ));
-      const u32x4_t& val = i < Cf::kPiecesKQ ? k[j] : q[j];
+    if (i < kT3) {
+      const int tile = i / kKQ, j = i % kKQ;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(base + tile * Cf::kOffQ);
+      const u32x4_t& val = tile == 0 ? k[j] : tile == 1 ? q[j] : kb[Cf::kTiles == 3 ? j : 0];
       const int p = tid + j * kT, r = p >> 4, c8 = 8 * (p & 15);
       // logical columns c8 .. c8+3 and c8+4 .. c8+7 land as two 8-byte runs
       *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8)) = make_uint2(val[0], val[1]);
       *reinterpret_cast<uint2*>(dst + r * kWP + wave_col(c8 + 4)) = make_uint2(val[2], val[3]);
-    } else if (i < 2 * Cf::kPiecesKQ + Cf::kPiecesV) {
-      const int j = i - 2 * Cf::kPiecesKQ;
+    } else if (i < kT3 + Cf::kPiecesV) {
+      const int j = i - kT3;
       const int p = tid + j * kT, r = p / (Cf::kRows / 8), c8 = 8 * (p % (Cf::kRows / 8));
       *reinterpret_cast<u32x4_t*>(base + Cf::kOffV + 2 * (r * Cf::kVP + c8)) = v[j];
     } else if (i < Cf::kLoads - 1) {
-      const int j = i - 2 * Cf::kPiecesKQ - Cf::kPiecesV;
+      const int j = i - kT3 - Cf::kPiecesV;
       const int p = tid + j * kT;
       if (p < Cf::kTriFrags * kWave) *reinterpret_cast<u32x4_t*>(base + Cf::kOffTri + 16 * p) = tri[j];
     } else {
@@ -1754,14 +1679,14 @@ struct FusedNorm {
   float eps;
 };
 
-template <int kNW, int kLoaders, typename To, bool kNorm = false>
+template <int kNW, int kLoaders, typename To, bool kNorm = false, bool kPC = false>
 __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, int64_t qk_stride,
-    const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ kb,
+    int64_t qk_stride, const uint16_t* __restrict__ v, int64_t v_stride, const float* __restrict__ init_state,
     const int32_t* __restrict__ cu, int n_seq, int hk, int hv, const uint8_t* __restrict__ ws,
     To* __restrict__ out, float* final_state, FusedNorm nrm) {
-  using Cf = SpineCfg<kNW * kWave, 16 * kNW>;
-  using StageCf = SpineCfg<(kLoaders > 0 ? kLoaders : kNW) * kWave, Cf::kRows>;   // same LDS layout
+  using Cf = SpineCfg<kNW * kWave, 16 * kNW, kPC>;
+  using StageCf = SpineCfg<(kLoaders > 0 ? kLoaders : kNW) * kWave, Cf::kRows, kPC>;   // same LDS layout
   static_assert(!kNorm || kNW * 16 == kD, "the fused norm needs a whole value head per workgroup");
   constexpr int kKS = 4;                          // 32-key steps of a wave's state
   constexpr int kJT = 8;                          // 16-key tiles of a wave's state
@@ -1795,8 +1720,11 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 
   const bool loader = kLoaders > 0 && wave >= kNW;
   ChunkStage<StageCf> stage;
-  stage.kp = k + kh * kD;
-  stage.qp = q + kh * kD;
+  // scalar decay: khat, qtil of the key head; per-key-channel decay: Kt, Qt, Kb of the value head
+  const int rh = kPC ? h : kh;
+  stage.kp = k + rh * kD;
+  stage.qp = q + rh * kD;
+  stage.kbp = kb + rh * kD;
   stage.vp = v + h * kD + i0;
   stage.qk_stride = qk_stride;
   stage.v_stride = v_stride;
@@ -1862,6 +1790,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     const uint8_t* base = s_in[slot];
     const uint16_t* sk = reinterpret_cast<const uint16_t*>(base);
     const uint16_t* sq = reinterpret_cast<const uint16_t*>(base + Cf::kOffQ);
+    // the state update's row tile: khat itself, or Kb with per-key-channel decay
+    const uint16_t* skb = reinterpret_cast<const uint16_t*>(base + (kPC ? Cf::kOffKb : 0));
     const uint16_t* sv = reinterpret_cast<const uint16_t*>(base + Cf::kOffV);
     const uint8_t* tri = base + Cf::kOffTri;
     const float* vec = reinterpret_cast<const float*>(base + Cf::kOffVec);
@@ -1881,7 +1811,8 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       vv[mt] = lds_read_tr4(sv + (16 * mt + 4 * g + (m >> 2)) * Cf::kVP + iw + 4 * (m & 3));
-      va[mt] = *reinterpret_cast<const f32x4_t*>(vec + 16 * mt + 4 * g);
+      // per-key-channel decay: the decay is in Kt, Qt and Kb, a = b = c = 1
+      va[mt] = kPC ? f32x4_t{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4_t*>(vec + 16 * mt + 4 * g);
     }
 
     // state as B operands (and, for Z^T = S Q^T, as A operands): k step ks = key tiles 2ks, 2ks+1
@@ -1946,7 +1877,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     auto read_kt = [&](int k0, f16x8_t* dst) {
 #pragma unroll
       for (int jt = 0; jt < kJT; ++jt)
-        dst[jt] = __builtin_bit_cast(f16x8_t, lds_read_tr8(sk + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP));
+        dst[jt] = __builtin_bit_cast(f16x8_t, lds_read_tr8(skb + (k0 + 4 * g + (m >> 2)) * kWP + wave_col(16 * jt + 4 * (m & 3)), 16 * kWP));
     };
 
     // ---- R = V - a Y (accumulator layout: rows 16 mt + 4 g + e, column iw + m) ----
@@ -1980,7 +1911,7 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       f32x4_t w[4];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4_t c = *reinterpret_cast<const f32x4_t*>(vec + 2 * kC + 16 * mt + 4 * g);
+        const f32x4_t c = kPC ? f32x4_t{1.f, 1.f, 1.f, 1.f} : *reinterpret_cast<const f32x4_t*>(vec + 2 * kC + 16 * mt + 4 * g);
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[mt][e] = c[e] * vn[mt][e];
       }
@@ -2022,8 +1953,15 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
 
-    // ---- S <- d S + U ----
-    {
+    // ---- S <- d S + U (per-key-channel decay: d per key, S^T's rows) ----
+    if constexpr (kPC) {
+#pragma unroll
+      for (int jt = 0; jt < kJT; ++jt) {
+        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(vec + 16 * jt + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sst[jt][e] = fmaf(d[e], sst[jt][e], u[jt][e]);
+      }
+    } else {
       const float d = vec[3 * kC];
 #pragma unroll
       for (int jt = 0; jt < kJT; ++jt)
@@ -2033,11 +1971,13 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 
     // ---- O^T = Z^T diag(b) + Vnew^T Pt^T on this wave's token tiles ----
     // (rows i, columns t: A = Vnew pairs, B = Pt fragments)
+    if constexpr (!kPC) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const float b = vec[kC + 16 * mt + m];
+      for (int mt = 0; mt < 4; ++mt) {
+        const float b = vec[kC + 16 * mt + m];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
+        for (int e = 0; e < 4; ++e) zt[mt][e] *= b;
+      }
     }
     {
 #pragma unroll
@@ -2105,7 +2045,10 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
 }
 
 int chunk_spine_kind(const Dims& d, bool in_bf16, int n) {
-  if (!in_bf16 || d.per_channel) return kSpineLds;
+  if (!in_bf16) return kSpineLds;
+  // per-key-channel decay stages three row tiles: only the 32-row shape's two
+  // slots of them fit LDS
+  if (d.per_channel) return kSpineRows;
   return n * d.hv >= kWaveSpineMinBlocks ? kSpineWave : kSpineRows;
 }
 
@@ -2115,11 +2058,14 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
                       const int32_t* cu_dev, int n, int t, int total_chunks, void* out,
                       float* final_state, void* ws, const FusedNorm& nrm, hipStream_t s) {
   uint8_t* w = static_cast<uint8_t*>(ws);
-  // register-resident spines: normalised fp16 rows written by the intra kernel
-  // (khat [T][Hk][dk], then qtil)
-  uint16_t* khat = F32 || kPC ? nullptr : reinterpret_cast<uint16_t*>(w + hat_offset(n, t, d.hv));
-  uint16_t* qhat = khat ? khat + (size_t)t * d.hk * kD : nullptr;
-  const int64_t hat_stride = (int64_t)d.hk * kD;
+  // register-resident spines: the fp16 row tiles the intra kernel writes after
+  // its records -- scalar decay: khat, qtil [T][Hk][dk] (khat also the state
+  // update's tile); per-key-channel decay: Kt, Qt, Kb [T][Hv][dk]
+  uint16_t* khat = F32 ? nullptr : reinterpret_cast<uint16_t*>(w + hat_offset(n, t, d.hv));
+  const int hat_heads = kPC ? d.hv : d.hk;
+  uint16_t* qhat = khat ? khat + (size_t)t * hat_heads * kD : nullptr;
+  uint16_t* kbar = khat ? (kPC ? qhat + (size_t)t * hat_heads * kD : khat) : nullptr;
+  const int64_t hat_stride = (int64_t)hat_heads * kD;
   // bf16 inputs with scalar decay run a register-resident spine: a whole
   // value head per workgroup (eight waves, two per SIMD, so one wave's VALU
   // work overlaps the other's MFMAs, and the gated norm can be fused) once
@@ -2138,7 +2084,7 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
     if constexpr (kPC)
       hipLaunchKernelGGL((chunk_intra_pc_kernel<F32, Tin>), dim3(total_chunks, d.hv), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt.g, gt.beta,
-                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w);
+                         cu_dev, n, d.hk, d.hv, d.l2norm, d.l2_eps, d.q_scale, w, khat);
     else   // bf16: records in the paired-tile k order of the register-resident spines
       hipLaunchKernelGGL((chunk_intra_kernel<F32, Tin, !F32>), dim3(total_chunks, d.hk), dim3(kThreads), 0, s,
                          static_cast<const Tin*>(q), static_cast<const Tin*>(k), qk_stride, gt,
@@ -2150,26 +2096,27 @@ hipError_t chunk_impl(const Dims& d, const void* q, const void* k, int64_t qk_st
   if (!F32 && spine == kSpineWave) {
     const int members = d.hv / d.hk;
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    if constexpr (std::is_same_v<To, _Float16>) return hipErrorInvalidValue;   // never asked for
+    // (per-key-channel decay and an fp16 output always take the 32-row shape)
+    if constexpr (kPC || std::is_same_v<To, _Float16>) return hipErrorInvalidValue;
     else if (nrm.z)
       hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To, true>), dim3(blocks), dim3(8 * kWave), 0, s,
-                         qhat, khat, hat_stride,
+                         qhat, khat, kbar, hat_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
     else
       hipLaunchKernelGGL((chunk_spine_wave_kernel<8, 0, To>), dim3(blocks), dim3(8 * kWave), 0, s,
-                         qhat, khat, hat_stride,
+                         qhat, khat, kbar, hat_stride,
                          static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                          static_cast<To*>(out), final_state, nrm);
   } else if (!F32 && spine == kSpineRows) {
     const int members = (d.hv / d.hk) * (kD / (16 * kRowsNW));
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
-    hipLaunchKernelGGL((chunk_spine_wave_kernel<kRowsNW, kRowsLoaders, To>), dim3(blocks),
+    hipLaunchKernelGGL((chunk_spine_wave_kernel<kRowsNW, kRowsLoaders, To, false, kPC>), dim3(blocks),
                        dim3((kRowsNW + kRowsLoaders) * kWave), 0, s,
-                       qhat, khat, hat_stride,
+                       qhat, khat, kbar, hat_stride,
                        static_cast<const uint16_t*>(v), v_stride, init_state, cu_dev, n, d.hk, d.hv, w,
                        static_cast<To*>(out), final_state, nrm);
-  } else if constexpr (F32 || kPC) {
+  } else if constexpr (F32) {
     const int members = (d.hv / d.hk) * (kD / kTile);
     const int blocks = (groups + kXcds - 1) / kXcds * kXcds * members;
     hipLaunchKernelGGL((chunk_spine_kernel<F32, kPC, Tin, To>), dim3(blocks), dim3(kSpineThreads), 0, s,
@@ -2186,10 +2133,8 @@ hipError_t chunk_dispatch(const Dims& d, bool in_bf16, bool out_bf16, bool out_f
                           const float* init_state, const int32_t* cu_dev, int n, int t,
                           int total, void* out, float* final_state, void* ws, const FusedNorm& nrm,
                           hipStream_t s) {
-  if constexpr (!kPC) {
-    if (in_bf16 && out_f16)
-      return chunk_impl<false, kPC, uint16_t, _Float16>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
-  }
+  if (in_bf16 && out_f16)
+    return chunk_impl<false, kPC, uint16_t, _Float16>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
   if (in_bf16)
     return out_bf16 ? chunk_impl<false, kPC, uint16_t, uint16_t>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s)
                     : chunk_impl<false, kPC, uint16_t, float>(d, q, k, qk_stride, v, v_stride, gt, init_state, cu_dev, n, t, total, out, final_state, ws, nrm, s);
@@ -2212,7 +2157,8 @@ size_t chunk_workspace_bytes(const Dims& d, int n, int t) {
   // the larger of the two layouts: hi/lo or fp32 records (fp32 inputs, per-key-channel
   // decay), or fp16 records and the normalised rows (the register-resident spines)
   const size_t split = records_offset(n) + max_chunks * d.hv * kRecBytes;
-  const size_t half = hat_offset(n, t, d.hv) + 2 * (size_t)t * d.hk * kD * sizeof(uint16_t);
+  const size_t half = hat_offset(n, t, d.hv) +
+                      (d.per_channel ? 3 * (size_t)d.hv : 2 * (size_t)d.hk) * t * kD * sizeof(uint16_t);
   return std::max(split, half);
 }
 
