@@ -1763,9 +1763,15 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
   };
   if constexpr (kNorm) load_z(0, zr);
 
+  // Per-key-channel decay: the loader waves hold the chunk after next in
+  // registers (its row tiles are the value head's own, read from HBM, not
+  // shared through L2 by a key head's value heads, so their latency shows;
+  // with scalar decay the deeper prefetch measured no gain)
+  constexpr bool kAhead2 = kPC && kLoaders > 0;
   if (n_chunks > 0 && (kLoaders == 0 || loader)) {
     stage.load_all(stage.rsrc(0));
     stage.commit_all(s_in[0]);
+    if constexpr (kAhead2) stage.load_all(stage.rsrc(1));
   }
   // Let every load issued so far land here, once: otherwise the compiler's
   // wait for the initial state (first used at the top of the chunk loop) is
@@ -1780,8 +1786,13 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     if (loader) {
       // stage chunk cl+1 into the other slot (free since the last barrier),
       // meeting the compute waves at each of their barriers
-      stage.load_all(stage.rsrc(cl + 1));
-      stage.commit_all(s_in[slot ^ 1]);
+      if constexpr (kAhead2) {
+        stage.commit_all(s_in[slot ^ 1]);   // loaded during chunk cl-1
+        stage.load_all(stage.rsrc(cl + 2));
+      } else {
+        stage.load_all(stage.rsrc(cl + 1));
+        stage.commit_all(s_in[slot ^ 1]);
+      }
       __syncthreads();
       continue;
     }

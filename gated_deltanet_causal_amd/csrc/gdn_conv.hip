@@ -7,8 +7,10 @@
 // conv slice (a step equals the full width-4 causal conv).  Tap w[c][3] meets
 // the current token; carried state rows are oldest first.
 //
-// Memory: each thread owns 8 adjacent channels (one 16-byte bf16 vector) and a
-// tile of 16 tokens.  Inside a sequence it loads the tile's 16 rows and the 3
+// Memory: each thread owns 4 adjacent channels (8 bytes of bf16, 16 of fp32)
+// and a tile of 16 tokens (with 8 channels the 19 rows held 136 VGPRs and
+// three waves per SIMD, and a 4096-token prefill's 1,280 workgroups ran in
+// 1.7 rounds; with 4, twice the workgroups at higher occupancy: -3.5 us).  Inside a sequence it loads the tile's 16 rows and the 3
 // before it at once and then computes, so x is read about once (19 rows per 16
 // tokens, the extra 3 mostly from L2) and y written once (HBM-bound: 2 + 2 bytes
 // per element in bf16).  Tiles that meet a sequence start walk token by token,
@@ -20,40 +22,33 @@ namespace gdn {
 namespace {
 
 constexpr int kConvTile = 16;     // tokens per thread
-constexpr int kConvVec = 8;       // channels per thread
+constexpr int kConvVec = 4;       // channels per thread
 constexpr int kConvThreads = 256;
 
 template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[kConvVec]) {
+__device__ __forceinline__ void load4(const T* p, float (&v)[kConvVec]) {
   if constexpr (sizeof(T) == 2) {
-    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(u[i] << 16);
-      v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
-    }
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16);
+    v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16);
+    v[3] = __uint_as_float(u.y & 0xffff0000u);
   } else {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
-    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[4 + i] = b[i]; }
+    for (int i = 0; i < 4; ++i) v[i] = a[i];
   }
 }
 
 template <typename T>
-__device__ __forceinline__ void store8(T* p, const float (&v)[kConvVec]) {
+__device__ __forceinline__ void store4(T* p, const float (&v)[kConvVec]) {
   if constexpr (sizeof(T) == 2) {
-    u32x4_t u;   // pairs through one conversion each (round to nearest even)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      u[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2 * i], v[2 * i + 1]}, bf16x2_t));
-    *reinterpret_cast<u32x4_t*>(p) = u;
+    uint2 u;   // pairs through one conversion each (round to nearest even)
+    u.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[0], v[1]}, bf16x2_t));
+    u.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{v[2], v[3]}, bf16x2_t));
+    *reinterpret_cast<uint2*>(p) = u;
   } else {
-    f32x4_t a, b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[4 + i]; }
-    *reinterpret_cast<f32x4_t*>(p) = a;
-    *reinterpret_cast<f32x4_t*>(p + 4) = b;
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{v[0], v[1], v[2], v[3]};
   }
 }
 
@@ -101,7 +96,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_prefill_kernel(
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
       const int pos = min(t_begin - 3 + i, t_end - 1);   // rows past the tile end are never used
-      load8(x + (int64_t)pos * x_stride + c0, rows[i]);
+      load4(x + (int64_t)pos * x_stride + c0, rows[i]);
     }
 #pragma unroll
     for (int i = 0; i < kConvTile; ++i) {
@@ -115,7 +110,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_prefill_kernel(
           acc = fmaf(wt[3][e], rows[i + 3][e], acc);
           out[e] = conv_activation(acc, act);
         }
-        store8(y + (int64_t)(t_begin + i) * y_stride + c0, out);
+        store4(y + (int64_t)(t_begin + i) * y_stride + c0, out);
       }
     }
     return;
@@ -128,9 +123,9 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_prefill_kernel(
     for (int j = 0; j < 3; ++j) {
       const int pos = t - 3 + j;
       if (pos >= seq_start) {
-        load8(x + (int64_t)pos * x_stride + c0, hist[j]);
+        load4(x + (int64_t)pos * x_stride + c0, hist[j]);
       } else if (cs_in) {
-        load8(cs_in + ((int64_t)n * 3 + (3 + pos - seq_start)) * cc + c0, hist[j]);
+        load4(cs_in + ((int64_t)n * 3 + (3 + pos - seq_start)) * cc + c0, hist[j]);
       } else {
 #pragma unroll
         for (int e = 0; e < kConvVec; ++e) hist[j][e] = 0.0f;
@@ -146,7 +141,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_prefill_kernel(
       fill_history(t);
     }
     float cur[kConvVec], out[kConvVec];
-    load8(x + (int64_t)t * x_stride + c0, cur);
+    load4(x + (int64_t)t * x_stride + c0, cur);
 #pragma unroll
     for (int e = 0; e < kConvVec; ++e) {
       float acc = wt[0][e] * hist[0][e];
@@ -158,7 +153,7 @@ __global__ __launch_bounds__(kConvThreads) void conv1d_prefill_kernel(
       hist[1][e] = hist[2][e];
       hist[2][e] = cur[e];
     }
-    store8(y + (int64_t)t * y_stride + c0, out);
+    store4(y + (int64_t)t * y_stride + c0, out);
   }
 }
 

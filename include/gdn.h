@@ -233,9 +233,12 @@ gdn_status_t gdn_prefill_workspace_size(const gdn_config_t* cfg, gdn_dtype_t dty
  * Consumer section: conv, then the chunked delta rule, then the gated norm):
  * gdn_conv1d_prefill over x, q | k | v taken from the conv output rows,
  * gdn_chunk_prefill, and gdn_gated_rmsnorm of its output, with the same
- * arithmetic as those calls made in that order (the pre-norm output is kept
- * in fp32).  Where the geometry allows, the chunk kernels apply the gated norm
- * to each chunk's output themselves and the pre-norm output is never stored.
+ * arithmetic as those calls made in that order.  Where a workgroup of the
+ * chunk kernels holds a whole value head (many sequences), they apply the
+ * gated norm to each chunk's output themselves and the pre-norm output is
+ * never stored; otherwise it goes through the workspace, as fp16 for bf16
+ * inputs (whose chunk products already round their operands to fp16) and
+ * fp32 for fp32 inputs.
  *   dtype            dtype of x, the conv states and z
  *   out_dtype        dtype of out
  *   x                [T][Cc] raw projected rows, row stride x_stride (>= Cc,
