@@ -223,58 +223,6 @@ __global__ __launch_bounds__(kThreads) void chunk_plan_kernel(const int32_t* __r
   }
 }
 
-// Load a 64 x 128 tile of raw key or query rows (zero rows past L) into LDS.
-template <bool F32, typename Tin>
-__device__ __forceinline__ void load_rows(typename Ops<F32>::E* dst, int pitch, const Tin* src,
-                                          int64_t stride, int L) {
-  // each thread moves 16-byte pieces: 8 bf16 (bf16 input) or 4 fp32 (fp32 input)
-  constexpr int kPer = 16 / sizeof(Tin);
-  constexpr int kPieces = kC * kD / kPer;
-  for (int p = threadIdx.x; p < kPieces; p += kThreads) {
-    const int r = p / (kD / kPer);
-    const int c = (p % (kD / kPer)) * kPer;
-    typename Ops<F32>::E* d = dst + r * pitch + c;
-    if constexpr (F32) {
-      f32x4_t v = {0.f, 0.f, 0.f, 0.f};
-      if (r < L) v = *reinterpret_cast<const f32x4_t*>(src + r * stride + c);
-      *reinterpret_cast<f32x4_t*>(d) = v;
-    } else {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (r < L) v = *reinterpret_cast<const u32x4_t*>(src + r * stride + c);
-      *reinterpret_cast<u32x4_t*>(d) = v;
-    }
-  }
-}
-
-
-// 64 x 32 value tile (rows past L zero) as fp32 into LDS, 16-byte loads.
-template <typename Tin>
-__device__ __forceinline__ void load_values(float* sV, int pitch, const Tin* src, int64_t stride, int L) {
-  constexpr int kPer = 16 / sizeof(Tin);
-  for (int p = threadIdx.x; p < kC * (kTile / kPer); p += kThreads) {
-    const int t = p / (kTile / kPer);
-    const int i = (p % (kTile / kPer)) * kPer;
-    float vals[kPer];
-    if constexpr (sizeof(Tin) == 2) {
-      u32x4_t u = {0u, 0u, 0u, 0u};
-      if (t < L) u = *reinterpret_cast<const u32x4_t*>(src + (int64_t)t * stride + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vals[2 * e] = __uint_as_float(u[e] << 16);
-        vals[2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
-      }
-    } else {
-      f32x4_t u = {0.f, 0.f, 0.f, 0.f};
-      if (t < L) u = *reinterpret_cast<const f32x4_t*>(src + (int64_t)t * stride + i);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) vals[e] = u[e];
-    }
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) sV[t * pitch + i + e] = vals[e];
-  }
-}
-
-
 // 16x16x16 fp32 product on fp32 MFMA: acc += X Y with X, Y in LDS (pitches px, py).
 __device__ __forceinline__ f32x4_t mm16_f32(const float* X, int px, const float* Y, int py, f32x4_t acc) {
   const int l = threadIdx.x % kWave;
@@ -544,20 +492,51 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   const int t0 = cu[n] + (c - plan_first(first, n_seq, n)) * kC;
   const int L = min(kC, cu[n + 1] - t0);
 
-  load_rows<F32>(sK, kPitch, k + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-  load_rows<F32>(sQ, kPitch, q + (int64_t)t0 * qk_stride + kh * kD, qk_stride, L);
-  for (int p = tid; p < kC * kD / 4; p += kThreads) {
-    const int r = p / (kD / 4), c4 = 4 * (p % (kD / 4));
-    f32x4_t gv = {0.f, 0.f, 0.f, 0.f};
-    if (r < L) gv = *reinterpret_cast<const f32x4_t*>(g + ((int64_t)(t0 + r) * hv + h) * kD + c4);
-    if constexpr (F32) {
+  // K, Q and g rows: every load issued before the first LDS store (a load, wait,
+  // store loop puts one memory round trip per piece on the workgroup's path);
+  // rows past L are read at row L - 1 and stored as zero
+  {
+    constexpr int kPer = 16 / sizeof(Tin);
+    constexpr int kIt = kC * kD / kPer / kThreads;
+    constexpr int kItG = kC * kD / 4 / kThreads;
+    u32x4_t rk_[kIt], rq_[kIt];
+    f32x4_t rg_[kItG];
+    const Tin* kb = k + (int64_t)t0 * qk_stride + kh * kD;
+    const Tin* qb = q + (int64_t)t0 * qk_stride + kh * kD;
+    const float* gb = g + ((int64_t)t0 * hv + h) * kD;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sGam[r * kGP + c4 + e] = gv[e];
-    } else {
-      *reinterpret_cast<f32x4_t*>(sGam + r * kGP + c4) = gv;
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / kPer), c = (p % (kD / kPer)) * kPer;
+      const int rr = min(r, L - 1);
+      rk_[it] = *reinterpret_cast<const u32x4_t*>(kb + (int64_t)rr * qk_stride + c);
+      rq_[it] = *reinterpret_cast<const u32x4_t*>(qb + (int64_t)rr * qk_stride + c);
     }
+#pragma unroll
+    for (int it = 0; it < kItG; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / 4), c4 = 4 * (p % (kD / 4));
+      rg_[it] = *reinterpret_cast<const f32x4_t*>(gb + (int64_t)min(r, L - 1) * hv * kD + c4);
+    }
+    const float bv = tid < L ? beta[(int64_t)(t0 + tid) * hv + h] : 0.0f;
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / kPer), c = (p % (kD / kPer)) * kPer;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(sK + r * kPitch + c) = r < L ? rk_[it] : z;
+      *reinterpret_cast<u32x4_t*>(sQ + r * kPitch + c) = r < L ? rq_[it] : z;
+    }
+#pragma unroll
+    for (int it = 0; it < kItG; ++it) {
+      const int p = tid + it * kThreads, r = p / (kD / 4), c4 = 4 * (p % (kD / 4));
+      const f32x4_t gv = r < L ? rg_[it] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (F32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sGam[r * kGP + c4 + e] = gv[e];
+      } else {
+        *reinterpret_cast<f32x4_t*>(sGam + r * kGP + c4) = gv;
+      }
+    }
+    if (tid < kC) s_beta[tid] = bv;
   }
-  if (tid < kC) s_beta[tid] = tid < L ? beta[(int64_t)(t0 + tid) * hv + h] : 0.0f;
   __syncthreads();
 
   {  // row norms: 4 threads per row
