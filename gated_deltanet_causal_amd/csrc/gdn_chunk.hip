@@ -420,6 +420,30 @@ __device__ __forceinline__ void decayed_frag(const typename Ops<F32>::E* raw, in
   }
 }
 
+// The same operand for bf16 inputs as one fp16 fragment, for tiles whose
+// factors are all e^{<= 0} (|x| <= |raw| rs, inside fp16 range).
+__device__ __forceinline__ f16x8_t decayed_frag_h(const uint16_t* raw, int pitch, const float* gam, int gpitch,
+                                                 const float* ref, const float* rs, int row0, int k0, float sgn) {
+  const int l = threadIdx.x % kWave;
+  const int r = row0 + (l & 15);
+  const int c0 = k0 + 8 * (l >> 4);
+  const float s = rs[r];
+  const u32x4_t u = *reinterpret_cast<const u32x4_t*>(raw + r * pitch + c0);
+  const f32x4_t g0 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0);
+  const f32x4_t g1 = *reinterpret_cast<const f32x4_t*>(gam + r * gpitch + c0 + 4);
+  const f32x4_t f0 = *reinterpret_cast<const f32x4_t*>(ref + c0);
+  const f32x4_t f1 = *reinterpret_cast<const f32x4_t*>(ref + c0 + 4);
+  uint32_t hp[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float ga = e < 2 ? g0[2 * e] - f0[2 * e] : g1[2 * e - 4] - f1[2 * e - 4];
+    const float gb = e < 2 ? g0[2 * e + 1] - f0[2 * e + 1] : g1[2 * e - 3] - f1[2 * e - 3];
+    hp[e] = pack_f16x2(__uint_as_float(u[e] << 16) * s * __expf(sgn * ga),
+                       __uint_as_float(u[e] & 0xffff0000u) * s * __expf(sgn * gb));
+  }
+  return as_f16x8(u32x4_t{hp[0], hp[1], hp[2], hp[3]});
+}
+
 // product with both operands split: hi*hi + hi*lo + lo*hi (fp32: one exact product)
 template <bool F32>
 __device__ __forceinline__ f32x4_t mma3(typename Ops<F32>::F ah, typename Ops<F32>::F al,
@@ -631,17 +655,32 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
   }
   for (int ks = 0; ks < kD; ks += O::kKs) {
     F kah, kal, qah, qal;
-    if (wave > 0) {   // row side of the tiles left of the diagonal (reference 16 wave)
-      decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * wave, ks, 1.0f, kah, kal);
-      decayed_frag<F32, GT>(sQ, kPitch, sGam, kGP, ref_off, s_rq, 16 * wave, ks, 1.0f, qah, qal);
-    }
+    if constexpr (F32) {
+      if (wave > 0) {   // row side of the tiles left of the diagonal (reference 16 wave)
+        decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * wave, ks, 1.0f, kah, kal);
+        decayed_frag<F32, GT>(sQ, kPitch, sGam, kGP, ref_off, s_rq, 16 * wave, ks, 1.0f, qah, qal);
+      }
 #pragma unroll
-    for (int nt = 0; nt < 3; ++nt) {
-      if (nt < wave) {
-        F bh, bl;
-        decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * nt, ks, -1.0f, bh, bl);
-        accG[nt] = mma3<F32>(kah, kal, bh, bl, accG[nt]);
-        accH[nt] = mma3<F32>(qah, qal, bh, bl, accH[nt]);
+      for (int nt = 0; nt < 3; ++nt) {
+        if (nt < wave) {
+          F bh, bl;
+          decayed_frag<F32, GT>(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * nt, ks, -1.0f, bh, bl);
+          accG[nt] = mma3<F32>(kah, kal, bh, bl, accG[nt]);
+          accH[nt] = mma3<F32>(qah, qal, bh, bl, accH[nt]);
+        }
+      }
+    } else if (wave > 0) {
+      // bf16 inputs: the tiles left of the diagonal (every factor e^{<= 0}) on
+      // single fp16 operands, as the spine that consumes them rounds Tt and Pt
+      const f16x8_t ka = decayed_frag_h(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * wave, ks, 1.0f);
+      const f16x8_t qa = decayed_frag_h(sQ, kPitch, sGam, kGP, ref_off, s_rq, 16 * wave, ks, 1.0f);
+#pragma unroll
+      for (int nt = 0; nt < 3; ++nt) {
+        if (nt < wave) {
+          const f16x8_t kb = decayed_frag_h(sK, kPitch, sGam, kGP, ref_off, s_rk, 16 * nt, ks, -1.0f);
+          accG[nt] = mfma_f16(ka, kb, accG[nt]);
+          accH[nt] = mfma_f16(qa, kb, accH[nt]);
+        }
       }
     }
     if (dia_mfma) {   // the diagonal tile (reference 16 wave + 8)
