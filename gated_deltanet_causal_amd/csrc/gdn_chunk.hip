@@ -599,20 +599,24 @@ __global__ __launch_bounds__(kThreads) void chunk_intra_pc_kernel(
     // the chunk's end belong to the next sequence); gam_L = gam of row 63
     const int64_t plane = (int64_t)cu[n_seq] * hv * kD;   // [T][Hv][dk]
     if (tid < kD) s_dl[tid] = __expf(sGam[(kC - 1) * kGP + tid]);
-#pragma unroll 1
+#pragma unroll
     for (int p = tid; p < kC * kD / 8; p += kThreads) {
       const int r = p / (kD / 8), c8 = 8 * (p % (kD / 8));
       if (r >= L) continue;
       const u32x4_t ku = *reinterpret_cast<const u32x4_t*>(sK + r * kPitch + c8);
       const u32x4_t qu = *reinterpret_cast<const u32x4_t*>(sQ + r * kPitch + c8);
+      const f32x4_t ga = *reinterpret_cast<const f32x4_t*>(sGam + r * kGP + c8);
+      const f32x4_t gb = *reinterpret_cast<const f32x4_t*>(sGam + r * kGP + c8 + 4);
+      const f32x4_t la = *reinterpret_cast<const f32x4_t*>(sGam + (kC - 1) * kGP + c8);
+      const f32x4_t lb = *reinterpret_cast<const f32x4_t*>(sGam + (kC - 1) * kGP + c8 + 4);
       const float rk = s_rk[r], rq = s_rq[r];
       u32x4_t kt, qt, kb;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const int c0 = c8 + 2 * w;
-        const float g0 = sGam[r * kGP + c0], g1 = sGam[r * kGP + c0 + 1];
+        const float g0 = w < 2 ? ga[2 * w] : gb[2 * w - 4], g1 = w < 2 ? ga[2 * w + 1] : gb[2 * w - 3];
+        const float l0 = w < 2 ? la[2 * w] : lb[2 * w - 4], l1 = w < 2 ? la[2 * w + 1] : lb[2 * w - 3];
         const float e0 = __expf(g0), e1 = __expf(g1);
-        const float f0 = __expf(sGam[(kC - 1) * kGP + c0] - g0), f1 = __expf(sGam[(kC - 1) * kGP + c0 + 1] - g1);
+        const float f0 = __expf(l0 - g0), f1 = __expf(l1 - g1);
         const float k0 = __uint_as_float(ku[w] << 16) * rk, k1 = __uint_as_float(ku[w] & 0xffff0000u) * rk;
         const float q0 = __uint_as_float(qu[w] << 16) * rq, q1 = __uint_as_float(qu[w] & 0xffff0000u) * rq;
         kt[w] = pack_f16x2(k0 * e0, k1 * e1);
