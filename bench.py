@@ -26,7 +26,7 @@ at least 20 calls.  Every launch is a library call on torch's current stream
 (the stream the library enqueues on), timed with events on that stream: the
 mean from one event pair around all timed calls, median / p10 / p90 from a
 second pass with an event after each call.  The prefill-side workloads also
-report an ``mfma`` block (the method's algorithmic flops against the dense bf16
+report an ``mfma`` block (the method's algorithmic flops against the dense bf16 / fp16
 peak).  ``cpu_baseline`` runs the fp64 oracle (test infrastructure) over a
 bounded sample of the same workload, on every host core and on one thread.
 ``--calibration-copy`` only runs 256 MiB device copies (the known-size
@@ -119,9 +119,9 @@ def rotated(tensors, n_sets):
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 213.9e6 + 206.1e6          # both launches of a step
-PREFILL_S4096_TRAFFIC_BYTES = 454.8e6 + 328.6e6    # gdn_prefill, all its kernels
-VARLEN_TRAFFIC_BYTES = 3190.3e6 + 1838.8e6
-KDA_TRAFFIC_BYTES = 3019.9e6 + 683.7e6
+PREFILL_S4096_TRAFFIC_BYTES = 366.1e6 + 278.1e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 2855.3e6 + 1758.2e6
+KDA_TRAFFIC_BYTES = 2430.5e6 + 1287.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
@@ -143,12 +143,13 @@ RULE_FLOPS_PER_TOKEN_HEAD = (3 * CHUNK_C * (CHUNK_C - 1) * D + 2 * CHUNK_C * (CH
 PIPE_EXTRA_FLOPS_PER_TOKEN = 2 * 4 * CC + 2 * 2 * HK * D + 5 * HV * D
 PREFILL_FLOPS_PER_TOKEN = HV * RULE_FLOPS_PER_TOKEN_HEAD + PIPE_EXTRA_FLOPS_PER_TOKEN
 KDA_FLOPS_PER_TOKEN = KDA_H * RULE_FLOPS_PER_TOKEN_HEAD
-PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 and fp16 MFMA (the same rate)
 
 
 def mfma_block(flops, ms):
-    """Achieved matrix throughput from algorithmic flops (the chunk form's contractions are
-    issued on bf16 MFMA, fp32 operands as hi / lo pairs) against the dense bf16 peak."""
+    """Achieved matrix throughput from algorithmic flops (the spines' contractions are
+    issued on fp16 MFMA, the intra kernels' Gram products on bf16 MFMA) against the dense
+    bf16 / fp16 peak."""
     achieved = flops / (ms * 1e-3) / 1e12
     return {"achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
             "flops_per_call": flops}
@@ -501,7 +502,7 @@ def main():
         workloads["prefill_s4096_bf16"] = dict(
             metric="tokens/s", value=pre["tokens_per_s"], ms=pre["ms"], call="gdn_prefill",
             separate_calls=pre["separate_calls"], roofline=pre["roofline"], mfma=pre["mfma"],
-            roofline_ms=pre["roofline_ms"], dtype="bf16 storage; bf16 hi/lo-split MFMA, f32 accumulate",
+            roofline_ms=pre["roofline_ms"], dtype="bf16 storage; fp16-operand MFMA (bf16 in the intra Gram products), f32 accumulate and state",
             input_sets=3, **{k: pre[k] for k in ("median_ms", "p10_ms", "p90_ms", "timed_calls",
                                                   "serial_chunk_steps", "chunk_call_us_per_serial_step")})
         if cpu:
