@@ -1852,6 +1852,17 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     f16x8_t sb[kKS];
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) sb[ks] = f16_pair(sst[2 * ks], sst[2 * ks + 1]);
+    // Whole-head shape (no loader waves): the state's decay is applied here, off the
+    // chain's end, and the update U accumulates into the state tiles themselves
+    // (varlen one-call prefill 1.092 -> 1.082 ms; no gain with the 32-row shape)
+    constexpr bool kDecayFirst = kLoaders == 0 && !kPC;
+    if constexpr (kDecayFirst) {
+      const float d = vec[3 * kC];
+#pragma unroll
+      for (int jt = 0; jt < kJT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sst[jt][e] *= d;
+    }
 
     // ---- Y = khat S0^T (rows t, columns i) and Z^T = S0 qtil^T (rows i, columns t), over this wave's keys ----
     f32x4_t y[4], zt[4];
@@ -1967,11 +1978,12 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     };
 
     // ---- U = K^T W on this wave's key tiles (the state update without the decay) ----
-    f32x4_t u[kJT];
+    f32x4_t u_own[kDecayFirst ? 1 : kJT];
+    f32x4_t* u = kDecayFirst ? sst : u_own;
 #pragma unroll
     for (int jt = 0; jt < kJT; ++jt) {
       commit_group(jt);
-      u[jt] = mfma_f16(kt[jt], wb[0], zero4);
+      u[jt] = mfma_f16(kt[jt], wb[0], kDecayFirst ? u[jt] : zero4);
       if constexpr (kLoaders == 0) __builtin_amdgcn_sched_barrier(0);
     }
     read_kt(32, kt);   // the second k step reuses kt
@@ -1987,7 +1999,9 @@ __global__ __launch_bounds__((kNW + kLoaders) * kWave) void chunk_spine_wave_ker
     }
 
     // ---- S <- d S + U (per-key-channel decay: d per key, S^T's rows) ----
-    if constexpr (kPC) {
+    if constexpr (kDecayFirst) {
+      // done: S was decayed before the update accumulated into it
+    } else if constexpr (kPC) {
 #pragma unroll
       for (int jt = 0; jt < kJT; ++jt) {
         const f32x4_t d = *reinterpret_cast<const f32x4_t*>(vec + 16 * jt + 4 * g);
