@@ -138,7 +138,12 @@ gdn_status_t gdn_chunk_prefill_workspace_size(const gdn_config_t* cfg, int32_t N
  * computes, in exact arithmetic,
  *     S <- S * exp(g)           (per key channel: column j scaled by exp(g[j]))
  *     u  = beta * (v - S khat);  S <- S + u khat^T;  o = S qtil
- * The library evaluates this in 64-token chunks in the WY form.
+ * The library evaluates this in 64-token chunks in the WY form.  Precision:
+ * with bf16 inputs the chunk products round their operands (normalised rows,
+ * the chunk-start state, the per-chunk intermediates) once to fp16 and
+ * accumulate in fp32, the state staying fp32 (max-relative error ~1e-3 against
+ * exact arithmetic); values, states and outputs must then stay within fp16
+ * range (|x| < 65504).  fp32 inputs take fp32 products throughout (~1e-6).
  *   in_dtype         dtype of q, k, v
  *   out_dtype        dtype of out
  *   q, k             [T][Hk][dk] with row stride qk_stride (elements per token)
