@@ -119,9 +119,9 @@ def rotated(tensors, n_sets):
 # HBM bytes per launch measured with the FETCH_SIZE / WRITE_SIZE counters, scaled by a known-size
 # copy (profiles/hbm_traffic_pmc.txt); valid for the kernels as they stand when it was taken.
 DECODE_TRAFFIC_BYTES = 213.9e6 + 206.1e6          # both launches of a step
-PREFILL_S4096_TRAFFIC_BYTES = 366.1e6 + 278.1e6    # gdn_prefill, all its kernels
-VARLEN_TRAFFIC_BYTES = 2855.3e6 + 1758.2e6
-KDA_TRAFFIC_BYTES = 2430.5e6 + 1287.7e6
+PREFILL_S4096_TRAFFIC_BYTES = 366.1e6 + 278.0e6    # gdn_prefill, all its kernels
+VARLEN_TRAFFIC_BYTES = 2843.8e6 + 1758.4e6
+KDA_TRAFFIC_BYTES = 2430.6e6 + 1287.7e6
 
 
 def roofline(bytes_alg, ms, traffic=None):
