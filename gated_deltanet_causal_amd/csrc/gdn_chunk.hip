@@ -470,7 +470,10 @@ __device__ __forceinline__ f32x4_t mma3(typename Ops<F32>::F ah, typename Ops<F3
 //          Where some channel of the tile decays by more than kDiagLim over
 //          those 8 tokens (|g| > ~10 per token sustained), the tile is
 //          instead summed element by element with e^{gam_r - gam_j} <= 1.
-// The operands are formed in registers from raw K / Q and gam, split hi/lo.
+// The operands are formed in registers from raw K / Q and gam: for bf16 inputs
+// single fp16 fragments left of the diagonal (every factor e^{<= 0}) and hi/lo
+// bf16 pairs on the diagonal (factors up to e^{kDiagLim}, beyond fp16 range);
+// fp32 fragments on the fp32 path.
 // bf16 inputs: the kernel also writes what the register-resident spine
 // multiplies, each rounded once to fp16 (every factor e^{<= 0}):
 //   Kt[t] = khat_t e^{gam_t},  Qt[t] = qtil_t e^{gam_t},  Kb[t] = khat_t e^{gam_L - gam_t}
